@@ -1,0 +1,150 @@
+/*
+ * stg_oracle.h -- plain, single-threaded CPU oracle for bounds-checked tile
+ * movement and the bounded-edge GEMM that consumes the tiles.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, includes
+ * or calls this code; only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark load it.  It shares no source with the HIP
+ * path: its own header, its own types, its own conversions.
+ *
+ * Every function is a direct transcription of the definition it cites, with
+ * no blocking, fusion or reordering.  Coordinates are int64; element data is
+ * moved as raw bytes (memcpy of the element size) and never passes through a
+ * floating-point register, so NaN payloads and -0.0 survive.  The GEMM sums
+ * in fp64, where each bf16 product is exact.
+ *
+ * All indices are 0-based (the Warp, Tylo and Mojo pages are 0-based; the
+ * cuTile.jl pages are 1-based and are read with 1 subtracted).
+ *
+ * Pins: every function here is checked by CPU tests against values the pages
+ * print, closed forms, special cases that reduce to a library routine, and
+ * brute force on tiny inputs written in a second, independent formulation.
+ */
+#ifndef STG_ORACLE_H
+#define STG_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A strided array of rank 1..4; strides and shape are in elements. */
+typedef struct {
+  void* data;
+  int32_t esize; /* bytes per element: 1, 2, 4 or 8 */
+  int32_t rank;
+  int64_t shape[4];
+  int64_t stride[4];
+} orc_array;
+
+/* Element types known to the padding conversion. */
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F16 = 2, ORC_I32 = 3, ORC_U8 = 4, ORC_F64 = 5, ORC_I64 = 6 };
+
+/* Number of tile origins origin, origin+tile, ... that start before
+ * `extent` (cuTile.jl Memory, "Tile windows": host-side count is a ceiling
+ * division; Tylo.jl Boundary tiles, "Accumulator stores and GEMM": ceiling
+ * division for the output grid and K loop).  0 when origin >= extent. */
+int64_t orc_tile_grid(int64_t extent, int64_t origin, int64_t tile);
+
+/* Round a double to the binary interchange format with `ebits` exponent bits
+ * and `mbits` stored mantissa bits, to nearest with ties to even; returns the
+ * bit pattern (sign bit at position ebits+mbits).  Overflow gives infinity,
+ * NaN gives the canonical quiet NaN of that sign. */
+uint64_t orc_round_to_format(double v, int ebits, int mbits);
+
+/* Convert the padding value to the element type `dtype` and write its bits
+ * to `out` (element-size bytes).  Integer types take the value truncated
+ * toward zero.  Returns 0, or -1 when the value is not representable. */
+int orc_padding_bits(double v, int dtype, void* out);
+
+/* Indexed tile gather (Warp tile_load_indexed page, description and
+ * parameters).  Tiles are stacked along `axis`: tile t uses
+ * indices[t*T .. t*T+T) with T = tile_shape[axis].  For out element with
+ * coordinate o (o[axis] = t*T + c[axis]):
+ *   s[d]    = offset[d] + o[d]                      for d != axis
+ *   s[axis] = offset[axis] + indices[o[axis]]
+ *   out[o]  = all s[d] in [0, a.shape[d]) ? a[s] : 0 bits.
+ * out has shape tile_shape with out.shape[axis] = n_indices. */
+void orc_tile_gather(const orc_array* a, const int32_t* indices, int64_t n_indices,
+                     const int64_t* tile_shape, const int64_t* offset, int32_t axis,
+                     orc_array* out);
+
+/* Masked gather (cuTile.jl Memory, the gather call with mask and
+ * padding_value).  Like orc_tile_gather, except an element is filled with
+ * the padding bits `pad` when mask[o[axis]] == 0 or any coordinate is out
+ * of range; one mask byte per index. */
+void orc_tile_gather_masked(const orc_array* a, const int32_t* indices, const uint8_t* mask,
+                            int64_t n_indices, const int64_t* tile_shape, const int64_t* offset,
+                            int32_t axis, const void* pad, orc_array* out);
+
+/* Masked scatter (cuTile.jl Memory, the scatter call with mask; "Sparse
+ * views": stores clip, conflicting stores are undefined).  For every tile
+ * element o with mask[o[axis]] != 0 and all s[d] in range: a[s] = tile[o].
+ * Nothing else is written.  Duplicate active destinations are undefined by
+ * the pages; this oracle applies them in index order (last writer wins). */
+void orc_tile_scatter_masked(orc_array* a, const int32_t* indices, const uint8_t* mask,
+                             int64_t n_indices, const int64_t* tile_shape, const int64_t* offset,
+                             int32_t axis, const orc_array* tile);
+
+/* Boundary-tile copy with zero fill (Tylo.jl Boundary tiles, opening
+ * section and "A concrete edge"; cuTile.jl Memory, "Bounds checking").
+ * src is rank 2 (M, N) with arbitrary strides.  For grid tile (gr, gc),
+ * origin (R, C) = (origin_row + gr*TM, origin_col + gc*TN):
+ *   out[gr][gc][i][j] = (0 <= R+i < M and 0 <= C+j < N) ? src[R+i][C+j] : 0 bits
+ * out is dense (G_r, G_c, TM, TN) row-major, G = orc_tile_grid(...). */
+void orc_tile_copy_bounded(const orc_array* src, int64_t tm, int64_t tn, int64_t origin_row,
+                           int64_t origin_col, void* tiles_out);
+
+/* Clipped tile store (Tylo.jl Boundary tiles, "Accumulator stores and
+ * GEMM": invalid coordinates are suppressed and padding is left unchanged;
+ * cuTile.jl Memory, "Bounds checking": stores clip).  Same grid as the copy;
+ * only valid (i, j) write dst[R+i][C+j] = tiles[gr][gc][i][j]. */
+void orc_tile_store_clipped(const void* tiles_in, int32_t esize, int64_t tm, int64_t tn,
+                            int64_t origin_row, int64_t origin_col, orc_array* dst);
+
+/* Ragged schedule: the tiles that cover a packed varlen batch.  Sequence s
+ * of length L_s starts at row cu[s] = L_0 + ... + L_{s-1}; for u in
+ * [0, ceil(L_s/bm_seq)) and m in [0, middle_dim), in lexicographic order
+ * (s, u, m):  (ragged_idx, dynamic_dim, middle_idx) =
+ *   (cu[s] + u*bm_seq, min(bm_seq, L_s - u*bm_seq), m).
+ * Writes the triples when the output pointers are non-NULL; returns the
+ * number of tiles. */
+int64_t orc_ragged_schedule(const int64_t* seq_lens, int64_t n_seqs, int32_t bm_seq,
+                            int32_t middle_dim, uint32_t* ragged_idx, uint32_t* dynamic_dim,
+                            uint32_t* middle_idx);
+
+/* Ragged varlen 3-D tile load (Mojo RaggedTMA3DTile page: description,
+ * parameters BM/BN/middle_dim/group, comptime BM_seq, and the copy
+ * arguments ragged_idx/dynamic_dim/middle_idx).  X is contiguous
+ * (total_rows, middle_dim*group, depth).  With BM_seq = BM/group, for tile
+ * k, s < BM_seq, g < group, c < BN:
+ *   out[k][s*group + g][c] = (s < dyn and ri+s < total_rows and col0+c < depth)
+ *                            ? X[ri+s][mi*group + g][col0+c] : 0 bits
+ * out is dense (n_tiles, BM, BN). */
+void orc_ragged_tile_load(const void* X, int32_t esize, int64_t total_rows, int32_t middle_dim,
+                          int32_t group, int32_t depth, int32_t BM, int32_t BN, int32_t col0,
+                          const uint32_t* ragged_idx, const uint32_t* dynamic_dim,
+                          const uint32_t* middle_idx, int64_t n_tiles, void* tiles_out);
+
+/* Decode one bf16 bit pattern to double (exact: bf16 is the top half of
+ * an IEEE binary32). */
+double orc_bf16_to_f64(uint16_t h);
+
+/* Bounded GEMM reference (cuTile.jl Operations, muladd: bf16 inputs
+ * accumulate in f32 -- here in f64, where each product is exact; Tylo.jl
+ * Boundary tiles, "Accumulator stores and GEMM").  A is (M, K) bf16 with row
+ * stride lda, B is (K, N) bf16 with row stride ldb.  Writes
+ * C64[r*ldc + c] = sum_k A[r][k] * B[k][c] in double, for r < M, c < N. */
+void orc_gemm_f64(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, double* C64,
+                  int64_t ldc, int64_t M, int64_t N, int64_t K);
+
+/* Same sum for n selected output coordinates (rows[i], cols[i]). */
+void orc_gemm_sample_f64(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                         int64_t K, const int64_t* rows, const int64_t* cols, int64_t n,
+                         double* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* STG_ORACLE_H */

@@ -1,0 +1,29 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+@pytest.fixture(scope="session")
+def orc():
+    import oracle
+
+    oracle._load()
+    return oracle
+
+
+@pytest.fixture(scope="session")
+def stg():
+    """The product binding; the HIP library must already be built in-tree."""
+    import scatter_tile_gather_amd as stg
+
+    stg.load_library()
+    return stg
