@@ -1,0 +1,208 @@
+/*
+ * stg.h -- C ABI of libstg, bounds-checked tile movement between global memory
+ * and tiles on AMD Instinct MI355X (gfx950), plus the bounded-edge GEMM that
+ * consumes such tiles.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Indices and coordinates are 0-based (as on the Warp, Tylo.jl and Mojo
+ *   pages; the cuTile.jl pages count from 1).  Strides are in elements.
+ * - Every data pointer (tensor data, indices, masks, tile buffers, ragged
+ *   triples) is a DEVICE pointer on the current HIP device.  Small parameter
+ *   arrays (tile_shape, offset, sequence lengths) are HOST pointers.
+ * - The caller owns every buffer.  The library never allocates, frees or
+ *   synchronises: work is enqueued on `stream` (a hipStream_t passed as
+ *   void*, NULL = the default stream) and the caller synchronises, just as the
+ *   caller of an asynchronous tile copy synchronises producers and consumers
+ *   (Tylo.jl Boundary tiles, "Copy completion and buffer reuse").
+ * - Return value: STG_OK (0) on success, otherwise an stg_status code; the
+ *   message of the last failure on the calling thread is stg_last_error().
+ *   Nothing is enqueued when an argument check fails.  No C++ exception
+ *   crosses this boundary.
+ * - Out-of-range indices and coordinates are DEFINED behaviour: loads read
+ *   zero (or the padding value), stores skip the element.  They never form an
+ *   address outside the logical extent.  Undefined, and not checked: two
+ *   active scatter lanes with the same destination, and output storage that
+ *   overlaps an input or itself.
+ * - Data movement copies element bits; no floating-point arithmetic touches
+ *   them, so NaN payloads and -0.0 are preserved bit-exactly.
+ */
+#ifndef STG_H
+#define STG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  STG_F32 = 0,
+  STG_BF16 = 1,
+  STG_F16 = 2,
+  STG_I32 = 3,
+  STG_U8 = 4,
+  STG_F64 = 5,
+  STG_I64 = 6
+} stg_dtype;
+
+typedef enum {
+  STG_OK = 0,
+  STG_ERR_INVALID = 1,     /* null pointer, negative size, length mismatch, bad rank/axis ... */
+  STG_ERR_UNSUPPORTED = 2, /* dtype or layout the entry point does not handle */
+  STG_ERR_RANGE = 3,       /* a size or byte range exceeds what the kernels address */
+  STG_ERR_LAUNCH = 4       /* the HIP launch itself failed */
+} stg_status;
+
+/* A strided device array: the logical extent `shape` of a (possibly larger)
+ * allocation.  rank is 1..4; entries past rank are ignored.  Strides are in
+ * elements and must be >= 0. */
+typedef struct {
+  void* data;
+  int32_t dtype; /* stg_dtype */
+  int32_t rank;
+  int64_t shape[4];
+  int64_t stride[4];
+} stg_tensor;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int stg_version(void);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* stg_last_error(void);
+
+/* Number of tiles of size `tile` whose origins origin, origin+tile, ... start
+ * before `extent`: ceil((extent - origin) / tile), or 0 when origin >= extent
+ * (cuTile.jl Memory, "Tile windows": the host-side window count is a ceiling
+ * division; Tylo.jl Boundary tiles, "Accumulator stores and GEMM": ceiling
+ * division for the output grid and the K loop).  Returns -1 if tile <= 0. */
+int64_t stg_tile_grid(int64_t extent, int64_t origin, int64_t tile);
+
+/* Indexed tile gather along one axis (Warp, warp.tile_load_indexed:
+ * description, parameters `indices`, `shape`, `offset`, `axis`).
+ *
+ * Tiles of shape tile_shape[0..rank) are stacked along `axis` in `out`: tile t
+ * uses indices[t*T .. t*T+T), T = tile_shape[axis], so n_indices must be a
+ * multiple of T and out->shape must equal tile_shape except
+ * out->shape[axis] == n_indices.  For every out coordinate o:
+ *   s[d]    = offset[d] + o[d]                  (d != axis)
+ *   s[axis] = offset[axis] + indices[o[axis]]
+ *   out[o]  = (0 <= s[d] < a->shape[d] for all d) ? a[s] : 0
+ * so -1 works as a padding sentinel.  Every coordinate is checked against
+ * both bounds before an address is formed.
+ *   a, out      rank 1..4, same dtype; out must not overlap a.
+ *   indices     device int32[n_indices].
+ *   tile_shape  host int64[rank], entries >= 1.
+ *   offset      host int64[rank] (may be NULL = all zero); any sign.
+ * Each workgroup stages its slice of the index tile in LDS (the page keeps the
+ * index tile in shared memory). */
+int tile_gather(const stg_tensor* a, const int32_t* indices, int64_t n_indices,
+                const int64_t* tile_shape, const int64_t* offset, int32_t axis,
+                const stg_tensor* out, void* stream);
+
+/* Masked gather with a padding value (cuTile.jl Memory: gather with a
+ * per-element mask and padding_value for masked-out elements).
+ * As tile_gather, except out[o] = padding when mask[o[axis]] == 0 or any
+ * coordinate is out of range; one mask byte per index (nonzero = true), so a
+ * mask entry applies to the whole slice gathered by that index.  mask may be
+ * NULL (all true).  padding_value is converted to the element type by rounding
+ * to nearest even (floats; infinities on overflow) or by truncation toward zero
+ * (integers; STG_ERR_INVALID if not representable). */
+int tile_gather_masked(const stg_tensor* a, const int32_t* indices, const uint8_t* mask,
+                       int64_t n_indices, const int64_t* tile_shape, const int64_t* offset,
+                       int32_t axis, double padding_value, const stg_tensor* out,
+                       void* stream);
+
+/* Masked scatter (cuTile.jl Memory: scatter writes only where the mask is
+ * true; "Sparse views": partially out-of-bounds stores clip and conflicting
+ * stores are undefined).  The inverse of tile_gather_masked: for every
+ * coordinate o of `tile` (shape as `out` of the gather) with
+ * mask[o[axis]] != 0 and s fully in range, a[s] = tile[o].  Nothing else in
+ * `a` is written.  Two active elements with the same destination: undefined.
+ * Active rows of each workgroup are compacted with wavefront ballots before
+ * the copy, so inactive rows cost neither reads nor writes. */
+int tile_scatter_masked(const stg_tensor* a, const int32_t* indices, const uint8_t* mask,
+                        int64_t n_indices, const int64_t* tile_shape, const int64_t* offset,
+                        int32_t axis, const stg_tensor* tile, void* stream);
+
+/* Boundary-tile copy with zero fill (Tylo.jl Boundary tiles: opening section,
+ * "A concrete edge"; cuTile.jl Memory, "Bounds checking": loads pad).
+ * src is rank 2, logical (M, N), any strides (leading stride need not be
+ * aligned).  The tiles of a grid based at (origin_row, origin_col) -- either may
+ * be negative -- with step equal to the tile shape, G_r = stg_tile_grid(M,
+ * origin_row, tile_rows) by G_c = stg_tile_grid(N, origin_col, tile_cols),
+ * are written densely to tiles_out, row-major (G_r, G_c, tile_rows, tile_cols):
+ *   tiles_out[gr][gc][i][j] = (0 <= R+i < M and 0 <= C+j < N) ? src[R+i][C+j] : 0
+ * with (R, C) = (origin_row + gr*tile_rows, origin_col + gc*tile_cols).
+ * tiles_out is a device buffer of G_r*G_c*tile_rows*tile_cols elements of
+ * src's dtype, not overlapping src. */
+int tile_copy_bounded(const stg_tensor* src, int64_t tile_rows, int64_t tile_cols,
+                      int64_t origin_row, int64_t origin_col, void* tiles_out, void* stream);
+
+/* Clipped tile store (Tylo.jl Boundary tiles, "Accumulator stores and GEMM":
+ * invalid coordinates are suppressed and padding outside the logical extent
+ * is left unchanged; cuTile.jl Memory, "Bounds checking": stores clip).
+ * The inverse of tile_copy_bounded over the same grid: for valid (i, j) only,
+ * dst[R+i][C+j] = tiles_in[gr][gc][i][j].  Elements outside the logical
+ * extent of dst (for example the columns between N and the row stride) are
+ * never written. */
+int tile_store_clipped(const void* tiles_in, int64_t tile_rows, int64_t tile_cols,
+                       int64_t origin_row, int64_t origin_col, const stg_tensor* dst,
+                       void* stream);
+
+/* Host helper: the tiles that cover a packed varlen batch for ragged_tile_load.
+ * Sequence s (length seq_lens[s] >= 0) starts at row cu[s] = sum of the earlier
+ * lengths; for u in [0, ceil(L_s/bm_seq)) and m in [0, middle_dim), in that
+ * nesting order, one tile (ragged_idx, dynamic_dim, middle_idx) =
+ * (cu[s] + u*bm_seq, min(bm_seq, L_s - u*bm_seq), m).
+ * All pointers are HOST pointers; the three outputs may be NULL to only count.
+ * *n_tiles receives the count.  STG_ERR_RANGE if a row index exceeds 2^32-1. */
+int ragged_tile_schedule(const int64_t* seq_lens, int64_t n_seqs, int32_t bm_seq,
+                         int32_t middle_dim, uint32_t* ragged_idx, uint32_t* dynamic_dim,
+                         uint32_t* middle_idx, int64_t* n_tiles);
+
+/* Ragged varlen 3-D tile load (Mojo, layout.tma_async.RaggedTMA3DTile:
+ * description, parameters BM, BN, middle_dim, group, comptime BM_seq, and the
+ * per-copy arguments ragged_idx, dynamic_dim, middle_idx).
+ * src is contiguous (total_rows, middle_dim*group, depth) of `dtype`; with
+ * group > 1 it is the 4-D view (rows, middle_dim, group, depth).  The page's
+ * merged selector coordinate (ragged_idx + dynamic_dim)*middle_dim + middle_idx
+ * addresses, relative to a descriptor based BM_seq rows in front of the data,
+ * exactly the rows ragged_idx .. ragged_idx+dynamic_dim-1 of head middle_idx;
+ * this entry point reads those rows directly, so nothing needs to be
+ * allocated in front of src.  With BM_seq = BM / group, for tile k,
+ * s < BM_seq, g < group, c < BN:
+ *   tiles_out[k][s*group + g][c] =
+ *       (s < dynamic_dim[k] and ragged_idx[k]+s < total_rows and col0+c < depth)
+ *       ? src[ragged_idx[k]+s][middle_idx[k]*group + g][col0+c] : 0
+ * Host-checked requirements (else STG_ERR_INVALID): group >= 1, BM % group == 0,
+ * BN >= 1, 0 <= col0 < depth, middle_dim >= 1.  The triples live on the device
+ * and are not checked on the host; instead the kernel guards them: a
+ * dynamic_dim above BM_seq simply makes every row valid, and a middle_idx >=
+ * middle_dim yields an all-zero tile without reading src.  Rows that fail the
+ * predicate are written as zero and never read.  The three triple arrays are
+ * device uint32[n_tiles]; tiles_out is a device buffer (n_tiles, BM, BN). */
+int ragged_tile_load(const void* src, int32_t dtype, int64_t total_rows, int32_t middle_dim,
+                     int32_t group, int32_t depth, int32_t BM, int32_t BN, int32_t col0,
+                     const uint32_t* ragged_idx, const uint32_t* dynamic_dim,
+                     const uint32_t* middle_idx, int64_t n_tiles, void* tiles_out,
+                     void* stream);
+
+/* Bounded-edge GEMM C = A . B (cuTile.jl Operations, muladd: bf16 operands
+ * accumulate in f32; Tylo.jl Boundary tiles, "Accumulator stores and GEMM":
+ * ceiling-division output grid and K loop, zero-filled edge stages, and an
+ * epilogue that converts the f32 accumulator to the destination type and
+ * suppresses invalid coordinates).
+ *   A  bf16 (M, K) row-major, row stride lda >= K (any alignment).
+ *   B  bf16 (K, N) row-major, row stride ldb >= N (any alignment).
+ *   C  (M, N) row-major, row stride ldc >= N, c_dtype STG_BF16 (f32 rounded to
+ *      nearest even) or STG_F32.  Only C[r][c] with r < M, c < N is written.
+ * M, N, K >= 0; K == 0 writes zeros.  Summation order is unspecified (results
+ * match an exact reference to accumulation rounding). */
+int gemm_bounded(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                 int64_t M, int64_t N, int64_t K, int32_t c_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* STG_H */

@@ -26,9 +26,17 @@ DTYPE_CODES = {"f32": 0, "bf16": 1, "f16": 2, "i32": 3, "u8": 4, "f64": 5, "i64"
 DTYPE_SIZES = {"f32": 4, "bf16": 2, "f16": 2, "i32": 4, "u8": 1, "f64": 8, "i64": 8}
 
 
+def _stale() -> bool:
+    if not os.path.exists(_LIB_PATH):
+        return True
+    built = os.path.getmtime(_LIB_PATH)
+    return any(os.path.getmtime(os.path.join(_HERE, f)) > built for f in ("stg_oracle.c", "stg_oracle.h"))
+
+
 def build(force: bool = True) -> str:
-    """Compile the oracle with gcc into ``oracle/libstg_oracle.so``."""
-    if force or not os.path.exists(_LIB_PATH):
+    """Compile the oracle with gcc into ``oracle/libstg_oracle.so`` (when
+    forced, or when the library is missing or older than its source)."""
+    if force or _stale():
         tmp = _LIB_PATH + ".tmp"
         subprocess.check_call(
             ["gcc", "-O2", "-std=c11", "-shared", "-fPIC", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
@@ -57,8 +65,7 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
-        build(force=False)
+    build(force=False)
     lib = ctypes.CDLL(_LIB_PATH)
     sig = {
         "orc_tile_grid": (_I64, [_I64, _I64, _I64]),

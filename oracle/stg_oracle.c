@@ -263,7 +263,7 @@ void orc_ragged_tile_load(const void* X, int32_t esize, int64_t total_rows, int3
         for (int32_t c = 0; c < BN; ++c) {
           char* dst = out + ((k * BM + (int64_t)s * group + g) * BN + c) * (int64_t)esize;
           const int64_t row = ri + s, head = mi * group + g, col = (int64_t)col0 + c;
-          if (s < dyn && row < total_rows && col < depth)
+          if (s < dyn && row < total_rows && col < depth && mi < middle_dim)
             memcpy(dst, x + ((row * heads + head) * depth + col) * (int64_t)esize, (size_t)esize);
           else
             memset(dst, 0, (size_t)esize);

@@ -119,7 +119,8 @@ int64_t orc_ragged_schedule(const int64_t* seq_lens, int64_t n_seqs, int32_t bm_
  * arguments ragged_idx/dynamic_dim/middle_idx).  X is contiguous
  * (total_rows, middle_dim*group, depth).  With BM_seq = BM/group, for tile
  * k, s < BM_seq, g < group, c < BN:
- *   out[k][s*group + g][c] = (s < dyn and ri+s < total_rows and col0+c < depth)
+ *   out[k][s*group + g][c] = (s < dyn and ri+s < total_rows and col0+c < depth
+ *                             and mi < middle_dim)
  *                            ? X[ri+s][mi*group + g][col0+c] : 0 bits
  * out is dense (n_tiles, BM, BN). */
 void orc_ragged_tile_load(const void* X, int32_t esize, int64_t total_rows, int32_t middle_dim,

@@ -1,2 +1,23 @@
-"""Bounds-checked tile movement for MI355X (gfx950)."""
+"""Bounds-checked tile movement for AMD Instinct MI355X (gfx950).
+
+The compute path is the HIP library libstg.so (C ABI in include/stg.h); this
+package is its ctypes binding (same function names) plus the seeded synthetic
+input generators used by the tests and the benchmark.
+"""
 from . import inputs  # noqa: F401
+from ._binding import (  # noqa: F401
+    LIB_PATH,
+    StgError,
+    exported_names,
+    gemm_bounded,
+    load_library,
+    ragged_tile_load,
+    ragged_tile_schedule,
+    stg_tile_grid,
+    stg_version,
+    tile_copy_bounded,
+    tile_gather,
+    tile_gather_masked,
+    tile_scatter_masked,
+    tile_store_clipped,
+)

@@ -1,0 +1,296 @@
+"""ctypes binding of libstg.so: argument marshalling only.
+
+Each function here has the name of the C entry point it calls.  Tensors are
+torch tensors on the GPU (PyTorch supplies device memory and the stream);
+nothing is computed in Python and there is no fallback: if the HIP library is
+missing or a tensor is not on the GPU the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libstg.so")
+
+STG_F32, STG_BF16, STG_F16, STG_I32, STG_U8, STG_F64, STG_I64 = range(7)
+
+
+class StgError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[stg status {code}] {message}")
+        self.code = code
+
+
+class StgTensor(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("rank", ctypes.c_int32),
+        ("shape", ctypes.c_int64 * 4),
+        ("stride", ctypes.c_int64 * 4),
+    ]
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_TP = ctypes.POINTER(StgTensor)
+_I64P = ctypes.POINTER(ctypes.c_int64)
+
+_SIGNATURES = {
+    "stg_version": (ctypes.c_int, []),
+    "stg_last_error": (ctypes.c_char_p, []),
+    "stg_tile_grid": (_I64, [_I64, _I64, _I64]),
+    "tile_gather": (ctypes.c_int, [_TP, _P, _I64, _I64P, _I64P, _I32, _TP, _P]),
+    "tile_gather_masked": (ctypes.c_int, [_TP, _P, _P, _I64, _I64P, _I64P, _I32, ctypes.c_double, _TP, _P]),
+    "tile_scatter_masked": (ctypes.c_int, [_TP, _P, _P, _I64, _I64P, _I64P, _I32, _TP, _P]),
+    "tile_copy_bounded": (ctypes.c_int, [_TP, _I64, _I64, _I64, _I64, _P, _P]),
+    "tile_store_clipped": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _TP, _P]),
+    "ragged_tile_schedule": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _I64P]),
+    "ragged_tile_load": (ctypes.c_int, [_P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _P, _P]),
+    "gemm_bounded": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _I32, _P]),
+}
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the in-tree libstg.so (built by scatter_tile_gather_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libstg.so is not built ({LIB_PATH}); run scatter_tile_gather_amd.build.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def exported_names():
+    return list(_SIGNATURES)
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    table = {
+        torch.float32: STG_F32,
+        torch.bfloat16: STG_BF16,
+        torch.float16: STG_F16,
+        torch.int32: STG_I32,
+        torch.uint8: STG_U8,
+        torch.float64: STG_F64,
+        torch.int64: STG_I64,
+    }
+    if t.dtype not in table:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return table[t.dtype]
+
+
+def _on_gpu(t, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+
+
+def _desc(t, name: str) -> StgTensor:
+    _on_gpu(t, name)
+    if t.dim() < 1 or t.dim() > 4:
+        raise ValueError(f"{name}: rank must be 1..4")
+    d = StgTensor()
+    d.data = t.data_ptr()
+    d.dtype = _dtype_code(t)
+    d.rank = t.dim()
+    for i in range(4):
+        d.shape[i] = t.shape[i] if i < t.dim() else 1
+        d.stride[i] = t.stride(i) if i < t.dim() else 0
+    return d
+
+
+def _i64arr(vals):
+    arr = (ctypes.c_int64 * 4)()
+    for i, v in enumerate(vals):
+        arr[i] = int(v)
+    return arr
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise StgError(rc, load_library().stg_last_error().decode())
+
+
+def _dev_array(x, dtype, name: str):
+    _on_gpu(x, name)
+    if x.dtype != dtype or not x.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor")
+    return x.data_ptr()
+
+
+# ---- entry points -----------------------------------------------------------
+
+def stg_version() -> int:
+    return int(load_library().stg_version())
+
+
+def stg_tile_grid(extent: int, origin: int, tile: int) -> int:
+    return int(load_library().stg_tile_grid(extent, origin, tile))
+
+
+def _gather_out_shape(tile_shape, n, axis):
+    shape = list(tile_shape)
+    shape[axis] = n
+    return shape
+
+
+def tile_gather(a, indices, tile_shape, offset=None, axis: int = 0, out=None, stream=None):
+    torch = _torch()
+    lib = load_library()
+    n = indices.numel()
+    if out is None:
+        out = torch.empty(_gather_out_shape(tile_shape, n, axis), dtype=a.dtype, device=a.device)
+    ad, od = _desc(a, "a"), _desc(out, "out")
+    _check(lib.tile_gather(ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"), n, _i64arr(tile_shape),
+                           None if offset is None else _i64arr(offset), axis, ctypes.byref(od), _stream(stream)))
+    return out
+
+
+def tile_gather_masked(a, indices, mask, tile_shape, offset=None, axis: int = 0, padding_value: float = 0.0,
+                       out=None, stream=None):
+    torch = _torch()
+    lib = load_library()
+    n = indices.numel()
+    if out is None:
+        out = torch.empty(_gather_out_shape(tile_shape, n, axis), dtype=a.dtype, device=a.device)
+    ad, od = _desc(a, "a"), _desc(out, "out")
+    mp = None if mask is None else _dev_array(mask, torch.uint8, "mask")
+    _check(lib.tile_gather_masked(ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"), mp, n,
+                                  _i64arr(tile_shape), None if offset is None else _i64arr(offset), axis,
+                                  float(padding_value), ctypes.byref(od), _stream(stream)))
+    return out
+
+
+def tile_scatter_masked(a, indices, mask, tile_shape, tile, offset=None, axis: int = 0, stream=None):
+    torch = _torch()
+    lib = load_library()
+    n = indices.numel()
+    ad, td = _desc(a, "a"), _desc(tile, "tile")
+    mp = None if mask is None else _dev_array(mask, torch.uint8, "mask")
+    _check(lib.tile_scatter_masked(ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"), mp, n,
+                                   _i64arr(tile_shape), None if offset is None else _i64arr(offset), axis,
+                                   ctypes.byref(td), _stream(stream)))
+    return a
+
+
+def tile_copy_bounded(src, tile_rows: int, tile_cols: int, origin_row: int = 0, origin_col: int = 0, out=None,
+                      stream=None):
+    torch = _torch()
+    lib = load_library()
+    if src.dim() != 2:
+        raise ValueError("src must be 2-D")
+    gr = stg_tile_grid(src.shape[0], origin_row, tile_rows)
+    gc = stg_tile_grid(src.shape[1], origin_col, tile_cols)
+    if out is None:
+        out = torch.empty((max(gr, 0), max(gc, 0), tile_rows, tile_cols), dtype=src.dtype, device=src.device)
+    _on_gpu(out, "out")
+    if out.dtype != src.dtype or not out.is_contiguous() or out.numel() < max(gr, 0) * max(gc, 0) * tile_rows * tile_cols:
+        raise ValueError("out must be a contiguous tile buffer of the source dtype and grid size")
+    sd = _desc(src, "src")
+    _check(lib.tile_copy_bounded(ctypes.byref(sd), tile_rows, tile_cols, origin_row, origin_col, out.data_ptr(),
+                                 _stream(stream)))
+    return out
+
+
+def tile_store_clipped(tiles, origin_row: int, origin_col: int, dst, stream=None):
+    lib = load_library()
+    _on_gpu(tiles, "tiles")
+    if tiles.dim() != 4 or not tiles.is_contiguous() or tiles.dtype != dst.dtype:
+        raise ValueError("tiles must be a contiguous (G_r, G_c, tile_rows, tile_cols) buffer of dst's dtype")
+    tr, tc = tiles.shape[2], tiles.shape[3]
+    if (tiles.shape[0], tiles.shape[1]) != (stg_tile_grid(dst.shape[0], origin_row, tr),
+                                            stg_tile_grid(dst.shape[1], origin_col, tc)):
+        raise ValueError("tile buffer grid does not match dst and origin")
+    dd = _desc(dst, "dst")
+    _check(lib.tile_store_clipped(tiles.data_ptr(), tr, tc, origin_row, origin_col, ctypes.byref(dd),
+                                  _stream(stream)))
+    return dst
+
+
+def ragged_tile_schedule(seq_lens, bm_seq: int, middle_dim: int):
+    """Host helper: (ragged_idx, dynamic_dim, middle_idx) uint32 numpy arrays."""
+    lib = load_library()
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int64)
+    n = ctypes.c_int64(0)
+    lp = lens.ctypes.data if lens.size else None
+    _check(lib.ragged_tile_schedule(lp, lens.size, bm_seq, middle_dim, None, None, None, ctypes.byref(n)))
+    ri = np.zeros(n.value, dtype=np.uint32)
+    dyn = np.zeros(n.value, dtype=np.uint32)
+    mi = np.zeros(n.value, dtype=np.uint32)
+    if n.value:
+        _check(lib.ragged_tile_schedule(lp, lens.size, bm_seq, middle_dim, ri.ctypes.data, dyn.ctypes.data,
+                                        mi.ctypes.data, ctypes.byref(n)))
+    return ri, dyn, mi
+
+
+def ragged_tile_load(src, middle_dim: int, group: int, BM: int, BN: int, ragged_idx, dynamic_dim, middle_idx,
+                     col0: int = 0, out=None, stream=None):
+    """src: contiguous (total_rows, middle_dim*group, depth); triples: device int32/uint32-valued tensors."""
+    torch = _torch()
+    lib = load_library()
+    _on_gpu(src, "src")
+    if src.dim() != 3 or not src.is_contiguous() or src.shape[1] != middle_dim * group:
+        raise ValueError("src must be contiguous (total_rows, middle_dim*group, depth)")
+    n = ragged_idx.numel()
+    if dynamic_dim.numel() != n or middle_idx.numel() != n:
+        raise ValueError("ragged triples must have equal lengths")
+    if out is None:
+        out = torch.empty((n, BM, BN), dtype=src.dtype, device=src.device)
+    for t, nm in ((ragged_idx, "ragged_idx"), (dynamic_dim, "dynamic_dim"), (middle_idx, "middle_idx")):
+        _on_gpu(t, nm)
+        if t.dtype not in (torch.int32, torch.uint32) or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous 32-bit integer tensor")
+    _on_gpu(out, "out")
+    _check(lib.ragged_tile_load(src.data_ptr(), _dtype_code(src), src.shape[0], middle_dim, group, src.shape[2], BM,
+                                BN, col0, ragged_idx.data_ptr(), dynamic_dim.data_ptr(), middle_idx.data_ptr(), n,
+                                out.data_ptr(), _stream(stream)))
+    return out
+
+
+def gemm_bounded(A, B, out=None, out_dtype=None, stream=None):
+    """C = A @ B for bf16 A (M, K) and B (K, N) views with unit column stride."""
+    torch = _torch()
+    lib = load_library()
+    _on_gpu(A, "A")
+    _on_gpu(B, "B")
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16 or A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-D bf16 tensors")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    if (A.stride(1) != 1 and K > 1) or (B.stride(1) != 1 and N > 1):
+        raise ValueError("A and B need unit column stride")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=A.device)
+    _on_gpu(out, "out")
+    if out.dim() != 2 or tuple(out.shape) != (M, N) or (out.stride(1) != 1 and N > 1):
+        raise ValueError("out must be (M, N) with unit column stride")
+    code = _dtype_code(out)
+    _check(lib.gemm_bounded(A.data_ptr(), A.stride(0), B.data_ptr(), B.stride(0), out.data_ptr(), out.stride(0), M,
+                            N, K, code, _stream(stream)))
+    return out

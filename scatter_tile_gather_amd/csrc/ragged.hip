@@ -1,0 +1,164 @@
+// Ragged varlen 3-D tile load.
+//
+// Semantics (Mojo, layout.tma_async.RaggedTMA3DTile: description, parameters
+// BM / BN / middle_dim / group, comptime BM_seq, and the per-copy arguments
+// ragged_idx / dynamic_dim / middle_idx): sequences are packed row after row
+// with no padding; a tile of BM = BM_seq * group rows covers BM_seq consecutive
+// sequence positions starting at ragged_idx for head middle_idx (group heads
+// fused per position when group > 1), and only dynamic_dim of those positions
+// belong to the sequence -- the rest of the tile is zero.
+//
+// The page reaches this with a TMA descriptor whose outermost coordinate folds
+// the (rows, middle_dim) selectors into one, (ragged_idx + dynamic_dim) *
+// middle_dim + middle_idx, from a base pointer BM_seq rows in front of the data
+// so that the box's out-of-range rows are the ones past the sequence.  gfx950
+// has no TMA; the equivalent here is a buffer resource rebased at the tile's
+// first row with num_records ending at the last row of the array: every 16-byte
+// vector of an invalid position is given an offset past num_records and loads
+// zeros, so no storage in front of the pointer is needed.
+//
+// One workgroup per tile; a wavefront moves 64 x 16 bytes per instruction.
+// With group > 1 the `group` heads of one position are adjacent in memory, so
+// each position is a single contiguous run of group * depth elements.
+#include "stg_internal.h"
+
+namespace stg {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;
+
+struct RaggedParams {
+  const char* src;
+  char* out;
+  const uint32_t* ragged_idx;
+  const uint32_t* dynamic_dim;
+  const uint32_t* middle_idx;
+  int64_t total_rows;
+  int64_t row_b;   // bytes per packed row: middle_dim * group * depth * esize
+  int64_t head_b;  // bytes per head: depth * esize
+  int64_t tile_b;  // bytes per output tile: BM * BN * esize
+  int32_t middle_dim, group, bm_seq;
+  int32_t col0_b;     // col0 * esize
+  int32_t out_row_b;  // BN * esize
+  int32_t valid_b;    // bytes of an output row backed by source columns
+  int32_t cpr;        // 16-byte chunks per output row
+  uint32_t cpr_magic, group_magic;
+  int32_t items;      // BM * cpr
+};
+
+template <int ESIZE>
+__global__ __launch_bounds__(kThreads) void ragged_load_kernel(RaggedParams p) {
+  constexpr int V = 16 / ESIZE;
+  const int64_t k = blockIdx.x;
+  const int64_t ri = p.ragged_idx[k];
+  const int64_t mi = p.middle_idx[k];
+  int64_t dyn = p.dynamic_dim[k];
+  // positions that exist: below dynamic_dim, inside the array, valid head
+  if (ri + dyn > p.total_rows) dyn = p.total_rows > ri ? p.total_rows - ri : 0;
+  if (mi >= p.middle_dim) dyn = 0;
+  const int64_t base_row = ri < p.total_rows ? ri : 0;
+  const char* base = p.src + base_row * p.row_b + mi * p.group * p.head_b + p.col0_b;
+  int64_t avail = (p.total_rows - base_row) * p.row_b - mi * p.group * p.head_b - p.col0_b;
+  if (dyn <= 0 || avail < 0) avail = 0;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, (uint32_t)(avail < (int64_t)kOOB ? avail : (int64_t)kOOB - 1));
+  char* out = p.out + k * p.tile_b;
+  for (int b0 = 0; b0 < p.items; b0 += kThreads * kUnroll) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int it = b0 + u * kThreads + threadIdx.x;
+      v[u] = (u32x4){0, 0, 0, 0};
+      if (it < p.items) {
+        const int j = (int)div_small((uint32_t)it, p.cpr_magic);  // tile row = s * group + g
+        const int b = (it - j * p.cpr) * 16;
+        const int s = (int)div_small((uint32_t)j, p.group_magic);
+        const int g = j - s * p.group;
+        const bool row_ok = s < dyn;
+        const uint32_t roff = (uint32_t)(s * p.row_b + g * p.head_b);
+        const bool full = row_ok && b + 16 <= p.valid_b;
+        v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, full ? roff + b : kOOB, 0, 0);
+        if (row_ok && !full && b < p.valid_b) {
+#pragma unroll
+          for (int e = 0; e < V; ++e)
+            if (b + e * ESIZE < p.valid_b) vec_set<ESIZE>(v[u], e, load_elem<ESIZE>(base + roff + b + e * ESIZE));
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int it = b0 + u * kThreads + threadIdx.x;
+      if (it < p.items) {
+        const int j = (int)div_small((uint32_t)it, p.cpr_magic);
+        const int b = (it - j * p.cpr) * 16;
+        char* d = out + (int64_t)j * p.out_row_b + b;
+        if (b + 16 <= p.out_row_b) {
+          st16(d, v[u]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < V; ++e)
+            if (b + e * ESIZE < p.out_row_b) store_elem<ESIZE>(d + e * ESIZE, vec_get<ESIZE>(v[u], e));
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+}  // namespace stg
+
+using namespace stg;
+
+extern "C" int ragged_tile_load(const void* src, int32_t dtype, int64_t total_rows, int32_t middle_dim,
+                                int32_t group, int32_t depth, int32_t BM, int32_t BN, int32_t col0,
+                                const uint32_t* ragged_idx, const uint32_t* dynamic_dim,
+                                const uint32_t* middle_idx, int64_t n_tiles, void* tiles_out, void* stream) {
+  clear_error();
+  const char* name = "ragged_tile_load";
+  const int es = dtype_size(dtype);
+  if (!es) return fail(STG_ERR_UNSUPPORTED, "%s: unknown dtype %d", name, dtype);
+  if (total_rows < 0 || n_tiles < 0) return fail(STG_ERR_INVALID, "%s: negative size", name);
+  if (middle_dim < 1 || group < 1 || depth < 1 || BM < 1 || BN < 1)
+    return fail(STG_ERR_INVALID, "%s: middle_dim, group, depth, BM and BN must be >= 1", name);
+  if (BM % group) return fail(STG_ERR_INVALID, "%s: BM %d is not a multiple of group %d", name, BM, group);
+  if (col0 < 0 || col0 >= depth) return fail(STG_ERR_INVALID, "%s: col0 %d not in [0, depth)", name, col0);
+  if (n_tiles == 0) return STG_OK;
+  if (!tiles_out || !ragged_idx || !dynamic_dim || !middle_idx)
+    return fail(STG_ERR_INVALID, "%s: null tile buffer or tile triples", name);
+  if (total_rows > 0 && !src) return fail(STG_ERR_INVALID, "%s: null src", name);
+  RaggedParams p{};
+  p.src = (const char*)src;
+  p.out = (char*)tiles_out;
+  p.ragged_idx = ragged_idx;
+  p.dynamic_dim = dynamic_dim;
+  p.middle_idx = middle_idx;
+  p.total_rows = total_rows;
+  p.head_b = (int64_t)depth * es;
+  p.row_b = (int64_t)middle_dim * group * p.head_b;
+  p.middle_dim = middle_dim;
+  p.group = group;
+  p.bm_seq = BM / group;
+  p.col0_b = col0 * es;
+  p.out_row_b = BN * es;
+  p.tile_b = (int64_t)BM * BN * es;
+  const int64_t valid_cols = depth - col0 < BN ? depth - col0 : BN;
+  p.valid_b = (int32_t)(valid_cols * es);
+  p.cpr = (p.out_row_b + 15) / 16;
+  if ((int64_t)BM * p.cpr > 65535 || p.cpr >= 32768 || group >= 32768)
+    return fail(STG_ERR_RANGE, "%s: tile of %d x %d elements is too large", name, BM, BN);
+  if ((int64_t)p.bm_seq * p.row_b + p.out_row_b >= kMaxOffset32)
+    return fail(STG_ERR_RANGE, "%s: BM_seq rows span more than 2^31 bytes", name);
+  if (n_tiles > INT32_MAX) return fail(STG_ERR_RANGE, "%s: too many tiles", name);
+  p.items = BM * p.cpr;
+  p.cpr_magic = div_magic((uint32_t)p.cpr);
+  p.group_magic = div_magic((uint32_t)group);
+  const hipStream_t s = as_stream(stream);
+  const dim3 grid((unsigned)n_tiles), block(kThreads);
+  switch (es) {
+    case 1: hipLaunchKernelGGL(ragged_load_kernel<1>, grid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL(ragged_load_kernel<2>, grid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL(ragged_load_kernel<4>, grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL(ragged_load_kernel<8>, grid, block, 0, s, p); break;
+  }
+  return check_launch(name);
+}

@@ -10,6 +10,14 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    # build only what is missing; a present library is used as it is
+    from scatter_tile_gather_amd import build as stg_build
+
+    if not os.path.exists(stg_build.LIB):
+        stg_build.build()
+    import oracle
+
+    oracle.build(force=False)
 
 
 @pytest.fixture(scope="session")
@@ -22,7 +30,7 @@ def orc():
 
 @pytest.fixture(scope="session")
 def stg():
-    """The product binding; the HIP library must already be built in-tree."""
+    """The product binding over the in-tree HIP library."""
     import scatter_tile_gather_amd as stg
 
     stg.load_library()

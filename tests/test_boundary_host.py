@@ -1,0 +1,169 @@
+"""CPU checks of the C-ABI library: it loads, exports every entry point that
+include/stg.h declares, and its host-only logic (grid sizing, ragged
+schedule, argument validation) behaves as documented.  No kernel is launched:
+every call here either is host-only or fails validation before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import scatter_tile_gather_amd as stg_pkg
+from scatter_tile_gather_amd._binding import StgTensor
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "stg.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\**\s+\**([A-Za-z_]\w*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol(stg):
+    lib = stg.load_library()
+    names = header_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(stg_pkg.exported_names()) == names
+    assert stg.stg_version() >= 100
+    assert lib.stg_last_error() is not None
+
+
+def test_tile_grid_matches_oracle(stg, orc):
+    for extent in range(0, 50):
+        for origin in range(-20, 52, 3):
+            for t in (1, 2, 7, 16, 64):
+                assert stg.stg_tile_grid(extent, origin, t) == orc.tile_grid(extent, origin, t)
+    assert stg.stg_tile_grid(10, 0, 0) == -1
+    assert stg.stg_tile_grid(8191, -16, 64) == 129
+    assert stg.stg_tile_grid(4097, 0, 32) == 129
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_ragged_schedule_matches_oracle(stg, orc, seed):
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, 300, rng.integers(1, 20))
+    for bm_seq, md in [(128, 8), (32, 2), (7, 3), (1, 1)]:
+        got = stg.ragged_tile_schedule(lens, bm_seq, md)
+        want = orc.ragged_schedule(lens, bm_seq, md)
+        for g, w in zip(got, want):
+            np.testing.assert_array_equal(g, w)
+
+
+def test_ragged_schedule_workload_count(stg):
+    lens = stg_pkg.inputs.ragged()["seq_lens"]
+    for bm_seq, md in [(128, 8), (32, 2)]:
+        ri, dyn, mi = stg.ragged_tile_schedule(lens, bm_seq, md)
+        assert len(ri) == md * int(sum(-(-int(L) // bm_seq) for L in lens))
+        assert int(dyn.sum()) == md * int(lens.sum())
+
+
+def _t(shape, dtype=0, data=0x1000, stride=None):
+    d = StgTensor()
+    d.data = data
+    d.dtype = dtype
+    d.rank = len(shape)
+    st = stride or [int(np.prod(shape[i + 1:])) for i in range(len(shape))]
+    for i in range(4):
+        d.shape[i] = shape[i] if i < len(shape) else 1
+        d.stride[i] = st[i] if i < len(shape) else 0
+    return d
+
+
+def _i64(vals):
+    a = (ctypes.c_int64 * 4)()
+    for i, v in enumerate(vals):
+        a[i] = v
+    return a
+
+
+def test_gather_argument_errors(stg):
+    lib = stg.load_library()
+    a, out = _t([16, 8]), _t([8, 8])
+    ts = _i64([4, 8])
+    B = ctypes.byref
+    assert lib.tile_gather(None, 0x10, 8, ts, None, 0, B(out), None) == 1
+    assert b"null tensor" in lib.stg_last_error()
+    assert lib.tile_gather(B(a), None, 8, ts, None, 0, B(out), None) == 1
+    assert lib.tile_gather(B(a), 0x10, 7, ts, None, 0, B(out), None) == 1  # not a multiple of 4
+    assert b"multiple" in lib.stg_last_error()
+    assert lib.tile_gather(B(a), 0x10, 8, ts, None, 2, B(out), None) == 1  # axis out of range
+    assert lib.tile_gather(B(a), 0x10, 12, ts, None, 0, B(out), None) == 1  # out shape mismatch
+    assert lib.tile_gather(B(a), 0x10, 8, _i64([0, 8]), None, 0, B(out), None) == 1  # empty tile dim
+    assert lib.tile_gather(B(_t([16, 8], dtype=9)), 0x10, 8, ts, None, 0, B(out), None) == 2  # dtype
+    assert lib.tile_gather(B(_t([16, 8], dtype=1)), 0x10, 8, ts, None, 0, B(out), None) == 1  # dtype mismatch
+    bad = _t([16, 8])
+    bad.rank = 5
+    assert lib.tile_gather(B(bad), 0x10, 8, ts, None, 0, B(out), None) == 1
+    assert lib.tile_gather(B(_t([16, 8], data=0)), 0x10, 8, ts, None, 0, B(out), None) == 1  # null data
+    neg = _t([16, 8], stride=[-8, 1])
+    assert lib.tile_gather(B(neg), 0x10, 8, ts, None, 0, B(out), None) == 1
+    assert lib.tile_gather(B(a), 0x10, 8, ts, _i64([1 << 50, 0]), 0, B(out), None) == 3  # offset range
+    # padding value not representable in the element type
+    ai, oi = _t([16, 8], dtype=4), _t([8, 8], dtype=4)
+    assert lib.tile_gather_masked(B(ai), 0x10, None, 8, ts, None, 0, 300.0, B(oi), None) == 1
+    assert b"padding" in lib.stg_last_error()
+    assert lib.tile_scatter_masked(B(a), 0x10, None, 8, ts, None, 0, None, None) == 1
+
+
+def test_copy_argument_errors(stg):
+    lib = stg.load_library()
+    B = ctypes.byref
+    assert lib.tile_copy_bounded(B(_t([4, 4, 4])), 2, 2, 0, 0, 0x10, None) == 1  # rank 3
+    assert lib.tile_copy_bounded(B(_t([8, 8])), 0, 2, 0, 0, 0x10, None) == 1
+    assert lib.tile_copy_bounded(B(_t([8, 8])), 2, 2, 0, 0, None, None) == 1  # null tile buffer
+    assert lib.tile_copy_bounded(B(_t([8, 8])), 2, 2, -(1 << 41), 0, 0x10, None) == 3
+    assert lib.tile_store_clipped(None, 2, 2, 0, 0, B(_t([8, 8])), None) == 1
+    assert lib.tile_store_clipped(0x10, 2, 2, 0, 0, None, None) == 1
+    # grids that are empty are a successful no-op without touching the GPU
+    assert lib.tile_copy_bounded(B(_t([8, 8])), 2, 2, 8, 0, None, None) == 0
+
+
+def test_ragged_argument_errors(stg):
+    lib = stg.load_library()
+    args = dict(src=0x10, dtype=1, total_rows=100, middle_dim=8, group=1, depth=128, BM=128, BN=128, col0=0,
+                ri=0x10, dyn=0x10, mi=0x10, n=4, out=0x10)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.ragged_tile_load(a["src"], a["dtype"], a["total_rows"], a["middle_dim"], a["group"], a["depth"],
+                                    a["BM"], a["BN"], a["col0"], a["ri"], a["dyn"], a["mi"], a["n"], a["out"], None)
+
+    assert call(group=3) == 1  # BM % group
+    assert b"multiple of group" in lib.stg_last_error()
+    assert call(col0=128) == 1
+    assert call(col0=-1) == 1
+    assert call(dtype=11) == 2
+    assert call(ri=None) == 1
+    assert call(out=None) == 1
+    assert call(middle_dim=0) == 1
+    assert call(n=0, out=None) == 0  # nothing to do
+    n = ctypes.c_int64()
+    assert lib.ragged_tile_schedule(None, 3, 4, 1, None, None, None, ctypes.byref(n)) == 1
+    lens = np.array([3, -1], dtype=np.int64)
+    assert lib.ragged_tile_schedule(lens.ctypes.data, 2, 4, 1, None, None, None, ctypes.byref(n)) == 1
+    big = np.array([1 << 33, 5], dtype=np.int64)
+    assert lib.ragged_tile_schedule(big.ctypes.data, 2, 1 << 30, 1, None, None, None, ctypes.byref(n)) == 3
+
+
+def test_gemm_argument_errors(stg):
+    lib = stg.load_library()
+    # bad output dtype, strides below the row length, negative sizes
+    assert lib.gemm_bounded(0x10, 8, 0x10, 8, 0x10, 8, 8, 8, 8, 3, None) in (1, 2)
+    assert lib.gemm_bounded(0x10, 4, 0x10, 8, 0x10, 8, 8, 8, 8, 1, None) in (1, 2)
+    assert lib.gemm_bounded(0x10, 8, 0x10, 8, 0x10, 8, -1, 8, 8, 1, None) in (1, 2)
+    assert lib.gemm_bounded(None, 8, 0x10, 8, 0x10, 8, 8, 8, 8, 1, None) in (1, 2)
+
+
+def test_binding_rejects_host_tensors(stg):
+    import torch
+
+    a = torch.zeros(4, 4)
+    idx = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        stg.tile_gather(a, idx, (4, 4))

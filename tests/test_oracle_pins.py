@@ -485,6 +485,10 @@ def test_ragged_rows_past_total_are_zero(orc):
     out = orc.ragged_tile_load(X, 2, 1, 4, 4, 0, [1], [4], [1])
     np.testing.assert_array_equal(out[0, :2], X[1:3, 1])
     np.testing.assert_array_equal(out[0, 2:], 0)
+    # a head index past middle_dim selects nothing: the tile is all zero
+    out = orc.ragged_tile_load(X, 2, 1, 4, 4, 0, [0], [3], [2])
+    np.testing.assert_array_equal(out, 0)
+    np.testing.assert_array_equal(np_ragged(X, 2, 1, 4, 4, 0, [0], [3], [2]), 0)
 
 
 # ---------------------------------------------------------------------------
