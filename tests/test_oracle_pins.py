@@ -423,7 +423,7 @@ def np_ragged(X, middle_dim, group, BM, BN, col0, ri, dyn, mi):
     for k in range(len(ri)):
         block = X[ri[k]:ri[k] + dyn[k], mi[k] * group:(mi[k] + 1) * group, col0:col0 + BN]
         pad = np.zeros((bm_seq, group, BN), dtype=X.dtype)
-        pad[:block.shape[0], :, :block.shape[2]] = block
+        pad[:block.shape[0], :block.shape[1], :block.shape[2]] = block
         out[k] = pad.reshape(BM, BN)
     return out
 
