@@ -1,0 +1,378 @@
+#!/usr/bin/env python3
+"""Benchmark of the bounded tile-movement path on one MI355X.
+
+A step is one pass over the bounded 2-D tile copy workload: bf16 matrix of
+logical shape (8191, 4097) with row stride 4103, swept by (64, 32) tiles over
+the ceil-div grids based at (0, 0) and (-16, -16); each sweep zero-fills a
+dense tile buffer (tile_copy_bounded) and clip-stores it back into a second
+matrix of the same layout (tile_store_clipped).  `value` is effective HBM GB/s
+over algorithmic bytes (valid elements read, every tile slot written by the
+copy; valid elements read and written by the store).
+
+The same run also measures the other workloads of the path (row gather,
+masked gather, masked scatter, ragged varlen load at group 1 and 4, bounded
+GEMM) and reports them under "ops"; the CPU oracle is timed on the host on the
+headline step ("cpu_baseline").  Inputs are synthetic and seeded, resident in
+HBM before timing starts.
+
+One GPU only: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only", default="all",
+                    help="comma list of: copy,gather,masked,ragged,gemm (rocprof runs); 'all' for the full report")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU time budget of the oracle baseline")
+    return ap.parse_args()
+
+
+def _dev(x, bf16=False):
+    import torch
+
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    return torch.from_numpy(x).to("cuda:0")
+
+
+class EventTimer:
+    """Per-kernel durations from HIP events recorded on the launch stream."""
+
+    def __init__(self, names):
+        import torch
+
+        self.torch = torch
+        self.names = names
+        self.acc = {n: 0.0 for n in names}
+        self.count = {n: 0 for n in names}
+        self.pending = []
+
+    def run(self, fns):
+        torch = self.torch
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+        evs[0].record()
+        for i, (name, fn) in enumerate(fns):
+            fn()
+            evs[i + 1].record()
+        self.pending.append(([n for n, _ in fns], evs))
+
+    def collect(self):
+        for names, evs in self.pending:
+            for i, n in enumerate(names):
+                self.acc[n] += evs[i].elapsed_time(evs[i + 1])
+                self.count[n] += 1
+        self.pending = []
+        return {n: self.acc[n] / max(self.count[n], 1) for n in self.names}
+
+
+def source_hash(*files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_file, profile_name, per_launch_algo):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", profile_name)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"traffic_record:\s*(\{.*\})", text)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_hash") != source_hash(*kernel_file):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+
+def copy_workload(stg, inputs):
+    import torch
+
+    w = inputs.bounded_copy()
+    M, N, ld = w["M"], w["N"], w["ld"]
+    tm, tn = w["tile"]
+    src = _dev(w["src"])[:, :N]
+    dsts = [_dev(w["dst"])[:, :N] for _ in w["origins"]]
+    bufs = []
+    for (r0, c0) in w["origins"]:
+        gr, gc = stg.stg_tile_grid(M, r0, tm), stg.stg_tile_grid(N, c0, tn)
+        bufs.append(torch.empty((gr, gc, tm, tn), dtype=torch.bfloat16, device="cuda:0"))
+    valid = M * N * 2
+    kernels = []
+    algo = {}
+    for k, (r0, c0) in enumerate(w["origins"]):
+        cn, sn = f"tile_copy_bounded@{r0},{c0}", f"tile_store_clipped@{r0},{c0}"
+        kernels.append((cn, (lambda b=bufs[k], r0=r0, c0=c0: stg.tile_copy_bounded(src, tm, tn, r0, c0, out=b))))
+        kernels.append((sn, (lambda b=bufs[k], d=dsts[k], r0=r0, c0=c0: stg.tile_store_clipped(b, r0, c0, d))))
+        algo[cn] = valid + bufs[k].numel() * 2
+        algo[sn] = 2 * valid
+    return w, kernels, algo
+
+
+def run_copy(stg, inputs, steps, warmup):
+    import torch
+
+    w, kernels, algo = copy_workload(stg, inputs)
+    names = [n for n, _ in kernels]
+    for _ in range(warmup):
+        for _, fn in kernels:
+            fn()
+    torch.cuda.synchronize()
+    timer = EventTimer(names)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        timer.run(kernels)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = timer.collect()
+    step_ms = sum(per.values())
+    step_bytes = sum(algo.values())
+    return {"w": w, "per_kernel_ms": per, "algo": algo, "step_ms": step_ms, "wall_ms": wall * 1e3 / steps,
+            "step_bytes": step_bytes}
+
+
+def time_fn(fn, iters, warmup):
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def gbs(nbytes, ms):
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def op_entry(workload, nbytes, ms):
+    v = gbs(nbytes, ms)
+    return {"workload": workload, "value": round(v, 1), "unit": "GB/s", "ms": round(ms, 5),
+            "algorithmic_bytes": int(nbytes), "frac_of_hbm_peak": round(v / HBM_PEAK_GBS, 4)}
+
+
+def run_gather(stg, inputs, steps, warmup):
+    w = inputs.row_gather()
+    a, idx = _dev(w["a"]), _dev(w["indices"])
+    import torch
+
+    out = torch.empty((idx.numel(), w["a"].shape[1]), dtype=torch.float32, device="cuda:0")
+    fn = lambda: stg.tile_gather(a, idx, w["tile_shape"], w["offset"], w["axis"], out=out)
+    ms = time_fn(fn, steps, warmup)
+    n_valid = int(((w["indices"] >= 0) & (w["indices"] < w["a"].shape[0])).sum())
+    row_b = w["a"].shape[1] * 4
+    nbytes = idx.numel() * 4 + n_valid * row_b + idx.numel() * row_b
+    return op_entry("row gather fp32 (1024,256), 4096 int32 indices in [-64,1087], (64,256) tiles", nbytes, ms)
+
+
+def run_masked(stg, inputs, steps, warmup):
+    import torch
+
+    w = inputs.masked()
+    table, idx, gm = _dev(w["table"]), _dev(w["indices"]), _dev(w["gmask"])
+    rows, cols = w["table"].shape
+    out = torch.empty((idx.numel(), cols), dtype=torch.float32, device="cuda:0")
+    fn = lambda: stg.tile_gather_masked(table, idx, gm, (64, cols), None, 0, w["padding_value"], out=out)
+    ms_g = time_fn(fn, steps, warmup)
+    n_true = int(w["gmask"].sum())
+    row_b = cols * 4
+    g_bytes = idx.numel() * 5 + n_true * row_b + idx.numel() * row_b
+    del out
+    vals, perm, sm = _dev(w["vals"]), _dev(w["perm"]), _dev(w["smask"])
+    dst = table.clone()
+    fn = lambda: stg.tile_scatter_masked(dst, perm, sm, (64, cols), vals, None, 0)
+    ms_s = time_fn(fn, steps, warmup)  # rewrites the same rows each call: same traffic
+    s_true = int(w["smask"].sum())
+    s_bytes = perm.numel() * 5 + 2 * s_true * row_b
+    return (op_entry("masked gather fp32 table (1048576,128), 4194304 indices, Bernoulli(0.9) mask, pad -1.0",
+                     g_bytes, ms_g),
+            op_entry("masked scatter fp32 (1048576,128) rows to a permutation, Bernoulli(0.5) mask", s_bytes, ms_s))
+
+
+def run_ragged(stg, inputs, steps, warmup):
+    import torch
+
+    w = inputs.ragged()
+    X = _dev(w["X"])
+    res = []
+    for group in (1, 4):
+        md = w["heads"] // group
+        ri, dyn, mi = stg.ragged_tile_schedule(w["seq_lens"], 128 // group, md)
+        tri = [torch.from_numpy(x.astype(np.int32)).to("cuda:0") for x in (ri, dyn, mi)]
+        out = torch.empty((len(ri), 128, 128), dtype=torch.bfloat16, device="cuda:0")
+        fn = lambda: stg.ragged_tile_load(X, md, group, 128, 128, *tri, out=out)
+        ms = time_fn(fn, steps, warmup)
+        nbytes = w["X"].nbytes + out.numel() * 2 + len(ri) * 12
+        res.append(op_entry(f"ragged varlen load bf16 ({w['X'].shape[0]},8,128), 64 seqs, BM=128, group={group}",
+                            nbytes, ms))
+        del out
+    return res
+
+
+def run_gemm(stg, inputs, steps, warmup):
+    import torch
+
+    M, N, K = 8191, 8193, 4097
+    g = inputs.gemm(M, N, K)
+    A, B = _dev(g["A"]), _dev(g["B"])
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    fn = lambda: stg.gemm_bounded(A, B, out=C)
+    try:
+        fn()
+    except Exception as e:  # reported, not hidden
+        return {"workload": "bounded GEMM bf16 (8191,8193,4097)", "error": str(e)}
+    ms = time_fn(fn, steps, warmup)
+    flop = 2.0 * M * N * K
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"workload": "bounded GEMM bf16 A(8191,4097) B(4097,8193), fp32 accumulate, bf16 clipped output",
+            "value": round(tf, 1), "unit": "TFLOP/s", "ms": round(ms, 4), "flop": flop,
+            "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+
+
+def cpu_baseline(inputs, budget_s):
+    """The oracle, single-threaded on one host core, on the headline step."""
+    import oracle
+
+    w = inputs.bounded_copy()
+    M, N = w["M"], w["N"]
+    tm, tn = w["tile"]
+    src = w["src"][:, :N]
+    dst = w["dst"].copy()
+    step_bytes = 0
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        for (r0, c0) in w["origins"]:
+            tiles = oracle.tile_copy_bounded(src, tm, tn, r0, c0)
+            oracle.tile_store_clipped(tiles, r0, c0, dst[:, :N])
+            if steps == 0:
+                step_bytes += M * N * 2 + tiles.nbytes + 2 * M * N * 2
+        steps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(step_bytes * steps / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} full headline steps (copy + clipped store at both grid bases), "
+                      f"{dt:.1f} s on one host core"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); nothing run.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import scatter_tile_gather_amd as stg
+    from scatter_tile_gather_amd import inputs
+
+    stg.load_library()
+    only = set(args.only.split(",")) if args.only != "all" else {"copy", "gather", "masked", "ragged", "gemm"}
+    ops = {}
+    head = None
+    if "copy" in only:
+        head = run_copy(stg, inputs, args.steps, args.warmup)
+        print(f"[bench] copy step {head['step_ms']:.4f} ms", file=sys.stderr, flush=True)
+    if "gather" in only:
+        ops["row_gather"] = run_gather(stg, inputs, args.steps, args.warmup)
+        print("[bench] row gather done", file=sys.stderr, flush=True)
+    if "masked" in only:
+        ops["masked_gather"], ops["masked_scatter"] = run_masked(stg, inputs, args.steps, args.warmup)
+        print("[bench] masked gather/scatter done", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+    if "ragged" in only:
+        ops["ragged_group1"], ops["ragged_group4"] = run_ragged(stg, inputs, args.steps, args.warmup)
+        print("[bench] ragged done", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+    if "gemm" in only:
+        ops["gemm_bounded"] = run_gemm(stg, inputs, max(args.steps // 2, 1), args.warmup)
+        print("[bench] gemm done", file=sys.stderr, flush=True)
+    if head is None:
+        print(json.dumps({"ops": ops}))
+        return
+    per = head["per_kernel_ms"]
+    dom = max(per, key=lambda n: per[n])
+    achieved = gbs(head["algo"][dom], per[dom])
+    kernel_files = {"tile_copy_bounded": ("scatter_tile_gather_amd/csrc/copy.hip",),
+                    "tile_store_clipped": ("scatter_tile_gather_amd/csrc/copy.hip",)}
+    base = dom.split("@")[0]
+    traffic = traffic_from_profile(kernel_files[base], f"{base}.bounded_copy_workload.md", head["algo"][dom])
+    value = gbs(head["step_bytes"], head["step_ms"])
+    line = {
+        "metric": "effective HBM GB/s (gather/copy/scatter, % of peak); bounded GEMM TFLOP/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "bounded 2-D tile copy + clipped store: bf16 (8191,4097) row stride 4103, (64,32) tiles, "
+                        "ceil-div grids based at (0,0) and (-16,-16)",
+            "tiles_per_step": 16512 + 16641,
+            "algorithmic_bytes_per_step": int(head["step_bytes"]),
+            "step_wall_ms": round(head["wall_ms"], 5),
+            "per_kernel_ms": {k: round(v, 5) for k, v in per.items()},
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dom,
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(head["algo"][dom]),
+        },
+        "ops": ops,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inputs, args.cpu_seconds)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
