@@ -1,0 +1,133 @@
+"""GPU parity of gemm_bounded against the fp64 CPU oracle.
+
+Tolerance (derived from the arithmetic; the bound 1e-2 is the one the target
+states for outputs ~N(0,1)): with fp32 output, |C - C64| <= 1e-2 everywhere --
+fp32 accumulation of K <= 4097 bf16 products of size ~1/sqrt(K) errs by ~1e-5.
+With bf16 output the final rounding adds up to half a bf16 ulp, which exceeds
+1e-2 once |C| >= 4 (half ulp = 2^-6 there); so |C - C64| <= 1e-2 where
+|C64| < 4 and |C - C64| <= one bf16 ulp of |C64| elsewhere.  Row-selection
+operands make the product exact, and those cases are compared bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+from scatter_tile_gather_amd import inputs
+from gpu_util import say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def bf16_ulp(x):
+    ax = np.maximum(np.abs(x), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(ax)) - 7)
+
+
+def check(C, C64, out_f32):
+    err = np.abs(C - C64)
+    if out_f32:
+        assert err.max() <= 1e-2, err.max()
+    else:
+        small = np.abs(C64) < 4
+        assert err[small].max(initial=0) <= 1e-2, err[small].max()
+        assert np.all(err[~small] <= bf16_ulp(C64[~small])), err[~small].max(initial=0)
+    return float(err.max())
+
+
+def run(stg, A, B, out_f32, ldc_pad=0, As=None, Bs=None):
+    M, K = A.shape
+    N = B.shape[1]
+    Ad = to_dev(A) if As is None else As
+    Bd = to_dev(B) if Bs is None else Bs
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    store = torch.full((M, N + ldc_pad), 7.0, dtype=dt, device="cuda:0")
+    out = store[:, :N]
+    stg.gemm_bounded(Ad, Bd, out=out)
+    torch.cuda.synchronize()
+    full = to_host(store)
+    if out_f32:
+        C = full[:, :N].astype(np.float64)
+    else:
+        C = inputs.bf16_bits_to_f32(full[:, :N]).astype(np.float64)
+    return C, full
+
+
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_gemm_correctness_shape(stg, orc, out_f32):
+    g = inputs.gemm(65, 97, 73)
+    say("gemm 65x97x73 fp32 out" if out_f32 else "gemm 65x97x73 bf16 out")
+    C, _ = run(stg, g["A"], g["B"], out_f32)
+    err = check(C, orc.gemm_f64(g["A"], g["B"]), out_f32)
+    if out_f32:
+        assert err < 1e-4
+
+
+@pytest.mark.parametrize("shape", [(65, 97, 73), (300, 520, 200), (257, 513, 129), (256, 256, 64), (1, 1, 1),
+                                   (129, 1000, 17)])
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_gemm_row_selection_exact(stg, orc, shape, out_f32):
+    M, N, K = shape
+    rng = np.random.default_rng(M * 7 + N)
+    B = inputs.f32_to_bf16_bits(rng.standard_normal((K, N)).astype(np.float32))
+    sel = rng.integers(0, K, M)
+    A = np.zeros((M, K), dtype=np.uint16)
+    A[np.arange(M), sel] = 0x3F80
+    say("gemm row selection", shape, "f32" if out_f32 else "bf16")
+    C, _ = run(stg, A, B, out_f32)
+    want = inputs.bf16_bits_to_f32(B[sel]).astype(np.float64)
+    np.testing.assert_array_equal(C, want)
+
+
+@pytest.mark.parametrize("shape", [(31, 33, 17), (256, 512, 4096), (513, 260, 70), (2, 300, 1), (64, 257, 65),
+                                   (1000, 255, 130), (257, 769, 33)])
+def test_gemm_random_shapes(stg, orc, shape):
+    M, N, K = shape
+    g = inputs.gemm(M, N, K, seed=M + N + K)
+    say("gemm random shape", shape)
+    C, _ = run(stg, g["A"], g["B"], True)
+    check(C, orc.gemm_f64(g["A"], g["B"]), True)
+
+
+def test_gemm_k_zero_writes_zeros(stg):
+    A = np.zeros((5, 0), dtype=np.uint16)
+    B = np.zeros((0, 7), dtype=np.uint16)
+    say("gemm K = 0")
+    Ad = torch.zeros((5, 1), dtype=torch.bfloat16, device="cuda:0")[:, :0]
+    Bd = torch.zeros((1, 7), dtype=torch.bfloat16, device="cuda:0")[:0]
+    C, _ = run(stg, A, B, True, As=Ad, Bs=Bd)
+    assert not C.any()
+
+
+def test_gemm_strided_operands_and_clipped_epilogue(stg, orc):
+    M, N, K = 130, 300, 95
+    g = inputs.gemm(M, N, K, seed=11)
+    As = np.full((M, K + 3), 0x7FA5, dtype=np.uint16)
+    As[:, :K] = g["A"]
+    Bs = np.full((K, N + 5), 0x7FA5, dtype=np.uint16)
+    Bs[:, :N] = g["B"]
+    say("gemm strided operands, padded output")
+    for out_f32 in (True, False):
+        C, full = run(stg, g["A"], g["B"], out_f32, ldc_pad=9, As=to_dev(As)[:, :K], Bs=to_dev(Bs)[:, :N])
+        check(C, orc.gemm_f64(g["A"], g["B"]), out_f32)
+        pad = full[:, N:]
+        if out_f32:
+            assert np.all(pad == 7.0)
+        else:
+            assert np.all(pad == 0x40E0)  # bf16 7.0: the padding is never written
+
+
+def test_gemm_large_shape_sampled(stg, orc):
+    M, N, K = 8191, 8193, 4097
+    g = inputs.gemm(M, N, K)
+    say("gemm 8191x8193x4097 bf16 out (bench configuration)")
+    Ad, Bd = to_dev(g["A"]), to_dev(g["B"])
+    C = stg.gemm_bounded(Ad, Bd)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(99)
+    rows = [np.full(N, M - 1), np.full(N, 7936), np.arange(M), np.arange(M), rng.integers(0, M, 65536)]
+    cols = [np.arange(N), np.arange(N), np.full(M, N - 1), np.full(M, 8191), rng.integers(0, N, 65536)]
+    r = np.concatenate(rows).astype(np.int64)
+    c = np.concatenate(cols).astype(np.int64)
+    got = inputs.bf16_bits_to_f32(to_host(C[torch.from_numpy(r).cuda(), torch.from_numpy(c).cuda()])).astype(np.float64)
+    want = orc.gemm_sample_f64(g["A"], g["B"], r, c)
+    check(got, want, False)
