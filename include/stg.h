@@ -10,8 +10,9 @@
  * - Every data pointer (tensor data, indices, masks, tile buffers, ragged
  *   triples) is a DEVICE pointer on the current HIP device.  Small parameter
  *   arrays (tile_shape, offset, sequence lengths) are HOST pointers.
- * - The caller owns every buffer.  The library never allocates, frees or
- *   synchronises: work is enqueued on `stream` (a hipStream_t passed as
+ * - The caller owns every buffer.  The library never allocates or frees
+ *   memory and never synchronises (kernel tracing, when switched on, keeps a
+ *   pool of HIP events): work is enqueued on `stream` (a hipStream_t passed as
  *   void*, NULL = the default stream) and the caller synchronises, just as the
  *   caller of an asynchronous tile copy synchronises producers and consumers
  *   (Tylo.jl Boundary tiles, "Copy completion and buffer reuse").
@@ -201,6 +202,22 @@ int ragged_tile_load(const void* src, int32_t dtype, int64_t total_rows, int32_t
  * match an exact reference to accumulation rounding). */
 int gemm_bounded(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
                  int64_t M, int64_t N, int64_t K, int32_t c_dtype, void* stream);
+
+/* Kernel tracing, for measurement.  While enabled (on != 0) on the calling
+ * thread, every kernel the library launches from that thread records a
+ * start/stop hipEvent pair that is part of its own dispatch
+ * (hipExtLaunchKernel), so the pair times the kernel alone, without the queue
+ * gaps between dependent launches.  Returns the previous setting.  Tracing
+ * creates events lazily and keeps them for reuse until the process ends. */
+int stg_trace_enable(int on);
+
+/* After the caller has synchronised the streams the traced kernels ran on:
+ * writes up to `cap` records, oldest first -- names[i] (a static string naming
+ * the entry point and, where it launches more than one kernel, the kernel) and
+ * ms[i] (milliseconds, -1 if that kernel had not completed) -- then clears the
+ * log (records beyond `cap` are dropped).  Returns the number written, or a
+ * negative stg_status on bad arguments. */
+int stg_trace_read(int cap, const char** names, float* ms);
 
 #ifdef __cplusplus
 }

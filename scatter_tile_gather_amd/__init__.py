@@ -14,6 +14,8 @@ from ._binding import (  # noqa: F401
     ragged_tile_load,
     ragged_tile_schedule,
     stg_tile_grid,
+    stg_trace_enable,
+    stg_trace_read,
     stg_version,
     tile_copy_bounded,
     tile_gather,

@@ -52,6 +52,8 @@ _SIGNATURES = {
     "ragged_tile_schedule": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _I64P]),
     "ragged_tile_load": (ctypes.c_int, [_P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _P, _P]),
     "gemm_bounded": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _I32, _P]),
+    "stg_trace_enable": (ctypes.c_int, [ctypes.c_int]),
+    "stg_trace_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float)]),
 }
 
 _lib = None
@@ -143,6 +145,22 @@ def _dev_array(x, dtype, name: str):
 
 
 # ---- entry points -----------------------------------------------------------
+
+def stg_trace_enable(on: bool = True) -> bool:
+    """Per-launch kernel timing on this thread; returns the previous setting."""
+    return bool(load_library().stg_trace_enable(1 if on else 0))
+
+
+def stg_trace_read(cap: int = 4096):
+    """[(kernel name, milliseconds)] recorded since the last read; synchronise first."""
+    lib = load_library()
+    names = (ctypes.c_char_p * cap)()
+    ms = (ctypes.c_float * cap)()
+    n = lib.stg_trace_read(cap, names, ms)
+    if n < 0:
+        raise StgError(-n, lib.stg_last_error().decode())
+    return [(names[i].decode(), float(ms[i])) for i in range(n)]
+
 
 def stg_version() -> int:
     return int(load_library().stg_version())

@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <vector>
+
 #include "stg_internal.h"
 
 namespace stg {
@@ -130,9 +132,68 @@ int check_tensor(const stg_tensor* t, const char* name) {
   return STG_OK;
 }
 
+// ---- kernel tracing -----------------------------------------------------
+
+namespace {
+struct TraceRecord {
+  const char* name;
+  TraceEvents ev;
+};
+// Events are recycled through `pool` and kept until the process ends (they
+// are not destroyed at thread exit, when the HIP runtime may be gone).
+struct TraceState {
+  bool on = false;
+  std::vector<TraceRecord> log;
+  std::vector<TraceEvents> pool;
+};
+thread_local TraceState g_trace;
+}  // namespace
+
+bool trace_enabled() { return g_trace.on; }
+
+TraceEvents trace_next(const char* kernel_name) {
+  TraceEvents ev;
+  if (!g_trace.pool.empty()) {
+    ev = g_trace.pool.back();
+    g_trace.pool.pop_back();
+  } else if (hipEventCreate(&ev.start) != hipSuccess || hipEventCreate(&ev.stop) != hipSuccess) {
+    if (ev.start) (void)hipEventDestroy(ev.start);
+    return TraceEvents{};  // untraced launch
+  }
+  g_trace.log.push_back({kernel_name, ev});
+  return ev;
+}
+
 }  // namespace stg
 
 using namespace stg;
+
+extern "C" int stg_trace_enable(int on) {
+  const int prev = g_trace.on ? 1 : 0;
+  g_trace.on = on != 0;
+  return prev;
+}
+
+extern "C" int stg_trace_read(int cap, const char** names, float* ms) {
+  clear_error();
+  if (cap < 0 || (cap > 0 && (!names || !ms))) return -fail(STG_ERR_INVALID, "stg_trace_read: bad output arrays");
+  int n = 0;
+  for (auto& r : g_trace.log) {
+    if (n < cap) {
+      float t = 0.f;
+      if (hipEventElapsedTime(&t, r.ev.start, r.ev.stop) != hipSuccess) {
+        (void)hipGetLastError();
+        t = -1.f;  // not complete: the caller did not synchronise
+      }
+      names[n] = r.name;
+      ms[n] = t;
+      ++n;
+    }
+    g_trace.pool.push_back(r.ev);
+  }
+  g_trace.log.clear();
+  return n;
+}
 
 extern "C" int stg_version(void) { return 100; }  // 0.1.0
 

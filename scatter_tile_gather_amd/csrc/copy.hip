@@ -238,7 +238,7 @@ int launch(const char* name, const stg_tensor* mat, int64_t tm, int64_t tn, int6
       const dim3 grid((unsigned)n_wg);
       {
 #define STG_LAUNCH_VEC(ES)                                                                         \
-  hipLaunchKernelGGL((STORE ? store_clipped_kernel<ES> : copy_bounded_kernel<ES>), grid, dim3(kThreads), 0, s, p)
+  launch_kernel(name, (STORE ? store_clipped_kernel<ES> : copy_bounded_kernel<ES>), grid, dim3(kThreads), 0, s, p)
         switch (es) {
           case 1: STG_LAUNCH_VEC(1); break;
           case 2: STG_LAUNCH_VEC(2); break;
@@ -258,7 +258,7 @@ int launch(const char* name, const stg_tensor* mat, int64_t tm, int64_t tn, int6
   p.n = G_r * G_c * tm * tn;
   const int64_t want = (p.n + kThreads - 1) / kThreads;
   const dim3 grid((unsigned)(want < 65536 ? want : 65536));
-#define STG_LAUNCH_EL(ES) hipLaunchKernelGGL((copy_elem_kernel<ES, STORE>), grid, dim3(kThreads), 0, s, p)
+#define STG_LAUNCH_EL(ES) launch_kernel(name, (copy_elem_kernel<ES, STORE>), grid, dim3(kThreads), 0, s, p)
   switch (es) {
     case 1: STG_LAUNCH_EL(1); break;
     case 2: STG_LAUNCH_EL(2); break;

@@ -259,17 +259,17 @@ int launch_rows(Op op, int esize, const RowParams& p, int64_t grid, hipStream_t 
   const dim3 g((unsigned)grid), b(kThreads);
   if (op == Op::Scatter) {
     switch (esize) {
-      case 1: hipLaunchKernelGGL(scatter_rows_kernel<1>, g, b, 0, s, p); break;
-      case 2: hipLaunchKernelGGL(scatter_rows_kernel<2>, g, b, 0, s, p); break;
-      case 4: hipLaunchKernelGGL(scatter_rows_kernel<4>, g, b, 0, s, p); break;
-      default: hipLaunchKernelGGL(scatter_rows_kernel<8>, g, b, 0, s, p); break;
+      case 1: launch_kernel(op_name(op), scatter_rows_kernel<1>, g, b, 0, s, p); break;
+      case 2: launch_kernel(op_name(op), scatter_rows_kernel<2>, g, b, 0, s, p); break;
+      case 4: launch_kernel(op_name(op), scatter_rows_kernel<4>, g, b, 0, s, p); break;
+      default: launch_kernel(op_name(op), scatter_rows_kernel<8>, g, b, 0, s, p); break;
     }
   } else {
     switch (esize) {
-      case 1: hipLaunchKernelGGL(gather_rows_kernel<1>, g, b, 0, s, p); break;
-      case 2: hipLaunchKernelGGL(gather_rows_kernel<2>, g, b, 0, s, p); break;
-      case 4: hipLaunchKernelGGL(gather_rows_kernel<4>, g, b, 0, s, p); break;
-      default: hipLaunchKernelGGL(gather_rows_kernel<8>, g, b, 0, s, p); break;
+      case 1: launch_kernel(op_name(op), gather_rows_kernel<1>, g, b, 0, s, p); break;
+      case 2: launch_kernel(op_name(op), gather_rows_kernel<2>, g, b, 0, s, p); break;
+      case 4: launch_kernel(op_name(op), gather_rows_kernel<4>, g, b, 0, s, p); break;
+      default: launch_kernel(op_name(op), gather_rows_kernel<8>, g, b, 0, s, p); break;
     }
   }
   return check_launch(op_name(op));
@@ -280,17 +280,17 @@ int launch_elems(Op op, int esize, const ElemParams& p, hipStream_t s) {
   const dim3 g((unsigned)(want < 65536 ? want : 65536)), b(kThreads);
   if (op == Op::Scatter) {
     switch (esize) {
-      case 1: hipLaunchKernelGGL(scatter_elem_kernel<1>, g, b, 0, s, p); break;
-      case 2: hipLaunchKernelGGL(scatter_elem_kernel<2>, g, b, 0, s, p); break;
-      case 4: hipLaunchKernelGGL(scatter_elem_kernel<4>, g, b, 0, s, p); break;
-      default: hipLaunchKernelGGL(scatter_elem_kernel<8>, g, b, 0, s, p); break;
+      case 1: launch_kernel(op_name(op), scatter_elem_kernel<1>, g, b, 0, s, p); break;
+      case 2: launch_kernel(op_name(op), scatter_elem_kernel<2>, g, b, 0, s, p); break;
+      case 4: launch_kernel(op_name(op), scatter_elem_kernel<4>, g, b, 0, s, p); break;
+      default: launch_kernel(op_name(op), scatter_elem_kernel<8>, g, b, 0, s, p); break;
     }
   } else {
     switch (esize) {
-      case 1: hipLaunchKernelGGL(gather_elem_kernel<1>, g, b, 0, s, p); break;
-      case 2: hipLaunchKernelGGL(gather_elem_kernel<2>, g, b, 0, s, p); break;
-      case 4: hipLaunchKernelGGL(gather_elem_kernel<4>, g, b, 0, s, p); break;
-      default: hipLaunchKernelGGL(gather_elem_kernel<8>, g, b, 0, s, p); break;
+      case 1: launch_kernel(op_name(op), gather_elem_kernel<1>, g, b, 0, s, p); break;
+      case 2: launch_kernel(op_name(op), gather_elem_kernel<2>, g, b, 0, s, p); break;
+      case 4: launch_kernel(op_name(op), gather_elem_kernel<4>, g, b, 0, s, p); break;
+      default: launch_kernel(op_name(op), gather_elem_kernel<8>, g, b, 0, s, p); break;
     }
   }
   return check_launch(op_name(op));

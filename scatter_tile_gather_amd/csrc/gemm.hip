@@ -72,6 +72,9 @@ struct Cfg {
   static constexpr int A_STAGE_B = BM * BK * 2;
   static constexpr int B_STAGE_B = BK * B_PITCH_B;
   static constexpr int STAGE_B = A_STAGE_B + B_STAGE_B;
+  static constexpr int EPI_PITCH_B = WTN * 2 + 16;  // bytes per row of a wave's bf16 output tile
+  static constexpr int EPI_WAVE_B = WTM * EPI_PITCH_B;
+  static constexpr int LDS_B = 2 * STAGE_B > WM * WN * EPI_WAVE_B ? 2 * STAGE_B : WM * WN * EPI_WAVE_B;
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold whole 32x32 MFMA blocks");
 };
 
@@ -110,7 +113,7 @@ __device__ __forceinline__ void tile_of(uint32_t t, int tiles_m, int tiles_n, in
 }
 
 template <class CF>
-__global__ __launch_bounds__(CF::NT) void gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(CF::NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -130,6 +133,7 @@ __global__ __launch_bounds__(CF::NT) void gemm_kernel(GemmParams p) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   u32x4 ra[CF::A_PER_T], rb[CF::B_PER_T];
+  bf16x8 fa[2][CF::FM], fb[2][CF::FN];
 
   auto load_stage = [&](int kt) {
     const int64_t k0 = (int64_t)kt * BK;
@@ -175,80 +179,118 @@ __global__ __launch_bounds__(CF::NT) void gemm_kernel(GemmParams p) {
       if (c < CF::B_CHUNKS) *(u32x4*)(bs + (c / (CF::BN / 8)) * CF::B_PITCH_B + (c % (CF::BN / 8)) * 16) = rb[q];
     }
   };
+  // MFMA operands of K sub-step ks (16 K values) of stage `buf` into slot s
+  auto read_frags = [&](int buf, int ks, int s) {
+    const char* as = smem + buf * CF::STAGE_B;
+    const char* bs = as + CF::A_STAGE_B;
+#pragma unroll
+    for (int i = 0; i < CF::FM; ++i) {
+      const int r = wm * CF::WTM + i * 32 + (lane & 31);
+      fa[s][i] = *(const bf16x8*)(as + a_lds(r, 2 * ks + (lane >> 5)));
+    }
+#pragma unroll
+    for (int j = 0; j < CF::FN; ++j) {
+      // transpose read: lane t of 16-lane group g points at row
+      // 16ks + 8(g/2) + 4h + t/4, columns nb + 16(g%2) + 4(t%4) .. +3
+      const int g = lane >> 4, t = lane & 15;
+      const int col = wn * CF::WTN + j * 32 + 16 * (g & 1) + 4 * (t & 3);
+      const int row = 16 * ks + 8 * (g >> 1) + (t >> 2);
+      const char* p0 = bs + row * CF::B_PITCH_B + col * 2;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * CF::B_PITCH_B));
+      const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      fb[s][j] = __builtin_bit_cast(bf16x8, both);
+    }
+  };
 
   if (nk > 0) {
     load_stage(0);
     store_stage(0);
   }
   __syncthreads();
+  if (nk > 0) read_frags(0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) load_stage(kt + 1);
-    const char* as = smem + buf * CF::STAGE_B;
-    const char* bs = as + CF::A_STAGE_B;
+    const bool more = kt + 1 < nk;
+    // next stage's global loads fly during this stage's MFMAs
+    if (more) load_stage(kt + 1);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[CF::FM], bfr[CF::FN];
-#pragma unroll
-      for (int i = 0; i < CF::FM; ++i) {
-        const int r = wm * CF::WTM + i * 32 + (lane & 31);
-        af[i] = *(const bf16x8*)(as + a_lds(r, 2 * ks + (lane >> 5)));
-      }
-#pragma unroll
-      for (int j = 0; j < CF::FN; ++j) {
-        // transpose read: lane l of 16-lane group g points at row
-        // 16ks + 8(g/2) + 4h + t/4, columns nb + 16(g%2) + 4(t%4) .. +3
-        const int g = lane >> 4, t = lane & 15;
-        const int col = wn * CF::WTN + j * 32 + 16 * (g & 1) + 4 * (t & 3);
-        const int row = 16 * ks + 8 * (g >> 1) + (t >> 2);
-        const char* p0 = bs + row * CF::B_PITCH_B + col * 2;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * CF::B_PITCH_B));
-        const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        bfr[j] = __builtin_bit_cast(bf16x8, both);
-      }
+      const int cur = ks & 1;
+      if (ks + 1 < BK / 16) read_frags(buf, ks + 1, cur ^ 1);
+      // the other stage was released by the barrier that ended the last step
+      if (ks == BK / 16 - 1 && more) store_stage(buf ^ 1);
 #pragma unroll
       for (int i = 0; i < CF::FM; ++i)
 #pragma unroll
         for (int j = 0; j < CF::FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) store_stage(buf ^ 1);
     __syncthreads();
+    if (more) read_frags(buf ^ 1, 0, 0);
   }
 
   // clipped epilogue: lane l, accumulator r of block (i, j) is
   // row 8(r/4) + 4(l/32) + r%4, column l%32 of that 32x32 block
+  if (p.c_f32) {
+#pragma unroll
+    for (int i = 0; i < CF::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < CF::FN; ++j) {
+        const int64_t col = n0 + wn * CF::WTN + j * 32 + (lane & 31);
+        if (col >= p.N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + wm * CF::WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (row < p.M) *(float*)(p.C + (row * p.ldc + col) * 4) = acc[i][j][r];
+        }
+      }
+    return;
+  }
+  // bf16: round to nearest even, stage the wave's tile in LDS (every wave has
+  // its own region; the stages are no longer read), then write whole 16-byte
+  // row chunks; only chunks crossing column N are written element by element
+  char* ep = smem + wave * CF::EPI_WAVE_B;
 #pragma unroll
   for (int i = 0; i < CF::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < CF::FN; ++j) {
-      const int64_t col = n0 + wn * CF::WTN + j * 32 + (lane & 31);
-      if (col >= p.N) continue;
+    for (int j = 0; j < CF::FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * CF::WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < p.M) {
-          if (p.c_f32)
-            *(float*)(p.C + (row * p.ldc + col) * 4) = acc[i][j][r];
-          else
-            *(__bf16*)(p.C + (row * p.ldc + col) * 2) = (__bf16)acc[i][j][r];
-        }
+        const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int col = j * 32 + (lane & 31);
+        *(__bf16*)(ep + row * CF::EPI_PITCH_B + col * 2) = (__bf16)acc[i][j][r];
       }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  constexpr int CPR = CF::WTN / 8;  // 16-byte chunks per wave-tile row
+  for (int c = lane; c < CF::WTM * CPR; c += 64) {
+    const int row = c / CPR, ch = c % CPR;
+    const int64_t grow = m0 + wm * CF::WTM + row;
+    const int64_t gcol = n0 + wn * CF::WTN + ch * 8;
+    if (grow >= p.M || gcol >= p.N) continue;
+    const u32x4 v = *(const u32x4*)(ep + row * CF::EPI_PITCH_B + ch * 16);
+    char* dst = p.C + (grow * p.ldc + gcol) * 2;
+    if (gcol + 8 <= p.N) {
+      st16(dst, v);
+    } else {
+      for (int e = 0; e < 8; ++e)
+        if (gcol + e < p.N) store_elem<2>(dst + e * 2, vec_get<2>(v, e));
     }
+  }
 }
 
-using MainCfg = Cfg<256, 256, 4, 2>;
+using MainCfg = Cfg<256, 256, 2, 2>;
 using EdgeCfg = Cfg<128, 32, 4, 1>;
 
 template <class CF>
-int launch(GemmParams p, int64_t cols, hipStream_t s) {
+int launch(const char* name, GemmParams p, int64_t cols, hipStream_t s) {
   p.tiles_m = (int32_t)((p.M + CF::BM - 1) / CF::BM);
   p.tiles_n = (int32_t)((cols + CF::BN - 1) / CF::BN);
   const int64_t n_wg = (int64_t)p.tiles_m * p.tiles_n;
   if (n_wg == 0) return STG_OK;
-  const size_t lds = 2 * CF::STAGE_B;
-  hipLaunchKernelGGL(gemm_kernel<CF>, dim3((unsigned)n_wg), dim3(CF::NT), lds, s, p);
+  const size_t lds = CF::LDS_B;
+  launch_kernel(name, gemm_kernel<CF>, dim3((unsigned)n_wg), dim3(CF::NT), lds, s, p);
   return check_launch("gemm_bounded");
 }
 
@@ -276,9 +318,9 @@ extern "C" int gemm_bounded(const void* A, int64_t lda, const void* B, int64_t l
     return fail(STG_ERR_RANGE, "%s: a stage of A or B spans more than 2^31 bytes", name);
   if (!lds_configured) {
     if (hipFuncSetAttribute((const void*)gemm_kernel<MainCfg>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            2 * MainCfg::STAGE_B) != hipSuccess ||
+                            MainCfg::LDS_B) != hipSuccess ||
         hipFuncSetAttribute((const void*)gemm_kernel<EdgeCfg>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            2 * EdgeCfg::STAGE_B) != hipSuccess)
+                            EdgeCfg::LDS_B) != hipSuccess)
       return fail(STG_ERR_LAUNCH, "%s: cannot reserve LDS: %s", name, hipGetErrorString(hipGetLastError()));
     lds_configured = true;
   }
@@ -293,8 +335,8 @@ extern "C" int gemm_bounded(const void* A, int64_t lda, const void* B, int64_t l
   const int64_t n_main = (N / MainCfg::BN) * MainCfg::BN;
   int rc;
   p.n_base = 0;
-  if (n_main > 0 && (rc = launch<MainCfg>(p, n_main, s))) return rc;
+  if (n_main > 0 && (rc = launch<MainCfg>("gemm_bounded/main", p, n_main, s))) return rc;
   p.n_base = n_main;
-  if (N > n_main && (rc = launch<EdgeCfg>(p, N - n_main, s))) return rc;
+  if (N > n_main && (rc = launch<EdgeCfg>("gemm_bounded/edge", p, N - n_main, s))) return rc;
   return STG_OK;
 }

@@ -155,10 +155,10 @@ extern "C" int ragged_tile_load(const void* src, int32_t dtype, int64_t total_ro
   const hipStream_t s = as_stream(stream);
   const dim3 grid((unsigned)n_tiles), block(kThreads);
   switch (es) {
-    case 1: hipLaunchKernelGGL(ragged_load_kernel<1>, grid, block, 0, s, p); break;
-    case 2: hipLaunchKernelGGL(ragged_load_kernel<2>, grid, block, 0, s, p); break;
-    case 4: hipLaunchKernelGGL(ragged_load_kernel<4>, grid, block, 0, s, p); break;
-    default: hipLaunchKernelGGL(ragged_load_kernel<8>, grid, block, 0, s, p); break;
+    case 1: launch_kernel(name, ragged_load_kernel<1>, grid, block, 0, s, p); break;
+    case 2: launch_kernel(name, ragged_load_kernel<2>, grid, block, 0, s, p); break;
+    case 4: launch_kernel(name, ragged_load_kernel<4>, grid, block, 0, s, p); break;
+    default: launch_kernel(name, ragged_load_kernel<8>, grid, block, 0, s, p); break;
   }
   return check_launch(name);
 }

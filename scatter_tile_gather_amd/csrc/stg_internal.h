@@ -1,6 +1,7 @@
 // Internal helpers shared by the libstg translation units (host and device).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -35,6 +36,27 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 int check_tensor(const stg_tensor* t, const char* name);
 
 constexpr int64_t kMaxOffset32 = (int64_t(1) << 31) - 1;  // voffset range used by buffer ops
+
+// Kernel tracing: while enabled on this thread, each launch carries a
+// start/stop event pair inside its own dispatch packet, so the recorded time
+// covers the kernel alone (not the queue gaps between dependent launches).
+struct TraceEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+bool trace_enabled();
+TraceEvents trace_next(const char* kernel_name);
+
+template <typename K, typename... Args>
+void launch_kernel(const char* name, K kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t s, Args... args) {
+  if (trace_enabled()) {
+    const TraceEvents ev = trace_next(name);
+    if (ev.start) {
+      hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, ev.start, ev.stop, 0, args...);
+      return;
+    }
+  }
+  hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+}
 
 // ---- device side -----------------------------------------------------------
 

@@ -167,3 +167,12 @@ def test_binding_rejects_host_tensors(stg):
     idx = torch.zeros(4, dtype=torch.int32)
     with pytest.raises(ValueError):
         stg.tile_gather(a, idx, (4, 4))
+
+
+def test_trace_host_paths(stg):
+    lib = stg.load_library()
+    prev = stg.stg_trace_enable(False)
+    assert stg.stg_trace_enable(False) is False
+    assert stg.stg_trace_read() == []  # nothing launched: an empty log
+    assert lib.stg_trace_read(3, None, None) < 0  # bad output arrays
+    stg.stg_trace_enable(prev)
