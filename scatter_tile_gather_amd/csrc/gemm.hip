@@ -7,31 +7,36 @@
 // coordinates, leaving padding untouched).
 //
 // gfx950 design:
-//  * Workgroup tile BM x BN x 64, waves WM x WN, each wave owning a
+//  * Workgroup tile BM x BN x 32, waves WM x WN, each wave owning a
 //    (BM/WM) x (BN/WN) block of v_mfma_f32_32x32x16_bf16 accumulators.  Every
 //    lane issues every MFMA; bounds only select the data that was staged.
 //  * Staging (Tylo.jl Boundary tiles, opening section and "A concrete edge",
-//    recast): each lane owns fixed 16-byte chunks of the A and B stage.  A
-//    chunk whose eight source values are all valid is one dwordx4 buffer load
-//    at its (2-byte aligned, for odd leading dimensions) offset; a chunk with
-//    no valid value gets an offset past num_records and loads zeros; only a
-//    chunk straddling the K or N edge is assembled element by element.  An
-//    address is formed only for valid coordinates.
-//  * LDS: A is row-major with K contiguous (the MFMA A operand is eight
-//    consecutive K values of one row) and the 16-byte chunk index is XOR-
-//    swizzled by the tile-local row, so the 32 rows an MFMA operand read
-//    touches spread over all banks.  The swizzle is a function of the
-//    tile-local (window) coordinate, and zero-filled chunks go through the
-//    same mapping, so the edge does not disturb the swizzle phase (Tylo.jl
-//    Boundary tiles, "A concrete edge", swizzled windows).  B stays row-major
-//    (N contiguous, rows padded by 32 bytes) and the MFMA B operand -- eight
-//    consecutive K values of one column -- is read with ds_read_b64_tr_b16,
-//    the gfx950 LDS transpose read, so no transpose pass is needed.
-//  * Two LDS stages: the global loads of stage k+1 are in flight while stage
-//    k feeds the MFMAs; one barrier per K step.
+//    recast for gfx950): the A and B stages are filled by LDS DMA
+//    (buffer_load_dwordx4 ... lds), which writes each lane's 16 bytes straight
+//    into LDS without passing through registers.  A lane whose 16-byte chunk
+//    (eight bf16 values, at any 2-byte alignment) lies fully inside the
+//    logical extent gets its offset; a chunk with no valid value gets an offset
+//    past the buffer's num_records and lands as zeros.  Only a stage that holds
+//    a chunk straddling the K or N edge is patched afterwards, element by
+//    element, by the lane that owns the chunk.  No address is formed for an
+//    invalid coordinate.
+//  * LDS layout: a DMA instruction writes 64 lanes x 16 bytes linearly, so the
+//    swizzle is realised by choosing which chunk each lane fetches.  A rows are
+//    64 bytes (K contiguous, the MFMA A operand is eight consecutive K of one
+//    row) with chunk c stored at c ^ (((row >> 2) ^ (row >> 1)) & 3); B rows are N
+//    contiguous with chunk pairs XOR-ed by the row, and the MFMA B operand
+//    (eight consecutive K of one column) is read with ds_read_b64_tr_b16, the
+//    gfx950 LDS transpose read.  Both swizzles are functions of the
+//    tile-local (window) coordinate and zero-filled chunks take the same
+//    mapping, so an edge never disturbs the swizzle phase (Tylo.jl Boundary
+//    tiles, "A concrete edge", swizzled windows).  Operand reads are
+//    bank-conflict free.
+//  * Pipeline: a ring of NSTAGE stages; the DMA for stage k+NSTAGE-1 is
+//    issued while stage k feeds the MFMAs, the first operands of stage k+1 are
+//    read before the barrier that ends step k, and each step waits only for
+//    stage k+2.  One barrier per 32 K values.
 //  * Grid: a main launch of 256 x 256 tiles over the columns that fill whole
-//    tiles, and an edge launch of 128 x 32 tiles for the remaining columns,
-//    so a one-column remainder (N = 8193) does not cost a full tile wave.
+//    tiles, and an edge launch of 64 x 32 tiles for the remaining columns.
 //    Tile ids are renumbered so that consecutive ids run on one XCD and walk
 //    4-row-panel groups, keeping A and B panels resident in that XCD's L2.
 #include "stg_internal.h"
@@ -45,7 +50,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int BK = 64;
+constexpr int BK = 32;  // K values per stage
 
 struct GemmParams {
   const char* A;  // bf16 (M, K), row stride lda elements
@@ -58,46 +63,58 @@ struct GemmParams {
   int32_t c_f32;  // 1: fp32 output, 0: bf16
 };
 
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int NS_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-  static constexpr int NT = WM * WN * 64;
+  static constexpr int NSTAGE = NS_;  // LDS ring depth; stage k+NSTAGE-1 is in flight during step k
+  static constexpr int NW = WM * WN, NT = NW * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
-  static constexpr int A_CHUNKS = BM * BK / 8;
-  static constexpr int B_CHUNKS = BK * BN / 8;
-  static constexpr int A_PER_T = (A_CHUNKS + NT - 1) / NT;
-  static constexpr int B_PER_T = (B_CHUNKS + NT - 1) / NT;
-  static constexpr int B_PITCH_B = BN * 2 + 32;  // bytes per LDS row of B
-  static constexpr int A_STAGE_B = BM * BK * 2;
-  static constexpr int B_STAGE_B = BK * B_PITCH_B;
+  static constexpr int A_STAGE_B = BM * BK * 2;  // 64-byte rows
+  static constexpr int B_STAGE_B = BK * BN * 2;
   static constexpr int STAGE_B = A_STAGE_B + B_STAGE_B;
+  static constexpr int A_DMA_W = A_STAGE_B / 1024 / NW;  // DMA instructions per wave and stage
+  static constexpr int B_DMA_W = B_STAGE_B / 1024 / NW;
+  static constexpr int DMA_W = A_DMA_W + B_DMA_W;
+  static constexpr int B_CPR = BN / 8;  // 16-byte chunks per B row
   static constexpr int EPI_PITCH_B = WTN * 2 + 16;  // bytes per row of a wave's bf16 output tile
   static constexpr int EPI_WAVE_B = WTM * EPI_PITCH_B;
-  static constexpr int LDS_B = 2 * STAGE_B > WM * WN * EPI_WAVE_B ? 2 * STAGE_B : WM * WN * EPI_WAVE_B;
+  static constexpr int LDS_B = NSTAGE * STAGE_B > NW * EPI_WAVE_B ? NSTAGE * STAGE_B : NW * EPI_WAVE_B;
+  static_assert(NSTAGE >= 3 && (NSTAGE - 3) * DMA_W <= 63, "ring depth vs vmcnt range");
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold whole 32x32 MFMA blocks");
+  static_assert(A_DMA_W * NW * 1024 == A_STAGE_B && B_DMA_W * NW * 1024 == B_STAGE_B,
+                "stages must split into whole 1 KiB DMA instructions per wave");
+  static_assert(BN == 32 || BN % 64 == 0, "B swizzle assumes 64-byte rows or multiples of 128 bytes");
 };
 
-// Byte offset of A chunk (row r, 16-byte chunk kc) inside an A stage.
-__device__ __forceinline__ int a_lds(int r, int kc) { return r * (BK * 2) + ((kc ^ (r & 7)) << 4); }
+// s_waitcnt immediate: vmcnt <= n, other counters unconstrained (gfx9 layout).
+#define STG_VMCNT(n) (((n)&0xF) | (((n) >> 4) << 14) | 0x0F70)
 
-// Load the eight bf16 values at (row, col .. col+7) of a row-major matrix
-// whose valid region is rows < rows_valid, cols < cols_valid.  `rs` is
-// based at `base` (element (row0, col0)); (r, c) are relative to it.
-__device__ __forceinline__ u32x4 load_chunk(const __amdgpu_buffer_rsrc_t rs, const char* base, int64_t ld, int r,
-                                            int c, bool row_ok, int64_t cols_left) {
-  // cols_left: valid columns from c onward (may be <= 0)
-  const bool full = row_ok && cols_left >= 8;
-  const uint32_t off = full ? (uint32_t)(r * ld * 2 + c * 2) : kOOB;
-  u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-  if (row_ok && !full && cols_left > 0) {
-    const uint16_t* p = (const uint16_t*)(base + r * ld * 2 + c * 2);
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (e < cols_left) vec_set<2>(v, e, p[e]);
-  }
-  return v;
+// Physical 16-byte chunk of logical chunk c in A row r (4 chunks per row):
+// the 16 rows one ds_read_b128 phase touches cover all 16 bank groups of the
+// 256-byte LDS bank sweep (and any 8 consecutive rows cover a 128-byte one).
+__device__ __forceinline__ int a_phys(int r, int c) { return c ^ (((r >> 2) ^ (r >> 1)) & 3); }
+// XOR applied to the chunk index of B row k: the 4 rows x 64 bytes that one
+// ds_read_b64_tr_b16 phase of 32 lanes touches land in distinct bank groups.
+template <int CPR>
+__device__ __forceinline__ int b_swz(int k) {
+  return CPR >= 16 ? 4 * (k & 3) : CPR >= 8 ? 2 * (k & 3) : 2 * ((k >> 1) & 1);
 }
+
+// Wait until at most n (0..63) vector-memory operations of this wave are
+// outstanding; n is only known at run time here, the instruction needs it as
+// an immediate.
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+#define STG_W(i) case i: __builtin_amdgcn_s_waitcnt(STG_VMCNT(i)); break;
+#define STG_W8(b) STG_W(b) STG_W(b + 1) STG_W(b + 2) STG_W(b + 3) STG_W(b + 4) STG_W(b + 5) STG_W(b + 6) STG_W(b + 7)
+    STG_W8(0) STG_W8(8) STG_W8(16) STG_W8(24) STG_W8(32) STG_W8(40) STG_W8(48) STG_W8(56)
+#undef STG_W8
+#undef STG_W
+    default: __builtin_amdgcn_s_waitcnt(STG_VMCNT(0));
+  }
+}
+
 
 // Tile (tm, tn) of logical id t: consecutive ids on one XCD, grouped by 4
 // row panels so neighbouring workgroups share A and B panels in L2.
@@ -110,6 +127,33 @@ __device__ __forceinline__ void tile_of(uint32_t t, int tiles_m, int tiles_n, in
   const int in = t - group * per_group;
   tm = first + in % gm;
   tn = in / gm;
+}
+
+typedef uint32_t u32x4_s __attribute__((ext_vector_type(4)));
+
+// Raw-buffer descriptor words (gfx9 layout, stride 0) over [base, base+bytes),
+// made wave-uniform so they live in SGPRs.
+__device__ __forceinline__ u32x4_s rsrc_words(const char* base, int64_t avail) {
+  const uint32_t bytes = (uint32_t)(avail <= 0 ? 0 : avail < (int64_t)kOOB ? avail : (int64_t)kOOB - 1);
+  const uint64_t a = (uint64_t)base;
+  u32x4_s w;
+  w[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  w[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu);
+  w[2] = __builtin_amdgcn_readfirstlane(bytes);
+  w[3] = 0x00020000u;
+  return w;
+}
+
+// LDS DMA of 16 bytes per lane: lane L's chunk at buffer offset `off` lands at
+// LDS byte lds_base + 16 L; an offset past num_records writes zeros.  Issued
+// through inline asm so the compiler does not guard every later LDS read with
+// a wait on all outstanding loads; completion is awaited explicitly with
+// s_waitcnt vmcnt before the barrier that publishes the stage.
+__device__ __forceinline__ void dma16(const u32x4_s& rs, uint32_t off, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(off), "s"(rs)
+               : "memory", "m0");
 }
 
 template <class CF>
@@ -131,62 +175,114 @@ __global__ __launch_bounds__(CF::NT) __attribute__((amdgpu_waves_per_eu(1, 2))) 
     for (int j = 0; j < CF::FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  u32x4 ra[CF::A_PER_T], rb[CF::B_PER_T];
   bf16x8 fa[2][CF::FM], fb[2][CF::FN];
 
-  auto load_stage = [&](int kt) {
+  // chunk owned by this lane in DMA instruction q of the A / B stage
+  auto a_chunk = [&](int q, int& r, int& c) {
+    const int pos = (wave * CF::A_DMA_W + q) * 64 + lane;
+    r = pos >> 2;
+    c = a_phys(r, pos & 3);
+  };
+  auto b_chunk = [&](int q, int& k, int& c) {
+    const int pos = (wave * CF::B_DMA_W + q) * 64 + lane;
+    k = pos / CF::B_CPR;
+    c = (pos % CF::B_CPR) ^ b_swz<CF::B_CPR>(k);
+  };
+
+  // Per-lane DMA offsets are the same for every stage (the descriptors move
+  // with k0): rows of A past M and columns of B past N are folded in once
+  // here; only a stage reaching past K needs a per-chunk test.
+  uint32_t a_off[CF::A_DMA_W], b_off[CF::B_DMA_W];
+  int a_kc[CF::A_DMA_W], b_k[CF::B_DMA_W];
+#pragma unroll
+  for (int q = 0; q < CF::A_DMA_W; ++q) {
+    int r, c;
+    a_chunk(q, r, c);
+    a_kc[q] = 8 * c;
+    a_off[q] = m0 + r < p.M ? (uint32_t)(r * p.lda * 2 + c * 16) : kOOB;
+  }
+#pragma unroll
+  for (int q = 0; q < CF::B_DMA_W; ++q) {
+    int k, c;
+    b_chunk(q, k, c);
+    b_k[q] = k;
+    b_off[q] = n0 + 8 * c + 8 <= p.N ? (uint32_t)(k * p.ldb * 2 + c * 16) : kOOB;
+  }
+
+  // 32-bit LDS address of the dynamic shared memory (wave-uniform)
+  const uint32_t smem_lds =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem);
+
+  // issue the LDS DMA of stage kt into ring slot kt % NSTAGE
+  auto issue_stage = [&](int kt) {
+    const uint32_t st = smem_lds + (kt % CF::NSTAGE) * CF::STAGE_B;
     const int64_t k0 = (int64_t)kt * BK;
-    // A: rows m0.., cols k0..; B: rows k0.., cols n0..
-    const char* abase = p.A + (m0 * p.lda + k0) * 2;
-    const char* bbase = p.B + (k0 * p.ldb + n0) * 2;
-    const int64_t a_avail = ((p.M - 1 - m0) * p.lda + (p.K - k0)) * 2;
-    const int64_t b_avail = ((p.K - 1 - k0) * p.ldb + (p.N - n0)) * 2;
-    const __amdgpu_buffer_rsrc_t rsa =
-        make_rsrc(abase, (uint32_t)(a_avail <= 0 ? 0 : a_avail < (int64_t)kOOB ? a_avail : (int64_t)kOOB - 1));
-    const __amdgpu_buffer_rsrc_t rsb =
-        make_rsrc(bbase, (uint32_t)(b_avail <= 0 ? 0 : b_avail < (int64_t)kOOB ? b_avail : (int64_t)kOOB - 1));
+    const u32x4_s rsa = rsrc_words(p.A + (m0 * p.lda + k0) * 2, ((p.M - 1 - m0) * p.lda + (p.K - k0)) * 2);
+    const u32x4_s rsb = rsrc_words(p.B + (k0 * p.ldb + n0) * 2, ((p.K - 1 - k0) * p.ldb + (p.N - n0)) * 2);
+    if (k0 + BK <= p.K) {
 #pragma unroll
-    for (int q = 0; q < CF::A_PER_T; ++q) {
-      const int c = tid + q * CF::NT;
-      ra[q] = (u32x4){0, 0, 0, 0};
-      if (c < CF::A_CHUNKS) {
-        const int r = c / (BK / 8), kc = c % (BK / 8);
-        ra[q] = load_chunk(rsa, abase, p.lda, r, kc * 8, m0 + r < p.M, p.K - k0 - kc * 8);
+      for (int q = 0; q < CF::A_DMA_W; ++q) dma16(rsa, a_off[q], st + (wave * CF::A_DMA_W + q) * 1024);
+#pragma unroll
+      for (int q = 0; q < CF::B_DMA_W; ++q) dma16(rsb, b_off[q], st + CF::A_STAGE_B + (wave * CF::B_DMA_W + q) * 1024);
+    } else {
+      const int kleft = (int)(p.K - k0);  // valid K values in this stage, 1..BK-1
+#pragma unroll
+      for (int q = 0; q < CF::A_DMA_W; ++q)
+        dma16(rsa, a_kc[q] + 8 <= kleft ? a_off[q] : kOOB, st + (wave * CF::A_DMA_W + q) * 1024);
+#pragma unroll
+      for (int q = 0; q < CF::B_DMA_W; ++q)
+        dma16(rsb, b_k[q] < kleft ? b_off[q] : kOOB, st + CF::A_STAGE_B + (wave * CF::B_DMA_W + q) * 1024);
+    }
+  };
+
+  // after this lane's DMA of stage kt completed: write the chunks that
+  // straddle the K edge (A) or the N edge (B), which the DMA left zero
+  auto fix_stage = [&](int kt) {
+    const int64_t k0 = (int64_t)kt * BK;
+    const bool a_edge = k0 + BK > p.K && (p.K & 7);
+    const bool b_edge = n0 + CF::BN > p.N && (p.N & 7);
+    if (!a_edge && !b_edge) return;
+    char* st = smem + (kt % CF::NSTAGE) * CF::STAGE_B;
+    if (a_edge) {
+#pragma unroll
+      for (int q = 0; q < CF::A_DMA_W; ++q) {
+        int r, c;
+        a_chunk(q, r, c);
+        const int64_t col = k0 + 8 * c, left = p.K - col;
+        if (m0 + r < p.M && left > 0 && left < 8) {
+          const uint16_t* src = (const uint16_t*)(p.A + ((m0 + r) * p.lda + col) * 2);
+          u32x4 v = {0, 0, 0, 0};
+          for (int e = 0; e < 8; ++e)
+            if (e < left) vec_set<2>(v, e, src[e]);
+          *(u32x4*)(st + (wave * CF::A_DMA_W + q) * 1024 + lane * 16) = v;
+        }
       }
     }
+    if (b_edge) {
 #pragma unroll
-    for (int q = 0; q < CF::B_PER_T; ++q) {
-      const int c = tid + q * CF::NT;
-      rb[q] = (u32x4){0, 0, 0, 0};
-      if (c < CF::B_CHUNKS) {
-        const int r = c / (CF::BN / 8), nc = c % (CF::BN / 8);
-        rb[q] = load_chunk(rsb, bbase, p.ldb, r, nc * 8, k0 + r < p.K, p.N - n0 - nc * 8);
+      for (int q = 0; q < CF::B_DMA_W; ++q) {
+        int k, c;
+        b_chunk(q, k, c);
+        const int64_t col = n0 + 8 * c, left = p.N - col;
+        if (k0 + k < p.K && left > 0 && left < 8) {
+          const uint16_t* src = (const uint16_t*)(p.B + ((k0 + k) * p.ldb + col) * 2);
+          u32x4 v = {0, 0, 0, 0};
+          for (int e = 0; e < 8; ++e)
+            if (e < left) vec_set<2>(v, e, src[e]);
+          *(u32x4*)(st + CF::A_STAGE_B + (wave * CF::B_DMA_W + q) * 1024 + lane * 16) = v;
+        }
       }
     }
   };
-  auto store_stage = [&](int buf) {
-    char* as = smem + buf * CF::STAGE_B;
-    char* bs = as + CF::A_STAGE_B;
-#pragma unroll
-    for (int q = 0; q < CF::A_PER_T; ++q) {
-      const int c = tid + q * CF::NT;
-      if (c < CF::A_CHUNKS) *(u32x4*)(as + a_lds(c / (BK / 8), c % (BK / 8))) = ra[q];
-    }
-#pragma unroll
-    for (int q = 0; q < CF::B_PER_T; ++q) {
-      const int c = tid + q * CF::NT;
-      if (c < CF::B_CHUNKS) *(u32x4*)(bs + (c / (CF::BN / 8)) * CF::B_PITCH_B + (c % (CF::BN / 8)) * 16) = rb[q];
-    }
-  };
-  // MFMA operands of K sub-step ks (16 K values) of stage `buf` into slot s
-  auto read_frags = [&](int buf, int ks, int s) {
-    const char* as = smem + buf * CF::STAGE_B;
+
+  // MFMA operands of K sub-step ks (16 K values) of stage kt into slot s
+  auto read_frags = [&](int kt, int ks, int s) {
+    const char* as = smem + (kt % CF::NSTAGE) * CF::STAGE_B;
     const char* bs = as + CF::A_STAGE_B;
 #pragma unroll
     for (int i = 0; i < CF::FM; ++i) {
       const int r = wm * CF::WTM + i * 32 + (lane & 31);
-      fa[s][i] = *(const bf16x8*)(as + a_lds(r, 2 * ks + (lane >> 5)));
+      fa[s][i] = *(const bf16x8*)(as + r * (BK * 2) + (a_phys(r, 2 * ks + (lane >> 5)) << 4));
     }
 #pragma unroll
     for (int j = 0; j < CF::FN; ++j) {
@@ -195,39 +291,44 @@ __global__ __launch_bounds__(CF::NT) __attribute__((amdgpu_waves_per_eu(1, 2))) 
       const int g = lane >> 4, t = lane & 15;
       const int col = wn * CF::WTN + j * 32 + 16 * (g & 1) + 4 * (t & 3);
       const int row = 16 * ks + 8 * (g >> 1) + (t >> 2);
-      const char* p0 = bs + row * CF::B_PITCH_B + col * 2;
+      const int off = ((col >> 3) ^ b_swz<CF::B_CPR>(row)) * 16 + (col & 7) * 2;  // rows 4 apart share the XOR
+      const char* p0 = bs + row * (CF::BN * 2) + off;
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * CF::B_PITCH_B));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * CF::BN * 2));
       const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       fb[s][j] = __builtin_bit_cast(bf16x8, both);
     }
   };
+  auto mfmas = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < CF::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < CF::FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
+  };
 
-  if (nk > 0) {
-    load_stage(0);
-    store_stage(0);
-  }
+  // prologue: NSTAGE - 1 stages in flight, wait for the first two
+  for (int s = 0; s < CF::NSTAGE - 1 && s < nk; ++s) issue_stage(s);
+  wait_vmcnt(max(0, min(nk, CF::NSTAGE - 1) - 2) * CF::DMA_W);
+  if (nk > 0) fix_stage(0);
+  if (nk > 1) fix_stage(1);
   __syncthreads();
   if (nk > 0) read_frags(0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < nk;
-    // next stage's global loads fly during this stage's MFMAs
-    if (more) load_stage(kt + 1);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < BK / 16) read_frags(buf, ks + 1, cur ^ 1);
-      // the other stage was released by the barrier that ended the last step
-      if (ks == BK / 16 - 1 && more) store_stage(buf ^ 1);
-#pragma unroll
-      for (int i = 0; i < CF::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < CF::FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+    // ring slot (kt + NSTAGE - 1) % NSTAGE was last read in step kt - 1,
+    // released by its barrier
+    if (kt + CF::NSTAGE - 1 < nk) issue_stage(kt + CF::NSTAGE - 1);
+    read_frags(kt, 1, 1);
+    mfmas(0);
+    // stage kt + 1 became visible at the previous barrier
+    if (kt + 1 < nk) read_frags(kt + 1, 0, 0);
+    mfmas(1);
+    if (kt + 2 < nk) {
+      // stage kt + 2 must have landed; the stages issued after it may fly on
+      wait_vmcnt((min(nk - 1, kt + CF::NSTAGE - 1) - (kt + 2)) * CF::DMA_W);
+      fix_stage(kt + 2);
     }
     __syncthreads();
-    if (more) read_frags(buf ^ 1, 0, 0);
   }
 
   // clipped epilogue: lane l, accumulator r of block (i, j) is
@@ -248,8 +349,9 @@ __global__ __launch_bounds__(CF::NT) __attribute__((amdgpu_waves_per_eu(1, 2))) 
     return;
   }
   // bf16: round to nearest even, stage the wave's tile in LDS (every wave has
-  // its own region; the stages are no longer read), then write whole 16-byte
-  // row chunks; only chunks crossing column N are written element by element
+  // its own region; the ring is no longer read after the last barrier), then
+  // write whole 16-byte row chunks; only chunks crossing column N are written
+  // element by element
   char* ep = smem + wave * CF::EPI_WAVE_B;
 #pragma unroll
   for (int i = 0; i < CF::FM; ++i)
@@ -280,8 +382,11 @@ __global__ __launch_bounds__(CF::NT) __attribute__((amdgpu_waves_per_eu(1, 2))) 
   }
 }
 
-using MainCfg = Cfg<256, 256, 2, 2>;
-using EdgeCfg = Cfg<128, 32, 4, 1>;
+// main: 8 waves of 64 x 128 accumulators (two waves per SIMD), 4-stage ring;
+// edge strip: small stages, so a deep ring hides the load latency of its
+// long K loop
+using MainCfg = Cfg<256, 256, 4, 2, 4>;
+using EdgeCfg = Cfg<64, 32, 2, 1, 16>;
 
 template <class CF>
 int launch(const char* name, GemmParams p, int64_t cols, hipStream_t s) {
@@ -289,8 +394,7 @@ int launch(const char* name, GemmParams p, int64_t cols, hipStream_t s) {
   p.tiles_n = (int32_t)((cols + CF::BN - 1) / CF::BN);
   const int64_t n_wg = (int64_t)p.tiles_m * p.tiles_n;
   if (n_wg == 0) return STG_OK;
-  const size_t lds = CF::LDS_B;
-  launch_kernel(name, gemm_kernel<CF>, dim3((unsigned)n_wg), dim3(CF::NT), lds, s, p);
+  launch_kernel(name, gemm_kernel<CF>, dim3((unsigned)n_wg), dim3(CF::NT), (uint32_t)CF::LDS_B, s, p);
   return check_launch("gemm_bounded");
 }
 
