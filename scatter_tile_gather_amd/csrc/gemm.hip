@@ -36,7 +36,8 @@
 //    read before the barrier that ends step k, and each step waits only for
 //    stage k+2.  One barrier per 32 K values.
 //  * Grid: a main launch of 256 x 256 tiles over the columns that fill whole
-//    tiles, and an edge launch of 64 x 32 tiles for the remaining columns.
+//    tiles; the remaining columns go to an edge launch of 64 x 32 tiles, or,
+//    when at most 8 remain (N = 8193 leaves one), to a skinny vector kernel.
 //    Tile ids are renumbered so that consecutive ids run on one XCD and walk
 //    4-row-panel groups, keeping A and B panels resident in that XCD's L2.
 #include "stg_internal.h"
@@ -382,6 +383,92 @@ __global__ __launch_bounds__(CF::NT) __attribute__((amdgpu_waves_per_eu(1, 2))) 
   }
 }
 
+// Skinny strip: C[:, n_base + j] for j < R <= 8 remaining columns.  The strip
+// is a matrix-vector shape (all of A against a few columns of B), bound by
+// reading A once, so it runs on the vector ALUs: B's R columns of each K block
+// are staged once in LDS as fp32, every row of A is split over 8 lanes that
+// stream 16-byte chunks (element loads only for the chunk crossing K), each
+// lane keeps R fp32 partial sums, and the 8 lanes reduce with cross-lane
+// shuffles before the clipped write.
+constexpr int SK_ROWS = 32;    // rows per workgroup (8 lanes per row)
+constexpr int SK_KB = 1024;    // K values per LDS block
+constexpr int SK_CHUNKS = SK_KB / 8 / 8;  // 16-byte A chunks per lane per block
+
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p, int R) {
+  __shared__ float sb[8 * SK_KB];  // [j][k] of the current K block
+  const int tid = threadIdx.x;
+  const int rl = tid >> 3, part = tid & 7;
+  const int64_t row = (int64_t)blockIdx.x * SK_ROWS + rl;
+  const bool row_ok = row < p.M;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  for (int64_t k0 = 0; k0 < p.K; k0 += SK_KB) {
+    const int kb = (int)(p.K - k0 < SK_KB ? p.K - k0 : SK_KB);
+    __syncthreads();  // the previous block's B is no longer read
+    for (int i = tid; i < R * SK_KB; i += 256) {
+      const int j = i / SK_KB, k = i - j * SK_KB;
+      float v = 0.f;
+      if (k < kb) {
+        const uint16_t h = *(const uint16_t*)(p.B + ((k0 + k) * p.ldb + p.n_base + j) * 2);
+        v = __uint_as_float((uint32_t)h << 16);
+      }
+      sb[j * SK_KB + k] = v;
+    }
+    __syncthreads();
+    if (row_ok) {
+      u32x4 a[SK_CHUNKS];
+      const char* arow = p.A + (row * p.lda + k0) * 2;
+#pragma unroll
+      for (int q = 0; q < SK_CHUNKS; ++q) {
+        const int c = (part + 8 * q) * 8;  // first K value of the chunk within the block
+        a[q] = (u32x4){0, 0, 0, 0};
+        if (c + 8 <= kb) {
+          a[q] = ld16(arow + c * 2);
+        } else if (c < kb) {
+          for (int e = 0; e < 8; ++e)
+            if (c + e < kb) vec_set<2>(a[q], e, load_elem<2>(arow + (c + e) * 2));
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < SK_CHUNKS; ++q) {
+        const int c = (part + 8 * q) * 8;
+        if (c >= kb) break;
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = __uint_as_float((uint32_t)vec_get<2>(a[q], e) << 16);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (j < R) {
+            const float4 b0 = *(const float4*)(sb + j * SK_KB + c);
+            const float4 b1 = *(const float4*)(sb + j * SK_KB + c + 4);
+            acc[j] += x[0] * b0.x + x[1] * b0.y + x[2] * b0.z + x[3] * b0.w + x[4] * b1.x + x[5] * b1.y +
+                      x[6] * b1.z + x[7] * b1.w;
+          }
+        }
+      }
+    }
+  }
+  // reduce over the 8 lanes of a row (consecutive lanes)
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    acc[j] += __shfl_xor(acc[j], 1);
+    acc[j] += __shfl_xor(acc[j], 2);
+    acc[j] += __shfl_xor(acc[j], 4);
+  }
+  if (row_ok && part < R) {
+    float v = acc[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j)
+      if (part == j) v = acc[j];
+    const int64_t col = p.n_base + part;
+    if (p.c_f32)
+      *(float*)(p.C + (row * p.ldc + col) * 4) = v;
+    else
+      *(__bf16*)(p.C + (row * p.ldc + col) * 2) = (__bf16)v;
+  }
+}
+
 // main: 8 waves of 64 x 128 accumulators (two waves per SIMD), 4-stage ring;
 // edge strip: small stages, so a deep ring hides the load latency of its
 // long K loop
@@ -441,6 +528,12 @@ extern "C" int gemm_bounded(const void* A, int64_t lda, const void* B, int64_t l
   p.n_base = 0;
   if (n_main > 0 && (rc = launch<MainCfg>("gemm_bounded/main", p, n_main, s))) return rc;
   p.n_base = n_main;
-  if (N > n_main && (rc = launch<EdgeCfg>("gemm_bounded/edge", p, N - n_main, s))) return rc;
+  const int64_t rem = N - n_main;
+  if (rem > 8) return launch<EdgeCfg>("gemm_bounded/edge", p, rem, s);
+  if (rem > 0) {
+    const unsigned grid = (unsigned)((M + SK_ROWS - 1) / SK_ROWS);
+    launch_kernel("gemm_bounded/skinny", gemm_skinny_kernel, dim3(grid), dim3(256), 0, s, p, (int)rem);
+    return check_launch(name);
+  }
   return STG_OK;
 }

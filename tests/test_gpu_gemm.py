@@ -79,7 +79,8 @@ def test_gemm_row_selection_exact(stg, orc, shape, out_f32):
 
 
 @pytest.mark.parametrize("shape", [(31, 33, 17), (256, 512, 4096), (513, 260, 70), (2, 300, 1), (64, 257, 65),
-                                   (1000, 255, 130), (257, 769, 33)])
+                                   (1000, 255, 130), (257, 769, 33), (100, 276, 3000), (70, 264, 2500),
+                                   (33, 7, 1100)])
 def test_gemm_random_shapes(stg, orc, shape):
     M, N, K = shape
     g = inputs.gemm(M, N, K, seed=M + N + K)
