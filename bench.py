@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default="all",
-                    help="comma list of: copy,gather,masked,ragged,gemm (rocprof runs); 'all' for the full report")
+                    help="comma list of: copy,gather,masked,ragged,gemm,calib (rocprof runs); 'all' for the full report")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU time budget of the oracle baseline")
     return ap.parse_args()
@@ -65,20 +65,20 @@ def source_hash(*files):
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(kernel_file, profile_name, per_launch_algo):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+def traffic_from_profile(kernel_files, profile_name, label):
+    """HBM bytes per launch of kernel `label` from the committed rocprofv3
+    counter summary (FETCH_SIZE and WRITE_SIZE runs, scaled by a plain copy of
+    known size), if it was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", profile_name)
     if not os.path.exists(path):
         return None
-    text = open(path).read()
-    m = re.search(r"traffic_record:\s*(\{.*\})", text)
+    m = re.search(r"traffic_record:\s*(\{.*\})", open(path).read())
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("source_hash") != source_hash(*kernel_file):
+    if rec.get("source_hash") != source_hash(*kernel_files):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("hbm_bytes_per_launch", {}).get(label)
 
 
 # ---------------------------------------------------------------------------
@@ -268,6 +268,20 @@ def run_gemm(stg, inputs, steps, warmup):
             "kernel_ms": {k: round(v, 4) for k, v in kern.items()}}
 
 
+def run_calibration(steps):
+    """A plain device-to-device copy of a known size (512 MiB read, 512 MiB
+    written), for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    n = 512 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"bytes_read": n, "bytes_written": n, "launches": steps}
+
+
 def cpu_baseline(inputs, budget_s):
     """The oracle, single-threaded on one host core, on the headline step."""
     import oracle
@@ -312,6 +326,8 @@ def main():
     only = set(args.only.split(",")) if args.only != "all" else {"copy", "gather", "masked", "ragged", "gemm"}
     ops = {}
     head = None
+    if "calib" in only:
+        ops["calibration_copy"] = run_calibration(args.steps)
     if "copy" in only:
         head = run_copy(stg, inputs, args.steps, args.warmup)
         print(f"[bench] copy step {head['step_ms']:.4f} ms", file=sys.stderr, flush=True)
@@ -335,10 +351,8 @@ def main():
     per = head["per_kernel_ms"]
     dom = max(per, key=lambda n: per[n])
     achieved = gbs(head["algo"][dom], per[dom])
-    kernel_files = {"tile_copy_bounded": ("scatter_tile_gather_amd/csrc/copy.hip",),
-                    "tile_store_clipped": ("scatter_tile_gather_amd/csrc/copy.hip",)}
-    base = dom.split("@")[0]
-    traffic = traffic_from_profile(kernel_files[base], f"{base}.bounded_copy_workload.md", head["algo"][dom])
+    traffic = traffic_from_profile(("scatter_tile_gather_amd/csrc/copy.hip", "scatter_tile_gather_amd/csrc/stg_internal.h"),
+                                   "tile_copy_bounded.bounded_copy_workload.md", dom)
     value = gbs(head["step_bytes"], head["step_ms"])
     line = {
         "metric": "effective HBM GB/s (gather/copy/scatter, % of peak); bounded GEMM TFLOP/s",
