@@ -30,7 +30,7 @@ namespace stg {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 1;  // vectors per lane per pass (measured best with 8-row workgroups)
 
 struct CopyParams {
   const char* m;  // element (0, 0) of the matrix (source of the copy, destination of the store)
@@ -227,7 +227,7 @@ int launch(const char* name, const stg_tensor* mat, int64_t tm, int64_t tn, int6
     p.cpt = (int32_t)(tn * es / 16);
     p.tiles_per_wg = 64 / p.cpt;  // one 64-lane row segment per wavefront
     if (p.tiles_per_wg > G_c) p.tiles_per_wg = (int32_t)G_c;
-    p.rows_per_wg = (int32_t)(tm < 16 ? tm : 16);
+    p.rows_per_wg = (int32_t)(tm < 8 ? tm : 8);
     p.row_blocks = (int32_t)((tm + p.rows_per_wg - 1) / p.rows_per_wg);
     p.span_magic = div_magic((uint32_t)(p.tiles_per_wg * p.cpt));
     p.cpt_magic = div_magic((uint32_t)p.cpt);
