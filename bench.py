@@ -45,6 +45,9 @@ def parse():
                     help="comma list of: copy,gather,masked,ragged,gemm,calib (rocprof runs); 'all' for the full report")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU time budget of the oracle baseline")
+    ap.add_argument("--spinup-ms", type=float, default=400.0,
+                    help="before each workload's warmup, run its step for this long (untimed) so the GPU's clocks "
+                         "leave their idle state; 0 disables")
     return ap.parse_args()
 
 
@@ -109,6 +112,25 @@ def copy_workload(stg, inputs):
     return w, kernels, algo
 
 
+SPINUP_MS = 0.0
+
+
+def spin_up(fn):
+    """Run `fn` repeatedly, untimed, for SPINUP_MS of wall time.  An idle
+    MI355X starts a burst of work at reduced clocks and reaches its steady
+    state only after tens of milliseconds under load; without this the timed
+    steps of a short workload would measure the ramp, not the kernels."""
+    import torch
+
+    if SPINUP_MS <= 0:
+        return
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < SPINUP_MS:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
 def run_copy(stg, inputs, steps, warmup):
     """Time `steps` headline steps between two events on the launch stream,
     untraced.  Then repeat the same steps with the library's kernel tracing on
@@ -119,6 +141,7 @@ def run_copy(stg, inputs, steps, warmup):
 
     w, kernels, algo = copy_workload(stg, inputs)
     names = [n for n, _ in kernels]
+    spin_up(lambda: [fn() for _, fn in kernels])
     for _ in range(warmup):
         for _, fn in kernels:
             fn()
@@ -157,6 +180,7 @@ def run_copy(stg, inputs, steps, warmup):
 def time_fn(fn, iters, warmup):
     import torch
 
+    spin_up(fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -310,7 +334,9 @@ def cpu_baseline(inputs, budget_s):
 
 
 def main():
+    global SPINUP_MS
     args = parse()
+    SPINUP_MS = args.spinup_ms
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); nothing run.", file=sys.stderr)
         sys.exit(2)
@@ -373,6 +399,7 @@ def main():
             "tiles_per_step": 16512 + 16641,
             "algorithmic_bytes_per_step": int(head["step_bytes"]),
             "step_host_wall_ms": round(head["wall_ms"], 5),
+            "spinup_ms_before_warmup": args.spinup_ms,
             "per_kernel_ms": {k: round(v, 5) for k, v in per.items()},
             "dispatch_gaps_ms_per_step": round(head["step_ms"] - sum(per.values()), 5),
         },

@@ -32,9 +32,11 @@
 //    tiles, "A concrete edge", swizzled windows).  Operand reads are
 //    bank-conflict free.
 //  * Pipeline: a ring of NSTAGE stages; the DMA for stage k+NSTAGE-1 is
-//    issued while stage k feeds the MFMAs, the first operands of stage k+1 are
-//    read before the barrier that ends step k, and each step waits only for
-//    stage k+2.  One barrier per 32 K values.
+//    issued while stage k feeds the MFMAs, one instruction after every few
+//    MFMAs (a wave issues in order, and a burst of DMA that fills the memory
+//    queue would stall the MFMAs behind it); the first operands of stage k+1
+//    are read before the barrier that ends step k, and each step waits only
+//    for stage k+2.  One barrier per 32 K values.
 //  * Grid: a main launch of 256 x 256 tiles over the columns that fill whole
 //    tiles; the remaining columns go to an edge launch of 64 x 32 tiles, or,
 //    when at most 8 remain (N = 8193 leaves one), to a skinny vector kernel.
@@ -308,6 +310,68 @@ __global__ __launch_bounds__(CF::NT) __attribute__((amdgpu_waves_per_eu(1, 2))) 
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
   };
 
+  // DMA instruction q (the A instructions first, then B) of stage kt; a
+  // stage reaching past K sends its chunks with no valid value out of range
+  auto stage_rsrc = [&](int kt, u32x4_s& rsa, u32x4_s& rsb) {
+    const int64_t k0 = (int64_t)kt * BK;
+    rsa = rsrc_words(p.A + (m0 * p.lda + k0) * 2, ((p.M - 1 - m0) * p.lda + (p.K - k0)) * 2);
+    rsb = rsrc_words(p.B + (k0 * p.ldb + n0) * 2, ((p.K - 1 - k0) * p.ldb + (p.N - n0)) * 2);
+  };
+  auto dma_one = [&](int kt, int q, const u32x4_s& rsa, const u32x4_s& rsb) {
+    const uint32_t st = smem_lds + (kt % CF::NSTAGE) * CF::STAGE_B;
+    const int kleft = (int)(p.K - (int64_t)kt * BK);
+    if (q < CF::A_DMA_W) {
+      dma16(rsa, a_kc[q] + 8 <= kleft ? a_off[q] : kOOB, st + (wave * CF::A_DMA_W + q) * 1024);
+    } else {
+      const int qb = q - CF::A_DMA_W;
+      dma16(rsb, b_k[qb] < kleft ? b_off[qb] : kOOB, st + CF::A_STAGE_B + (wave * CF::B_DMA_W + qb) * 1024);
+    }
+  };
+  // MFMAs of operand slot s with DMA instructions q0 .. q0+nq-1 of stage kd
+  // spread evenly among them: a wave whose memory instructions cannot issue
+  // (the vector-memory queue is full) stalls in order, so a burst of DMA
+  // would hold back the MFMAs queued behind it.  The scheduling barriers keep
+  // the compiler from regrouping them.
+  auto mfmas_dma = [&](int s, int kd, int q0, int nq, const u32x4_s& rsa, const u32x4_s& rsb) {
+    constexpr int NM = CF::FM * CF::FN;
+#pragma unroll
+    for (int i = 0; i < CF::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < CF::FN; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
+        const int m = i * CF::FN + j;
+#pragma unroll
+        for (int d = 0; d < nq; ++d) {
+          // instruction d goes after MFMA max(0, (d + 1) NM / nq - 1)
+          const int after = ((d + 1) * NM) / nq - 1;
+          if ((after < 0 ? 0 : after) == m) {
+            __builtin_amdgcn_sched_barrier(0);
+            dma_one(kd, q0 + d, rsa, rsb);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+  };
+  // one K step: operands of stage kt (second half) and kt + 1 (first half)
+  // feed the MFMAs while stage kt + NSTAGE - 1 is issued (when `dma`)
+  auto step = [&](int kt, bool dma) {
+    constexpr int H = CF::DMA_W / 2;
+    u32x4_s rsa, rsb;
+    if (dma) stage_rsrc(kt + CF::NSTAGE - 1, rsa, rsb);
+    read_frags(kt, 1, 1);
+    mfmas_dma(0, kt + CF::NSTAGE - 1, 0, dma ? H : 0, rsa, rsb);
+    // stage kt + 1 became visible at the previous barrier
+    if (kt + 1 < nk) read_frags(kt + 1, 0, 0);
+    mfmas_dma(1, kt + CF::NSTAGE - 1, H, dma ? CF::DMA_W - H : 0, rsa, rsb);
+    if (kt + 2 < nk) {
+      // stage kt + 2 must have landed; the stages issued after it may fly on
+      wait_vmcnt((min(nk - 1, kt + CF::NSTAGE - 1) - (kt + 2)) * CF::DMA_W);
+      fix_stage(kt + 2);
+    }
+    // ring slot (kt + NSTAGE) % NSTAGE = kt % NSTAGE is free after this
+    __syncthreads();
+  };
+
   // prologue: NSTAGE - 1 stages in flight, wait for the first two
   for (int s = 0; s < CF::NSTAGE - 1 && s < nk; ++s) issue_stage(s);
   wait_vmcnt(max(0, min(nk, CF::NSTAGE - 1) - 2) * CF::DMA_W);
@@ -315,22 +379,11 @@ __global__ __launch_bounds__(CF::NT) __attribute__((amdgpu_waves_per_eu(1, 2))) 
   if (nk > 1) fix_stage(1);
   __syncthreads();
   if (nk > 0) read_frags(0, 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    // ring slot (kt + NSTAGE - 1) % NSTAGE was last read in step kt - 1,
-    // released by its barrier
-    if (kt + CF::NSTAGE - 1 < nk) issue_stage(kt + CF::NSTAGE - 1);
-    read_frags(kt, 1, 1);
-    mfmas(0);
-    // stage kt + 1 became visible at the previous barrier
-    if (kt + 1 < nk) read_frags(kt + 1, 0, 0);
-    mfmas(1);
-    if (kt + 2 < nk) {
-      // stage kt + 2 must have landed; the stages issued after it may fly on
-      wait_vmcnt((min(nk - 1, kt + CF::NSTAGE - 1) - (kt + 2)) * CF::DMA_W);
-      fix_stage(kt + 2);
-    }
-    __syncthreads();
-  }
+  // ring slot (kt + NSTAGE - 1) % NSTAGE, written during step kt, was last
+  // read in step kt - 1 and released by its barrier
+  int kt = 0;
+  for (; kt + CF::NSTAGE - 1 < nk; ++kt) step(kt, true);
+  for (; kt < nk; ++kt) step(kt, false);
 
   // clipped epilogue: lane l, accumulator r of block (i, j) is
   // row 8(r/4) + 4(l/32) + r%4, column l%32 of that 32x32 block
@@ -469,10 +522,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p, int R) {
   }
 }
 
-// main: 8 waves of 64 x 128 accumulators (two waves per SIMD), 4-stage ring;
+// main: 8 waves of 128 x 64 accumulators (two waves per SIMD), 4-stage ring;
 // edge strip: small stages, so a deep ring hides the load latency of its
 // long K loop
-using MainCfg = Cfg<256, 256, 4, 2, 4>;
+using MainCfg = Cfg<256, 256, 2, 4, 4>;
 using EdgeCfg = Cfg<64, 32, 2, 1, 16>;
 
 template <class CF>
