@@ -438,24 +438,28 @@ __global__ __launch_bounds__(CF::NT) __attribute__((amdgpu_waves_per_eu(1, 2))) 
 
 // Skinny strip: C[:, n_base + j] for j < R <= 8 remaining columns.  The strip
 // is a matrix-vector shape (all of A against a few columns of B), bound by
-// reading A once, so it runs on the vector ALUs: B's R columns of each K block
-// are staged once in LDS as fp32, every row of A is split over 8 lanes that
-// stream 16-byte chunks (element loads only for the chunk crossing K), each
-// lane keeps R fp32 partial sums, and the 8 lanes reduce with cross-lane
-// shuffles before the clipped write.
-constexpr int SK_ROWS = 32;    // rows per workgroup (8 lanes per row)
-constexpr int SK_KB = 1024;    // K values per LDS block
-constexpr int SK_CHUNKS = SK_KB / 8 / 8;  // 16-byte A chunks per lane per block
+// reading A once, so it runs on the vector ALUs.  B's R columns of each K block
+// are staged once per workgroup in LDS as fp32; a wave owns SK_RPW rows and
+// covers a block's K with its 64 lanes, one 16-byte chunk of A (eight bf16)
+// per lane and row at a time (element loads only for the chunk crossing K),
+// issuing all of its rows' loads before the arithmetic; each lane keeps R fp32
+// partial sums per row, reduced across the wave with cross-lane shuffles
+// before the clipped write.
+constexpr int SK_KB = 1024;                 // K values per LDS block
+constexpr int SK_CPL = SK_KB / 8 / 64;      // 16-byte chunks per lane and row in a block (2)
+constexpr int SK_RPW = 4;                   // rows per wave
+constexpr int SK_ROWS = SK_RPW * 4;         // rows per workgroup (4 waves)
 
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p, int R) {
+template <int R>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
   __shared__ float sb[8 * SK_KB];  // [j][k] of the current K block
-  const int tid = threadIdx.x;
-  const int rl = tid >> 3, part = tid & 7;
-  const int64_t row = (int64_t)blockIdx.x * SK_ROWS + rl;
-  const bool row_ok = row < p.M;
-  float acc[8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row0 = (int64_t)blockIdx.x * SK_ROWS + wave * SK_RPW;
+  float acc[SK_RPW][R];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  for (int r = 0; r < SK_RPW; ++r)
+#pragma unroll
+    for (int j = 0; j < R; ++j) acc[r][j] = 0.f;
   for (int64_t k0 = 0; k0 < p.K; k0 += SK_KB) {
     const int kb = (int)(p.K - k0 < SK_KB ? p.K - k0 : SK_KB);
     __syncthreads();  // the previous block's B is no longer read
@@ -469,56 +473,63 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p, int R) {
       sb[j * SK_KB + k] = v;
     }
     __syncthreads();
-    if (row_ok) {
-      u32x4 a[SK_CHUNKS];
+    u32x4 a[SK_RPW][SK_CPL];
+#pragma unroll
+    for (int r = 0; r < SK_RPW; ++r) {
+      const int64_t row = row0 + r;
       const char* arow = p.A + (row * p.lda + k0) * 2;
 #pragma unroll
-      for (int q = 0; q < SK_CHUNKS; ++q) {
-        const int c = (part + 8 * q) * 8;  // first K value of the chunk within the block
-        a[q] = (u32x4){0, 0, 0, 0};
-        if (c + 8 <= kb) {
-          a[q] = ld16(arow + c * 2);
-        } else if (c < kb) {
-          for (int e = 0; e < 8; ++e)
-            if (c + e < kb) vec_set<2>(a[q], e, load_elem<2>(arow + (c + e) * 2));
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < SK_CHUNKS; ++q) {
-        const int c = (part + 8 * q) * 8;
-        if (c >= kb) break;
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = __uint_as_float((uint32_t)vec_get<2>(a[q], e) << 16);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (j < R) {
-            const float4 b0 = *(const float4*)(sb + j * SK_KB + c);
-            const float4 b1 = *(const float4*)(sb + j * SK_KB + c + 4);
-            acc[j] += x[0] * b0.x + x[1] * b0.y + x[2] * b0.z + x[3] * b0.w + x[4] * b1.x + x[5] * b1.y +
-                      x[6] * b1.z + x[7] * b1.w;
+      for (int q = 0; q < SK_CPL; ++q) {
+        const int c = (lane + 64 * q) * 8;  // first K value of the chunk within the block
+        a[r][q] = (u32x4){0, 0, 0, 0};
+        if (row < p.M) {
+          if (c + 8 <= kb) {
+            a[r][q] = ld16(arow + c * 2);
+          } else if (c < kb) {
+            for (int e = 0; e < 8; ++e)
+              if (c + e < kb) vec_set<2>(a[r][q], e, load_elem<2>(arow + (c + e) * 2));
           }
         }
       }
     }
-  }
-  // reduce over the 8 lanes of a row (consecutive lanes)
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    acc[j] += __shfl_xor(acc[j], 1);
-    acc[j] += __shfl_xor(acc[j], 2);
-    acc[j] += __shfl_xor(acc[j], 4);
-  }
-  if (row_ok && part < R) {
-    float v = acc[0];
+    for (int q = 0; q < SK_CPL; ++q) {
+      const int c = (lane + 64 * q) * 8;
+      if (c >= kb) continue;
 #pragma unroll
-    for (int j = 1; j < 8; ++j)
-      if (part == j) v = acc[j];
-    const int64_t col = p.n_base + part;
-    if (p.c_f32)
-      *(float*)(p.C + (row * p.ldc + col) * 4) = v;
-    else
-      *(__bf16*)(p.C + (row * p.ldc + col) * 2) = (__bf16)v;
+      for (int j = 0; j < R; ++j) {
+        const float4 b0 = *(const float4*)(sb + j * SK_KB + c);
+        const float4 b1 = *(const float4*)(sb + j * SK_KB + c + 4);
+#pragma unroll
+        for (int r = 0; r < SK_RPW; ++r) {
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = __uint_as_float((uint32_t)vec_get<2>(a[r][q], e) << 16);
+          acc[r][j] += x[0] * b0.x + x[1] * b0.y + x[2] * b0.z + x[3] * b0.w + x[4] * b1.x + x[5] * b1.y +
+                       x[6] * b1.z + x[7] * b1.w;
+        }
+      }
+    }
+  }
+  // reduce over the wave's 64 lanes; lane j (< R) writes column j of each row
+#pragma unroll
+  for (int r = 0; r < SK_RPW; ++r) {
+    const int64_t row = row0 + r;
+    float mine = 0.f;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      float v = acc[r][j];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+      if (lane == j) mine = v;
+    }
+    if (row < p.M && lane < R) {
+      const int64_t col = p.n_base + lane;
+      if (p.c_f32)
+        *(float*)(p.C + (row * p.ldc + col) * 4) = mine;
+      else
+        *(__bf16*)(p.C + (row * p.ldc + col) * 2) = (__bf16)mine;
+    }
   }
 }
 
@@ -585,7 +596,11 @@ extern "C" int gemm_bounded(const void* A, int64_t lda, const void* B, int64_t l
   if (rem > 8) return launch<EdgeCfg>("gemm_bounded/edge", p, rem, s);
   if (rem > 0) {
     const unsigned grid = (unsigned)((M + SK_ROWS - 1) / SK_ROWS);
-    launch_kernel("gemm_bounded/skinny", gemm_skinny_kernel, dim3(grid), dim3(256), 0, s, p, (int)rem);
+    switch (rem) {
+#define STG_SK(r) case r: launch_kernel("gemm_bounded/skinny", gemm_skinny_kernel<r>, dim3(grid), dim3(256), 0, s, p); break;
+      STG_SK(1) STG_SK(2) STG_SK(3) STG_SK(4) STG_SK(5) STG_SK(6) STG_SK(7) STG_SK(8)
+#undef STG_SK
+    }
     return check_launch(name);
   }
   return STG_OK;
