@@ -81,7 +81,9 @@ __device__ __forceinline__ void resolve_row(const RowParams& p, int64_t g, int64
   t_off = o_ax * p.t_ax_b + op * p.t_p_b + oq * p.t_q_b;
 }
 
-template <int ESIZE>
+// FULL: the row is whole 16-byte vectors and every column is in bounds
+// (lo_b = 0, hi_b = row_bytes), so no vector takes the element path.
+template <int ESIZE, bool FULL>
 __global__ __launch_bounds__(kThreads) void gather_rows_kernel(RowParams p) {
   constexpr int V = 16 / ESIZE;
   __shared__ int64_t s_src[kMaxRowsPerWg];
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(RowParams p) {
         const int b = (it - r * p.n_chunks) * 16;
         const int64_t so = s_src[r];
         if (so != kNoRow) {
-          if (b >= p.lo_b && b + 16 <= p.hi_b) {
+          if (FULL || (b >= p.lo_b && b + 16 <= p.hi_b)) {
             v[u] = ld16(p.a + so + b);
           } else if (b + 16 > p.lo_b && b < p.hi_b) {
 #pragma unroll
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(RowParams p) {
         const int r = (int)div_small((uint32_t)it, p.chunk_magic);
         const int b = (it - r * p.n_chunks) * 16;
         char* d = p.t + s_dst[r] + b;
-        if (b + 16 <= p.row_bytes) {
+        if (FULL || b + 16 <= p.row_bytes) {
           st16(d, v[u]);
         } else {
 #pragma unroll
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(RowParams p) {
   }
 }
 
-template <int ESIZE>
+template <int ESIZE, bool FULL>
 __global__ __launch_bounds__(kThreads) void scatter_rows_kernel(RowParams p) {
   constexpr int V = 16 / ESIZE;
   __shared__ int64_t s_dst[kMaxRowsPerWg];  // offset into a (the scatter destination)
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void scatter_rows_kernel(RowParams p) {
       if (it < items) {
         const int r = (int)div_small((uint32_t)it, p.chunk_magic);
         const int b = (it - r * p.n_chunks) * 16;
-        if (b >= p.lo_b && b + 16 <= p.hi_b) v[u] = ld16(p.t + s_src[r] + b);
+        if (FULL || (b >= p.lo_b && b + 16 <= p.hi_b)) v[u] = ld16(p.t + s_src[r] + b);
       }
     }
 #pragma unroll
@@ -188,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void scatter_rows_kernel(RowParams p) {
       if (it < items) {
         const int r = (int)div_small((uint32_t)it, p.chunk_magic);
         const int b = (it - r * p.n_chunks) * 16;
-        if (b >= p.lo_b && b + 16 <= p.hi_b) {
+        if (FULL || (b >= p.lo_b && b + 16 <= p.hi_b)) {
           st16(const_cast<char*>(p.a) + s_dst[r] + b, v[u]);
         } else if (b + 16 > p.lo_b && b < p.hi_b) {
           const char* src = p.t + s_src[r] + b;
@@ -257,21 +259,25 @@ const char* op_name(Op op) {
 
 int launch_rows(Op op, int esize, const RowParams& p, int64_t grid, hipStream_t s) {
   const dim3 g((unsigned)grid), b(kThreads);
+  const bool full = p.lo_b == 0 && p.hi_b == p.row_bytes && p.row_bytes % 16 == 0;
+#define STG_ROWS(K, E) \
+  full ? launch_kernel(op_name(op), K<E, true>, g, b, 0, s, p) : launch_kernel(op_name(op), K<E, false>, g, b, 0, s, p)
   if (op == Op::Scatter) {
     switch (esize) {
-      case 1: launch_kernel(op_name(op), scatter_rows_kernel<1>, g, b, 0, s, p); break;
-      case 2: launch_kernel(op_name(op), scatter_rows_kernel<2>, g, b, 0, s, p); break;
-      case 4: launch_kernel(op_name(op), scatter_rows_kernel<4>, g, b, 0, s, p); break;
-      default: launch_kernel(op_name(op), scatter_rows_kernel<8>, g, b, 0, s, p); break;
+      case 1: STG_ROWS(scatter_rows_kernel, 1); break;
+      case 2: STG_ROWS(scatter_rows_kernel, 2); break;
+      case 4: STG_ROWS(scatter_rows_kernel, 4); break;
+      default: STG_ROWS(scatter_rows_kernel, 8); break;
     }
   } else {
     switch (esize) {
-      case 1: launch_kernel(op_name(op), gather_rows_kernel<1>, g, b, 0, s, p); break;
-      case 2: launch_kernel(op_name(op), gather_rows_kernel<2>, g, b, 0, s, p); break;
-      case 4: launch_kernel(op_name(op), gather_rows_kernel<4>, g, b, 0, s, p); break;
-      default: launch_kernel(op_name(op), gather_rows_kernel<8>, g, b, 0, s, p); break;
+      case 1: STG_ROWS(gather_rows_kernel, 1); break;
+      case 2: STG_ROWS(gather_rows_kernel, 2); break;
+      case 4: STG_ROWS(gather_rows_kernel, 4); break;
+      default: STG_ROWS(gather_rows_kernel, 8); break;
     }
   }
+#undef STG_ROWS
   return check_launch(op_name(op));
 }
 
