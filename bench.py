@@ -173,8 +173,9 @@ def run_copy(stg, inputs, steps, warmup):
             raise RuntimeError(f"trace order mismatch: {kname} vs {label}")
         per[label] += ms / steps
     step_bytes = sum(algo.values())
+    cold = cold_entry(step_bytes, lambda: [fn() for _, fn in kernels])
     return {"w": w, "per_kernel_ms": per, "algo": algo, "step_ms": step_ms, "wall_ms": wall * 1e3 / steps,
-            "step_bytes": step_bytes}
+            "step_bytes": step_bytes, "cold": cold}
 
 
 def time_fn(fn, iters, warmup):
@@ -193,14 +194,69 @@ def time_fn(fn, iters, warmup):
     return s.elapsed_time(e) / iters
 
 
+_FLUSH = None
+
+
+def cold_call_ms(fn, calls=10):
+    """Per-call times with cold caches: before each call a 1 GiB buffer is
+    written (outside the timed region), which evicts L2 and the 256 MB
+    Infinity Cache; each call is bracketed by its own events and followed by
+    a synchronize.  Returns (median, min, max) in ms."""
+    import torch
+
+    global _FLUSH
+    if _FLUSH is None:
+        _FLUSH = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for i in range(calls):
+        _FLUSH.fill_(i & 0xFF)
+        s.record()
+        fn()
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e))
+    times.sort()
+    return times[len(times) // 2], times[0], times[-1]
+
+
+def cold_entry(nbytes, fn, calls=10):
+    med, lo, hi = cold_call_ms(fn, calls)
+    return {"median_ms": round(med, 5), "min_ms": round(lo, 5), "max_ms": round(hi, 5),
+            "GBps_at_median": round(gbs(nbytes, med), 1), "calls": calls}
+
+
+def traced_kernel_ms(stg, fn, steps):
+    """Per-kernel GPU durations (ms per call) of `fn`, from the library's
+    dispatch tracing (start/stop events inside each dispatch)."""
+    import torch
+
+    torch.cuda.synchronize()
+    stg.stg_trace_read()
+    stg.stg_trace_enable(True)
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    stg.stg_trace_enable(False)
+    kern = {}
+    for kname, kms in stg.stg_trace_read():
+        kern[kname] = kern.get(kname, 0.0) + kms / steps
+    return {k: round(v, 5) for k, v in kern.items()}
+
+
 def gbs(nbytes, ms):
     return nbytes / (ms * 1e-3) / 1e9
 
 
-def op_entry(workload, nbytes, ms):
+def op_entry(workload, nbytes, ms, kernel_ms=None):
     v = gbs(nbytes, ms)
-    return {"workload": workload, "value": round(v, 1), "unit": "GB/s", "ms": round(ms, 5),
-            "algorithmic_bytes": int(nbytes), "frac_of_hbm_peak": round(v / HBM_PEAK_GBS, 4)}
+    e = {"workload": workload, "value": round(v, 1), "unit": "GB/s", "ms": round(ms, 5),
+         "algorithmic_bytes": int(nbytes), "frac_of_hbm_peak": round(v / HBM_PEAK_GBS, 4)}
+    if kernel_ms:
+        kt = sum(kernel_ms.values())
+        e["kernel_ms"] = kernel_ms
+        e["kernel_GBps"] = round(gbs(nbytes, kt), 1)
+    return e
 
 
 def run_gather(stg, inputs, steps, warmup):
@@ -211,10 +267,14 @@ def run_gather(stg, inputs, steps, warmup):
     out = torch.empty((idx.numel(), w["a"].shape[1]), dtype=torch.float32, device="cuda:0")
     fn = lambda: stg.tile_gather(a, idx, w["tile_shape"], w["offset"], w["axis"], out=out)
     ms = time_fn(fn, steps, warmup)
+    kms = traced_kernel_ms(stg, fn, steps)
     n_valid = int(((w["indices"] >= 0) & (w["indices"] < w["a"].shape[0])).sum())
     row_b = w["a"].shape[1] * 4
     nbytes = idx.numel() * 4 + n_valid * row_b + idx.numel() * row_b
-    return op_entry("row gather fp32 (1024,256), 4096 int32 indices in [-64,1087], (64,256) tiles", nbytes, ms)
+    e = op_entry("row gather fp32 (1024,256), 4096 int32 indices in [-64,1087], (64,256) tiles", nbytes, ms, kms)
+    e["cold_cache"] = cold_entry(nbytes, fn)
+    e["note"] = "about 8 MB per call: bound by launch latency and host call overhead, not by HBM"
+    return e
 
 
 def run_masked(stg, inputs, steps, warmup):
@@ -226,19 +286,26 @@ def run_masked(stg, inputs, steps, warmup):
     out = torch.empty((idx.numel(), cols), dtype=torch.float32, device="cuda:0")
     fn = lambda: stg.tile_gather_masked(table, idx, gm, (64, cols), None, 0, w["padding_value"], out=out)
     ms_g = time_fn(fn, steps, warmup)
+    kms_g = traced_kernel_ms(stg, fn, steps)
     n_true = int(w["gmask"].sum())
     row_b = cols * 4
     g_bytes = idx.numel() * 5 + n_true * row_b + idx.numel() * row_b
+    cold_g = cold_entry(g_bytes, fn)
     del out
     vals, perm, sm = _dev(w["vals"]), _dev(w["perm"]), _dev(w["smask"])
     dst = table.clone()
     fn = lambda: stg.tile_scatter_masked(dst, perm, sm, (64, cols), vals, None, 0)
     ms_s = time_fn(fn, steps, warmup)  # rewrites the same rows each call: same traffic
+    kms_s = traced_kernel_ms(stg, fn, steps)
     s_true = int(w["smask"].sum())
     s_bytes = perm.numel() * 5 + 2 * s_true * row_b
-    return (op_entry("masked gather fp32 table (1048576,128), 4194304 indices, Bernoulli(0.9) mask, pad -1.0",
-                     g_bytes, ms_g),
-            op_entry("masked scatter fp32 (1048576,128) rows to a permutation, Bernoulli(0.5) mask", s_bytes, ms_s))
+    eg = op_entry("masked gather fp32 table (1048576,128), 4194304 indices, Bernoulli(0.9) mask, pad -1.0",
+                  g_bytes, ms_g, kms_g)
+    eg["cold_cache"] = cold_g
+    es = op_entry("masked scatter fp32 (1048576,128) rows to a permutation, Bernoulli(0.5) mask", s_bytes, ms_s,
+                  kms_s)
+    es["cold_cache"] = cold_entry(s_bytes, fn)
+    return eg, es
 
 
 def run_ragged(stg, inputs, steps, warmup):
@@ -254,9 +321,12 @@ def run_ragged(stg, inputs, steps, warmup):
         out = torch.empty((len(ri), 128, 128), dtype=torch.bfloat16, device="cuda:0")
         fn = lambda: stg.ragged_tile_load(X, md, group, 128, 128, *tri, out=out)
         ms = time_fn(fn, steps, warmup)
+        kms = traced_kernel_ms(stg, fn, steps)
         nbytes = w["X"].nbytes + out.numel() * 2 + len(ri) * 12
-        res.append(op_entry(f"ragged varlen load bf16 ({w['X'].shape[0]},8,128), 64 seqs, BM=128, group={group}",
-                            nbytes, ms))
+        e = op_entry(f"ragged varlen load bf16 ({w['X'].shape[0]},8,128), 64 seqs, BM=128, group={group}",
+                     nbytes, ms, kms)
+        e["cold_cache"] = cold_entry(nbytes, fn)
+        res.append(e)
         del out
     return res
 
@@ -274,22 +344,16 @@ def run_gemm(stg, inputs, steps, warmup):
     except Exception as e:  # reported, not hidden
         return {"workload": "bounded GEMM bf16 (8191,8193,4097)", "error": str(e)}
     ms = time_fn(fn, steps, warmup)
-    torch.cuda.synchronize()
-    stg.stg_trace_read()
-    stg.stg_trace_enable(True)
-    for _ in range(steps):
-        fn()
-    torch.cuda.synchronize()
-    stg.stg_trace_enable(False)
-    kern = {}
-    for kname, kms in stg.stg_trace_read():
-        kern[kname] = kern.get(kname, 0.0) + kms / steps
+    kern = traced_kernel_ms(stg, fn, steps)
     flop = 2.0 * M * N * K
     tf = flop / (ms * 1e-3) / 1e12
+    cmed, clo, chi = cold_call_ms(fn)
     return {"workload": "bounded GEMM bf16 A(8191,4097) B(4097,8193), fp32 accumulate, bf16 clipped output",
             "value": round(tf, 1), "unit": "TFLOP/s", "ms": round(ms, 4), "flop": flop,
             "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
-            "kernel_ms": {k: round(v, 4) for k, v in kern.items()}}
+            "kernel_ms": kern,
+            "cold_cache": {"median_ms": round(cmed, 4), "min_ms": round(clo, 4), "max_ms": round(chi, 4),
+                           "TFLOPs_at_median": round(flop / (cmed * 1e-3) / 1e12, 1), "calls": 10}}
 
 
 def run_calibration(steps):
@@ -402,6 +466,7 @@ def main():
             "spinup_ms_before_warmup": args.spinup_ms,
             "per_kernel_ms": {k: round(v, 5) for k, v in per.items()},
             "dispatch_gaps_ms_per_step": round(head["step_ms"] - sum(per.values()), 5),
+            "cold_cache_step": head["cold"],
         },
         "roofline": {
             "bound": "hbm",
