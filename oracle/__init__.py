@@ -78,6 +78,7 @@ def _load():
         "orc_tile_store_clipped": (None, [_P, _I32, _I64, _I64, _I64, _I64, _P]),
         "orc_ragged_schedule": (_I64, [_P, _I64, _I32, _I32, _P, _P, _P]),
         "orc_ragged_tile_load": (None, [_P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _P]),
+        "orc_ragged_tile_store": (None, [_P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _P]),
         "orc_bf16_to_f64": (ctypes.c_double, [ctypes.c_uint16]),
         "orc_gemm_f64": (None, [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64]),
         "orc_gemm_sample_f64": (None, [_P, _I64, _P, _I64, _I64, _P, _P, _I64, _P]),
@@ -235,6 +236,23 @@ def ragged_tile_load(X, middle_dim: int, group: int, BM: int, BN: int, col0: int
     out = np.empty((n, BM, BN), dtype=X.dtype)
     _load().orc_ragged_tile_load(_ptr(X), X.itemsize, X.shape[0], middle_dim, group, X.shape[2], BM, BN, col0,
                                  _ptr(ri), _ptr(dyn), _ptr(mi), n, _ptr(out))
+    return out
+
+
+def ragged_tile_store(tiles, X, middle_dim: int, group: int, col0: int, ri, dyn, mi) -> np.ndarray:
+    """tiles (n_tiles, BM, BN) into a copy of X (total_rows, middle_dim*group,
+    depth); returns the updated copy (elements no tile writes keep X's bits)."""
+    tiles = np.ascontiguousarray(tiles)
+    out = np.array(X, copy=True, order="C")
+    assert out.ndim == 3 and out.shape[1] == middle_dim * group and tiles.ndim == 3
+    assert tiles.dtype == out.dtype
+    ri = np.ascontiguousarray(ri, dtype=np.uint32)
+    dyn = np.ascontiguousarray(dyn, dtype=np.uint32)
+    mi = np.ascontiguousarray(mi, dtype=np.uint32)
+    n, BM, BN = tiles.shape
+    assert ri.size == n and dyn.size == n and mi.size == n
+    _load().orc_ragged_tile_store(_ptr(tiles), out.itemsize, out.shape[0], middle_dim, group, out.shape[2], BM, BN,
+                                  col0, _ptr(ri), _ptr(dyn), _ptr(mi), n, _ptr(out))
     return out
 
 

@@ -273,6 +273,27 @@ void orc_ragged_tile_load(const void* X, int32_t esize, int64_t total_rows, int3
 
 /* ---- bounded GEMM reference ------------------------------------------- */
 
+void orc_ragged_tile_store(const void* tiles_in, int32_t esize, int64_t total_rows, int32_t middle_dim,
+                           int32_t group, int32_t depth, int32_t BM, int32_t BN, int32_t col0,
+                           const uint32_t* ragged_idx, const uint32_t* dynamic_dim,
+                           const uint32_t* middle_idx, int64_t n_tiles, void* X) {
+  const int32_t bm_seq = BM / group;
+  const int64_t heads = (int64_t)middle_dim * group; /* X viewed as (rows, heads, depth) */
+  const char* in = (const char*)tiles_in;
+  char* x = (char*)X;
+  for (int64_t k = 0; k < n_tiles; ++k) {
+    const int64_t ri = ragged_idx[k], dyn = dynamic_dim[k], mi = middle_idx[k];
+    for (int32_t s = 0; s < bm_seq; ++s)
+      for (int32_t g = 0; g < group; ++g)
+        for (int32_t c = 0; c < BN; ++c) {
+          const int64_t row = ri + s, head = mi * group + g, col = (int64_t)col0 + c;
+          if (s < dyn && row < total_rows && col < depth && mi < middle_dim)
+            memcpy(x + ((row * heads + head) * depth + col) * (int64_t)esize,
+                   in + ((k * BM + (int64_t)s * group + g) * BN + c) * (int64_t)esize, (size_t)esize);
+        }
+  }
+}
+
 double orc_bf16_to_f64(uint16_t h) {
   uint32_t bits = (uint32_t)h << 16;
   float f;

@@ -128,6 +128,22 @@ void orc_ragged_tile_load(const void* X, int32_t esize, int64_t total_rows, int3
                           const uint32_t* ragged_idx, const uint32_t* dynamic_dim,
                           const uint32_t* middle_idx, int64_t n_tiles, void* tiles_out);
 
+/* Ragged varlen 3-D tile store, the store direction of the same descriptor
+ * (Mojo RaggedTMA3DTile page: async_copy_from_col and async_copy_batched --
+ * a copy from the shared-memory tile to global memory of dynamic_dim rows
+ * (sequence positions when group > 1) at ragged_idx for head middle_idx,
+ * with the part of the box that overhangs the array masked off).  tiles is
+ * dense (n_tiles, BM, BN); X is contiguous (total_rows, middle_dim*group,
+ * depth).  For tile k, s < BM_seq, g < group, c < BN, in tile order:
+ *   if s < dyn and ri+s < total_rows and col0+c < depth and mi < middle_dim:
+ *     X[ri+s][mi*group + g][col0+c] = tiles[k][s*group + g][c]
+ * Every other element of X is left as it was (tiles that write the same
+ * element: the later tile wins here; the product leaves that undefined). */
+void orc_ragged_tile_store(const void* tiles_in, int32_t esize, int64_t total_rows, int32_t middle_dim,
+                           int32_t group, int32_t depth, int32_t BM, int32_t BN, int32_t col0,
+                           const uint32_t* ragged_idx, const uint32_t* dynamic_dim,
+                           const uint32_t* middle_idx, int64_t n_tiles, void* X);
+
 /* Decode one bf16 bit pattern to double (exact: bf16 is the top half of
  * an IEEE binary32). */
 double orc_bf16_to_f64(uint16_t h);

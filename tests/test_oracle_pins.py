@@ -491,6 +491,79 @@ def test_ragged_rows_past_total_are_zero(orc):
     np.testing.assert_array_equal(np_ragged(X, 2, 1, 4, 4, 0, [0], [3], [2]), 0)
 
 
+@pytest.mark.parametrize("group", [1, 4])
+def test_ragged_store_multiple_of_bm_is_inverse_reshape(orc, group):
+    """Every sequence a multiple of BM_seq: the tiles of the schedule, stored,
+    are X rearranged from (blocks, head block, position, group, depth) back to
+    (rows, heads, depth) -- the inverse of the load's reshape."""
+    rng = np.random.default_rng(61)
+    bm, heads, depth = 8, 8, 16
+    bm_seq, md = bm // group, heads // group
+    lens = np.array([bm_seq * 2, bm_seq, bm_seq * 3], dtype=np.int64)
+    rows = int(lens.sum())
+    tiles = rng.integers(1, 60000, (rows // bm_seq * md, bm, depth)).astype(np.uint16)
+    ri, dyn, mi = orc.ragged_schedule(lens, bm_seq, md)
+    got = orc.ragged_tile_store(tiles, np.zeros((rows, heads, depth), np.uint16), md, group, 0, ri, dyn, mi)
+    want = tiles.reshape(-1, md, bm_seq, group, depth).transpose(0, 2, 1, 3, 4).reshape(rows, heads, depth)
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("group", [1, 2, 4])
+def test_ragged_store_load_round_trips(orc, group):
+    """Over a schedule that covers every row once: store(load(X)) rebuilds X
+    from a sentinel-filled array, and load(store(T)) keeps exactly the tile
+    elements that have a place in X (rows below dynamic_dim, columns inside
+    depth) and reads zero for the others."""
+    rng = np.random.default_rng(70 + group)
+    heads, depth, BM = 8, 24, 16
+    bm_seq, md = BM // group, heads // group
+    lens = rng.integers(1, 40, 7).astype(np.int64)
+    rows = int(lens.sum())
+    X = rng.integers(1, 60000, (rows, heads, depth)).astype(np.uint16)
+    ri, dyn, mi = orc.ragged_schedule(lens, bm_seq, md)
+    sentinel = np.full_like(X, 0xFFFF)
+    tiles = orc.ragged_tile_load(X, md, group, BM, depth, 0, ri, dyn, mi)
+    np.testing.assert_array_equal(orc.ragged_tile_store(tiles, sentinel, md, group, 0, ri, dyn, mi), X)
+    # two column windows, the second overhanging depth by 8 columns
+    parts = sentinel
+    for col0 in (0, 16):
+        t = orc.ragged_tile_load(X, md, group, BM, 16, col0, ri, dyn, mi)
+        parts = orc.ragged_tile_store(t, parts, md, group, col0, ri, dyn, mi)
+    np.testing.assert_array_equal(parts, X)
+    T = rng.integers(1, 60000, (len(ri), BM, 16)).astype(np.uint16)
+    back = orc.ragged_tile_load(orc.ragged_tile_store(T, sentinel, md, group, 16, ri, dyn, mi), md, group, BM, 16, 16,
+                                ri, dyn, mi)
+    s_of_row = np.arange(BM) // group
+    keep = (s_of_row[None, :, None] < dyn[:, None, None].astype(np.int64)) & (np.arange(16)[None, None, :] < 8)
+    np.testing.assert_array_equal(back, np.where(keep, T, 0))
+
+
+def test_ragged_store_writes_nothing_outside(orc):
+    """Hand-worked case: X (5 rows, 2 heads, 4 columns), one tile of BM 4 at
+    ragged_idx 1 with dynamic_dim 2 for head 1 writes X[1:3, 1, :] only; rows
+    past total_rows, a head index past middle_dim and columns past depth are
+    never written."""
+    X = np.arange(40, dtype=np.int32).reshape(5, 2, 4)
+    t = -np.arange(1, 17, dtype=np.int32).reshape(1, 4, 4)
+    got = orc.ragged_tile_store(t, X, 2, 1, 0, [1], [2], [1])
+    want = X.copy()
+    want[1, 1] = [-1, -2, -3, -4]
+    want[2, 1] = [-5, -6, -7, -8]
+    np.testing.assert_array_equal(got, want)
+    # dynamic_dim 4 at ragged_idx 3: rows 3, 4 exist, rows 5, 6 do not
+    got = orc.ragged_tile_store(t, X, 2, 1, 0, [3], [4], [0])
+    want = X.copy()
+    want[3, 0] = [-1, -2, -3, -4]
+    want[4, 0] = [-5, -6, -7, -8]
+    np.testing.assert_array_equal(got, want)
+    # head 2 of middle_dim 2: nothing; col0 2 with BN 4: only columns 2, 3
+    np.testing.assert_array_equal(orc.ragged_tile_store(t, X, 2, 1, 0, [0], [4], [2]), X)
+    got = orc.ragged_tile_store(t, X, 2, 1, 2, [0], [1], [0])
+    want = X.copy()
+    want[0, 0, 2:] = [-1, -2]
+    np.testing.assert_array_equal(got, want)
+
+
 # ---------------------------------------------------------------------------
 # bounded GEMM reference
 # ---------------------------------------------------------------------------
