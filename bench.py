@@ -327,7 +327,20 @@ def run_ragged(stg, inputs, steps, warmup):
                      nbytes, ms, kms)
         e["cold_cache"] = cold_entry(nbytes, fn)
         res.append(e)
-        del out
+        # store direction: the loaded tiles back into a copy of X (every call
+        # rewrites the same elements); the schedule covers every row and head
+        # once, so the valid elements are all of X, read from the tiles once
+        # and written once
+        dst = X.clone()
+        fn = lambda: stg.ragged_tile_store(out, dst, md, group, *tri)
+        ms = time_fn(fn, steps, warmup)
+        kms = traced_kernel_ms(stg, fn, steps)
+        nbytes = 2 * w["X"].nbytes + len(ri) * 12
+        e = op_entry(f"ragged varlen store bf16 ({w['X'].shape[0]},8,128), 64 seqs, BM=128, group={group}",
+                     nbytes, ms, kms)
+        e["cold_cache"] = cold_entry(nbytes, fn)
+        res.append(e)
+        del out, dst
     return res
 
 
@@ -429,7 +442,8 @@ def main():
         print("[bench] masked gather/scatter done", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
     if "ragged" in only:
-        ops["ragged_group1"], ops["ragged_group4"] = run_ragged(stg, inputs, args.steps, args.warmup)
+        (ops["ragged_group1"], ops["ragged_store_group1"], ops["ragged_group4"],
+         ops["ragged_store_group4"]) = run_ragged(stg, inputs, args.steps, args.warmup)
         print("[bench] ragged done", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
     if "gemm" in only:

@@ -189,6 +189,27 @@ int ragged_tile_load(const void* src, int32_t dtype, int64_t total_rows, int32_t
                      const uint32_t* middle_idx, int64_t n_tiles, void* tiles_out,
                      void* stream);
 
+/* Ragged varlen 3-D tile store, the store direction of the same descriptor
+ * (Mojo, layout.tma_async.RaggedTMA3DTile: async_copy_from_col and
+ * async_copy_batched copy a tile from shared memory to global memory -- only
+ * dynamic_dim rows (sequence positions when group > 1) at ragged_idx for head
+ * middle_idx, with the part of the box that overhangs the array masked off).
+ * tiles_in is a device buffer (n_tiles, BM, BN) of `dtype`; dst is contiguous
+ * (total_rows, middle_dim*group, depth).  With BM_seq = BM / group, for tile
+ * k, s < BM_seq, g < group, c < BN:
+ *   if s < dynamic_dim[k] and ragged_idx[k]+s < total_rows and col0+c < depth
+ *      and middle_idx[k] < middle_dim:
+ *     dst[ragged_idx[k]+s][middle_idx[k]*group + g][col0+c] = tiles_in[k][s*group + g][c]
+ * No other element of dst is written (tile rows at or past dynamic_dim, columns
+ * past depth, rows past total_rows, a middle_idx >= middle_dim).  Two tiles
+ * that write the same element: undefined (the schedule of
+ * ragged_tile_schedule never does).  Host checks, triples and error codes as
+ * for ragged_tile_load; tiles_in must not overlap dst. */
+int ragged_tile_store(const void* tiles_in, int32_t dtype, int64_t total_rows, int32_t middle_dim,
+                      int32_t group, int32_t depth, int32_t BM, int32_t BN, int32_t col0,
+                      const uint32_t* ragged_idx, const uint32_t* dynamic_dim,
+                      const uint32_t* middle_idx, int64_t n_tiles, void* dst, void* stream);
+
 /* Bounded-edge GEMM C = A . B (cuTile.jl Operations, muladd: bf16 operands
  * accumulate in f32; Tylo.jl Boundary tiles, "Accumulator stores and GEMM":
  * ceiling-division output grid and K loop, zero-filled edge stages, and an

@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     gemm_bounded,
     load_library,
     ragged_tile_load,
+    ragged_tile_store,
     ragged_tile_schedule,
     stg_tile_grid,
     stg_trace_enable,

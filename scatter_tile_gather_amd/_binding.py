@@ -51,6 +51,7 @@ _SIGNATURES = {
     "tile_store_clipped": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _TP, _P]),
     "ragged_tile_schedule": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _I64P]),
     "ragged_tile_load": (ctypes.c_int, [_P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _P, _P]),
+    "ragged_tile_store": (ctypes.c_int, [_P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _P, _P]),
     "gemm_bounded": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _I32, _P]),
     "stg_trace_enable": (ctypes.c_int, [ctypes.c_int]),
     "stg_trace_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float)]),
@@ -287,6 +288,30 @@ def ragged_tile_load(src, middle_dim: int, group: int, BM: int, BN: int, ragged_
                                 BN, col0, ragged_idx.data_ptr(), dynamic_dim.data_ptr(), middle_idx.data_ptr(), n,
                                 out.data_ptr(), _stream(stream)))
     return out
+
+
+def ragged_tile_store(tiles, dst, middle_dim: int, group: int, ragged_idx, dynamic_dim, middle_idx, col0: int = 0,
+                      stream=None):
+    """tiles: (n_tiles, BM, BN) on the device; dst: contiguous (total_rows,
+    middle_dim*group, depth) of the same dtype, written in place; triples:
+    device int32/uint32-valued tensors.  Returns dst."""
+    torch = _torch()
+    lib = load_library()
+    _on_gpu(tiles, "tiles")
+    _on_gpu(dst, "dst")
+    if dst.dim() != 3 or not dst.is_contiguous() or dst.shape[1] != middle_dim * group:
+        raise ValueError("dst must be contiguous (total_rows, middle_dim*group, depth)")
+    if tiles.dim() != 3 or not tiles.is_contiguous() or tiles.dtype != dst.dtype:
+        raise ValueError("tiles must be a contiguous (n_tiles, BM, BN) tensor of dst's dtype")
+    n, BM, BN = tiles.shape
+    for t, nm in ((ragged_idx, "ragged_idx"), (dynamic_dim, "dynamic_dim"), (middle_idx, "middle_idx")):
+        _on_gpu(t, nm)
+        if t.dtype not in (torch.int32, torch.uint32) or not t.is_contiguous() or t.numel() != n:
+            raise ValueError(f"{nm} must be a contiguous 32-bit integer tensor with one entry per tile")
+    _check(lib.ragged_tile_store(tiles.data_ptr(), _dtype_code(dst), dst.shape[0], middle_dim, group, dst.shape[2], BM,
+                                 BN, col0, ragged_idx.data_ptr(), dynamic_dim.data_ptr(), middle_idx.data_ptr(), n,
+                                 dst.data_ptr(), _stream(stream)))
+    return dst
 
 
 def gemm_bounded(A, B, out=None, out_dtype=None, stream=None):

@@ -1,12 +1,15 @@
-// Ragged varlen 3-D tile load.
+// Ragged varlen 3-D tile load and store.
 //
 // Semantics (Mojo, layout.tma_async.RaggedTMA3DTile: description, parameters
 // BM / BN / middle_dim / group, comptime BM_seq, and the per-copy arguments
-// ragged_idx / dynamic_dim / middle_idx): sequences are packed row after row
-// with no padding; a tile of BM = BM_seq * group rows covers BM_seq consecutive
-// sequence positions starting at ragged_idx for head middle_idx (group heads
-// fused per position when group > 1), and only dynamic_dim of those positions
-// belong to the sequence -- the rest of the tile is zero.
+// ragged_idx / dynamic_dim / middle_idx of async_copy_from_col and
+// async_copy_batched): sequences are packed row after row with no padding; a
+// tile of BM = BM_seq * group rows covers BM_seq consecutive sequence
+// positions starting at ragged_idx for head middle_idx (group heads fused per
+// position when group > 1), and only dynamic_dim of those positions belong to
+// the sequence.  The load writes the rest of the tile as zero; the store
+// writes only the positions that belong, and no column past depth (the page
+// masks the part of the box that overhangs the array).
 //
 // The page reaches this with a TMA descriptor whose outermost coordinate folds
 // the (rows, middle_dim) selectors into one, (ragged_idx + dynamic_dim) *
@@ -14,8 +17,9 @@
 // so that the box's out-of-range rows are the ones past the sequence.  gfx950
 // has no TMA; the equivalent here is a buffer resource rebased at the tile's
 // first row with num_records ending at the last row of the array: every 16-byte
-// vector of an invalid position is given an offset past num_records and loads
-// zeros, so no storage in front of the pointer is needed.
+// vector of an invalid position is given an offset past num_records, so a load
+// returns zeros and a store is dropped, and no storage in front of the pointer
+// is needed.
 //
 // One workgroup per tile; a wavefront moves 64 x 16 bytes per instruction.
 // With group > 1 the `group` heads of one position are adjacent in memory, so
@@ -29,8 +33,8 @@ constexpr int kThreads = 256;
 constexpr int kUnroll = 8;
 
 struct RaggedParams {
-  const char* src;
-  char* out;
+  char* x;      // the packed 3-D array (load: source, store: destination)
+  char* tiles;  // dense (n_tiles, BM, BN) tile buffer (load: output, store: input)
   const uint32_t* ragged_idx;
   const uint32_t* dynamic_dim;
   const uint32_t* middle_idx;
@@ -47,6 +51,28 @@ struct RaggedParams {
   int32_t items;      // BM * cpr
 };
 
+// Tile k's view of the packed array: the positions that exist (below
+// dynamic_dim, inside the array, valid head), the address of its first element
+// and a buffer resource over the rest of the array from there.
+struct TileView {
+  int64_t dyn;
+  char* base;
+  __amdgpu_buffer_rsrc_t rs;
+};
+
+__device__ __forceinline__ TileView tile_view(const RaggedParams& p, int64_t k) {
+  const int64_t ri = p.ragged_idx[k];
+  const int64_t mi = p.middle_idx[k];
+  int64_t dyn = p.dynamic_dim[k];
+  if (ri + dyn > p.total_rows) dyn = p.total_rows > ri ? p.total_rows - ri : 0;
+  if (mi >= p.middle_dim) dyn = 0;
+  const int64_t base_row = ri < p.total_rows ? ri : 0;
+  char* base = p.x + base_row * p.row_b + mi * p.group * p.head_b + p.col0_b;
+  int64_t avail = (p.total_rows - base_row) * p.row_b - mi * p.group * p.head_b - p.col0_b;
+  if (dyn <= 0 || avail < 0) avail = 0;
+  return {dyn, base, make_rsrc(base, (uint32_t)(avail < (int64_t)kOOB ? avail : (int64_t)kOOB - 1))};
+}
+
 // FULL: every output row is whole 16-byte vectors, all backed by source
 // columns (BN * esize a multiple of 16, col0 + BN <= depth), and the tile is
 // a whole number of workgroup passes, so no vector needs the element path or
@@ -56,18 +82,11 @@ template <int ESIZE, bool FULL>
 __global__ __launch_bounds__(kThreads) void ragged_load_kernel(RaggedParams p) {
   constexpr int V = 16 / ESIZE;
   const int64_t k = blockIdx.x;
-  const int64_t ri = p.ragged_idx[k];
-  const int64_t mi = p.middle_idx[k];
-  int64_t dyn = p.dynamic_dim[k];
-  // positions that exist: below dynamic_dim, inside the array, valid head
-  if (ri + dyn > p.total_rows) dyn = p.total_rows > ri ? p.total_rows - ri : 0;
-  if (mi >= p.middle_dim) dyn = 0;
-  const int64_t base_row = ri < p.total_rows ? ri : 0;
-  const char* base = p.src + base_row * p.row_b + mi * p.group * p.head_b + p.col0_b;
-  int64_t avail = (p.total_rows - base_row) * p.row_b - mi * p.group * p.head_b - p.col0_b;
-  if (dyn <= 0 || avail < 0) avail = 0;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, (uint32_t)(avail < (int64_t)kOOB ? avail : (int64_t)kOOB - 1));
-  char* out = p.out + k * p.tile_b;
+  const TileView tv = tile_view(p, k);
+  const int64_t dyn = tv.dyn;
+  const char* base = tv.base;
+  const __amdgpu_buffer_rsrc_t rs = tv.rs;
+  char* out = p.tiles + k * p.tile_b;
   for (int b0 = 0; b0 < p.items; b0 += kThreads * kUnroll) {
     u32x4 v[kUnroll];
 #pragma unroll
@@ -111,18 +130,66 @@ __global__ __launch_bounds__(kThreads) void ragged_load_kernel(RaggedParams p) {
   }
 }
 
-}  // namespace
-}  // namespace stg
+// Store direction: tile vector `it` (row j = s * group + g, bytes b..b+15 of
+// the row) goes to position s, head slot g of the tile's view when s < dyn;
+// only those vectors are read from the tile.  A vector with no place in the
+// array gets an offset past num_records and its store is dropped; a vector
+// that crosses the end of depth is written element by element up to it.
+// FULL as for the load.
+template <int ESIZE, bool FULL>
+__global__ __launch_bounds__(kThreads) void ragged_store_kernel(RaggedParams p) {
+  constexpr int V = 16 / ESIZE;
+  const int64_t k = blockIdx.x;
+  const TileView tv = tile_view(p, k);
+  const char* in = p.tiles + k * p.tile_b;
+  for (int b0 = 0; b0 < p.items; b0 += kThreads * kUnroll) {
+    u32x4 v[kUnroll];
+    uint32_t off[kUnroll];  // byte offset of the vector in the view, kOOB when it has no place
+    int bb[kUnroll];        // byte of the vector within its row; -1 when nothing is stored
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int it = b0 + u * kThreads + threadIdx.x;
+      off[u] = kOOB;
+      bb[u] = -1;
+      v[u] = (u32x4){0, 0, 0, 0};
+      if (FULL || it < p.items) {
+        const int j = (int)div_small((uint32_t)it, p.cpr_magic);
+        const int b = (it - j * p.cpr) * 16;
+        const int s = (int)div_small((uint32_t)j, p.group_magic);
+        const int g = j - s * p.group;
+        if (s < tv.dyn && b < p.valid_b) {
+          bb[u] = b;
+          off[u] = (uint32_t)(s * p.row_b + g * p.head_b) + b;
+          const char* src = in + (int64_t)j * p.out_row_b + b;
+          if (FULL || b + 16 <= p.out_row_b) {
+            v[u] = ld16(src);
+          } else {
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+              if (b + e * ESIZE < p.out_row_b) vec_set<ESIZE>(v[u], e, load_elem<ESIZE>(src + e * ESIZE));
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const bool full = bb[u] >= 0 && (FULL || bb[u] + 16 <= p.valid_b);
+      __builtin_amdgcn_raw_buffer_store_b128(v[u], tv.rs, full ? off[u] : kOOB, 0, 0);
+      if (!FULL && bb[u] >= 0 && !full) {
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+          if (bb[u] + e * ESIZE < p.valid_b) store_elem<ESIZE>(tv.base + off[u] + e * ESIZE, vec_get<ESIZE>(v[u], e));
+      }
+    }
+  }
+}
 
-using namespace stg;
-
-extern "C" int ragged_tile_load(const void* src, int32_t dtype, int64_t total_rows, int32_t middle_dim,
-                                int32_t group, int32_t depth, int32_t BM, int32_t BN, int32_t col0,
-                                const uint32_t* ragged_idx, const uint32_t* dynamic_dim,
-                                const uint32_t* middle_idx, int64_t n_tiles, void* tiles_out, void* stream) {
-  clear_error();
-  const char* name = "ragged_tile_load";
-  const int es = dtype_size(dtype);
+// Shared argument checks and parameter setup of both directions.
+int ragged_setup(const char* name, const void* x, int32_t dtype, int64_t total_rows, int32_t middle_dim,
+                 int32_t group, int32_t depth, int32_t BM, int32_t BN, int32_t col0, const uint32_t* ragged_idx,
+                 const uint32_t* dynamic_dim, const uint32_t* middle_idx, int64_t n_tiles, const void* tiles,
+                 RaggedParams& p, int& es) {
+  es = dtype_size(dtype);
   if (!es) return fail(STG_ERR_UNSUPPORTED, "%s: unknown dtype %d", name, dtype);
   if (total_rows < 0 || n_tiles < 0) return fail(STG_ERR_INVALID, "%s: negative size", name);
   if (middle_dim < 1 || group < 1 || depth < 1 || BM < 1 || BN < 1)
@@ -130,12 +197,12 @@ extern "C" int ragged_tile_load(const void* src, int32_t dtype, int64_t total_ro
   if (BM % group) return fail(STG_ERR_INVALID, "%s: BM %d is not a multiple of group %d", name, BM, group);
   if (col0 < 0 || col0 >= depth) return fail(STG_ERR_INVALID, "%s: col0 %d not in [0, depth)", name, col0);
   if (n_tiles == 0) return STG_OK;
-  if (!tiles_out || !ragged_idx || !dynamic_dim || !middle_idx)
+  if (!tiles || !ragged_idx || !dynamic_dim || !middle_idx)
     return fail(STG_ERR_INVALID, "%s: null tile buffer or tile triples", name);
-  if (total_rows > 0 && !src) return fail(STG_ERR_INVALID, "%s: null src", name);
-  RaggedParams p{};
-  p.src = (const char*)src;
-  p.out = (char*)tiles_out;
+  if (total_rows > 0 && !x) return fail(STG_ERR_INVALID, "%s: null packed array", name);
+  p = RaggedParams{};
+  p.x = (char*)x;
+  p.tiles = (char*)tiles;
   p.ragged_idx = ragged_idx;
   p.dynamic_dim = dynamic_dim;
   p.middle_idx = middle_idx;
@@ -159,17 +226,62 @@ extern "C" int ragged_tile_load(const void* src, int32_t dtype, int64_t total_ro
   p.items = BM * p.cpr;
   p.cpr_magic = div_magic((uint32_t)p.cpr);
   p.group_magic = div_magic((uint32_t)group);
+  return STG_OK;
+}
+
+bool ragged_full(const RaggedParams& p) {
+  return p.out_row_b % 16 == 0 && p.valid_b == p.out_row_b && p.items % (kThreads * kUnroll) == 0;
+}
+
+}  // namespace
+}  // namespace stg
+
+using namespace stg;
+
+extern "C" int ragged_tile_load(const void* src, int32_t dtype, int64_t total_rows, int32_t middle_dim,
+                                int32_t group, int32_t depth, int32_t BM, int32_t BN, int32_t col0,
+                                const uint32_t* ragged_idx, const uint32_t* dynamic_dim,
+                                const uint32_t* middle_idx, int64_t n_tiles, void* tiles_out, void* stream) {
+  clear_error();
+  const char* name = "ragged_tile_load";
+  RaggedParams p;
+  int es, rc;
+  if ((rc = ragged_setup(name, src, dtype, total_rows, middle_dim, group, depth, BM, BN, col0, ragged_idx,
+                         dynamic_dim, middle_idx, n_tiles, tiles_out, p, es)) || n_tiles == 0)
+    return rc;
   const hipStream_t s = as_stream(stream);
   const dim3 grid((unsigned)n_tiles), block(kThreads);
-  const bool full = p.out_row_b % 16 == 0 && p.valid_b == p.out_row_b && p.items % (kThreads * kUnroll) == 0;
-#define STG_RAGGED(E)                                                              \
-  full ? launch_kernel(name, ragged_load_kernel<E, true>, grid, block, 0, s, p)   \
-       : launch_kernel(name, ragged_load_kernel<E, false>, grid, block, 0, s, p)
+  const bool full = ragged_full(p);
+#define STG_RAGGED(K, E) \
+  full ? launch_kernel(name, K<E, true>, grid, block, 0, s, p) : launch_kernel(name, K<E, false>, grid, block, 0, s, p)
   switch (es) {
-    case 1: STG_RAGGED(1); break;
-    case 2: STG_RAGGED(2); break;
-    case 4: STG_RAGGED(4); break;
-    default: STG_RAGGED(8); break;
+    case 1: STG_RAGGED(ragged_load_kernel, 1); break;
+    case 2: STG_RAGGED(ragged_load_kernel, 2); break;
+    case 4: STG_RAGGED(ragged_load_kernel, 4); break;
+    default: STG_RAGGED(ragged_load_kernel, 8); break;
+  }
+  return check_launch(name);
+}
+
+extern "C" int ragged_tile_store(const void* tiles_in, int32_t dtype, int64_t total_rows, int32_t middle_dim,
+                                 int32_t group, int32_t depth, int32_t BM, int32_t BN, int32_t col0,
+                                 const uint32_t* ragged_idx, const uint32_t* dynamic_dim,
+                                 const uint32_t* middle_idx, int64_t n_tiles, void* dst, void* stream) {
+  clear_error();
+  const char* name = "ragged_tile_store";
+  RaggedParams p;
+  int es, rc;
+  if ((rc = ragged_setup(name, dst, dtype, total_rows, middle_dim, group, depth, BM, BN, col0, ragged_idx,
+                         dynamic_dim, middle_idx, n_tiles, tiles_in, p, es)) || n_tiles == 0)
+    return rc;
+  const hipStream_t s = as_stream(stream);
+  const dim3 grid((unsigned)n_tiles), block(kThreads);
+  const bool full = ragged_full(p);
+  switch (es) {
+    case 1: STG_RAGGED(ragged_store_kernel, 1); break;
+    case 2: STG_RAGGED(ragged_store_kernel, 2); break;
+    case 4: STG_RAGGED(ragged_store_kernel, 4); break;
+    default: STG_RAGGED(ragged_store_kernel, 8); break;
   }
 #undef STG_RAGGED
   return check_launch(name);

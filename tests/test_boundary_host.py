@@ -176,3 +176,25 @@ def test_trace_host_paths(stg):
     assert stg.stg_trace_read() == []  # nothing launched: an empty log
     assert lib.stg_trace_read(3, None, None) < 0  # bad output arrays
     stg.stg_trace_enable(prev)
+
+
+def test_ragged_store_argument_errors(stg):
+    lib = stg.load_library()
+
+    def call(**kw):
+        a = dict(tiles=0x10, dtype=1, total_rows=100, middle_dim=8, group=1, depth=128, BM=128, BN=128, col0=0,
+                 ri=0x10, dyn=0x10, mi=0x10, n=4, dst=0x10)
+        a.update(kw)
+        return lib.ragged_tile_store(a["tiles"], a["dtype"], a["total_rows"], a["middle_dim"], a["group"], a["depth"],
+                                     a["BM"], a["BN"], a["col0"], a["ri"], a["dyn"], a["mi"], a["n"], a["dst"], None)
+
+    assert call(group=3) == 1  # BM % group
+    assert b"ragged_tile_store" in lib.stg_last_error()
+    assert call(col0=128) == 1
+    assert call(dtype=11) == 2
+    assert call(tiles=None) == 1
+    assert call(dst=None) == 1
+    assert call(mi=None) == 1
+    assert call(BN=0) == 1
+    assert call(n=0, tiles=None, dst=None) == 0  # nothing to do
+    assert call(BM=1 << 20, BN=1 << 10) == 3  # tile too large for the launch layout
