@@ -78,6 +78,8 @@ def _load():
         "orc_tile_store_clipped": (None, [_P, _I32, _I64, _I64, _I64, _I64, _P]),
         "orc_ragged_schedule": (_I64, [_P, _I64, _I32, _I32, _P, _P, _P]),
         "orc_ragged_tile_load": (None, [_P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _P]),
+        "orc_tile_copy_windows": (None, [_P, _I64, _I64, _I64, _I64, _I64, _I64, _P]),
+        "orc_tile_store_windows": (None, [_P, _I32, _I64, _I64, _I64, _I64, _I64, _I64, _P]),
         "orc_ragged_tile_store": (None, [_P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _P]),
         "orc_bf16_to_f64": (ctypes.c_double, [ctypes.c_uint16]),
         "orc_gemm_f64": (None, [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64]),
@@ -209,6 +211,31 @@ def tile_store_clipped(tiles, origin_row: int, origin_col: int, dst) -> None:
     assert tiles.shape[1] == tile_grid(dst.shape[1], origin_col, tn)
     dd = _arr(dst)
     _load().orc_tile_store_clipped(_ptr(tiles), tiles.itemsize, tm, tn, origin_row, origin_col, ctypes.byref(dd))
+
+
+def tile_copy_windows(src, tm: int, tn: int, step_rows: int, step_cols: int, origin_row: int,
+                      origin_col: int) -> np.ndarray:
+    """Dense (G_r, G_c, tm, tn) buffer of the windows of ``src`` whose origins
+    step by (step_rows, step_cols)."""
+    assert src.ndim == 2
+    gr = tile_grid(src.shape[0], origin_row, step_rows)
+    gc = tile_grid(src.shape[1], origin_col, step_cols)
+    out = np.empty((gr, gc, tm, tn), dtype=src.dtype)
+    sd = _arr(src)
+    _load().orc_tile_copy_windows(ctypes.byref(sd), tm, tn, step_rows, step_cols, origin_row, origin_col, _ptr(out))
+    return out
+
+
+def tile_store_windows(tiles, step_rows: int, step_cols: int, origin_row: int, origin_col: int, dst) -> None:
+    """Clipped store of every window of a dense (G_r, G_c, tm, tn) buffer into ``dst`` in place."""
+    tiles = np.ascontiguousarray(tiles)
+    assert tiles.ndim == 4 and dst.ndim == 2 and tiles.dtype == dst.dtype
+    tm, tn = tiles.shape[2], tiles.shape[3]
+    assert tiles.shape[0] == tile_grid(dst.shape[0], origin_row, step_rows)
+    assert tiles.shape[1] == tile_grid(dst.shape[1], origin_col, step_cols)
+    dd = _arr(dst)
+    _load().orc_tile_store_windows(_ptr(tiles), tiles.itemsize, tm, tn, step_rows, step_cols, origin_row, origin_col,
+                                   ctypes.byref(dd))
 
 
 # ---- ragged ----------------------------------------------------------------

@@ -226,6 +226,51 @@ void orc_tile_store_clipped(const void* tiles_in, int32_t esize, int64_t tm, int
 
 /* ---- ragged varlen 3-D tiles ------------------------------------------ */
 
+void orc_tile_copy_windows(const orc_array* src, int64_t tm, int64_t tn, int64_t step_rows,
+                           int64_t step_cols, int64_t origin_row, int64_t origin_col, void* tiles_out) {
+  const int64_t M = src->shape[0], N = src->shape[1];
+  const int64_t gr_n = orc_tile_grid(M, origin_row, step_rows);
+  const int64_t gc_n = orc_tile_grid(N, origin_col, step_cols);
+  const size_t es = (size_t)src->esize;
+  char* out = (char*)tiles_out;
+  for (int64_t gr = 0; gr < gr_n; ++gr)
+    for (int64_t gc = 0; gc < gc_n; ++gc) {
+      const int64_t R = origin_row + gr * step_rows, C = origin_col + gc * step_cols;
+      for (int64_t i = 0; i < tm; ++i)
+        for (int64_t j = 0; j < tn; ++j) {
+          char* dst = out + (((gr * gc_n + gc) * tm + i) * tn + j) * (int64_t)es;
+          const int64_t r = R + i, col = C + j;
+          if (r >= 0 && r < M && col >= 0 && col < N) {
+            const int64_t coord[2] = {r, col};
+            memcpy(dst, elem_ptr(src, coord), es);
+          } else {
+            memset(dst, 0, es);
+          }
+        }
+    }
+}
+
+void orc_tile_store_windows(const void* tiles_in, int32_t esize, int64_t tm, int64_t tn,
+                            int64_t step_rows, int64_t step_cols, int64_t origin_row,
+                            int64_t origin_col, orc_array* dst) {
+  const int64_t M = dst->shape[0], N = dst->shape[1];
+  const int64_t gr_n = orc_tile_grid(M, origin_row, step_rows);
+  const int64_t gc_n = orc_tile_grid(N, origin_col, step_cols);
+  const char* in = (const char*)tiles_in;
+  for (int64_t gr = 0; gr < gr_n; ++gr)
+    for (int64_t gc = 0; gc < gc_n; ++gc) {
+      const int64_t R = origin_row + gr * step_rows, C = origin_col + gc * step_cols;
+      for (int64_t i = 0; i < tm; ++i)
+        for (int64_t j = 0; j < tn; ++j) {
+          const int64_t r = R + i, col = C + j;
+          if (r < 0 || r >= M || col < 0 || col >= N) continue;
+          const int64_t coord[2] = {r, col};
+          memcpy(elem_ptr(dst, coord), in + (((gr * gc_n + gc) * tm + i) * tn + j) * (int64_t)esize,
+                 (size_t)esize);
+        }
+    }
+}
+
 int64_t orc_ragged_schedule(const int64_t* seq_lens, int64_t n_seqs, int32_t bm_seq,
                             int32_t middle_dim, uint32_t* ragged_idx, uint32_t* dynamic_dim,
                             uint32_t* middle_idx) {

@@ -103,6 +103,24 @@ void orc_tile_copy_bounded(const orc_array* src, int64_t tm, int64_t tn, int64_t
 void orc_tile_store_clipped(const void* tiles_in, int32_t esize, int64_t tm, int64_t tn,
                             int64_t origin_row, int64_t origin_col, orc_array* dst);
 
+/* Tile windows with a step (cuTile.jl Memory, "Tile windows": eachtile with
+ * step per dimension controlling the tile origins, not the element stride
+ * inside a tile; neighbouring windows overlap when step < shape and leave
+ * gaps when step > shape; the window count is cld(extent, step)).  Window
+ * (gr, gc) has origin (origin_row + gr*step_rows, origin_col + gc*step_cols);
+ * G_r = orc_tile_grid(M, origin_row, step_rows), G_c likewise.  The copy is
+ * the bounded copy of each window (zero outside the logical extent); with
+ * step equal to the shape this is orc_tile_copy_bounded. */
+void orc_tile_copy_windows(const orc_array* src, int64_t tm, int64_t tn, int64_t step_rows,
+                           int64_t step_cols, int64_t origin_row, int64_t origin_col, void* tiles_out);
+
+/* The clipped store of every window, windows taken in row-major grid order
+ * (where windows overlap the later one wins here; the product leaves
+ * conflicting stores undefined, as the page does for sparse views). */
+void orc_tile_store_windows(const void* tiles_in, int32_t esize, int64_t tm, int64_t tn,
+                            int64_t step_rows, int64_t step_cols, int64_t origin_row,
+                            int64_t origin_col, orc_array* dst);
+
 /* Ragged schedule: the tiles that cover a packed varlen batch.  Sequence s
  * of length L_s starts at row cu[s] = L_0 + ... + L_{s-1}; for u in
  * [0, ceil(L_s/bm_seq)) and m in [0, middle_dim), in lexicographic order

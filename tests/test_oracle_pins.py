@@ -565,6 +565,90 @@ def test_ragged_store_writes_nothing_outside(orc):
 
 
 # ---------------------------------------------------------------------------
+# tile windows with a step (eachtile with step != shape)
+# ---------------------------------------------------------------------------
+
+def np_windows(X, tm, tn, sr, sc, r0, c0):
+    """Windows as slices of a zero-padded copy of X (numpy slicing only)."""
+    M, N = X.shape
+    gr = -(-(M - r0) // sr) if M > r0 else 0
+    gc = -(-(N - c0) // sc) if N > c0 else 0
+    pad_r = max(tm + sr, abs(r0)) + 1
+    pad_c = max(tn + sc, abs(c0)) + 1
+    P = np.zeros((M + 2 * pad_r + gr * sr, N + 2 * pad_c + gc * sc), dtype=X.dtype)
+    P[pad_r:pad_r + M, pad_c:pad_c + N] = X
+    out = np.zeros((gr, gc, tm, tn), dtype=X.dtype)
+    for a in range(gr):
+        for b in range(gc):
+            R, C = r0 + a * sr + pad_r, c0 + b * sc + pad_c
+            out[a, b] = P[R:R + tm, C:C + tn]
+    return out
+
+
+def test_windows_with_step_equal_to_shape_are_the_bounded_copy(orc):
+    rng = np.random.default_rng(81)
+    X = rng.integers(1, 1000, (37, 29)).astype(np.int32)
+    for (tm, tn, r0, c0) in [(8, 8, 0, 0), (5, 7, -3, -2), (16, 4, 2, 5)]:
+        np.testing.assert_array_equal(orc.tile_copy_windows(X, tm, tn, tm, tn, r0, c0),
+                                      orc.tile_copy_bounded(X, tm, tn, r0, c0))
+        t = orc.tile_copy_bounded(X, tm, tn, r0, c0)
+        a = np.full_like(X, -1)
+        b = np.full_like(X, -1)
+        orc.tile_store_windows(t, tm, tn, r0, c0, a)
+        orc.tile_store_clipped(t, r0, c0, b)
+        np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("case", [(8, 8, 4, 8, 0, 0), (8, 8, 16, 8, 0, 0), (6, 5, 3, 7, -4, 2), (4, 9, 5, 2, 3, -6),
+                                  (1, 1, 3, 3, 0, 0), (7, 7, 1, 1, -2, -2)])
+def test_windows_copy_matches_padded_slices(orc, case):
+    tm, tn, sr, sc, r0, c0 = case
+    rng = np.random.default_rng(sum(case) + 90)
+    X = rng.integers(1, 60000, (23, 19)).astype(np.uint16)
+    got = orc.tile_copy_windows(X, tm, tn, sr, sc, r0, c0)
+    np.testing.assert_array_equal(got, np_windows(X, tm, tn, sr, sc, r0, c0))
+    # the page's window count: cld(extent, step) from a zero origin
+    if r0 == 0 and c0 == 0:
+        assert got.shape[:2] == (-(-23 // sr), -(-19 // sc))
+
+
+@pytest.mark.parametrize("case", [(8, 8, 16, 8, 0, 0), (4, 3, 4, 5, -1, -2), (5, 5, 7, 6, 2, 1)])
+def test_windows_store_without_overlap_is_slice_assignment(orc, case):
+    tm, tn, sr, sc, r0, c0 = case
+    assert sr >= tm and sc >= tn
+    rng = np.random.default_rng(sum(case) + 120)
+    dst = rng.integers(1, 1000, (21, 17)).astype(np.int32)
+    M, N = dst.shape
+    gr, gc = orc.tile_grid(M, r0, sr), orc.tile_grid(N, c0, sc)
+    tiles = rng.integers(-1000, -1, (gr, gc, tm, tn)).astype(np.int32)
+    want = dst.copy()
+    for a in range(gr):
+        for b in range(gc):
+            R, C = r0 + a * sr, c0 + b * sc
+            rs, cs = max(R, 0), max(C, 0)
+            re, ce = min(R + tm, M), min(C + tn, N)
+            if re > rs and ce > cs:
+                want[rs:re, cs:ce] = tiles[a, b, rs - R:re - R, cs - C:ce - C]
+    got = dst.copy()
+    orc.tile_store_windows(tiles, sr, sc, r0, c0, got)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_windows_overlapping_store_of_consistent_tiles_rebuilds_the_covered_region(orc):
+    X = np.arange(1, 1 + 30 * 26, dtype=np.int32).reshape(30, 26)
+    for (tm, tn, sr, sc, r0, c0) in [(8, 8, 4, 8, 0, 0), (6, 5, 3, 2, -2, -1), (5, 5, 8, 3, 1, 0)]:
+        t = orc.tile_copy_windows(X, tm, tn, sr, sc, r0, c0)
+        got = np.full_like(X, -1)
+        orc.tile_store_windows(t, sr, sc, r0, c0, got)
+        covered = np.zeros(X.shape, bool)
+        for a in range(t.shape[0]):
+            for b in range(t.shape[1]):
+                R, C = r0 + a * sr, c0 + b * sc
+                covered[max(R, 0):max(R + tm, 0), max(C, 0):max(C + tn, 0)] = True
+        np.testing.assert_array_equal(got, np.where(covered, X, -1))
+
+
+# ---------------------------------------------------------------------------
 # bounded GEMM reference
 # ---------------------------------------------------------------------------
 
