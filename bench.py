@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default="all",
-                    help="comma list of: copy,gather,masked,ragged,gemm,calib (rocprof runs); 'all' for the full report")
+                    help="comma list of: copy,full,gather,masked,ragged,gemm,calib (rocprof runs); 'all' for the full report")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU time budget of the oracle baseline")
     ap.add_argument("--spinup-ms", type=float, default=400.0,
@@ -259,6 +259,33 @@ def op_entry(workload, nbytes, ms, kernel_ms=None):
     return e
 
 
+def run_full_tiles(stg, steps, warmup):
+    """The unchecked full-tile path: bf16 (16384, 4096), row stride 4096, (64, 32)
+    tiles from (0, 0) -- every tile is full, so the copy and the store take the
+    instance without validity tests.  One call = copy + store; the working set
+    (source, tiles, destination: 403 MB) exceeds the 256 MB Infinity Cache, as
+    the headline step's does."""
+    import torch
+
+    M, N, tm, tn = 16384, 4096, 64, 32
+    g = torch.Generator(device="cpu").manual_seed(1006)
+    src = torch.randn((M, N), generator=g, dtype=torch.float32).to(torch.bfloat16).to("cuda:0")
+    dst = torch.empty_like(src)
+    tiles = torch.empty((M // tm, N // tn, tm, tn), dtype=torch.bfloat16, device="cuda:0")
+
+    def fn():
+        stg.tile_copy_windows(src, tm, tn, tm, tn, 0, 0, check_bounds=False, out=tiles)
+        stg.tile_store_windows(tiles, tm, tn, 0, 0, dst, check_bounds=False)
+
+    ms = time_fn(fn, steps, warmup)
+    kms = traced_kernel_ms(stg, fn, steps)
+    nbytes = 4 * M * N * 2  # copy: read + write every element; store: the same
+    e = op_entry("full-tile copy + store, unchecked: bf16 (16384,4096) ld 4096, (64,32) tiles from (0,0)", nbytes,
+                 ms, kms)
+    e["cold_cache"] = cold_entry(nbytes, fn)
+    return e
+
+
 def run_gather(stg, inputs, steps, warmup):
     w = inputs.row_gather()
     a, idx = _dev(w["a"]), _dev(w["indices"])
@@ -426,7 +453,7 @@ def main():
     from scatter_tile_gather_amd import inputs
 
     stg.load_library()
-    only = set(args.only.split(",")) if args.only != "all" else {"copy", "gather", "masked", "ragged", "gemm"}
+    only = set(args.only.split(",")) if args.only != "all" else {"copy", "full", "gather", "masked", "ragged", "gemm"}
     ops = {}
     head = None
     if "calib" in only:
@@ -434,6 +461,9 @@ def main():
     if "copy" in only:
         head = run_copy(stg, inputs, args.steps, args.warmup)
         print(f"[bench] copy step {head['step_ms']:.4f} ms", file=sys.stderr, flush=True)
+    if "full" in only:
+        ops["full_tile_unchecked"] = run_full_tiles(stg, args.steps, args.warmup)
+        print("[bench] full-tile unchecked done", file=sys.stderr, flush=True)
     if "gather" in only:
         ops["row_gather"] = run_gather(stg, inputs, args.steps, args.warmup)
         print("[bench] row gather done", file=sys.stderr, flush=True)

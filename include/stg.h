@@ -151,6 +151,37 @@ int tile_store_clipped(const void* tiles_in, int64_t tile_rows, int64_t tile_col
                        int64_t origin_row, int64_t origin_col, const stg_tensor* dst,
                        void* stream);
 
+/* Tile windows with a step, and the unchecked full-tile path.
+ * (cuTile.jl Memory, "Tile windows": eachtile's step sets the tile origins,
+ * not the element stride inside a tile -- windows overlap when step < shape
+ * and leave gaps when step > shape -- and there are cld(extent, step) of them;
+ * cuTile.jl Memory, "Bounds checking": check_bounds=false promises that every
+ * element of the tile is in the array and drops load padding; Tylo.jl Boundary
+ * tiles, "Accumulator stores and GEMM": bounds=false keeps the full-tile path.)
+ * Window (gr, gc) has origin (R, C) = (origin_row + gr*step_rows, origin_col +
+ * gc*step_cols) for gr < G_r = stg_tile_grid(M, origin_row, step_rows) and
+ * gc < G_c = stg_tile_grid(N, origin_col, step_cols); tiles are (G_r, G_c,
+ * tile_rows, tile_cols) row-major as for tile_copy_bounded, which is the case
+ * step = shape.
+ *   tile_copy_windows:  tiles_out[gr][gc][i][j] = in range ? src[R+i][C+j] : 0
+ *   tile_store_windows: dst[R+i][C+j] = tiles_in[gr][gc][i][j] for in-range
+ *                       (R+i, C+j) only; where windows overlap, conflicting
+ *                       stores are undefined (equal values are fine).
+ * check_bounds != 0: bounded semantics as above.  check_bounds == 0: the
+ * caller promises that every window lies inside the logical extent; the
+ * promise is verified on the host from the dimensions and a broken promise
+ * returns STG_ERR_INVALID (nothing is launched).  Whenever every window lies
+ * inside -- promised or not, and for tile_copy_bounded / tile_store_clipped
+ * too -- the launch uses the unchecked kernel instance, whose vectors need no
+ * validity test.  step_rows, step_cols >= 1 (else STG_ERR_INVALID); other
+ * arguments, ownership and errors as for tile_copy_bounded / tile_store_clipped. */
+int tile_copy_windows(const stg_tensor* src, int64_t tile_rows, int64_t tile_cols, int64_t step_rows,
+                      int64_t step_cols, int64_t origin_row, int64_t origin_col, int32_t check_bounds,
+                      void* tiles_out, void* stream);
+int tile_store_windows(const void* tiles_in, int64_t tile_rows, int64_t tile_cols, int64_t step_rows,
+                       int64_t step_cols, int64_t origin_row, int64_t origin_col, int32_t check_bounds,
+                       const stg_tensor* dst, void* stream);
+
 /* Host helper: the tiles that cover a packed varlen batch for ragged_tile_load.
  * Sequence s (length seq_lens[s] >= 0) starts at row cu[s] = sum of the earlier
  * lengths; for u in [0, ceil(L_s/bm_seq)) and m in [0, middle_dim), in that

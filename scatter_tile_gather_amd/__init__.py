@@ -19,8 +19,10 @@ from ._binding import (  # noqa: F401
     stg_trace_read,
     stg_version,
     tile_copy_bounded,
+    tile_copy_windows,
     tile_gather,
     tile_gather_masked,
     tile_scatter_masked,
     tile_store_clipped,
+    tile_store_windows,
 )

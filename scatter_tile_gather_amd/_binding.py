@@ -49,6 +49,8 @@ _SIGNATURES = {
     "tile_scatter_masked": (ctypes.c_int, [_TP, _P, _P, _I64, _I64P, _I64P, _I32, _TP, _P]),
     "tile_copy_bounded": (ctypes.c_int, [_TP, _I64, _I64, _I64, _I64, _P, _P]),
     "tile_store_clipped": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _TP, _P]),
+    "tile_copy_windows": (ctypes.c_int, [_TP, _I64, _I64, _I64, _I64, _I64, _I64, _I32, _P, _P]),
+    "tile_store_windows": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _I64, _I64, _I32, _TP, _P]),
     "ragged_tile_schedule": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _I64P]),
     "ragged_tile_load": (ctypes.c_int, [_P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _P, _P]),
     "ragged_tile_store": (ctypes.c_int, [_P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _P, _P]),
@@ -233,6 +235,42 @@ def tile_copy_bounded(src, tile_rows: int, tile_cols: int, origin_row: int = 0, 
     _check(lib.tile_copy_bounded(ctypes.byref(sd), tile_rows, tile_cols, origin_row, origin_col, out.data_ptr(),
                                  _stream(stream)))
     return out
+
+
+def tile_copy_windows(src, tile_rows: int, tile_cols: int, step_rows: int, step_cols: int, origin_row: int = 0,
+                      origin_col: int = 0, check_bounds: bool = True, out=None, stream=None):
+    """Windows of src whose origins step by (step_rows, step_cols); (G_r, G_c, tile_rows, tile_cols)."""
+    torch = _torch()
+    lib = load_library()
+    if src.dim() != 2:
+        raise ValueError("src must be 2-D")
+    gr = stg_tile_grid(src.shape[0], origin_row, step_rows)
+    gc = stg_tile_grid(src.shape[1], origin_col, step_cols)
+    if out is None:
+        out = torch.empty((max(gr, 0), max(gc, 0), tile_rows, tile_cols), dtype=src.dtype, device=src.device)
+    _on_gpu(out, "out")
+    if out.dtype != src.dtype or not out.is_contiguous() or out.numel() < max(gr, 0) * max(gc, 0) * tile_rows * tile_cols:
+        raise ValueError("out must be a contiguous tile buffer of the source dtype and grid size")
+    sd = _desc(src, "src")
+    _check(lib.tile_copy_windows(ctypes.byref(sd), tile_rows, tile_cols, step_rows, step_cols, origin_row, origin_col,
+                                 1 if check_bounds else 0, out.data_ptr(), _stream(stream)))
+    return out
+
+
+def tile_store_windows(tiles, step_rows: int, step_cols: int, origin_row: int, origin_col: int, dst,
+                       check_bounds: bool = True, stream=None):
+    lib = load_library()
+    _on_gpu(tiles, "tiles")
+    if tiles.dim() != 4 or not tiles.is_contiguous() or tiles.dtype != dst.dtype:
+        raise ValueError("tiles must be a contiguous (G_r, G_c, tile_rows, tile_cols) buffer of dst's dtype")
+    tr, tc = tiles.shape[2], tiles.shape[3]
+    if (tiles.shape[0], tiles.shape[1]) != (stg_tile_grid(dst.shape[0], origin_row, step_rows),
+                                            stg_tile_grid(dst.shape[1], origin_col, step_cols)):
+        raise ValueError("tile buffer grid does not match dst, step and origin")
+    dd = _desc(dst, "dst")
+    _check(lib.tile_store_windows(tiles.data_ptr(), tr, tc, step_rows, step_cols, origin_row, origin_col,
+                                  1 if check_bounds else 0, ctypes.byref(dd), _stream(stream)))
+    return dst
 
 
 def tile_store_clipped(tiles, origin_row: int, origin_col: int, dst, stream=None):

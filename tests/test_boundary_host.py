@@ -198,3 +198,22 @@ def test_ragged_store_argument_errors(stg):
     assert call(BN=0) == 1
     assert call(n=0, tiles=None, dst=None) == 0  # nothing to do
     assert call(BM=1 << 20, BN=1 << 10) == 3  # tile too large for the launch layout
+
+
+def test_window_argument_errors_and_broken_promise(stg):
+    lib = stg.load_library()
+    B = ctypes.byref
+    m = _t([64, 64], dtype=1)
+    # step below 1
+    assert lib.tile_copy_windows(B(m), 8, 8, 0, 8, 0, 0, 1, 0x10, None) == 1
+    assert b"step" in lib.stg_last_error()
+    assert lib.tile_store_windows(0x10, 8, 8, 8, -1, 0, 0, 1, B(m), None) == 1
+    # check_bounds = 0 with a grid that leaves the array: rejected on the host, nothing launched
+    assert lib.tile_copy_windows(B(m), 8, 8, 8, 8, -1, 0, 0, 0x10, None) == 1  # negative origin
+    assert b"promises" in lib.stg_last_error()
+    assert lib.tile_copy_windows(B(_t([63, 64], dtype=1)), 8, 8, 8, 8, 0, 0, 0, 0x10, None) == 1  # last row band short
+    assert lib.tile_store_windows(0x10, 8, 8, 6, 8, 0, 0, 0, B(m), None) == 1  # windows at rows 60.. overhang
+    assert lib.tile_copy_windows(B(m), 8, 8, 8, 8, 0, 0, 0, None, None) == 1  # promise holds: null buffer caught
+    assert b"null" in lib.stg_last_error()
+    # an empty grid is a successful no-op without touching the GPU
+    assert lib.tile_copy_windows(B(m), 8, 8, 8, 8, 64, 0, 1, None, None) == 0

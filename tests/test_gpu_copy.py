@@ -114,3 +114,74 @@ def test_bounded_copy_workload_full(stg, orc, origin):
     tm, tn = w["tile"]
     say("bounded copy workload (8191,4097) ld 4103 bf16, tiles (64,32), origin", origin)
     _copy_store_case(stg, orc, w["src"], N, tm, tn, *origin)
+
+
+# ---- tile windows with a step, unchecked full-tile path ----------------------
+
+def _windows_case(stg, orc, store, N, tm, tn, sr, sc, r0, c0, check=True):
+    """Copy the windows, then store them back into a sentinel-filled copy of
+    the layout; overlapping windows carry equal values (they were copied from
+    the same source), so the overlapped stores agree."""
+    M = store.shape[0]
+    src_h = store[:, :N]
+    src_d = to_dev(store)[:, :N]
+    gr, gc = orc.tile_grid(M, r0, sr), orc.tile_grid(N, c0, sc)
+    tiles = torch.zeros((gr, gc, tm, tn), dtype=src_d.dtype, device="cuda:0")
+    tiles.view(torch.uint8).fill_(0xA5)
+    stg.tile_copy_windows(src_d, tm, tn, sr, sc, r0, c0, check_bounds=check, out=tiles)
+    torch.cuda.synchronize()
+    want = orc.tile_copy_windows(src_h, tm, tn, sr, sc, r0, c0)
+    np.testing.assert_array_equal(to_host(tiles), want)
+    dst_h = np.full_like(store, 0)
+    dst_h.view(np.uint8)[...] = 0xA5
+    dst = to_dev(dst_h)
+    stg.tile_store_windows(tiles, sr, sc, r0, c0, dst[:, :N], check_bounds=check)
+    torch.cuda.synchronize()
+    want_dst = dst_h.copy()
+    orc.tile_store_windows(want, sr, sc, r0, c0, want_dst[:, :N])
+    np.testing.assert_array_equal(to_host(dst), want_dst)
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_windows_random(stg, orc, seed):
+    rng = np.random.default_rng(7000 + seed)
+    dt = [np.uint16, np.float32, np.uint8, np.float64][seed % 4]
+    M, N = int(rng.integers(1, 70)), int(rng.integers(1, 90))
+    ld = N + int(rng.integers(0, 9))
+    es = np.dtype(dt).itemsize
+    tn = int(rng.choice([16 // es, 32 // es, 64 // es, 3, 5])) if seed % 3 else int(rng.integers(1, 12))
+    tn = max(tn, 1)
+    tm = int(rng.integers(1, 24))
+    sr = int(rng.integers(1, 2 * tm + 3))  # overlapping, adjacent or gapped row windows
+    sc = int(rng.integers(1, 2 * tn + 3))
+    r0 = int(rng.integers(-tm - 3, 4))
+    c0 = int(rng.integers(-tn - 3, 4))
+    store = random_bits(rng, (M, ld), dt)
+    say("windows random", seed, dt.__name__, (M, N, ld), "tile", (tm, tn), "step", (sr, sc), "origin", (r0, c0))
+    _windows_case(stg, orc, store, N, tm, tn, sr, sc, r0, c0)
+
+
+@pytest.mark.parametrize("case", [(16, 32, 16, 32, 0, 0), (8, 16, 12, 16, 0, 8), (4, 8, 4, 40, 3, 0),
+                                  (1, 8, 3, 8, 0, 0)])
+@pytest.mark.parametrize("check", [False, True])
+def test_windows_inside_unchecked(stg, orc, case, check):
+    """Grids whose windows all lie inside the array: the unchecked instance,
+    requested (check_bounds = 0) or chosen by the host."""
+    tm, tn, sr, sc, r0, c0 = case
+    rng = np.random.default_rng(sum(case))
+    G_r, G_c = 5, 6
+    M, N = r0 + (G_r - 1) * sr + tm, c0 + (G_c - 1) * sc + tn
+    M, N = max(M, r0 + (G_r - 1) * sr + 1), max(N, c0 + (G_c - 1) * sc + 1)
+    store = random_bits(rng, (M, N + 5), np.uint16)
+    say("windows inside", case, "check_bounds", check, "matrix", (M, N))
+    _windows_case(stg, orc, store, N, tm, tn, sr, sc, r0, c0, check=check)
+
+
+def test_full_tile_workload_unchecked(stg, orc):
+    """(8192, 4096) bf16 with unit-aligned row stride and (64, 32) tiles from
+    (0, 0): every tile is full, so tile_copy_bounded takes the unchecked
+    instance by itself; the result is the bounded copy's."""
+    rng = np.random.default_rng(4242)
+    src = random_bits(rng, (8192, 4096), np.uint16)
+    say("full-tile workload (8192,4096) bf16 tiles (64,32), automatic unchecked dispatch")
+    _copy_store_case(stg, orc, src, 4096, 64, 32, 0, 0)
