@@ -78,6 +78,7 @@ def _load():
         "orc_tile_store_clipped": (None, [_P, _I32, _I64, _I64, _I64, _I64, _P]),
         "orc_ragged_schedule": (_I64, [_P, _I64, _I32, _I32, _P, _P, _P]),
         "orc_ragged_tile_load": (None, [_P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _P]),
+        "orc_tile_gather_backward": (None, [_P, _P, _I64, _P, _P, _I32, _P, _P, _P, _P]),
         "orc_tile_copy_windows": (None, [_P, _I64, _I64, _I64, _I64, _I64, _I64, _P]),
         "orc_tile_store_windows": (None, [_P, _I32, _I64, _I64, _I64, _I64, _I64, _I64, _P]),
         "orc_ragged_tile_store": (None, [_P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _P]),
@@ -211,6 +212,27 @@ def tile_store_clipped(tiles, origin_row: int, origin_col: int, dst) -> None:
     assert tiles.shape[1] == tile_grid(dst.shape[1], origin_col, tn)
     dd = _arr(dst)
     _load().orc_tile_store_clipped(_ptr(tiles), tiles.itemsize, tm, tn, origin_row, origin_col, ctypes.byref(dd))
+
+
+def tile_gather_backward(a_grad, indices, tile_shape, grad_out, offset=None, axis=0):
+    """Adjoint of tile_gather accumulated into a copy of ``a_grad`` (float32 or
+    float64): returns (acc, abs_sum, count) -- the fp64 sums, the fp64 sum of
+    magnitudes (initial |a_grad| plus every |term|) and the number of terms
+    per element, all of a_grad's shape."""
+    a_grad = np.asarray(a_grad)
+    grad_out = np.asarray(grad_out)
+    assert a_grad.dtype in (np.float32, np.float64) and grad_out.dtype == a_grad.dtype
+    idx = np.ascontiguousarray(indices, dtype=np.int32)
+    offset = [0] * a_grad.ndim if offset is None else offset
+    assert grad_out.shape == tuple(_gather_out(a_grad, idx.size, tile_shape, axis).shape)
+    acc = np.ascontiguousarray(a_grad, dtype=np.float64).copy()
+    abs_sum = np.abs(acc)
+    count = np.zeros(a_grad.shape, dtype=np.int64)
+    gd = _arr(grad_out)
+    ts, of, sh = _i64v(tile_shape, a_grad.ndim), _i64v(offset, a_grad.ndim), _i64v(a_grad.shape, a_grad.ndim)
+    _load().orc_tile_gather_backward(ctypes.byref(gd), _ptr(idx), idx.size, _ptr(ts), _ptr(of), axis, _ptr(sh),
+                                     _ptr(acc), _ptr(abs_sum), _ptr(count))
+    return acc, abs_sum, count
 
 
 def tile_copy_windows(src, tm: int, tn: int, step_rows: int, step_cols: int, origin_row: int,

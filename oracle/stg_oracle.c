@@ -226,6 +226,47 @@ void orc_tile_store_clipped(const void* tiles_in, int32_t esize, int64_t tm, int
 
 /* ---- ragged varlen 3-D tiles ------------------------------------------ */
 
+void orc_tile_gather_backward(const orc_array* grad_out, const int32_t* indices, int64_t n_indices,
+                              const int64_t* tile_shape, const int64_t* offset, int32_t axis,
+                              const int64_t* a_shape, double* acc, double* abs_sum, int64_t* count) {
+  const int rank = grad_out->rank;
+  const int64_t T = tile_shape[axis];
+  const int64_t n_tiles = T > 0 ? n_indices / T : 0;
+  int64_t ts[4], as4[4];
+  shape4(tile_shape, rank, ts);
+  shape4(a_shape, rank, as4);
+  int64_t c[4];
+  for (int64_t t = 0; t < n_tiles; ++t)
+    for (c[0] = 0; c[0] < ts[0]; ++c[0])
+      for (c[1] = 0; c[1] < ts[1]; ++c[1])
+        for (c[2] = 0; c[2] < ts[2]; ++c[2])
+          for (c[3] = 0; c[3] < ts[3]; ++c[3]) {
+            int64_t o[4], s[4] = {0, 0, 0, 0};
+            for (int d = 0; d < 4; ++d) o[d] = c[d];
+            o[axis] += t * T;
+            int valid = 1;
+            for (int d = 0; d < rank; ++d) {
+              s[d] = d == axis ? offset[axis] + (int64_t)indices[o[axis]] : offset[d] + o[d];
+              if (s[d] < 0 || s[d] >= a_shape[d]) valid = 0;
+            }
+            if (!valid) continue;
+            const char* gp = elem_ptr(grad_out, o);
+            double g;
+            if (grad_out->esize == 4) {
+              float f;
+              memcpy(&f, gp, 4);
+              g = (double)f;
+            } else {
+              memcpy(&g, gp, 8);
+            }
+            int64_t lin = 0; /* row-major position of s in a's shape */
+            for (int d = 0; d < 4; ++d) lin = lin * as4[d] + s[d];
+            acc[lin] += g;
+            abs_sum[lin] += g < 0 ? -g : g;
+            count[lin] += 1;
+          }
+}
+
 void orc_tile_copy_windows(const orc_array* src, int64_t tm, int64_t tn, int64_t step_rows,
                            int64_t step_cols, int64_t origin_row, int64_t origin_col, void* tiles_out) {
   const int64_t M = src->shape[0], N = src->shape[1];

@@ -103,6 +103,22 @@ void orc_tile_copy_bounded(const orc_array* src, int64_t tm, int64_t tn, int64_t
 void orc_tile_store_clipped(const void* tiles_in, int32_t esize, int64_t tm, int64_t tn,
                             int64_t origin_row, int64_t origin_col, orc_array* dst);
 
+/* Backward of the indexed gather (Warp, warp.tile_load_indexed: the
+ * function is differentiable, and in a backward pass the adjoint of the
+ * returned tile is accumulated atomically into a.grad at the same gathered
+ * locations).  For every coordinate o of grad_out (the gather's output
+ * shape) whose source coordinate s -- as in orc_tile_gather -- is in range:
+ *   acc[s] += grad_out[o];  abs_sum[s] += |grad_out[o]|;  count[s] += 1
+ * Out-of-range sources contribute nothing; repeated indices add up.
+ * grad_out holds float (esize 4) or double (esize 8) values; acc, abs_sum
+ * and count are dense row-major arrays of a's shape a_shape[0..rank-1]
+ * (rank = grad_out's), initialised by the caller (acc with a.grad's initial
+ * values, abs_sum with their magnitudes, count with zeros).  The sums are in
+ * fp64, in coordinate order. */
+void orc_tile_gather_backward(const orc_array* grad_out, const int32_t* indices, int64_t n_indices,
+                              const int64_t* tile_shape, const int64_t* offset, int32_t axis,
+                              const int64_t* a_shape, double* acc, double* abs_sum, int64_t* count);
+
 /* Tile windows with a step (cuTile.jl Memory, "Tile windows": eachtile with
  * step per dimension controlling the tile origins, not the element stride
  * inside a tile; neighbouring windows overlap when step < shape and leave

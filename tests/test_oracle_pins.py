@@ -565,6 +565,58 @@ def test_ragged_store_writes_nothing_outside(orc):
 
 
 # ---------------------------------------------------------------------------
+# backward of the indexed gather (adjoint accumulated into a.grad)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", [
+    ((40, 24), (8, 24), (0, 0), 0, 64),     # rows, full width
+    ((40, 24), (8, 16), (0, 5), 0, 48),     # column window partly past the edge
+    ((30, 50), (12, 7), (-3, 0), 1, 35),    # gather along the last axis, negative row offset
+    ((6, 20, 9), (4, 5, 9), (1, 0, 0), 1, 40),  # rank 3, middle axis
+    ((5, 7, 4, 6), (2, 3, 4, 6), (0, 2, 0, 0), 2, 12),  # rank 4
+])
+def test_gather_backward_is_the_adjoint_of_the_gather(orc, case):
+    """<gather(a), g> = <a, backward(g)> for every a and g: the backward is the
+    transpose of the gather's linear map (indices out of range included)."""
+    shape, tile, off, axis, n_idx = case
+    rng = np.random.default_rng(sum(shape) + n_idx)
+    idx = rng.integers(-4, shape[axis] + 4, n_idx).astype(np.int32)
+    a = rng.standard_normal(shape)
+    g_shape = list(tile)
+    g_shape[axis] = n_idx
+    g = rng.standard_normal(g_shape)
+    fwd = orc.tile_gather(a, idx, tile, off, axis)
+    back, _, _ = orc.tile_gather_backward(np.zeros(shape), idx, tile, g, off, axis)
+    lhs = float(np.sum(fwd * g))
+    rhs = float(np.sum(a * back))
+    assert abs(lhs - rhs) <= 1e-11 * (np.sum(np.abs(fwd * g)) + 1.0)
+
+
+def test_gather_backward_with_unique_indices_is_a_scatter(orc):
+    rng = np.random.default_rng(404)
+    idx = rng.permutation(64)[:48].astype(np.int32)
+    g = rng.standard_normal((48, 16)).astype(np.float32)
+    back, _, count = orc.tile_gather_backward(np.zeros((64, 16), np.float32), idx, (16, 16), g)
+    want = np.zeros((64, 16), np.float32)
+    orc.tile_scatter_masked(want, idx, np.ones(48, np.uint8), (16, 16), g)
+    np.testing.assert_array_equal(back, want.astype(np.float64))
+    assert set(np.unique(count)) <= {0, 1}
+
+
+def test_gather_backward_counts_repeated_indices(orc):
+    """With a gradient of ones every element of a.grad receives one term per
+    occurrence of its row among the in-range indices (bincount)."""
+    rng = np.random.default_rng(405)
+    idx = rng.integers(-10, 40, 200).astype(np.int32)
+    a0 = rng.standard_normal((32, 8))
+    back, abs_sum, count = orc.tile_gather_backward(a0, idx, (20, 8), np.ones((200, 8)))
+    occ = np.bincount(idx[(idx >= 0) & (idx < 32)], minlength=32)
+    np.testing.assert_array_equal(count, np.repeat(occ[:, None], 8, axis=1))
+    np.testing.assert_allclose(back, a0 + count, rtol=0, atol=1e-12)  # accumulates onto a.grad's values
+    np.testing.assert_allclose(abs_sum, np.abs(a0) + count, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
 # tile windows with a step (eachtile with step != shape)
 # ---------------------------------------------------------------------------
 
