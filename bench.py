@@ -42,7 +42,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default="all",
-                    help="comma list of: copy,full,gather,masked,ragged,gemm,calib (rocprof runs); 'all' for the full report")
+                    help="comma list of: copy,full,gather,masked,backward,ragged,gemm,calib (rocprof runs); 'all' for the "
+                         "full report")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU time budget of the oracle baseline")
     ap.add_argument("--spinup-ms", type=float, default=400.0,
@@ -335,6 +336,39 @@ def run_masked(stg, inputs, steps, warmup):
     return eg, es
 
 
+def run_gather_backward(stg, inputs, steps, warmup):
+    """Backward of the indexed gather at embedding scale: a.grad fp32
+    (1048576, 128), the masked workload's 4,194,304 uniform indices (about
+    four terms per row), an N(0,1) output gradient (4194304, 128), (64, 128)
+    tiles.  Every call accumulates into the same a.grad."""
+    import torch
+
+    w = inputs.masked()
+    idx = _dev(w["indices"])
+    rows, cols = w["table"].shape
+    g = torch.Generator(device="cuda:0").manual_seed(1007)
+    grad_out = torch.randn((idx.numel(), cols), generator=g, dtype=torch.float32, device="cuda:0")
+    a_grad = torch.zeros((rows, cols), dtype=torch.float32, device="cuda:0")
+    touched = int(np.unique(w["indices"]).size)
+    nbytes = idx.numel() * 4 + idx.numel() * cols * 4 + 2 * touched * cols * 4
+    res = []
+    nws = stg.tile_gather_backward_workspace(a_grad, idx.numel(), (64, cols), 0)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda:0")
+    for label, wsp in (("grouped by destination row, no float atomics", ws), ("hardware fp32 atomic adds", None)):
+        fn = lambda: stg.tile_gather_backward(a_grad, idx, (64, cols), grad_out, workspace=wsp)
+        ms = time_fn(fn, steps, warmup)
+        kms = traced_kernel_ms(stg, fn, steps)
+        e = op_entry(f"gather backward ({label}): a.grad fp32 (1048576,128), 4194304 uniform indices, (64,128) "
+                     f"tiles", nbytes, ms, kms)
+        e["note"] = ("algorithmic bytes: indices, the output gradient read once, each touched a.grad row read "
+                     "and written once")
+        if wsp is not None:
+            e["workspace_bytes"] = int(nws)
+        e["cold_cache"] = cold_entry(nbytes, fn)
+        res.append(e)
+    return res
+
+
 def run_ragged(stg, inputs, steps, warmup):
     import torch
 
@@ -453,7 +487,8 @@ def main():
     from scatter_tile_gather_amd import inputs
 
     stg.load_library()
-    only = set(args.only.split(",")) if args.only != "all" else {"copy", "full", "gather", "masked", "ragged", "gemm"}
+    only = set(args.only.split(",")) if args.only != "all" else {"copy", "full", "gather", "masked", "backward", "ragged",
+                                                                             "gemm"}
     ops = {}
     head = None
     if "calib" in only:
@@ -470,6 +505,11 @@ def main():
     if "masked" in only:
         ops["masked_gather"], ops["masked_scatter"] = run_masked(stg, inputs, args.steps, args.warmup)
         print("[bench] masked gather/scatter done", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+    if "backward" in only:
+        ops["gather_backward_grouped"], ops["gather_backward_atomic"] = run_gather_backward(stg, inputs, args.steps,
+                                                                                            args.warmup)
+        print("[bench] gather backward done", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
     if "ragged" in only:
         (ops["ragged_group1"], ops["ragged_store_group1"], ops["ragged_group4"],

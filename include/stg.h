@@ -126,6 +126,41 @@ int tile_scatter_masked(const stg_tensor* a, const int32_t* indices, const uint8
                         int64_t n_indices, const int64_t* tile_shape, const int64_t* offset,
                         int32_t axis, const stg_tensor* tile, void* stream);
 
+/* Backward of tile_gather (Warp, warp.tile_load_indexed: the function is
+ * differentiable; in a backward pass the adjoint of the returned tile is
+ * accumulated atomically into a.grad at the same gathered locations).
+ * grad_out has the shape of tile_gather's `out` for the same indices,
+ * tile_shape, offset and axis; for every coordinate o of grad_out whose source
+ * coordinate s (as in tile_gather) is in range:
+ *   a_grad[s] += grad_out[o]
+ * Out-of-range sources contribute nothing; repeated indices add up, in an
+ * unspecified order (the sum is exact up to fp rounding of that order).
+ * a_grad and grad_out are STG_F32 or STG_F64 (else STG_ERR_UNSUPPORTED) of one
+ * dtype.  Other arguments, checks and errors as for tile_gather.
+ *
+ * Two executions, same result up to summation order:
+ *  - workspace == NULL: every term is a hardware float atomic add into a_grad
+ *    (a_grad must be device memory from hipMalloc, coarse-grained; the
+ *    hardware add may flush subnormal values).
+ *  - workspace != NULL: a device buffer of at least
+ *    tile_gather_backward_workspace(...) bytes, 256-byte aligned, owned by the
+ *    caller and not used by anything else until the work completes; for the
+ *    row layout (gather axis not the last, unit last-dimension strides) the
+ *    terms are grouped by destination row and each row of a_grad is summed and
+ *    written once, without float atomics (STG_ERR_INVALID if the buffer is
+ *    too small).  For any other layout the workspace is not used. */
+int tile_gather_backward(const stg_tensor* a_grad, const int32_t* indices, int64_t n_indices,
+                         const int64_t* tile_shape, const int64_t* offset, int32_t axis,
+                         const stg_tensor* grad_out, void* workspace, int64_t workspace_bytes,
+                         void* stream);
+
+/* Workspace bytes tile_gather_backward's grouped execution needs for a_grad's
+ * layout, n_indices indices and tile_shape along axis (0 when the layout is
+ * not the row layout, which always runs on atomics); a negative status code on
+ * invalid arguments.  Host only. */
+int64_t tile_gather_backward_workspace(const stg_tensor* a_grad, int64_t n_indices,
+                                       const int64_t* tile_shape, int32_t axis);
+
 /* Boundary-tile copy with zero fill (Tylo.jl Boundary tiles: opening section,
  * "A concrete edge"; cuTile.jl Memory, "Bounds checking": loads pad).
  * src is rank 2, logical (M, N), any strides (leading stride need not be

@@ -21,6 +21,8 @@ from ._binding import (  # noqa: F401
     tile_copy_bounded,
     tile_copy_windows,
     tile_gather,
+    tile_gather_backward,
+    tile_gather_backward_workspace,
     tile_gather_masked,
     tile_scatter_masked,
     tile_store_clipped,

@@ -47,6 +47,8 @@ _SIGNATURES = {
     "tile_gather": (ctypes.c_int, [_TP, _P, _I64, _I64P, _I64P, _I32, _TP, _P]),
     "tile_gather_masked": (ctypes.c_int, [_TP, _P, _P, _I64, _I64P, _I64P, _I32, ctypes.c_double, _TP, _P]),
     "tile_scatter_masked": (ctypes.c_int, [_TP, _P, _P, _I64, _I64P, _I64P, _I32, _TP, _P]),
+    "tile_gather_backward": (ctypes.c_int, [_TP, _P, _I64, _I64P, _I64P, _I32, _TP, _P, _I64, _P]),
+    "tile_gather_backward_workspace": (_I64, [_TP, _I64, _I64P, _I32]),
     "tile_copy_bounded": (ctypes.c_int, [_TP, _I64, _I64, _I64, _I64, _P, _P]),
     "tile_store_clipped": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _TP, _P]),
     "tile_copy_windows": (ctypes.c_int, [_TP, _I64, _I64, _I64, _I64, _I64, _I64, _I32, _P, _P]),
@@ -204,6 +206,41 @@ def tile_gather_masked(a, indices, mask, tile_shape, offset=None, axis: int = 0,
                                   _i64arr(tile_shape), None if offset is None else _i64arr(offset), axis,
                                   float(padding_value), ctypes.byref(od), _stream(stream)))
     return out
+
+
+def tile_gather_backward_workspace(a_grad, n_indices: int, tile_shape, axis: int = 0) -> int:
+    """Bytes of workspace the grouped (atomic-free) execution needs; 0 when the
+    layout always runs on atomics."""
+    lib = load_library()
+    ad = _desc(a_grad, "a_grad")
+    n = int(lib.tile_gather_backward_workspace(ctypes.byref(ad), n_indices, _i64arr(tile_shape), axis))
+    if n < 0:
+        raise StgError(-n, lib.stg_last_error().decode())
+    return n
+
+
+def tile_gather_backward(a_grad, indices, tile_shape, grad_out, offset=None, axis: int = 0, workspace=None,
+                         stream=None):
+    """a_grad += adjoint of tile_gather(a, indices, tile_shape, offset, axis) for
+    the output gradient grad_out (fp32 or fp64).  workspace: None (hardware
+    float atomics), a device uint8 tensor of at least
+    tile_gather_backward_workspace(...) bytes, or "auto" to allocate one here
+    (grouped execution, no float atomics)."""
+    torch = _torch()
+    lib = load_library()
+    n = indices.numel()
+    ad, gd = _desc(a_grad, "a_grad"), _desc(grad_out, "grad_out")
+    if isinstance(workspace, str) and workspace == "auto":
+        nb = tile_gather_backward_workspace(a_grad, n, tile_shape, axis)
+        workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=a_grad.device) if nb else None
+    ws_ptr, ws_n = None, 0
+    if workspace is not None:
+        _on_gpu(workspace, "workspace")
+        ws_ptr, ws_n = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(lib.tile_gather_backward(ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"), n,
+                                    _i64arr(tile_shape), None if offset is None else _i64arr(offset), axis,
+                                    ctypes.byref(gd), ws_ptr, ws_n, _stream(stream)))
+    return a_grad
 
 
 def tile_scatter_masked(a, indices, mask, tile_shape, tile, offset=None, axis: int = 0, stream=None):

@@ -19,7 +19,24 @@
 //    masked-out rows cost no memory traffic at all.
 //  * element path -- anything else (gather along the innermost axis, strided
 //    innermost dimension): one element per lane.
+//
+// Backward of the gather (Warp, warp.tile_load_indexed: differentiable; in a
+// backward pass the adjoint of the returned tile is accumulated atomically
+// into a.grad at the same gathered locations): the scatter kernels with every
+// store replaced by a hardware float atomic add (fp32 or fp64, relaxed, device
+// scope), unmasked; rows whose source is out of range are compacted away like
+// masked-out scatter rows.  Repeated indices add up in an unspecified order.
+// The chip retires about 77 G lane-wise float atomic adds per second whatever
+// the table size, so with a caller-provided workspace the row layout takes an
+// atomic-free path instead: a histogram of destination rows, a scan into
+// segment offsets, a fill of each term's row id into its destination's
+// segment (the histogram's integer atomics return each term's rank within its
+// row, so the fill is a plain scatter), and a reduction in
+// which one group of lanes owns a destination row, adds its terms and writes
+// the row once with plain stores.
 #include "stg_internal.h"
+
+#include <algorithm>
 
 namespace stg {
 namespace {
@@ -142,7 +159,23 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(RowParams p) {
   }
 }
 
-template <int ESIZE, bool FULL>
+// a.grad[...] += value, hardware float atomics (fp32 / fp64 only)
+template <int ESIZE>
+__device__ __forceinline__ void accum_elem(char* dst, uint64_t bits) {
+  if constexpr (ESIZE == 4) {
+    unsafeAtomicAdd((float*)dst, __uint_as_float((uint32_t)bits));
+  } else if constexpr (ESIZE == 8) {
+    unsafeAtomicAdd((double*)dst, __longlong_as_double((long long)bits));
+  }
+}
+
+template <int ESIZE>
+__device__ __forceinline__ void accum16(char* dst, const u32x4& v) {
+#pragma unroll
+  for (int e = 0; e < 16 / ESIZE; ++e) accum_elem<ESIZE>(dst + e * ESIZE, vec_get<ESIZE>(v, e));
+}
+
+template <int ESIZE, bool FULL, bool ACCUM>
 __global__ __launch_bounds__(kThreads) void scatter_rows_kernel(RowParams p) {
   constexpr int V = 16 / ESIZE;
   __shared__ int64_t s_dst[kMaxRowsPerWg];  // offset into a (the scatter destination)
@@ -191,14 +224,22 @@ __global__ __launch_bounds__(kThreads) void scatter_rows_kernel(RowParams p) {
         const int r = (int)div_small((uint32_t)it, p.chunk_magic);
         const int b = (it - r * p.n_chunks) * 16;
         if (FULL || (b >= p.lo_b && b + 16 <= p.hi_b)) {
-          st16(const_cast<char*>(p.a) + s_dst[r] + b, v[u]);
+          if (ACCUM)
+            accum16<ESIZE>(const_cast<char*>(p.a) + s_dst[r] + b, v[u]);
+          else
+            st16(const_cast<char*>(p.a) + s_dst[r] + b, v[u]);
         } else if (b + 16 > p.lo_b && b < p.hi_b) {
           const char* src = p.t + s_src[r] + b;
           char* dst = const_cast<char*>(p.a) + s_dst[r] + b;
 #pragma unroll
           for (int e = 0; e < V; ++e) {
             const int bb = b + e * ESIZE;
-            if (bb >= p.lo_b && bb < p.hi_b) copy_elem<ESIZE>(dst + e * ESIZE, src + e * ESIZE);
+            if (bb >= p.lo_b && bb < p.hi_b) {
+              if (ACCUM)
+                accum_elem<ESIZE>(dst + e * ESIZE, load_elem<ESIZE>(src + e * ESIZE));
+              else
+                copy_elem<ESIZE>(dst + e * ESIZE, src + e * ESIZE);
+            }
           }
         }
       }
@@ -239,22 +280,227 @@ __global__ __launch_bounds__(kThreads) void gather_elem_kernel(ElemParams p) {
   }
 }
 
-template <int ESIZE>
+template <int ESIZE, bool ACCUM>
 __global__ __launch_bounds__(kThreads) void scatter_elem_kernel(ElemParams p) {
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < p.n; i += (int64_t)gridDim.x * kThreads) {
     int64_t ao, to;
     bool masked_out;
-    if (resolve_elem(p, i, ao, to, masked_out))
-      copy_elem<ESIZE>(const_cast<char*>(p.a) + ao, p.t + to);
+    if (resolve_elem(p, i, ao, to, masked_out)) {
+      if (ACCUM)
+        accum_elem<ESIZE>(const_cast<char*>(p.a) + ao, load_elem<ESIZE>(p.t + to));
+      else
+        copy_elem<ESIZE>(const_cast<char*>(p.a) + ao, p.t + to);
+    }
+  }
+}
+
+// ---- sorted (segmented) backward -------------------------------------------
+//
+// Destination row id of grad_out row g: (sa * p_ext + sp) * q_ext + sq, dense
+// in [0, R) with R = ax_ext * p_ext * q_ext; -1 when the row has no in-range
+// source.  Workspace (int32): count[R] | offs[R + 1] | perm[n_rows] |
+// rank[n_rows] | bsum[nb].
+__device__ __forceinline__ int32_t dest_row_id(const RowParams& p, int64_t g, int64_t& t_off) {
+  int64_t o_ax, op = 0, oq = 0;
+  if (p.rest == 1) {
+    o_ax = g;
+  } else {
+    o_ax = g / p.rest;
+    const int64_t rr = g - o_ax * p.rest;
+    op = rr / p.q_n;
+    oq = rr - op * p.q_n;
+  }
+  const int64_t sa = p.ax_off + (int64_t)p.indices[o_ax];
+  const int64_t sp = p.p_off + op, sq = p.q_off + oq;
+  t_off = o_ax * p.t_ax_b + op * p.t_p_b + oq * p.t_q_b;
+  const bool ok = sa >= 0 && sa < p.ax_ext && sp >= 0 && sp < p.p_ext && sq >= 0 && sq < p.q_ext;
+  return ok ? (int32_t)((sa * p.p_ext + sp) * p.q_ext + sq) : -1;
+}
+
+constexpr int kScanBlock = 1024;  // counts per scan block (256 threads x 4)
+
+__global__ __launch_bounds__(kThreads) void seg_zero_kernel(int32_t* count, int64_t R) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < R; i += (int64_t)gridDim.x * kThreads) count[i] = 0;
+}
+
+// count[r] = terms of destination row r; rank[g] = place of term g among them
+__global__ __launch_bounds__(kThreads) void seg_hist_kernel(RowParams p, int32_t* count, int32_t* rank) {
+  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < p.n_rows; g += (int64_t)gridDim.x * kThreads) {
+    int64_t t_off;
+    const int32_t r = dest_row_id(p, g, t_off);
+    if (r >= 0) rank[g] = atomicAdd(count + r, 1);
+  }
+}
+
+// exclusive scan within a workgroup of 256 values (one per thread)
+__device__ __forceinline__ int32_t wg_exclusive_scan(int32_t v, int32_t& total) {
+  __shared__ int32_t s_w[kThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_w[wave] = x;
+  __syncthreads();
+  int32_t before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) {
+    before += w < wave ? s_w[w] : 0;
+    total += s_w[w];
+  }
+  __syncthreads();
+  return before + x - v;
+}
+
+// block b: sum of count[b*1024 .. b*1024+1023]
+__global__ __launch_bounds__(kThreads) void seg_bsum_kernel(const int32_t* count, int64_t R, int32_t* bsum) {
+  const int64_t i0 = (int64_t)blockIdx.x * kScanBlock + threadIdx.x * 4;
+  int32_t v = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (i0 + e < R) v += count[i0 + e];
+  int32_t total;
+  wg_exclusive_scan(v, total);
+  if (threadIdx.x == 0) bsum[blockIdx.x] = total;
+}
+
+// one workgroup: exclusive scan of the nb block sums in place (running carry)
+__global__ __launch_bounds__(kThreads) void seg_bscan_kernel(int32_t* bsum, int64_t nb) {
+  int32_t carry = 0;
+  for (int64_t b0 = 0; b0 < nb; b0 += kThreads) {
+    const int64_t i = b0 + threadIdx.x;
+    const int32_t v = i < nb ? bsum[i] : 0;
+    int32_t total;
+    const int32_t ex = wg_exclusive_scan(v, total);
+    if (i < nb) bsum[i] = carry + ex;
+    carry += total;
+  }
+}
+
+// offs[i] = exclusive prefix of count; offs[R] = number of valid terms
+__global__ __launch_bounds__(kThreads) void seg_offs_kernel(int32_t* count, int64_t R, const int32_t* bsum,
+                                                            int32_t* offs) {
+  const int64_t i0 = (int64_t)blockIdx.x * kScanBlock + threadIdx.x * 4;
+  int32_t c[4], v = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    c[e] = i0 + e < R ? count[i0 + e] : 0;
+    v += c[e];
+  }
+  int32_t total;
+  int32_t run = bsum[blockIdx.x] + wg_exclusive_scan(v, total);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (i0 + e < R) offs[i0 + e] = run;
+    if (i0 + e == R - 1) offs[R] = run + c[e];
+    run += c[e];
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void seg_fill_kernel(RowParams p, const int32_t* rank, const int32_t* offs,
+                                                            int32_t* perm) {
+  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < p.n_rows; g += (int64_t)gridDim.x * kThreads) {
+    int64_t t_off;
+    const int32_t r = dest_row_id(p, g, t_off);
+    if (r >= 0) perm[offs[r] + rank[g]] = (int32_t)g;
+  }
+}
+
+// One group of LPR lanes per destination row: each lane owns 16-byte chunks
+// lane, lane + LPR, ... of the row's valid byte window, adds the terms of the
+// row's segment (four grad_out rows in flight) to a.grad's values and stores
+// the row once.  Rows with an empty segment are not touched.
+template <int ESIZE, int LPR>
+__global__ __launch_bounds__(kThreads) void seg_reduce_kernel(RowParams p, int64_t R, const int32_t* offs,
+                                                              const int32_t* perm) {
+  constexpr int V = 16 / ESIZE;
+  const int sub = threadIdx.x % LPR;
+  const int64_t r = (int64_t)blockIdx.x * (kThreads / LPR) + threadIdx.x / LPR;
+  if (r >= R) return;
+  const int32_t k0 = offs[r], k1 = offs[r + 1];
+  if (k0 == k1) return;
+  const int64_t sq = r % p.q_ext, rr = r / p.q_ext;
+  const int64_t sp = rr % p.p_ext, sa = rr / p.p_ext;
+  char* arow = const_cast<char*>(p.a) + sa * p.a_ax_b + sp * p.a_p_b + sq * p.a_q_b + p.a_col_b;
+  for (int b = p.lo_b - p.lo_b % 16 + sub * 16; b < p.hi_b; b += LPR * 16) {
+    // element e of this chunk is valid when b + e*ESIZE lies in [lo_b, hi_b)
+    const bool whole = b >= p.lo_b && b + 16 <= p.hi_b;
+    double acc[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const int bb = b + e * ESIZE;
+      acc[e] = 0.0;
+      if (bb >= p.lo_b && bb < p.hi_b) {
+        const uint64_t bits = load_elem<ESIZE>(arow + bb);
+        acc[e] = ESIZE == 4 ? (double)__uint_as_float((uint32_t)bits) : __longlong_as_double((long long)bits);
+      }
+    }
+    float accf[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) accf[e] = (float)acc[e];
+    for (int32_t k = k0; k < k1; k += 4) {
+      u32x4 v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[q] = (u32x4){0, 0, 0, 0};
+        if (k + q < k1) {
+          int64_t t_off;
+          dest_row_id(p, perm[k + q], t_off);
+          const char* trow = p.t + t_off;
+          if (whole) {
+            v[q] = ld16(trow + b);
+          } else {
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+              const int bb = b + e * ESIZE;
+              if (bb >= p.lo_b && bb < p.hi_b) vec_set<ESIZE>(v[q], e, load_elem<ESIZE>(trow + bb));
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (k + q >= k1) break;
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const uint64_t bits = vec_get<ESIZE>(v[q], e);
+          if (ESIZE == 4)
+            accf[e] += __uint_as_float((uint32_t)bits);
+          else
+            acc[e] += __longlong_as_double((long long)bits);
+        }
+      }
+    }
+    u32x4 out = {0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const uint64_t bits = ESIZE == 4 ? (uint64_t)__float_as_uint(accf[e]) : (uint64_t)__double_as_longlong(acc[e]);
+      vec_set<ESIZE>(out, e, bits);
+    }
+    if (whole) {
+      st16(arow + b, out);
+    } else {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const int bb = b + e * ESIZE;
+        if (bb >= p.lo_b && bb < p.hi_b) store_elem<ESIZE>(arow + bb, vec_get<ESIZE>(out, e));
+      }
+    }
   }
 }
 
 // ---- host side -------------------------------------------------------------
 
-enum class Op { Gather, GatherMasked, Scatter };
+enum class Op { Gather, GatherMasked, Scatter, GatherBackward };
 
 const char* op_name(Op op) {
-  return op == Op::Gather ? "tile_gather" : op == Op::GatherMasked ? "tile_gather_masked" : "tile_scatter_masked";
+  return op == Op::Gather         ? "tile_gather"
+         : op == Op::GatherMasked ? "tile_gather_masked"
+         : op == Op::Scatter      ? "tile_scatter_masked"
+                                  : "tile_gather_backward";
 }
 
 int launch_rows(Op op, int esize, const RowParams& p, int64_t grid, hipStream_t s) {
@@ -262,12 +508,20 @@ int launch_rows(Op op, int esize, const RowParams& p, int64_t grid, hipStream_t 
   const bool full = p.lo_b == 0 && p.hi_b == p.row_bytes && p.row_bytes % 16 == 0;
 #define STG_ROWS(K, E) \
   full ? launch_kernel(op_name(op), K<E, true>, g, b, 0, s, p) : launch_kernel(op_name(op), K<E, false>, g, b, 0, s, p)
-  if (op == Op::Scatter) {
+#define STG_ROWS_S(E, A)                                                                        \
+  full ? launch_kernel(op_name(op), scatter_rows_kernel<E, true, A>, g, b, 0, s, p)              \
+       : launch_kernel(op_name(op), scatter_rows_kernel<E, false, A>, g, b, 0, s, p)
+  if (op == Op::GatherBackward) {
+    if (esize == 4)
+      STG_ROWS_S(4, true);
+    else
+      STG_ROWS_S(8, true);
+  } else if (op == Op::Scatter) {
     switch (esize) {
-      case 1: STG_ROWS(scatter_rows_kernel, 1); break;
-      case 2: STG_ROWS(scatter_rows_kernel, 2); break;
-      case 4: STG_ROWS(scatter_rows_kernel, 4); break;
-      default: STG_ROWS(scatter_rows_kernel, 8); break;
+      case 1: STG_ROWS_S(1, false); break;
+      case 2: STG_ROWS_S(2, false); break;
+      case 4: STG_ROWS_S(4, false); break;
+      default: STG_ROWS_S(8, false); break;
     }
   } else {
     switch (esize) {
@@ -278,18 +532,24 @@ int launch_rows(Op op, int esize, const RowParams& p, int64_t grid, hipStream_t 
     }
   }
 #undef STG_ROWS
+#undef STG_ROWS_S
   return check_launch(op_name(op));
 }
 
 int launch_elems(Op op, int esize, const ElemParams& p, hipStream_t s) {
   const int64_t want = (p.n + kThreads - 1) / kThreads;
   const dim3 g((unsigned)(want < 65536 ? want : 65536)), b(kThreads);
-  if (op == Op::Scatter) {
+  if (op == Op::GatherBackward) {
+    if (esize == 4)
+      launch_kernel(op_name(op), scatter_elem_kernel<4, true>, g, b, 0, s, p);
+    else
+      launch_kernel(op_name(op), scatter_elem_kernel<8, true>, g, b, 0, s, p);
+  } else if (op == Op::Scatter) {
     switch (esize) {
-      case 1: launch_kernel(op_name(op), scatter_elem_kernel<1>, g, b, 0, s, p); break;
-      case 2: launch_kernel(op_name(op), scatter_elem_kernel<2>, g, b, 0, s, p); break;
-      case 4: launch_kernel(op_name(op), scatter_elem_kernel<4>, g, b, 0, s, p); break;
-      default: launch_kernel(op_name(op), scatter_elem_kernel<8>, g, b, 0, s, p); break;
+      case 1: launch_kernel(op_name(op), scatter_elem_kernel<1, false>, g, b, 0, s, p); break;
+      case 2: launch_kernel(op_name(op), scatter_elem_kernel<2, false>, g, b, 0, s, p); break;
+      case 4: launch_kernel(op_name(op), scatter_elem_kernel<4, false>, g, b, 0, s, p); break;
+      default: launch_kernel(op_name(op), scatter_elem_kernel<8, false>, g, b, 0, s, p); break;
     }
   } else {
     switch (esize) {
@@ -304,14 +564,67 @@ int launch_elems(Op op, int esize, const ElemParams& p, hipStream_t s) {
 
 // Shared argument checks and dispatch of the three entry points.  `a` is the
 // indexed array; `t` the dense side (gather output, scatter input).
+// Segmented backward: workspace layout and size (bytes) for R destination
+// rows and n_rows grad_out rows.
+struct SegLayout {
+  int64_t count, offs, perm, rank, bsum, bytes, nb;
+};
+
+SegLayout seg_layout(int64_t R, int64_t n_rows) {
+  SegLayout L;
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  L.nb = (R + kScanBlock - 1) / kScanBlock;
+  L.count = 0;
+  L.offs = up(L.count + R * 4);
+  L.perm = up(L.offs + (R + 1) * 4);
+  L.rank = up(L.perm + n_rows * 4);
+  L.bsum = up(L.rank + n_rows * 4);
+  L.bytes = up(L.bsum + L.nb * 4);
+  return L;
+}
+
+int launch_segmented(const char* name, int esize, const RowParams& p, int64_t R, char* ws, hipStream_t s) {
+  const SegLayout L = seg_layout(R, p.n_rows);
+  int32_t* count = (int32_t*)(ws + L.count);
+  int32_t* offs = (int32_t*)(ws + L.offs);
+  int32_t* perm = (int32_t*)(ws + L.perm);
+  int32_t* rank = (int32_t*)(ws + L.rank);
+  int32_t* bsum = (int32_t*)(ws + L.bsum);
+  auto gs = [](int64_t n) { return dim3((unsigned)std::min<int64_t>((n + kThreads - 1) / kThreads, 65536)); };
+  launch_kernel("tile_gather_backward/zero", seg_zero_kernel, gs(R), dim3(kThreads), 0, s, count, R);
+  launch_kernel("tile_gather_backward/hist", seg_hist_kernel, gs(p.n_rows), dim3(kThreads), 0, s, p, count, rank);
+  launch_kernel("tile_gather_backward/bsum", seg_bsum_kernel, dim3((unsigned)L.nb), dim3(kThreads), 0, s,
+                (const int32_t*)count, R, bsum);
+  launch_kernel("tile_gather_backward/bscan", seg_bscan_kernel, dim3(1), dim3(kThreads), 0, s, bsum, L.nb);
+  launch_kernel("tile_gather_backward/offs", seg_offs_kernel, dim3((unsigned)L.nb), dim3(kThreads), 0, s, count, R,
+                (const int32_t*)bsum, offs);
+  launch_kernel("tile_gather_backward/fill", seg_fill_kernel, gs(p.n_rows), dim3(kThreads), 0, s, p,
+                (const int32_t*)rank, (const int32_t*)offs, perm);
+  // lanes per destination row: enough for the row's chunks, at most a wavefront
+  const int chunks = p.n_chunks;
+  const int lpr = chunks <= 8 ? 8 : chunks <= 16 ? 16 : chunks <= 32 ? 32 : 64;
+  const dim3 grid((unsigned)((R + kThreads / lpr - 1) / (kThreads / lpr)));
+#define STG_SEG(E, LP) launch_kernel("tile_gather_backward/reduce", seg_reduce_kernel<E, LP>, grid, dim3(kThreads), 0, s, \
+                                     p, R, (const int32_t*)offs, (const int32_t*)perm)
+  if (esize == 4) {
+    if (lpr == 8) STG_SEG(4, 8); else if (lpr == 16) STG_SEG(4, 16); else if (lpr == 32) STG_SEG(4, 32); else STG_SEG(4, 64);
+  } else {
+    if (lpr == 8) STG_SEG(8, 8); else if (lpr == 16) STG_SEG(8, 16); else if (lpr == 32) STG_SEG(8, 32); else STG_SEG(8, 64);
+  }
+#undef STG_SEG
+  return check_launch(name);
+}
+
 int run(Op op, const stg_tensor* a, const int32_t* indices, const uint8_t* mask, int64_t n_indices,
         const int64_t* tile_shape, const int64_t* offset, int32_t axis, double padding_value,
-        const stg_tensor* t, void* stream) {
+        const stg_tensor* t, void* stream, void* workspace = nullptr, int64_t workspace_bytes = 0) {
   clear_error();
   const char* name = op_name(op);
   int rc;
   if ((rc = check_tensor(a, name)) || (rc = check_tensor(t, name))) return rc;
   if (a->dtype != t->dtype) return fail(STG_ERR_INVALID, "%s: dtype mismatch", name);
+  if (op == Op::GatherBackward && a->dtype != STG_F32 && a->dtype != STG_F64)
+    return fail(STG_ERR_UNSUPPORTED, "%s: gradients must be STG_F32 or STG_F64 (hardware float atomics)", name);
   if (a->rank != t->rank) return fail(STG_ERR_INVALID, "%s: rank mismatch", name);
   const int rank = a->rank;
   if (axis < 0 || axis >= rank) return fail(STG_ERR_INVALID, "%s: axis %d not in [0, %d)", name, axis, rank);
@@ -328,7 +641,8 @@ int run(Op op, const stg_tensor* a, const int32_t* indices, const uint8_t* mask,
     const int64_t want = d == axis ? n_indices : tile_shape[d];
     if (t->shape[d] != want)
       return fail(STG_ERR_INVALID, "%s: %s shape[%d] is %lld, expected %lld", name,
-                  op == Op::Scatter ? "tile" : "out", d, (long long)t->shape[d], (long long)want);
+                  op == Op::Scatter ? "tile" : op == Op::GatherBackward ? "grad_out" : "out", d,
+                  (long long)t->shape[d], (long long)want);
   }
   int64_t off[4] = {0, 0, 0, 0};
   if (offset)
@@ -354,7 +668,7 @@ int run(Op op, const stg_tensor* a, const int32_t* indices, const uint8_t* mask,
     p.a = (const char*)a->data;
     p.t = (char*)t->data;
     p.indices = indices;
-    p.mask = op == Op::Gather ? nullptr : mask;
+    p.mask = op == Op::Gather || op == Op::GatherBackward ? nullptr : mask;
     p.ax_off = off[axis];
     p.ax_ext = a->shape[axis];
     p.a_ax_b = a->stride[axis] * es;
@@ -393,13 +707,24 @@ int run(Op op, const stg_tensor* a, const int32_t* indices, const uint8_t* mask,
     p.rows_per_wg = (int32_t)rows;
     const int64_t grid = (p.n_rows + rows - 1) / rows;
     if (grid > INT32_MAX) return fail(STG_ERR_RANGE, "%s: too many rows", name);
+    if (op == Op::GatherBackward && workspace) {
+      const int64_t R = p.ax_ext * p.p_ext * p.q_ext;
+      if (R >= INT32_MAX || p.n_rows >= INT32_MAX)
+        return fail(STG_ERR_RANGE, "%s: the segmented path needs fewer than 2^31 rows and terms", name);
+      if (workspace_bytes < seg_layout(R, p.n_rows).bytes)
+        return fail(STG_ERR_INVALID, "%s: workspace of %lld bytes, %lld needed", name, (long long)workspace_bytes,
+                    (long long)seg_layout(R, p.n_rows).bytes);
+      if (((uintptr_t)workspace & 255) != 0) return fail(STG_ERR_INVALID, "%s: workspace must be 256-byte aligned", name);
+      if (R == 0) return STG_OK;
+      return launch_segmented(name, es, p, R, (char*)workspace, s);
+    }
     return launch_rows(op, es, p, grid, s);
   }
   ElemParams p{};
   p.a = (const char*)a->data;
   p.t = (char*)t->data;
   p.indices = indices;
-  p.mask = op == Op::Gather ? nullptr : mask;
+  p.mask = op == Op::Gather || op == Op::GatherBackward ? nullptr : mask;
   p.rank = rank;
   p.axis = axis;
   p.n = numel;
@@ -435,4 +760,34 @@ extern "C" int tile_scatter_masked(const stg_tensor* a, const int32_t* indices, 
                                    int64_t n_indices, const int64_t* tile_shape, const int64_t* offset,
                                    int32_t axis, const stg_tensor* tile, void* stream) {
   return run(Op::Scatter, a, indices, mask, n_indices, tile_shape, offset, axis, 0.0, tile, stream);
+}
+
+extern "C" int tile_gather_backward(const stg_tensor* a_grad, const int32_t* indices, int64_t n_indices,
+                                    const int64_t* tile_shape, const int64_t* offset, int32_t axis,
+                                    const stg_tensor* grad_out, void* workspace, int64_t workspace_bytes,
+                                    void* stream) {
+  return run(Op::GatherBackward, a_grad, indices, nullptr, n_indices, tile_shape, offset, axis, 0.0, grad_out, stream,
+             workspace, workspace_bytes);
+}
+
+extern "C" int64_t tile_gather_backward_workspace(const stg_tensor* a_grad, int64_t n_indices,
+                                                  const int64_t* tile_shape, int32_t axis) {
+  clear_error();
+  const char* name = "tile_gather_backward_workspace";
+  int rc;
+  if ((rc = check_tensor(a_grad, name))) return -rc;
+  const int rank = a_grad->rank, last = rank - 1;
+  if (axis < 0 || axis >= rank || !tile_shape || n_indices < 0)
+    return -fail(STG_ERR_INVALID, "%s: bad axis, tile_shape or n_indices", name);
+  for (int d = 0; d < rank; ++d)
+    if (tile_shape[d] < 1) return -fail(STG_ERR_INVALID, "%s: tile_shape[%d] < 1", name, d);
+  const int es = dtype_size(a_grad->dtype);
+  // the segmented path serves the row layout only (as the row kernels do)
+  if (rank < 2 || axis == last || a_grad->stride[last] != 1 || tile_shape[last] * es > 16 * 4096) return 0;
+  int64_t R = 1, rest = 1;
+  for (int d = 0; d < last; ++d) {
+    R *= a_grad->shape[d];
+    if (d != axis) rest *= tile_shape[d];
+  }
+  return seg_layout(R, n_indices * rest).bytes;
 }

@@ -217,3 +217,23 @@ def test_window_argument_errors_and_broken_promise(stg):
     assert b"null" in lib.stg_last_error()
     # an empty grid is a successful no-op without touching the GPU
     assert lib.tile_copy_windows(B(m), 8, 8, 8, 8, 64, 0, 1, None, None) == 0
+
+
+def test_gather_backward_workspace_query_and_errors(stg):
+    lib = stg.load_library()
+    B = ctypes.byref
+    g = _t([1024, 256], dtype=0)
+    ts = _i64([64, 256])
+    # row layout: count + offsets + terms + ranks + block sums, each 256-byte aligned
+    nbytes = lib.tile_gather_backward_workspace(B(g), 4096, ts, 0)
+    assert nbytes == 4096 + 4352 + 16384 + 16384 + 256
+    # gather along the last axis: atomics only, no workspace
+    assert lib.tile_gather_backward_workspace(B(g), 4096, _i64([1024, 64]), 1) == 0
+    assert lib.tile_gather_backward_workspace(B(g), 4096, ts, 2) < 0
+    # unsupported gradient dtype; a workspace too small
+    bf = _t([1024, 256], dtype=1)
+    assert lib.tile_gather_backward(B(bf), 0x10, 4096, ts, None, 0, B(_t([4096, 256], dtype=1)), None, 0, None) == 2
+    out = _t([4096, 256], dtype=0)
+    assert lib.tile_gather_backward(B(g), 0x10, 4096, ts, None, 0, B(out), 0x1000, 1024, None) == 1
+    assert b"workspace" in lib.stg_last_error()
+    assert lib.tile_gather_backward(B(g), 0x10, 4096, ts, None, 0, B(out), 0x1001, 1 << 20, None) == 1  # alignment

@@ -1,0 +1,116 @@
+"""GPU parity of tile_gather_backward against the fp64 CPU oracle.
+
+The accumulation is atomic, so the order of the terms that land on one
+element is unspecified.  Tolerance (derived from the arithmetic): an element
+that receives k terms, summed in any order in the gradient's precision with
+unit roundoff u (2^-24 for fp32, 2^-53 for fp64), differs from the exact sum
+by at most gamma_k * S, gamma_k = k u / (1 - k u), where S is the sum of the
+magnitudes of the initial value and of every term; the fp64 oracle's own
+rounding adds at most gamma_k(2^-53) * S.  Elements with no term keep their
+initial bits exactly, and a single term onto zero is exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+from scatter_tile_gather_amd import inputs
+from gpu_util import say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _gamma(k, u):
+    ku = k * u
+    return ku / (1.0 - ku)
+
+
+def check_backward(got, a0, acc, abs_sum, count):
+    u = 2.0 ** -24 if got.dtype == np.float32 else 2.0 ** -53
+    tol = (_gamma(count, u) + _gamma(count, 2.0 ** -53)) * abs_sum
+    err = np.abs(got.astype(np.float64) - acc)
+    assert np.all(err <= tol), float((err - tol).max())
+    untouched = count == 0
+    np.testing.assert_array_equal(got[untouched], a0[untouched])
+
+
+def run_case(stg, orc, a0, idx, tile, g, off=None, axis=0, ws=None):
+    a_dev = to_dev(a0.copy())
+    stg.tile_gather_backward(a_dev, to_dev(idx.astype(np.int32)), tile, to_dev(g), off, axis, workspace=ws)
+    torch.cuda.synchronize()
+    got = to_host(a_dev)
+    acc, abs_sum, count = orc.tile_gather_backward(a0, idx, tile, g, off, axis)
+    check_backward(got, a0, acc, abs_sum, count)
+    return got, count
+
+
+@pytest.mark.parametrize("ws", [None, "auto"])
+def test_backward_row_gather_workload(stg, orc, ws):
+    w = inputs.row_gather()
+    rng = np.random.default_rng(2024)
+    a0 = np.zeros(w["a"].shape, np.float32)
+    g = rng.standard_normal((w["indices"].size, w["a"].shape[1])).astype(np.float32)
+    say("gather backward: row gather workload (1024,256) fp32, 4096 indices with repeats and out-of-range, ws", ws)
+    _, count = run_case(stg, orc, a0, w["indices"], w["tile_shape"], g, w["offset"], w["axis"], ws)
+    assert count.max() >= 3  # repeated rows really accumulate
+
+
+@pytest.mark.parametrize("ws", [None, "auto"])
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_backward_permutation_is_exact(stg, orc, dtype, ws):
+    rng = np.random.default_rng(11)
+    idx = rng.permutation(512).astype(np.int32)
+    g = rng.standard_normal((512, 96)).astype(dtype)
+    say("gather backward: permutation (512,96)", np.dtype(dtype).name, "ws", ws)
+    got, _ = run_case(stg, orc, np.zeros((512, 96), dtype), idx, (64, 96), g, ws=ws)
+    want = np.zeros((512, 96), dtype)
+    want[idx] = g
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("ws", [None, "auto"])
+@pytest.mark.parametrize("seed", range(20))
+def test_backward_random(stg, orc, seed, ws):
+    rng = np.random.default_rng(6100 + seed)
+    dtype = [np.float32, np.float64][seed % 2]
+    rank = int(rng.integers(2, 5))
+    shape = [int(rng.integers(1, 12)) for _ in range(rank)]
+    shape[-1] = int(rng.integers(1, 70))
+    axis = int(rng.integers(0, rank))
+    tile = [int(rng.integers(1, s + 3)) for s in shape]
+    T = tile[axis]
+    n_idx = T * int(rng.integers(1, 6))
+    idx = rng.integers(-3, shape[axis] + 3, n_idx).astype(np.int32)  # repeats and out-of-range
+    off = [int(rng.integers(-2, 3)) for _ in range(rank)]
+    off[axis] = int(rng.integers(-1, 2))
+    g_shape = list(tile)
+    g_shape[axis] = n_idx
+    a0 = rng.standard_normal(shape).astype(dtype)
+    g = rng.standard_normal(g_shape).astype(dtype)
+    say("gather backward random", seed, np.dtype(dtype).name, "shape", shape, "tile", tile, "axis", axis, "off", off,
+        "n_idx", n_idx, "ws", ws)
+    run_case(stg, orc, a0, idx, tile, g, off, axis, ws)
+
+
+@pytest.mark.parametrize("ws", [None, "auto"])
+def test_backward_embedding_scale(stg, orc, ws):
+    """(262144, 128) fp32 gradient table, 1,048,576 indices drawn uniformly
+    (about four terms per row), (64, 128) tiles."""
+    rng = np.random.default_rng(77)
+    rows = 262144
+    idx = rng.integers(0, rows, 1048576).astype(np.int32)
+    g = rng.standard_normal((idx.size, 128)).astype(np.float32)
+    a0 = rng.standard_normal((rows, 128)).astype(np.float32)
+    say("gather backward: embedding scale (262144,128) fp32, 1048576 indices, ws", ws)
+    run_case(stg, orc, a0, idx, (64, 128), g, ws=ws)
+
+
+def test_backward_grouped_long_segments(stg, orc):
+    """Grouped execution with a skewed index list: one row takes 5000 terms,
+    a few others hundreds, most none."""
+    rng = np.random.default_rng(91)
+    idx = np.concatenate([np.full(5000, 7), rng.integers(0, 40, 3000), rng.integers(0, 4096, 192)]).astype(np.int32)
+    rng.shuffle(idx)
+    g = rng.standard_normal((idx.size, 40)).astype(np.float32)
+    a0 = rng.standard_normal((4096, 40)).astype(np.float32)
+    say("gather backward grouped: skewed segments")
+    run_case(stg, orc, a0, idx, (8, 40), g, ws="auto")
