@@ -81,6 +81,10 @@ def _load():
         "orc_tile_gather_backward": (None, [_P, _P, _I64, _P, _P, _I32, _P, _P, _P, _P]),
         "orc_tile_copy_windows": (None, [_P, _I64, _I64, _I64, _I64, _I64, _I64, _P]),
         "orc_tile_store_windows": (None, [_P, _I32, _I64, _I64, _I64, _I64, _I64, _I64, _P]),
+        "orc_decode_lowp": (ctypes.c_double, [ctypes.c_uint8, _I32]),
+        "orc_decode_scale": (ctypes.c_double, [ctypes.c_uint8, _I32]),
+        "orc_gemm_scaled": (None, [_P, _I32, _I64, _P, _I64, _P, _I32, _I64, _P, _I64, _I32, _P, _I64, _I64, _I64,
+                                   _I64, _I64, _P]),
         "orc_ragged_tile_store": (None, [_P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _P]),
         "orc_bf16_to_f64": (ctypes.c_double, [ctypes.c_uint16]),
         "orc_gemm_f64": (None, [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64]),
@@ -303,6 +307,45 @@ def ragged_tile_store(tiles, X, middle_dim: int, group: int, col0: int, ri, dyn,
     _load().orc_ragged_tile_store(_ptr(tiles), out.itemsize, out.shape[0], middle_dim, group, out.shape[2], BM, BN,
                                   col0, _ptr(ri), _ptr(dyn), _ptr(mi), n, _ptr(out))
     return out
+
+
+# ---- block-scaled GEMM -------------------------------------------------------
+
+LOWP = {"e4m3": 0, "e5m2": 1, "e2m1": 2}
+SCALES = {"e8m0": 0, "e4m3": 1}
+
+
+def decode_lowp(codes, fmt: str) -> np.ndarray:
+    """Exact fp64 values of e4m3 / e5m2 / e2m1 codes (e2m1: low 4 bits of each code)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    lib = _load()
+    return np.array([lib.orc_decode_lowp(int(c), LOWP[fmt]) for c in codes.ravel()]).reshape(codes.shape)
+
+
+def decode_scale(codes, fmt: str) -> np.ndarray:
+    codes = np.asarray(codes, dtype=np.uint8)
+    lib = _load()
+    return np.array([lib.orc_decode_scale(int(c), SCALES[fmt]) for c in codes.ravel()]).reshape(codes.shape)
+
+
+def gemm_scaled_f64(A, a_fmt, a_scale, Bt, b_fmt, b_scale, K: int, block: int, s_fmt="e8m0", acc=None) -> np.ndarray:
+    """fp64 (A . a_scale)(B . b_scale) + acc.  A: uint8 (M, bytes per row), Bt:
+    uint8 (N, bytes per row) = B transposed, K-major; e2m1 packs two values per
+    byte (low nibble first); scales uint8 (M, K/block) and (N, K/block)."""
+    A, Bt = np.ascontiguousarray(A, dtype=np.uint8), np.ascontiguousarray(Bt, dtype=np.uint8)
+    a_scale = np.ascontiguousarray(a_scale, dtype=np.uint8)
+    b_scale = np.ascontiguousarray(b_scale, dtype=np.uint8)
+    M, N = A.shape[0], Bt.shape[0]
+    assert K % block == 0 and a_scale.shape == (M, K // block) and b_scale.shape == (N, K // block)
+    C = np.empty((M, N), dtype=np.float64)
+    accp, ldacc = None, 0
+    if acc is not None:
+        acc = np.ascontiguousarray(acc, dtype=np.float32)
+        accp, ldacc = _ptr(acc), acc.shape[1]
+    _load().orc_gemm_scaled(_ptr(A), LOWP[a_fmt], A.shape[1], _ptr(a_scale), a_scale.shape[1], _ptr(Bt), LOWP[b_fmt],
+                            Bt.shape[1], _ptr(b_scale), b_scale.shape[1], SCALES[s_fmt], accp, ldacc, M, N, K, block,
+                            _ptr(C))
+    return C
 
 
 # ---- GEMM ------------------------------------------------------------------

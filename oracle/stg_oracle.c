@@ -380,6 +380,56 @@ void orc_ragged_tile_store(const void* tiles_in, int32_t esize, int64_t total_ro
   }
 }
 
+double orc_decode_lowp(uint8_t code, int32_t fmt) {
+  int s, e, m, ebits, mbits, bias;
+  if (fmt == ORC_LP_E4M3) {
+    ebits = 4, mbits = 3, bias = 7;
+  } else if (fmt == ORC_LP_E5M2) {
+    ebits = 5, mbits = 2, bias = 15;
+  } else {
+    ebits = 2, mbits = 1, bias = 1;
+    code &= 0xF;
+  }
+  s = (code >> (ebits + mbits)) & 1;
+  e = (code >> mbits) & ((1 << ebits) - 1);
+  m = code & ((1 << mbits) - 1);
+  const double sign = s ? -1.0 : 1.0;
+  if (fmt == ORC_LP_E4M3 && e == 15 && m == 7) return NAN;
+  if (fmt == ORC_LP_E5M2 && e == 31) return m == 0 ? sign * INFINITY : NAN;
+  if (e == 0) return sign * ldexp((double)m, 1 - bias - mbits); /* subnormal: m / 2^mbits * 2^(1 - bias) */
+  return sign * ldexp((double)((1 << mbits) + m), e - bias - mbits);
+}
+
+double orc_decode_scale(uint8_t code, int32_t fmt) {
+  if (fmt == ORC_SC_E8M0) return code == 0xFF ? NAN : ldexp(1.0, (int)code - 127);
+  return orc_decode_lowp(code, ORC_LP_E4M3);
+}
+
+/* element k of a row of low-precision values */
+static double lowp_at(const uint8_t* row, int64_t k, int32_t fmt) {
+  if (fmt == ORC_LP_E2M1) {
+    const uint8_t byte = row[k / 2];
+    return orc_decode_lowp((uint8_t)(k % 2 == 0 ? byte & 0xF : byte >> 4), fmt);
+  }
+  return orc_decode_lowp(row[k], fmt);
+}
+
+void orc_gemm_scaled(const uint8_t* A, int32_t a_fmt, int64_t lda_bytes, const uint8_t* a_scale,
+                     int64_t lds_a, const uint8_t* Bt, int32_t b_fmt, int64_t ldb_bytes,
+                     const uint8_t* b_scale, int64_t lds_b, int32_t s_fmt, const float* acc,
+                     int64_t ldacc, int64_t M, int64_t N, int64_t K, int64_t block, double* C) {
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = 0; n < N; ++n) {
+      double sum = acc ? (double)acc[m * ldacc + n] : 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const double a = lowp_at(A + m * lda_bytes, k, a_fmt) * orc_decode_scale(a_scale[m * lds_a + k / block], s_fmt);
+        const double b = lowp_at(Bt + n * ldb_bytes, k, b_fmt) * orc_decode_scale(b_scale[n * lds_b + k / block], s_fmt);
+        sum += a * b;
+      }
+      C[m * N + n] = sum;
+    }
+}
+
 double orc_bf16_to_f64(uint16_t h) {
   uint32_t bits = (uint32_t)h << 16;
   float f;

@@ -178,6 +178,38 @@ void orc_ragged_tile_store(const void* tiles_in, int32_t esize, int64_t total_ro
                            const uint32_t* ragged_idx, const uint32_t* dynamic_dim,
                            const uint32_t* middle_idx, int64_t n_tiles, void* X);
 
+/* Low-precision element and scale formats of block-scaled GEMM (cuTile.jl
+ * Operations, muladd_scaled: a / b are f8e4m3fn, f8e5m2 or f4e2m1fn; a_scale /
+ * b_scale are f8e8m0fnu or f8e4m3fn).  Decoded exactly to double from the
+ * format definitions:
+ *   e4m3fn  sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent 0 is
+ *           subnormal (m/8 * 2^-6); S.1111.111 is NaN; no infinities.
+ *   e5m2    sign, 5 exponent bits (bias 15), 2 mantissa bits, IEEE rules
+ *           (exponent 31: infinity when m = 0, else NaN).
+ *   e2m1    sign, 2 exponent bits (bias 1), 1 mantissa bit, no NaN or
+ *           infinity: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+ *   e8m0    unsigned exponent byte e: 2^(e - 127); 0xFF is NaN. */
+enum { ORC_LP_E4M3 = 0, ORC_LP_E5M2 = 1, ORC_LP_E2M1 = 2 };
+enum { ORC_SC_E8M0 = 0, ORC_SC_E4M3 = 1 };
+double orc_decode_lowp(uint8_t code, int32_t fmt); /* fmt ORC_LP_*; e2m1 uses the low 4 bits */
+double orc_decode_scale(uint8_t code, int32_t fmt); /* fmt ORC_SC_* */
+
+/* Block-scaled GEMM (cuTile.jl Operations, muladd_scaled: (a . a_scale) *
+ * (b . b_scale) + acc, each scale element multiplying a contiguous block of
+ * `block` = K / K_s values along K of its operand, f32 accumulation).
+ * A is (M, K) with K contiguous, row stride lda_bytes; B is given K-major as
+ * Bt (N, K) = B transposed, row stride ldb_bytes.  e2m1 operands hold two
+ * values per byte, element k at byte k/2, the even element in the low nibble
+ * (cuTile.jl Operations, reinterpret: a UInt8 tile of N bytes is an FP4 tile
+ * of 2N values).  a_scale is (M, K/block) bytes with row stride lds_a,
+ * b_scale (N, K/block) with row stride lds_b.  acc is (M, N) f32 with row
+ * stride ldacc, or NULL for zero.  C (M, N) dense row-major, in fp64:
+ *   C[m][n] = acc[m][n] + sum_k A(m,k) sa(m, k/block) B(k,n) sb(n, k/block) */
+void orc_gemm_scaled(const uint8_t* A, int32_t a_fmt, int64_t lda_bytes, const uint8_t* a_scale,
+                     int64_t lds_a, const uint8_t* Bt, int32_t b_fmt, int64_t ldb_bytes,
+                     const uint8_t* b_scale, int64_t lds_b, int32_t s_fmt, const float* acc,
+                     int64_t ldacc, int64_t M, int64_t N, int64_t K, int64_t block, double* C);
+
 /* Decode one bf16 bit pattern to double (exact: bf16 is the top half of
  * an IEEE binary32). */
 double orc_bf16_to_f64(uint16_t h);

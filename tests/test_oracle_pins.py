@@ -701,6 +701,101 @@ def test_windows_overlapping_store_of_consistent_tiles_rebuilds_the_covered_regi
 
 
 # ---------------------------------------------------------------------------
+# block-scaled GEMM: low-precision formats and the scaled product
+# ---------------------------------------------------------------------------
+
+def test_e2m1_decodes_to_its_value_set(orc):
+    mags = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    np.testing.assert_array_equal(orc.decode_lowp(np.arange(16), "e2m1"), mags + [-m for m in mags])
+
+
+def test_e5m2_is_the_top_byte_of_an_ieee_half(orc):
+    codes = np.arange(256, dtype=np.uint16)
+    want = (codes << 8).astype(np.uint16).view(np.float16).astype(np.float64)
+    np.testing.assert_array_equal(orc.decode_lowp(codes.astype(np.uint8), "e5m2"), want)
+
+
+def test_e4m3fn_structure(orc):
+    v = orc.decode_lowp(np.arange(256, dtype=np.uint8), "e4m3")
+    pos = v[:128]
+    assert np.isnan(pos[0x7F]) and np.isnan(v[0xFF]) and not np.isinf(v).any()
+    fin = pos[:0x7F]
+    assert np.all(np.diff(fin) > 0) and fin[0] == 0 and fin.size == 127  # monotone, 127 non-negative finite values
+    assert fin[-1] == 448 and pos[0x38] == 1.0 and pos[0x08] == 2.0 ** -6 and pos[0x01] == 2.0 ** -9
+    np.testing.assert_array_equal(v[128:255], -fin)  # the sign bit mirrors
+    # at most 4 significant bits: every value is an integer multiple of its
+    # leading power of two divided by 8, and subnormals are multiples of 2^-9
+    for x in fin[1:]:
+        e = np.floor(np.log2(x))
+        q = x / 2.0 ** max(e - 3, -9)
+        assert q == int(q)
+
+
+def test_e8m0_is_a_power_of_two(orc):
+    codes = np.arange(255, dtype=np.uint8)
+    np.testing.assert_array_equal(orc.decode_scale(codes, "e8m0"), np.ldexp(1.0, codes.astype(int) - 127))
+    assert np.isnan(orc.decode_scale([255], "e8m0")[0])
+    np.testing.assert_array_equal(orc.decode_scale([0x38, 0x7E], "e4m3"), [1.0, 448.0])
+
+
+def _pack_e2m1(codes):
+    codes = np.asarray(codes, dtype=np.uint8)
+    return (codes[..., 0::2] & 0xF) | ((codes[..., 1::2] & 0xF) << 4)
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e2m1", "e2m1")])
+def test_scaled_gemm_with_unit_scales_is_the_plain_product(orc, fa, fb):
+    rng = np.random.default_rng(500)
+    M, N, K, block = 9, 7, 96, 32
+
+    def codes(shape, fmt):
+        c = rng.integers(0, 256 if fmt != "e2m1" else 16, shape).astype(np.uint8)
+        if fmt == "e4m3":
+            c[(c & 0x7F) == 0x7F] = 0x38  # no NaN
+        if fmt == "e5m2":
+            c[(c & 0x7C) == 0x7C] = 0x3C  # no infinity or NaN
+        return c
+
+    ca, cb = codes((M, K), fa), codes((N, K), fb)
+    A = _pack_e2m1(ca) if fa == "e2m1" else ca
+    Bt = _pack_e2m1(cb) if fb == "e2m1" else cb
+    one = lambda r: np.full((r, K // block), 127, np.uint8)
+    got = orc.gemm_scaled_f64(A, fa, one(M), Bt, fb, one(N), K, block)
+    want = orc.decode_lowp(ca, fa) @ orc.decode_lowp(cb, fb).T
+    np.testing.assert_allclose(got, want, rtol=1e-14, atol=0)
+
+
+def test_scaled_gemm_scale_blocks_act_linearly(orc):
+    """Raising one a_scale element from 2^e to 2^(e+3) adds 7 times that
+    block's contribution to its row, and changes nothing else."""
+    rng = np.random.default_rng(501)
+    M, N, K, block = 4, 5, 128, 64
+    ca = rng.integers(0, 0x70, (M, K)).astype(np.uint8)
+    cb = rng.integers(0, 0x70, (N, K)).astype(np.uint8)
+    sa = rng.integers(120, 134, (M, K // block)).astype(np.uint8)
+    sb = rng.integers(120, 134, (N, K // block)).astype(np.uint8)
+    base = orc.gemm_scaled_f64(ca, "e4m3", sa, cb, "e4m3", sb, K, block)
+    sa2 = sa.copy()
+    sa2[2, 1] += 3
+    bumped = orc.gemm_scaled_f64(ca, "e4m3", sa2, cb, "e4m3", sb, K, block)
+    a = orc.decode_lowp(ca, "e4m3") * np.repeat(orc.decode_scale(sa, "e8m0"), block, axis=1)
+    b = orc.decode_lowp(cb, "e4m3") * np.repeat(orc.decode_scale(sb, "e8m0"), block, axis=1)
+    contrib = a[2, 64:] @ b[:, 64:].T
+    want = base.copy()
+    want[2] += 7 * contrib
+    np.testing.assert_allclose(bumped, want, rtol=1e-13, atol=1e-300)
+
+
+def test_scaled_gemm_fp4_nibble_order_and_accumulator(orc):
+    """Hand-worked: byte 0x21 holds the e2m1 values (0.5, 1.0) -- the even
+    element in the low nibble -- and 0x11 holds (0.5, 0.5); with block 2,
+    scales 2^1 and 2^-1 and acc 0.25: 0.25 + 2 * (0.5*0.5 + 1.0*0.5) / 2."""
+    got = orc.gemm_scaled_f64(np.array([[0x21]]), "e2m1", np.array([[128]]), np.array([[0x11]]), "e2m1",
+                              np.array([[126]]), 2, 2, acc=np.array([[0.25]], np.float32))
+    assert got[0, 0] == 0.25 + 0.75
+
+
+# ---------------------------------------------------------------------------
 # bounded GEMM reference
 # ---------------------------------------------------------------------------
 
