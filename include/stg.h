@@ -276,6 +276,33 @@ int ragged_tile_store(const void* tiles_in, int32_t dtype, int64_t total_rows, i
                       const uint32_t* ragged_idx, const uint32_t* dynamic_dim,
                       const uint32_t* middle_idx, int64_t n_tiles, void* dst, void* stream);
 
+/* Block-scaled GEMM (cuTile.jl Operations, muladd_scaled: (a . a_scale) *
+ * (b . b_scale) + acc, each scale element multiplying a contiguous block of
+ * `block` = K / K_s values along K of its operand; operands f8e4m3fn, f8e5m2
+ * or f4e2m1fn, scales f8e8m0fnu or f8e4m3fn, f32 accumulator; reinterpret:
+ * FP4 values travel two per byte).
+ *   A        (M, K) operand codes, K contiguous, row stride lda BYTES.
+ *   Bt       B given K-major: (N, K), K contiguous, row stride ldb BYTES.
+ *            e2m1 packs two values per byte, element k at byte k/2, the even
+ *            element in the low nibble.
+ *   a_scale  (M, K/block) scale bytes, row stride lds_a; b_scale (N, K/block),
+ *            row stride lds_b; scale_fmt STG_SC_E8M0 (2^(e-127)) or STG_SC_E4M3.
+ *   acc      (M, N) f32, row stride ldacc, or NULL for zero; C (M, N) f32, row
+ *            stride ldc (C may be acc: the sum is written in place).
+ *   C[m][n] = acc[m][n] + sum_k A(m,k) sa(m,k/block) B(k,n) sb(n,k/block)
+ * in fp32 accumulation.  Only C[m][n] with m < M, n < N is written.
+ * Requirements: K a multiple of block; fp4 operands pair with fp4 operands.
+ * Supported here (else STG_ERR_UNSUPPORTED): e8m0 scales with block a multiple
+ * of 32 -- the scale granularity of the gfx950 scaled MFMA; e4m3 scales are
+ * not powers of two and would need a different instruction path.
+ * Errors as for gemm_bounded. */
+typedef enum { STG_LP_E4M3 = 0, STG_LP_E5M2 = 1, STG_LP_E2M1 = 2 } stg_lowp_format;
+typedef enum { STG_SC_E8M0 = 0, STG_SC_E4M3 = 1 } stg_scale_format;
+int gemm_scaled(const void* A, int32_t a_fmt, int64_t lda, const void* a_scale, int64_t lds_a,
+                const void* Bt, int32_t b_fmt, int64_t ldb, const void* b_scale, int64_t lds_b,
+                int32_t scale_fmt, int64_t block, const float* acc, int64_t ldacc, float* C,
+                int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream);
+
 /* Bounded-edge GEMM C = A . B (cuTile.jl Operations, muladd: bf16 operands
  * accumulate in f32; Tylo.jl Boundary tiles, "Accumulator stores and GEMM":
  * ceiling-division output grid and K loop, zero-filled edge stages, and an

@@ -10,6 +10,7 @@ from ._binding import (  # noqa: F401
     StgError,
     exported_names,
     gemm_bounded,
+    gemm_scaled,
     load_library,
     ragged_tile_load,
     ragged_tile_store,

@@ -57,6 +57,8 @@ _SIGNATURES = {
     "ragged_tile_load": (ctypes.c_int, [_P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _P, _P]),
     "ragged_tile_store": (ctypes.c_int, [_P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I64, _P, _P]),
     "gemm_bounded": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _I32, _P]),
+    "gemm_scaled": (ctypes.c_int, [_P, _I32, _I64, _P, _I64, _P, _I32, _I64, _P, _I64, _I32, _I64, _P, _I64, _P, _I64,
+                                   _I64, _I64, _I64, _P]),
     "stg_trace_enable": (ctypes.c_int, [ctypes.c_int]),
     "stg_trace_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float)]),
 }
@@ -411,4 +413,39 @@ def gemm_bounded(A, B, out=None, out_dtype=None, stream=None):
     code = _dtype_code(out)
     _check(lib.gemm_bounded(A.data_ptr(), A.stride(0), B.data_ptr(), B.stride(0), out.data_ptr(), out.stride(0), M,
                             N, K, code, _stream(stream)))
+    return out
+
+
+LOWP_FORMATS = {"e4m3": 0, "e5m2": 1, "e2m1": 2}
+SCALE_FORMATS = {"e8m0": 0, "e4m3": 1}
+
+
+def gemm_scaled(A, a_fmt: str, a_scale, Bt, b_fmt: str, b_scale, K: int, block: int, scale_fmt: str = "e8m0",
+                acc=None, out=None, stream=None):
+    """C = (A . a_scale)(B . b_scale) + acc, fp32.  A: uint8 (M, >= K*bits/8)
+    operand codes (e2m1: two per byte, even element low); Bt: uint8 (N, ...)
+    = B K-major; scales uint8 (M, >= K/block) and (N, >= K/block); acc / out
+    float32 (M, N)."""
+    torch = _torch()
+    lib = load_library()
+    for t, nm in ((A, "A"), (Bt, "Bt"), (a_scale, "a_scale"), (b_scale, "b_scale")):
+        _on_gpu(t, nm)
+        if t.dtype != torch.uint8 or t.dim() != 2 or (t.stride(1) != 1 and t.shape[1] > 1):
+            raise ValueError(f"{nm} must be a 2-D uint8 tensor with unit column stride")
+    M, N = A.shape[0], Bt.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    _on_gpu(out, "out")
+    if out.dtype != torch.float32 or tuple(out.shape) != (M, N) or (out.stride(1) != 1 and N > 1):
+        raise ValueError("out must be float32 (M, N) with unit column stride")
+    accp, ldacc = None, 0
+    if acc is not None:
+        _on_gpu(acc, "acc")
+        if acc.dtype != torch.float32 or tuple(acc.shape) != (M, N) or (acc.stride(1) != 1 and N > 1):
+            raise ValueError("acc must be float32 (M, N) with unit column stride")
+        accp, ldacc = acc.data_ptr(), acc.stride(0)
+    _check(lib.gemm_scaled(A.data_ptr(), LOWP_FORMATS[a_fmt], A.stride(0), a_scale.data_ptr(), a_scale.stride(0),
+                           Bt.data_ptr(), LOWP_FORMATS[b_fmt], Bt.stride(0), b_scale.data_ptr(), b_scale.stride(0),
+                           SCALE_FORMATS[scale_fmt], block, accp, ldacc, out.data_ptr(), out.stride(0), M, N, K,
+                           _stream(stream)))
     return out

@@ -237,3 +237,26 @@ def test_gather_backward_workspace_query_and_errors(stg):
     assert lib.tile_gather_backward(B(g), 0x10, 4096, ts, None, 0, B(out), 0x1000, 1024, None) == 1
     assert b"workspace" in lib.stg_last_error()
     assert lib.tile_gather_backward(B(g), 0x10, 4096, ts, None, 0, B(out), 0x1001, 1 << 20, None) == 1  # alignment
+
+
+def test_gemm_scaled_argument_errors(stg):
+    lib = stg.load_library()
+
+    def call(**kw):
+        a = dict(A=0x10, fa=0, lda=64, sa=0x10, lds_a=2, B=0x10, fb=0, ldb=64, sb=0x10, lds_b=2, sf=0, block=32,
+                 acc=None, ldacc=0, C=0x10, ldc=8, M=8, N=8, K=64)
+        a.update(kw)
+        return lib.gemm_scaled(a["A"], a["fa"], a["lda"], a["sa"], a["lds_a"], a["B"], a["fb"], a["ldb"], a["sb"],
+                               a["lds_b"], a["sf"], a["block"], a["acc"], a["ldacc"], a["C"], a["ldc"], a["M"], a["N"],
+                               a["K"], None)
+
+    assert call(sf=1) == 2  # e4m3 scales: not on the scaled MFMA
+    assert b"e8m0" in lib.stg_last_error()
+    assert call(block=16) == 2
+    assert call(fa=2) == 2  # fp4 with fp8
+    assert call(fa=7) == 2
+    assert call(K=96, block=64) == 1  # K not a multiple of the block
+    assert call(lda=32) == 1  # row stride shorter than the row
+    assert call(C=None) == 1
+    assert call(M=-1) == 1
+    assert call(M=0) == 0  # nothing to do
