@@ -34,6 +34,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA, TFLOP/s
+FP4_PEAK_TFLOPS = 10100.0  # MI355X dense fp4 MFMA, TFLOP/s
 
 
 def parse():
@@ -42,7 +44,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default="all",
-                    help="comma list of: copy,full,gather,masked,backward,ragged,gemm,calib (rocprof runs); 'all' for the "
+                    help="comma list of: copy,full,gather,masked,backward,ragged,gemm,scaled,calib (rocprof runs); 'all' for the "
                          "full report")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU time budget of the oracle baseline")
@@ -430,6 +432,36 @@ def run_gemm(stg, inputs, steps, warmup):
                            "TFLOPs_at_median": round(flop / (cmed * 1e-3) / 1e12, 1), "calls": 10}}
 
 
+def run_gemm_scaled(stg, inputs, steps, warmup):
+    """Block-scaled GEMM, fp8 e4m3 and fp4 e2m1 operands with e8m0 scales per
+    32 K values, fp32 output, on the bounded GEMM's odd M and N."""
+    import torch
+
+    M, N, K = 8191, 8193, 4096
+    out = {}
+    for fmt, peak in (("e4m3", FP8_PEAK_TFLOPS), ("e2m1", FP4_PEAK_TFLOPS)):
+        g = inputs.scaled_gemm(M, N, K, fmt)
+        A, Bt, sa, sb = _dev(g["A"]), _dev(g["Bt"]), _dev(g["sa"]), _dev(g["sb"])
+        C = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+        fn = lambda: stg.gemm_scaled(A, fmt, sa, Bt, fmt, sb, K, 32, out=C)
+        name = f"gemm_scaled_{'fp8' if fmt == 'e4m3' else 'fp4'}"
+        try:
+            fn()
+        except Exception as e:  # reported, not hidden
+            out[name] = {"workload": f"block-scaled GEMM {fmt} (8191,8193,4096)", "error": str(e)}
+            continue
+        ms = time_fn(fn, steps, warmup)
+        kern = traced_kernel_ms(stg, fn, steps)
+        flop = 2.0 * M * N * K
+        tf = flop / (ms * 1e-3) / 1e12
+        out[name] = {"workload": f"block-scaled GEMM {fmt} x {fmt}, e8m0 scales per 32 K values, A(8191,4096) "
+                                 f"Bt(8193,4096), fp32 clipped output",
+                     "value": round(tf, 1), "unit": "TFLOP/s", "ms": round(ms, 4), "flop": flop,
+                     "frac_of_peak": round(tf / peak, 4), "peak_tflops": peak, "kernel_ms": kern}
+        del A, Bt, sa, sb, C
+    return out
+
+
 def run_calibration(steps):
     """A plain device-to-device copy of a known size (512 MiB read, 512 MiB
     written), for scaling the FETCH_SIZE / WRITE_SIZE counters."""
@@ -488,7 +520,7 @@ def main():
 
     stg.load_library()
     only = set(args.only.split(",")) if args.only != "all" else {"copy", "full", "gather", "masked", "backward", "ragged",
-                                                                             "gemm"}
+                                                                             "gemm", "scaled"}
     ops = {}
     head = None
     if "calib" in only:
@@ -519,6 +551,9 @@ def main():
     if "gemm" in only:
         ops["gemm_bounded"] = run_gemm(stg, inputs, max(args.steps // 2, 1), args.warmup)
         print("[bench] gemm done", file=sys.stderr, flush=True)
+    if "scaled" in only:
+        ops.update(run_gemm_scaled(stg, inputs, max(args.steps // 2, 1), args.warmup))
+        print("[bench] scaled gemm done", file=sys.stderr, flush=True)
     if head is None:
         print(json.dumps({"ops": ops}))
         return

@@ -291,11 +291,14 @@ int ragged_tile_store(const void* tiles_in, int32_t dtype, int64_t total_rows, i
  *            stride ldc (C may be acc: the sum is written in place).
  *   C[m][n] = acc[m][n] + sum_k A(m,k) sa(m,k/block) B(k,n) sb(n,k/block)
  * in fp32 accumulation.  Only C[m][n] with m < M, n < N is written.
+ * Precision: fp4 products are summed at fp32 precision; the scaled MFMA sums
+ * fp8 products at lower precision (measured error up to 2^-11.8 of
+ * sum |terms|, well below the inputs' own rounding to fp8).
  * Requirements: K a multiple of block; fp4 operands pair with fp4 operands.
- * Supported here (else STG_ERR_UNSUPPORTED): e8m0 scales with block a multiple
- * of 32 -- the scale granularity of the gfx950 scaled MFMA; e4m3 scales are
- * not powers of two and would need a different instruction path.
- * Errors as for gemm_bounded. */
+ * Supported here (else STG_ERR_UNSUPPORTED): e8m0 scales with block 32 times
+ * a power of two -- 32 is the scale granularity of the gfx950 scaled MFMA;
+ * e4m3 scales are not powers of two and would need a different instruction
+ * path.  Errors as for gemm_bounded. */
 typedef enum { STG_LP_E4M3 = 0, STG_LP_E5M2 = 1, STG_LP_E2M1 = 2 } stg_lowp_format;
 typedef enum { STG_SC_E8M0 = 0, STG_SC_E4M3 = 1 } stg_scale_format;
 int gemm_scaled(const void* A, int32_t a_fmt, int64_t lda, const void* a_scale, int64_t lds_a,

@@ -20,21 +20,27 @@
 // the 16-byte chunks 2p + l / 32 (p = 0, 1) of the step's 64-byte K run: K
 // values 32 p + 16 (l / 32) .. +15 of fp8, 32 p + 16 (l / 32) .. of fp4 at
 // twice the density.  The accumulator layout is the 32x32 MFMA layout.
-//  * Tiles 256 x 256, 8 waves of 128 x 64 accumulators (two waves per SIMD).
+//  * Tiles 256 x 256 on 4 waves, one per SIMD, each with 128 x 128
+//    accumulators: with a SIMD to itself a wave has 512 registers, enough to
+//    hold the next stage's operands while the current ones feed the MFMAs,
+//    and a 128 x 128 wave tile reads a third less LDS per MFMA than 128 x 64.
 //  * Both operands are staged by LDS DMA into 64-byte rows -- 64 fp8 or 128
 //    fp4 K values per stage -- with the conflict-free chunk swizzle of the bf16
-//    GEMM, out-of-range rows and K chunks landing as zeros; a 4-stage ring,
-//    the DMA of stage k+3 spread among stage k's MFMAs.
-//  * Each lane loads its scale bytes LA stages ahead (fp8: 2, fp4: 1 -- an fp4
-//    step has twice the MFMAs, and twice the scale bytes) into one of LA + 1
-//    register sets (the K loop is unrolled by LA + 1 so the set is known at
-//    compile time).  Vector-memory operations complete in issue order, so the
-//    compiler's own wait before a set's first use only forces DMA issued LA
-//    steps earlier, and the explicit wait at the end of step k (allowing the
-//    operations issued after stage k+1's scales to stay in flight) covers
-//    stage k+1's data and scales.  Every step issues its DMA; past the end of K the
-//    offsets fall outside the descriptor and the DMA writes zeros into ring
-//    slots nothing reads any more.
+//    GEMM, out-of-range rows and K chunks landing as zeros; a 4-slot ring, the
+//    DMA of stage k+4 spread among stage k's MFMAs (stage k itself was read
+//    into registers during step k-1).
+//  * The scale bytes travel the same way, once per group of 4 stages: per
+//    row the 16-byte aligned 32-byte window that holds the row's (at most
+//    16) scale bytes of the group is DMA'd into one of two window buffers,
+//    and each lane reads its bytes from LDS.  (Per-stage windows would cost
+//    one L2 request per row and stage for a few bytes, doubling the requests
+//    of the whole kernel.)  No load the compiler can see is in flight in the
+//    K loop, so its own waits never force a later stage's DMA to land early;
+//    one explicit wait per step (all but the two newest stages, and the window
+//    issued among them) publishes stage k+2 while stage k+1 is read into the
+//    second register set.  Scale bytes of K blocks past K are capped to a
+//    finite value, so a NaN byte beyond the matrix cannot reach the zero data
+//    there.
 //  * Clipped fp32 epilogue adding the optional accumulator input.
 #include "gemm_common.h"
 
@@ -43,35 +49,48 @@
 namespace stg {
 namespace {
 
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16_s __attribute__((ext_vector_type(16)));
 
 struct ScaledParams {
-  const char* A;  // (M, K), row stride lda bytes
-  const char* B;  // Bt (N, K), row stride ldb bytes
-  const uint8_t* sa;  // e8m0 (M, K / block), row stride lds_a
-  const uint8_t* sb;  // e8m0 (N, K / block), row stride lds_b
+  const char* A;      // (M, K), row stride lda bytes
+  const char* B;      // Bt (N, K), row stride ldb bytes
+  const char* sa;     // e8m0 (M, K / block) at sa + sa_delta, row stride lds_a; sa 16-byte aligned
+  const char* sb;     // e8m0 (N, K / block) at sb + sb_delta, row stride lds_b; sb 16-byte aligned
   const float* acc;   // (M, N) f32, row stride ldacc, or null
   float* C;           // (M, N) f32, row stride ldc
   int64_t lda, ldb, lds_a, lds_b, ldacc, ldc;
   int64_t M, N, K;
-  int32_t bq;   // block / 32
-  int32_t nkb;  // K / block
+  int64_t sa_bytes, sb_bytes;  // readable bytes from sa / sb (whole 16-byte chunks)
+  int32_t sa_delta, sb_delta;  // 0..15
+  int32_t lg_bq;               // log2(block / 32)
+  int32_t nkb;                 // K / block
   int32_t tiles_m, tiles_n;
 };
 
-constexpr int kSBM = 256, kSBN = 256, kSWN = 4, kSNW = 8, kSNT = kSNW * 64;
-constexpr int kSFM = 4, kSFN = 2;  // 32x32 blocks per wave: 128 x 64
-constexpr int kSNS = 4;            // ring depth
+constexpr int kSBM = 256, kSBN = 256, kSWN = 2, kSNW = 4, kSNT = kSNW * 64;
+constexpr int kSFM = 4, kSFN = 4;  // 32x32 blocks per wave: 128 x 128
+constexpr int kSNS = 4;            // ring slots
 constexpr int kRowB = 64;          // bytes per operand row per stage
-constexpr int kAStage = kSBM * kRowB, kBStage = kSBN * kRowB, kStage = kAStage + kBStage;
-constexpr int kADma = kAStage / 1024 / kSNW, kBDma = kBStage / 1024 / kSNW, kDma = kADma + kBDma;
-constexpr int kScaledLds = kSNS * kStage;  // 128 KiB
+constexpr int kSG = 4;             // stages per scale window group
+constexpr int kSWin = 32;          // bytes of scale window per row and group
+constexpr int kAStage = kSBM * kRowB, kBStage = kSBN * kRowB;
+constexpr int kSlot = kAStage + kBStage;  // 32 KiB
+constexpr int kASc = kSBM * kSWin, kBSc = kSBN * kSWin;
+constexpr int kScBuf = kASc + kBSc;  // 16 KiB per window buffer, two of them
+constexpr int kADma = kAStage / 1024 / kSNW, kBDma = kBStage / 1024 / kSNW;
+constexpr int kDma = kADma + kBDma;         // operand DMA instructions per thread and stage
+constexpr int kWDmaOp = kASc / 1024 / kSNW;  // window DMA instructions per thread and operand
+constexpr int kWDma = 2 * kWDmaOp;
+constexpr int kScaledLds = kSNS * kSlot + 2 * kScBuf;  // 160 KiB
+static_assert(kWDmaOp * kSNT * 16 == kASc && kASc == kBSc, "whole windows per DMA round");
+static_assert(kScaledLds <= 160 * 1024, "LDS");
 
 // FA / FB: operand format codes of the scaled MFMA (0 e4m3, 1 e5m2, 4 e2m1);
 // BITS: 8 for fp8 operands, 4 for fp4 (both operands of one width)
 template <int FA, int FB, int BITS>
-__global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_scaled_kernel(
+__global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_scaled_kernel(
     ScaledParams p) {
   constexpr int KS = kRowB * 8 / BITS;    // K values per stage: 64 (fp8) / 128 (fp4)
   constexpr int S = KS / 64;              // MFMA steps per stage
@@ -95,10 +114,10 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 2))) vo
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // DMA chunks of this lane (row r of the stage, logical chunk c): offsets are
-  // the same for every stage (the descriptors move with K)
+  // operand DMA chunks of this lane (row r of the stage, logical chunk c):
+  // offsets are the same for every stage (the descriptors move with K)
   uint32_t a_off[kADma], b_off[kBDma];
-  int a_kc[kADma], b_kc[kBDma];
+  int a_kc[kADma], b_kc[kBDma];  // first K value of the chunk within its stage
 #pragma unroll
   for (int q = 0; q < kADma; ++q) {
     const int pos = (wave * kADma + q) * 64 + lane;
@@ -113,18 +132,51 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 2))) vo
     b_kc[q] = c * CHUNK_K;
     b_off[q] = n0 + r < p.N ? (uint32_t)(r * p.ldb + c * 16) : kOOB;
   }
+  // window DMA q of this thread: 16-byte chunk t & 1 of the window of row
+  // t / 2, t = (wave * kWDmaOp + q) * 64 + lane; byte offsets of the rows'
+  // first scales from the 16-byte aligned bases (below 2^31)
+  uint32_t sa_row[kWDmaOp], sb_row[kWDmaOp], s_ch[kWDmaOp];
+  bool sa_ok[kWDmaOp], sb_ok[kWDmaOp];
+#pragma unroll
+  for (int q = 0; q < kWDmaOp; ++q) {
+    const int t = (wave * kWDmaOp + q) * 64 + lane, srow = t >> 1;
+    s_ch[q] = 16 * (t & 1);
+    sa_ok[q] = m0 + srow < p.M;
+    sb_ok[q] = n0 + srow < p.N;
+    sa_row[q] = sa_ok[q] ? (uint32_t)(p.sa_delta + (m0 + srow) * p.lds_a) : 0u;
+    sb_row[q] = sb_ok[q] ? (uint32_t)(p.sb_delta + (n0 + srow) * p.lds_b) : 0u;
+  }
+  const u32x4_s rs_sa = rsrc_words(p.sa, p.sa_bytes), rs_sb = rsrc_words(p.sb, p.sb_bytes);
+  // where this lane's scale rows start within their windows: (row offset) mod 16
+  int a_ph[kSFM], b_ph[kSFN];
+#pragma unroll
+  for (int i = 0; i < kSFM; ++i) {
+    const int64_t r = m0 + wm * 128 + i * 32 + (lane & 31);
+    a_ph[i] = (int)((p.sa_delta + (r < p.M ? r : 0) * p.lds_a) & 15);
+  }
+#pragma unroll
+  for (int j = 0; j < kSFN; ++j) {
+    const int64_t r = n0 + wn * 128 + j * 32 + (lane & 31);
+    b_ph[j] = (int)((p.sb_delta + (r < p.N ? r : 0) * p.lds_b) & 15);
+  }
   const uint32_t smem_lds =
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem);
 
+  auto first_block = [&](int kt) { return (int)(((uint32_t)kt * (KS / 32)) >> p.lg_bq); };
+  // K values of stage kt still inside K (clamped to the int range)
+  auto k_left = [&](int kt) {
+    const int64_t kl = p.K - (int64_t)kt * KS;
+    return (int)(kl < 0 ? 0 : kl > INT32_MAX ? INT32_MAX : kl);
+  };
   auto stage_rsrc = [&](int kt, u32x4_s& rsa, u32x4_s& rsb) {
     const int64_t kb = (int64_t)kt * kRowB;  // byte offset of the stage in a row
     rsa = rsrc_words(p.A + m0 * p.lda + kb, (p.M - 1 - m0) * p.lda + (row_bytes - kb));
     rsb = rsrc_words(p.B + n0 * p.ldb + kb, (p.N - 1 - n0) * p.ldb + (row_bytes - kb));
   };
-  // DMA instruction q (A first, then B) of stage kt; chunks at or past K land as zeros
-  auto dma_one = [&](int kt, int q, const u32x4_s& rsa, const u32x4_s& rsb) {
-    const uint32_t st = smem_lds + (kt % kSNS) * kStage;
-    const int64_t kleft = p.K - (int64_t)kt * KS;
+  // DMA instruction q of stage kt into its ring slot (A chunks, then B);
+  // chunks at or past K land as zeros
+  auto dma_one = [&](int slot, int kleft, int q, const u32x4_s& rsa, const u32x4_s& rsb) {
+    const uint32_t st = smem_lds + slot * kSlot;
     if (q < kADma) {
       dma16(rsa, a_kc[q] < kleft ? a_off[q] : kOOB, st + (wave * kADma + q) * 1024);
     } else {
@@ -132,67 +184,111 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 2))) vo
       dma16(rsb, b_kc[qb] < kleft ? b_off[qb] : kOOB, st + kAStage + (wave * kBDma + qb) * 1024);
     }
   };
+  // window DMA instruction q (A, then B) of group g into buffer g % 2; kb0:
+  // first scale block of the group; windows of groups past K and of rows past
+  // the matrix land as zeros
+  auto wdma_one = [&](int g, int kb0, int q) {
+    const uint32_t wb = smem_lds + kSNS * kSlot + (g & 1) * kScBuf;
+    const bool is_a = q < kWDmaOp;
+    const int qq = is_a ? q : q - kWDmaOp;
+    const uint32_t win = ((is_a ? sa_row[qq] : sb_row[qq]) + (uint32_t)kb0) & ~15u;
+    const uint32_t off = (is_a ? sa_ok[qq] : sb_ok[qq]) && kb0 < p.nkb ? win + s_ch[qq] : kOOB;
+    dma16(is_a ? rs_sa : rs_sb, off, wb + (is_a ? 0 : kASc) + (wave * kWDmaOp + qq) * 1024);
+  };
 
-  // scale bytes of stage kt for this lane's rows (A) and columns (B), into
-  // register set SLOT (a compile-time constant); indices past the matrix or
-  // past K are clamped (their data is zero)
-  constexpr int NSL = (kSFM + kSFN) * S;  // scale loads per stage
-  constexpr int LA = BITS == 8 ? 2 : 1;   // scales are loaded LA stages ahead
-  constexpr int NSET = LA + 1;            // register sets of scales
-  // operations issued after stage k+1's scales by the end of step k, in order:
-  // LA = 2: DMA(k+2), scales(k+2), DMA(k+3); LA = 1: DMA(k+3)
-  constexpr int IN_FLIGHT = LA == 2 ? 2 * kDma + NSL : kDma;
-  int sc_a[NSET][kSFM][S], sc_b[NSET][kSFN][S];
-  auto load_scales = [&](int kt, auto slot_tag) {
+  // Operand registers, double-buffered by step parity P; dwords 4h .. 4h+3
+  // of fa[P][i] / fb[P][j] hold the lane's 16-byte chunk 2h + half: fp8 --
+  // the one MFMA step's 32 bytes (scale blocks 0 and 1 of the step), in the
+  // register order the instruction takes; fp4 -- the 16 bytes of MFMA step h.
+  i32x8 fa[2][kSFM], fb[2][kSFN];
+  int sca[2][kSFM][S], scb[2][kSFN][S];
+  // LDS byte offsets of this lane's chunks half and 2 + half of its first A
+  // and B rows; rows 32 i further on keep the swizzle (bits 1-2 of r/2 and
+  // r/4 do not change), so the other blocks are at fixed distances
+  const int ra0 = wm * 128 + (lane & 31), rb0 = wn * 128 + (lane & 31);
+  const int a_l0 = ra0 * kRowB + (a_phys(ra0, half) << 4), a_l1 = ra0 * kRowB + (a_phys(ra0, 2 + half) << 4);
+  const int b_l0 = rb0 * kRowB + (a_phys(rb0, half) << 4), b_l1 = rb0 * kRowB + (a_phys(rb0, 2 + half) << 4);
+  // Read instruction q of stage kt (ring slot SLOT) into buffer P: q <
+  // NRD_A: half q % 2 of A block q / 2 (chunk half, then 2 + half); then the
+  // same for B; then the scale bytes, A blocks then B blocks for each MFMA
+  // step s.  The scale of 32-value K block kb is byte (phase + kb - kbg) of
+  // its row's window of group kt / 4 (kbg: the group's first block).  The
+  // 16-byte halves land in ta / tb and are joined into fa / fb by join().
+  constexpr int NRD_A = 2 * kSFM, NRD_B = 2 * kSFN, NRD_S = (kSFM + kSFN) * S;
+  constexpr int NRD = NRD_A + NRD_B + NRD_S;
+  i32x4 ta[kSFM][2], tb[kSFN][2];
+  auto read_one = [&](int kt, int q, auto p_tag, auto slot_tag) {
+    constexpr int P = decltype(p_tag)::value;
     constexpr int SLOT = decltype(slot_tag)::value;
+    const char* as = smem + SLOT * kSlot;
+    const char* bs = as + kAStage;
+    if (q < NRD_A) {
+      const int i = q >> 1, h = q & 1;
+      ta[i][h] = *(const i32x4*)(as + (h ? a_l1 : a_l0) + i * 32 * kRowB);
+    } else if (q < NRD_A + NRD_B) {
+      const int j = (q - NRD_A) >> 1, h = q & 1;
+      tb[j][h] = *(const i32x4*)(bs + (h ? b_l1 : b_l0) + j * 32 * kRowB);
+    } else {
+      const unsigned char* sas = (const unsigned char*)(smem + kSNS * kSlot + ((kt / kSG) & 1) * kScBuf);
+      const unsigned char* sbs = sas + kASc;
+      const int u = q - NRD_A - NRD_B, s = u / (kSFM + kSFN), w = u % (kSFM + kSFN);
+      const int kbg = first_block(kt & ~(kSG - 1));
+      const int kb = (int)(((uint32_t)kt * (KS / 32) + 2 * s + half) >> p.lg_bq);
+      if (w < kSFM)
+        sca[P][w][s] = sas[(ra0 + w * 32) * kSWin + ((a_ph[w] + kbg) & 15) + (kb - kbg)];
+      else
+        scb[P][w - kSFM][s] = sbs[(rb0 + (w - kSFM) * 32) * kSWin + ((b_ph[w - kSFM] + kbg) & 15) + (kb - kbg)];
+    }
+  };
+  auto join = [&](auto p_tag) {
+    constexpr int P = decltype(p_tag)::value;
+#pragma unroll
+    for (int i = 0; i < kSFM; ++i) fa[P][i] = __builtin_shufflevector(ta[i][0], ta[i][1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+    for (int j = 0; j < kSFN; ++j) fb[P][j] = __builtin_shufflevector(tb[j][0], tb[j][1], 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto read_stage = [&](int kt, auto p_tag, auto slot_tag) {
+#pragma unroll
+    for (int q = 0; q < NRD; ++q) read_one(kt, q, p_tag, slot_tag);
+    join(p_tag);
+  };
+
+  // one K step on stage kt (kt % 4 == PH), whose operands are in buffer P:
+  // stage kt + 1 (published) is read into buffer 1 - P and stage kt + 4's DMA
+  // goes to ring slot kt % 4 (stage kt, read before the last barrier), both
+  // alongside the MFMAs; when PH == 3 the window of group g = (kt + 5) / 4
+  // goes first, into window buffer g % 2 (last read for stage 4g - 5, before
+  // the last barrier).  At the end stage kt + 2 has landed once only what was
+  // issued after it is in flight (operations complete in order): stages kt +
+  // 3 and kt + 4, and the window of the step with PH == 3 among the last two;
+  // the barrier publishes it, and its fence waits for the reads of kt + 1.
+  auto step = [&](int kt, auto p_tag, auto ph_tag) {
+    constexpr int P = decltype(p_tag)::value;
+    constexpr int PH = decltype(ph_tag)::value;
+    constexpr int NM = kSFM * kSFN * S;
+    constexpr int NW = PH == 3 ? kWDma : 0;  // window instructions this step
+    constexpr int ND = NW + kDma;
+    u32x4_s rsa, rsb;
+    stage_rsrc(kt + kSNS, rsa, rsb);
+    const int g = (kt + 5) / kSG;
+    const int kbw = NW ? first_block(g * kSG) : 0;
+    const int kl_d = k_left(kt + kSNS);
+    // stage kt + 1 is in ring slot (PH + 1) % 4; its reads go two after each
+    // of the first MFMAs: issued in a burst, they would fill the LDS queue
+    // and hold back the MFMAs behind them
+    using PN = std::integral_constant<int, 1 - P>;
+    using SN = std::integral_constant<int, (PH + 1) % kSNS>;
+    // scale bytes of K blocks past K may be anything (NaN included): they
+    // are capped to a finite value, their data being zero; applied here, a
+    // step after the bytes were read, so that no wait holds the MFMAs
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      const uint32_t k32 = (uint32_t)kt * (KS / 32) + 2 * s + half;  // 32-value block of K
-      int64_t kb = k32 / (uint32_t)p.bq;
-      kb = kb < p.nkb ? kb : p.nkb - 1;
+      const int cap = (int)(((uint32_t)kt * (KS / 32) + 2 * s + half) >> p.lg_bq) < p.nkb ? 255 : 127;
 #pragma unroll
-      for (int i = 0; i < kSFM; ++i) {
-        int64_t r = m0 + wm * 128 + i * 32 + (lane & 31);
-        r = r < p.M ? r : p.M - 1;
-        sc_a[SLOT][i][s] = p.sa[r * p.lds_a + kb];
-      }
+      for (int i = 0; i < kSFM; ++i) sca[P][i][s] = min(sca[P][i][s], cap);
 #pragma unroll
-      for (int j = 0; j < kSFN; ++j) {
-        int64_t r = n0 + wn * 64 + j * 32 + (lane & 31);
-        r = r < p.N ? r : p.N - 1;
-        sc_b[SLOT][j][s] = p.sb[r * p.lds_b + kb];
-      }
+      for (int j = 0; j < kSFN; ++j) scb[P][j][s] = min(scb[P][j][s], cap);
     }
-  };
-
-  // operand chunks 2h + half (h = 0, 1) of stage kt: fp8 -- the lane's two
-  // 16-byte pieces of the one MFMA step (scale blocks 0 and 1 of the step);
-  // fp4 -- the lane's 16 bytes of MFMA step h
-  u32x4 fa[kSFM][2], fb[kSFN][2];
-  auto read_frags = [&](int kt) {
-    const char* as = smem + (kt % kSNS) * kStage;
-    const char* bs = as + kAStage;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = 2 * h + half;
-#pragma unroll
-      for (int i = 0; i < kSFM; ++i) {
-        const int r = (wave / kSWN) * 128 + i * 32 + (lane & 31);
-        fa[i][h] = *(const u32x4*)(as + r * kRowB + (a_phys(r, c) << 4));
-      }
-#pragma unroll
-      for (int j = 0; j < kSFN; ++j) {
-        const int r = wn * 64 + j * 32 + (lane & 31);
-        fb[j][h] = *(const u32x4*)(bs + r * kRowB + (a_phys(r, c) << 4));
-      }
-    }
-  };
-
-  // the MFMAs of one stage (scales from buffer SLOT) with the DMA
-  // instructions of stage kd spread among them
-  auto mfmas_dma = [&](auto slot_tag, int kd, int nq, const u32x4_s& rsa, const u32x4_s& rsb) {
-    constexpr int slot = decltype(slot_tag)::value;
-    constexpr int NM = kSFM * kSFN * S;
 #pragma unroll
     for (int s = 0; s < S; ++s)
 #pragma unroll
@@ -201,78 +297,75 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 2))) vo
         for (int j = 0; j < kSFN; ++j) {
           i32x8 av, bv;
           if (BITS == 8) {
-            av = (i32x8){(int)fa[i][0][0], (int)fa[i][0][1], (int)fa[i][0][2], (int)fa[i][0][3],
-                         (int)fa[i][1][0], (int)fa[i][1][1], (int)fa[i][1][2], (int)fa[i][1][3]};
-            bv = (i32x8){(int)fb[j][0][0], (int)fb[j][0][1], (int)fb[j][0][2], (int)fb[j][0][3],
-                         (int)fb[j][1][0], (int)fb[j][1][1], (int)fb[j][1][2], (int)fb[j][1][3]};
+            av = fa[P][i];
+            bv = fb[P][j];
+          } else if (s == 0) {  // fp4 reads only the first four registers
+            av = __builtin_shufflevector(fa[P][i], fa[P][i], 0, 1, 2, 3, -1, -1, -1, -1);
+            bv = __builtin_shufflevector(fb[P][j], fb[P][j], 0, 1, 2, 3, -1, -1, -1, -1);
           } else {
-            av = (i32x8){(int)fa[i][s][0], (int)fa[i][s][1], (int)fa[i][s][2], (int)fa[i][s][3], 0, 0, 0, 0};
-            bv = (i32x8){(int)fb[j][s][0], (int)fb[j][s][1], (int)fb[j][s][2], (int)fb[j][s][3], 0, 0, 0, 0};
+            av = __builtin_shufflevector(fa[P][i], fa[P][i], 4, 5, 6, 7, -1, -1, -1, -1);
+            bv = __builtin_shufflevector(fb[P][j], fb[P][j], 4, 5, 6, 7, -1, -1, -1, -1);
           }
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], FA, FB, 0, sc_a[slot][i][s],
-                                                                      0, sc_b[slot][j][s]);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              av, bv, acc[i][j], FA, FB, 0, sca[P][i][s], 0, scb[P][j][s]);
           const int m = (s * kSFM + i) * kSFN + j;
 #pragma unroll
-          for (int d = 0; d < nq; ++d) {
-            const int after = ((d + 1) * NM) / nq - 1;
+          for (int q = 2 * m; q < 2 * m + 2 && q < NRD; ++q) {
+            __builtin_amdgcn_sched_barrier(0);
+            read_one(kt + 1, q, PN(), SN());
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+          for (int d = 0; d < ND; ++d) {
+            const int after = ((d + 1) * NM) / ND - 1;
             if ((after < 0 ? 0 : after) == m) {
               __builtin_amdgcn_sched_barrier(0);
-              dma_one(kd, d, rsa, rsb);
+              if (d < NW)
+                wdma_one(g, kbw, d);
+              else
+                dma_one(PH, kl_d, d - NW, rsa, rsb);
               __builtin_amdgcn_sched_barrier(0);
             }
           }
         }
-  };
-
-  // one K step on stage kt, whose scales are in register set SLOT = kt % 3:
-  // issue stage kt+2's scales and stage kt+3's DMA (zeros past K) while stage
-  // kt feeds the MFMAs
-  auto step = [&](int kt, auto slot_tag) {
-    constexpr int SLOT = decltype(slot_tag)::value;
-    u32x4_s rsa, rsb;
-    load_scales(kt + LA, std::integral_constant<int, (SLOT + LA) % NSET>());
-    stage_rsrc(kt + kSNS - 1, rsa, rsb);
-    read_frags(kt);
-    mfmas_dma(slot_tag, kt + kSNS - 1, kDma, rsa, rsb);
-    // stage kt+1 and its scales have landed once only what was issued after
-    // those scales is still in flight (operations complete in order)
-    wait_vmcnt(IN_FLIGHT);
-    // publishes stage kt + 1; ring slot kt % NS is free after this
+    __builtin_amdgcn_sched_barrier(0);  // every MFMA is issued before the wait
+    join(PN());
+    wait_vmcnt(2 * kDma + (PH == 0 || PH == 3 ? kWDma : 0));
     __syncthreads();
   };
 
-  // prologue, in the steady state's issue order (a step issues the scales
-  // LA stages ahead, then the DMA three stages ahead):
-  //   LA = 2: DMA(0), scales(0), DMA(1), scales(1), DMA(2)
-  //   LA = 1: DMA(0), DMA(1), scales(0), DMA(2)
-  // (K = 0 has no stage and no scale: the epilogue writes acc or zeros)
+  // (K = 0 has no stage: the epilogue writes acc or zeros)
   if (nk > 0) {
-    for (int s = 0; s < kSNS - 1; ++s) {
+    // prologue, in the steady state's issue order: window 0, stages 0 .. 2,
+    // window 1, stage 3; then wait for window 0 and stages 0 and 1
+    for (int q = 0; q < kWDma; ++q) wdma_one(0, 0, q);
+    for (int s = 0; s < kSNS; ++s) {
+      if (s == kSNS - 1) {
+        const int kbw = first_block(kSG);
+        for (int q = 0; q < kWDma; ++q) wdma_one(1, kbw, q);
+      }
       u32x4_s rsa, rsb;
-      if (LA == 1 && s == 2) load_scales(0, std::integral_constant<int, 0>());
       stage_rsrc(s, rsa, rsb);
 #pragma unroll
-      for (int q = 0; q < kDma; ++q) dma_one(s, q, rsa, rsb);
-      if (LA == 2 && s == 0) load_scales(0, std::integral_constant<int, 0>());
-      if (LA == 2 && s == 1) load_scales(1, std::integral_constant<int, 1 % NSET>());
+      for (int q = 0; q < kDma; ++q) dma_one(s, k_left(s), q, rsa, rsb);
     }
-    wait_vmcnt(IN_FLIGHT);
+    wait_vmcnt(2 * kDma + kWDma);
     __syncthreads();
-    int kt = 0;
-    if constexpr (NSET == 3) {
-      for (; kt + 2 < nk; kt += 3) {
-        step(kt, std::integral_constant<int, 0>());
-        step(kt + 1, std::integral_constant<int, 1>());
-        step(kt + 2, std::integral_constant<int, 2>());
-      }
-      if (kt < nk) step(kt, std::integral_constant<int, 0>());
-      if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1>());
-    } else {
-      for (; kt + 1 < nk; kt += 2) {
-        step(kt, std::integral_constant<int, 0>());
-        step(kt + 1, std::integral_constant<int, 1>());
-      }
-      if (kt < nk) step(kt, std::integral_constant<int, 0>());
+    read_stage(0, std::integral_constant<int, 0>(), std::integral_constant<int, 0>());
+    // step 0 sends stage 4 into stage 0's slot: every wave's reads of it
+    // must be done (the barrier's fence waits for them)
+    __syncthreads();
+    // a multiple of 4 steps (whole window groups); the ones past nk run on
+    // stages whose data is all zeros and add nothing
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    for (int kt = 0; kt < nk; kt += kSG) {
+      step(kt, I0(), I0());
+      step(kt + 1, I1(), I1());
+      step(kt + 2, I0(), I2());
+      step(kt + 3, I1(), I3());
     }
   }
   // no LDS DMA may still be in flight when the workgroup ends
@@ -284,7 +377,7 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 2))) vo
   for (int i = 0; i < kSFM; ++i)
 #pragma unroll
     for (int j = 0; j < kSFN; ++j) {
-      const int64_t col = n0 + wn * 64 + j * 32 + (lane & 31);
+      const int64_t col = n0 + wn * 128 + j * 32 + (lane & 31);
       if (col >= p.N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -333,7 +426,8 @@ extern "C" int gemm_scaled(const void* A, int32_t a_fmt, int64_t lda, const void
   if (scale_fmt == STG_SC_E4M3)
     return fail(STG_ERR_UNSUPPORTED, "%s: e4m3 scales are not powers of two; the scaled MFMA takes e8m0 only", name);
   if (M < 0 || N < 0 || K < 0) return fail(STG_ERR_INVALID, "%s: negative size", name);
-  if (block < 32 || block % 32) return fail(STG_ERR_UNSUPPORTED, "%s: block must be a positive multiple of 32", name);
+  if (block < 32 || (block & (block - 1)))
+    return fail(STG_ERR_UNSUPPORTED, "%s: block must be 32 times a power of two", name);
   if (K % block) return fail(STG_ERR_INVALID, "%s: K %lld is not a multiple of the block %lld", name, (long long)K,
                              (long long)block);
   const int bits = a_fmt == STG_LP_E2M1 ? 4 : 8;
@@ -344,8 +438,10 @@ extern "C" int gemm_scaled(const void* A, int32_t a_fmt, int64_t lda, const void
   if (M == 0 || N == 0) return STG_OK;
   if (!C || (K > 0 && (!A || !Bt || !a_scale || !b_scale))) return fail(STG_ERR_INVALID, "%s: null operand", name);
   if ((int64_t)kSBM * lda + 256 >= kMaxOffset32 || (int64_t)kSBN * ldb + 256 >= kMaxOffset32 ||
-      M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2)
-    return fail(STG_ERR_RANGE, "%s: a stage spans more than 2^31 bytes or a size is too large", name);
+      M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2 ||
+      (M - 1) * lds_a + K / block + 64 >= kMaxOffset32 || (N - 1) * lds_b + K / block + 64 >= kMaxOffset32)
+    return fail(STG_ERR_RANGE, "%s: a stage or a scale matrix spans more than 2^31 bytes, or a size is too large",
+                name);
   if (!scaled_lds_configured) {
     if (!set_lds<0, 0, 8>() || !set_lds<0, 1, 8>() || !set_lds<1, 0, 8>() || !set_lds<1, 1, 8>() ||
         !set_lds<4, 4, 4>())
@@ -355,13 +451,23 @@ extern "C" int gemm_scaled(const void* A, int32_t a_fmt, int64_t lda, const void
   ScaledParams p{};
   p.A = (const char*)A;
   p.B = (const char*)Bt;
-  p.sa = (const uint8_t*)a_scale;
-  p.sb = (const uint8_t*)b_scale;
+  // scale windows are read as aligned 16-byte chunks from 16-byte aligned
+  // bases; the readable extent is rounded up to whole chunks (an aligned
+  // chunk never crosses a page, so the bytes beyond the matrix it holds are
+  // mapped)
+  const uintptr_t ua = (uintptr_t)a_scale, ub = (uintptr_t)b_scale;
+  p.sa = (const char*)(ua & ~(uintptr_t)15);
+  p.sb = (const char*)(ub & ~(uintptr_t)15);
+  p.sa_delta = (int32_t)(ua & 15);
+  p.sb_delta = (int32_t)(ub & 15);
+  p.sa_bytes = K > 0 ? (p.sa_delta + (M - 1) * lds_a + K / block + 15) & ~(int64_t)15 : 0;
+  p.sb_bytes = K > 0 ? (p.sb_delta + (N - 1) * lds_b + K / block + 15) & ~(int64_t)15 : 0;
   p.acc = acc;
   p.C = C;
   p.lda = lda, p.ldb = ldb, p.lds_a = lds_a, p.lds_b = lds_b, p.ldacc = ldacc, p.ldc = ldc;
   p.M = M, p.N = N, p.K = K;
-  p.bq = (int32_t)(block / 32);
+  p.lg_bq = 0;
+  while ((int64_t)32 << p.lg_bq < block) ++p.lg_bq;
   p.nkb = (int32_t)(K / block);
   p.tiles_m = (int32_t)((M + kSBM - 1) / kSBM);
   p.tiles_n = (int32_t)((N + kSBN - 1) / kSBN);

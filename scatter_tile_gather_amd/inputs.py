@@ -26,6 +26,11 @@ The workloads (shapes, value distributions, index and mask statistics):
                     lengths uniform in [1, 8192].
 * bounded GEMM      bf16 A (M, K) ~ N(0,1), B (K, N) ~ N(0,1)/sqrt(K);
                     (65, 97, 73) and (8191, 8193, 4097).
+* block-scaled GEMM operand codes uniform over every finite code of the
+                    format (e4m3, e5m2; e2m1 packed two per byte, even element
+                    in the low nibble), B given K-major as (N, K); e8m0 scale
+                    bytes uniform in [120, 133] (2^-7 .. 2^6), one per 32-value
+                    block; (8191, 8193, 4096).
 """
 from __future__ import annotations
 
@@ -36,6 +41,7 @@ SEED_BOUNDED_COPY = 1002
 SEED_MASKED = 1003
 SEED_RAGGED = 1004
 SEED_GEMM = 1005
+SEED_SCALED_GEMM = 1006
 
 # A bf16 bit pattern that a N(0,1) draw never produces (a signalling-NaN-like
 # payload); it marks padding columns and untouched destination elements.
@@ -125,3 +131,35 @@ def gemm(M: int, N: int, K: int, seed: int = SEED_GEMM, scale_a: bool = False):
         a = a / np.float32(np.sqrt(K))
     b = rb.standard_normal((K, N), dtype=np.float32) / np.float32(np.sqrt(K))
     return {"A": f32_to_bf16_bits(a), "B": f32_to_bf16_bits(b), "M": M, "N": N, "K": K}
+
+
+def lowp_codes(rng, shape, fmt: str) -> np.ndarray:
+    """Uniform finite codes of an 8-bit (e4m3, e5m2) or 4-bit (e2m1) format,
+    one code per uint8; NaN and infinity codes are redrawn as +1.5."""
+    if fmt == "e2m1":
+        return rng.integers(0, 16, shape, dtype=np.uint8)
+    c = rng.integers(0, 256, shape, dtype=np.uint8)
+    if fmt == "e4m3":
+        c[(c & 0x7F) == 0x7F] = 0x3C  # e4m3fn NaN
+    elif fmt == "e5m2":
+        c[(c & 0x7C) == 0x7C] = 0x3E  # e5m2 infinities and NaNs
+    else:
+        raise ValueError(fmt)
+    return c
+
+
+def pack_e2m1(codes: np.ndarray) -> np.ndarray:
+    """Two 4-bit codes per byte along the last axis, the even element low."""
+    return ((codes[..., 0::2] & 0xF) | ((codes[..., 1::2] & 0xF) << 4)).astype(np.uint8)
+
+
+def scaled_gemm(M: int, N: int, K: int, fmt: str = "e4m3", block: int = 32, seed: int = SEED_SCALED_GEMM):
+    """Operand codes A (M, K) and Bt (N, K) (packed for e2m1) and e8m0 scale
+    bytes (M, K/block), (N, K/block)."""
+    ra, rb, rs, rt = _rngs(seed, 4)
+    A, Bt = lowp_codes(ra, (M, K), fmt), lowp_codes(rb, (N, K), fmt)
+    if fmt == "e2m1":
+        A, Bt = pack_e2m1(A), pack_e2m1(Bt)
+    sa = rs.integers(120, 134, (M, K // block), dtype=np.uint8)
+    sb = rt.integers(120, 134, (N, K // block), dtype=np.uint8)
+    return {"A": A, "Bt": Bt, "sa": sa, "sb": sb, "fmt": fmt, "block": block, "M": M, "N": N, "K": K}

@@ -253,6 +253,7 @@ def test_gemm_scaled_argument_errors(stg):
     assert call(sf=1) == 2  # e4m3 scales: not on the scaled MFMA
     assert b"e8m0" in lib.stg_last_error()
     assert call(block=16) == 2
+    assert call(block=96, K=96) == 2  # not 32 times a power of two
     assert call(fa=2) == 2  # fp4 with fp8
     assert call(fa=7) == 2
     assert call(K=96, block=64) == 1  # K not a multiple of the block
