@@ -273,9 +273,11 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
     const int g = (kt + 5) / kSG;
     const int kbw = NW ? first_block(g * kSG) : 0;
     const int kl_d = k_left(kt + kSNS);
-    // stage kt + 1 is in ring slot (PH + 1) % 4; its reads go two after each
-    // of the first MFMAs: issued in a burst, they would fill the LDS queue
-    // and hold back the MFMAs behind them
+    // stage kt + 1 is in ring slot (PH + 1) % 4; its reads go between the
+    // MFMAs (fp8: two after each of the first ones; fp4: spread over all but
+    // the last two, which leave the last reads time to land before the
+    // barrier -- the faster placement for each, measured): issued in a burst,
+    // they would fill the LDS queue and hold back the MFMAs behind them
     using PN = std::integral_constant<int, 1 - P>;
     using SN = std::integral_constant<int, (PH + 1) % kSNS>;
     // scale bytes of K blocks past K may be anything (NaN included): they
@@ -310,10 +312,12 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
               av, bv, acc[i][j], FA, FB, 0, sca[P][i][s], 0, scb[P][j][s]);
           const int m = (s * kSFM + i) * kSFN + j;
 #pragma unroll
-          for (int q = 2 * m; q < 2 * m + 2 && q < NRD; ++q) {
-            __builtin_amdgcn_sched_barrier(0);
-            read_one(kt + 1, q, PN(), SN());
-            __builtin_amdgcn_sched_barrier(0);
+          for (int q = 0; q < NRD; ++q) {
+            if ((BITS == 8 ? q / 2 : (q * (NM - 2)) / NRD) == m) {
+              __builtin_amdgcn_sched_barrier(0);
+              read_one(kt + 1, q, PN(), SN());
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
 #pragma unroll
           for (int d = 0; d < ND; ++d) {
