@@ -154,3 +154,43 @@ def test_scaled_large_sampled(stg, orc):
     tol = (K * 2.0 ** -24 / (1 - K * 2.0 ** -24) + 2.0 ** -10) * mag + 1e-30
     err = np.abs(C[np.ix_(rows, cols)].astype(np.float64) - want)
     assert np.all(err <= tol), float((err - tol).max())
+
+
+@pytest.mark.parametrize("base", [1, 3, 8, 15])
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_scaled_unaligned_scale_views(stg, orc, base, fmt):
+    """Scale matrices as views at every 16-byte phase with odd row strides:
+    each row's bytes start at a different phase of its 16-byte aligned window.
+    Operands +-1, +-2 and scales 2^-1 .. 2^2 keep the result exact."""
+    M, N, K, block = 200, 150, 1024, 32
+    nkb = K // block
+    rng = np.random.default_rng(100 + base)
+    ca = np.array(EXACT_CODES[fmt], np.uint8)[rng.integers(0, 4, (M, K))]
+    cb = np.array(EXACT_CODES[fmt], np.uint8)[rng.integers(0, 4, (N, K))]
+    sa_full = rng.integers(126, 130, (M, nkb + 2 * base + 1)).astype(np.uint8)
+    sb_full = rng.integers(126, 130, (N, nkb + base + 3)).astype(np.uint8)
+    sa, sb = sa_full[:, base:base + nkb], sb_full[:, base + 1:base + 1 + nkb]
+    say("gemm_scaled unaligned scale views base", base, fmt, "strides", sa_full.shape[1], sb_full.shape[1])
+    sad, sbd = to_dev(sa_full)[:, base:base + nkb], to_dev(sb_full)[:, base + 1:base + 1 + nkb]
+    assert sad.data_ptr() % 16 == base % 16
+    C = to_host(stg.gemm_scaled(to_dev(pack(ca, fmt)), fmt, sad, to_dev(pack(cb, fmt)), fmt, sbd, K, block))
+    np.testing.assert_array_equal(C.astype(np.float64),
+                                  orc.gemm_scaled_f64(pack(ca, fmt), fmt, sa, pack(cb, fmt), fmt, sb, K, block))
+
+
+def test_scaled_output_may_alias_the_accumulator(stg, orc):
+    M, N, K = 140, 300, 256
+    rng = np.random.default_rng(77)
+    ca, cb = codes(rng, (M, K), "e5m2"), codes(rng, (N, K), "e5m2")
+    sa = rng.integers(124, 131, (M, K // 64)).astype(np.uint8)
+    sb = rng.integers(124, 131, (N, K // 64)).astype(np.uint8)
+    acc = rng.standard_normal((M, N)).astype(np.float32)
+    say("gemm_scaled in place: out is acc")
+    inout = to_dev(acc)
+    stg.gemm_scaled(to_dev(ca), "e5m2", to_dev(sa), to_dev(cb), "e5m2", to_dev(sb), K, 64, acc=inout, out=inout)
+    torch.cuda.synchronize()
+    want = orc.gemm_scaled_f64(ca, "e5m2", sa, cb, "e5m2", sb, K, 64, acc=acc)
+    mag = orc.gemm_scaled_f64(ca & 0x7F, "e5m2", sa, cb & 0x7F, "e5m2", sb, K, 64)
+    u = 2.0 ** -24
+    tol = (K * u / (1 - K * u) + 2.0 ** -10) * mag + np.abs(acc.astype(np.float64)) * u + 1e-30
+    assert np.all(np.abs(to_host(inout).astype(np.float64) - want) <= tol)
