@@ -476,10 +476,35 @@ def run_calibration(steps):
     return {"bytes_read": n, "bytes_written": n, "launches": steps}
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inputs, budget_s):
-    """The oracle, single-threaded on one host core, on the headline step."""
+    """The oracle, single-threaded and pinned to one host core, on the
+    headline step."""
     import oracle
 
+    allowed = sorted(os.sched_getaffinity(0))
+    pinned = allowed[-1]
+    os.sched_setaffinity(0, {pinned})
+    try:
+        res = _cpu_baseline_run(oracle, inputs, budget_s)
+    finally:
+        os.sched_setaffinity(0, set(allowed))
+    res["pinned_core"] = pinned
+    res["host_cores_available"] = len(allowed)
+    res["cpu_model"] = cpu_model()
+    return res
+
+
+def _cpu_baseline_run(oracle, inputs, budget_s):
     w = inputs.bounded_copy()
     M, N = w["M"], w["N"]
     tm, tn = w["tile"]
@@ -500,7 +525,7 @@ def cpu_baseline(inputs, budget_s):
     dt = time.perf_counter() - t0
     return {"value": round(step_bytes * steps / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{steps} full headline steps (copy + clipped store at both grid bases), "
-                      f"{dt:.1f} s on one host core"}
+                      f"{dt:.1f} s on one host core (pinned)"}
 
 
 def main():

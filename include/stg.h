@@ -119,7 +119,11 @@ int tile_gather_masked(const stg_tensor* a, const int32_t* indices, const uint8_
  * stores are undefined).  The inverse of tile_gather_masked: for every
  * coordinate o of `tile` (shape as `out` of the gather) with
  * mask[o[axis]] != 0 and s fully in range, a[s] = tile[o].  Nothing else in
- * `a` is written.  Two active elements with the same destination: undefined.
+ * `a` is written.  Two active elements with the same destination: undefined
+ * (not checked; with the environment variable STG_DEBUG set to anything but
+ * "0", the call first synchronizes `stream`, checks on the host that no two
+ * active indices in range along `axis` are equal, and fails with
+ * STG_ERR_INVALID if they are).
  * Active rows of each workgroup are compacted with wavefront ballots before
  * the copy, so inactive rows cost neither reads nor writes. */
 int tile_scatter_masked(const stg_tensor* a, const int32_t* indices, const uint8_t* mask,

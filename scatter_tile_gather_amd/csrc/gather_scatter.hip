@@ -37,6 +37,9 @@
 #include "stg_internal.h"
 
 #include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
 
 namespace stg {
 namespace {
@@ -615,6 +618,41 @@ int launch_segmented(const char* name, int esize, const RowParams& p, int64_t R,
   return check_launch(name);
 }
 
+// Debug mode, environment STG_DEBUG set to anything but "0": scatter checks
+// on the host that no two active indices send rows to the same destination
+// (such stores conflict, and their outcome is undefined).  It synchronizes the
+// stream and copies the indices and the mask to the host.
+bool debug_mode() {
+  const char* e = std::getenv("STG_DEBUG");
+  return e && *e && std::strcmp(e, "0") != 0;
+}
+
+int check_unique_destinations(const char* name, const int32_t* indices, const uint8_t* mask, int64_t n,
+                              int64_t ax_off, int64_t ax_ext, hipStream_t s) {
+  std::vector<int32_t> idx((size_t)n);
+  std::vector<uint8_t> msk(mask ? (size_t)n : 0);
+  if (hipStreamSynchronize(s) != hipSuccess ||
+      hipMemcpy(idx.data(), indices, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess ||
+      (mask && hipMemcpy(msk.data(), mask, (size_t)n, hipMemcpyDeviceToHost) != hipSuccess))
+    return fail(STG_ERR_LAUNCH, "%s: STG_DEBUG check cannot read the indices: %s", name,
+                hipGetErrorString(hipGetLastError()));
+  std::vector<int64_t> rows;
+  rows.reserve((size_t)n);
+  for (int64_t i = 0; i < n; ++i) {
+    if (mask && !msk[(size_t)i]) continue;
+    const int64_t r = ax_off + idx[(size_t)i];
+    if (r >= 0 && r < ax_ext) rows.push_back(r);
+  }
+  std::sort(rows.begin(), rows.end());
+  const auto dup = std::adjacent_find(rows.begin(), rows.end());
+  if (dup != rows.end())
+    return fail(STG_ERR_INVALID,
+                "%s: STG_DEBUG: destination %lld along the indexed axis is written by two active indices "
+                "(conflicting stores are undefined)",
+                name, (long long)*dup);
+  return STG_OK;
+}
+
 int run(Op op, const stg_tensor* a, const int32_t* indices, const uint8_t* mask, int64_t n_indices,
         const int64_t* tile_shape, const int64_t* offset, int32_t axis, double padding_value,
         const stg_tensor* t, void* stream, void* workspace = nullptr, int64_t workspace_bytes = 0) {
@@ -659,6 +697,9 @@ int run(Op op, const stg_tensor* a, const int32_t* indices, const uint8_t* mask,
   for (int d = 0; d < rank; ++d) numel *= t->shape[d];
   if (numel == 0) return STG_OK;
   const hipStream_t s = as_stream(stream);
+  if (op == Op::Scatter && debug_mode() &&
+      (rc = check_unique_destinations(name, indices, mask, n_indices, off[axis], a->shape[axis], s)))
+    return rc;
   const int last = rank - 1;
 
   const bool row_path = rank >= 2 && axis != last && a->stride[last] == 1 && t->stride[last] == 1 &&

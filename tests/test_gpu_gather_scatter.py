@@ -219,3 +219,26 @@ def test_scatter_workload_full(stg, orc):
     want = w["table"].copy()
     orc.tile_scatter_masked(want, w["perm"], w["smask"], (64, 128), w["vals"], None, 0)
     np.testing.assert_array_equal(to_host(dst).view(np.uint32), want.view(np.uint32))
+
+
+def test_scatter_debug_mode_rejects_duplicate_destinations(stg, monkeypatch):
+    """STG_DEBUG=1: two active indices with one destination row fail before
+    anything is written; duplicates among inactive or out-of-range indices
+    are fine; without STG_DEBUG the call is not checked."""
+    a = torch.zeros((16, 8), dtype=torch.float32, device="cuda:0")
+    vals = torch.ones((4, 8), dtype=torch.float32, device="cuda:0")
+    idx = to_dev(np.array([3, 5, 3, 20], dtype=np.int32))
+    say("scatter STG_DEBUG duplicate destinations")
+    monkeypatch.setenv("STG_DEBUG", "1")
+    with pytest.raises(stg.StgError, match="STG_DEBUG"):
+        stg.tile_scatter_masked(a, idx, to_dev(np.array([1, 1, 1, 1], np.uint8)), (4, 8), vals, None, 0)
+    torch.cuda.synchronize()
+    assert not a.any()  # nothing written
+    stg.tile_scatter_masked(a, idx, to_dev(np.array([1, 1, 0, 1], np.uint8)), (4, 8), vals, None, 0)
+    torch.cuda.synchronize()
+    assert a[3].eq(1).all() and a[5].eq(1).all() and a.sum().item() == 16
+    dup_out = to_dev(np.array([3, 5, 20, 20], dtype=np.int32))  # row 20 is out of range: nothing written there
+    stg.tile_scatter_masked(a, dup_out, to_dev(np.array([1, 1, 1, 1], np.uint8)), (4, 8), vals, None, 0)
+    monkeypatch.setenv("STG_DEBUG", "0")
+    stg.tile_scatter_masked(a, idx, to_dev(np.array([1, 1, 1, 1], np.uint8)), (4, 8), vals, None, 0)
+    torch.cuda.synchronize()
