@@ -52,6 +52,7 @@ namespace {
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16_s __attribute__((ext_vector_type(16)));
+typedef float f32x2_s __attribute__((ext_vector_type(2)));
 
 struct ScaledParams {
   const char* A;      // (M, K), row stride lda bytes
@@ -395,13 +396,117 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
     }
 }
 
-bool scaled_lds_configured = false;
+// The last N mod 256 <= 8 columns, when the big tiles' last column would
+// hold only those: a tile column of 256 for a handful of columns costs a whole
+// extra round of workgroups (at N = 8193 the grid is 1056 tiles where 1024
+// fill the chip exactly four times).  This kernel reads A once and the R
+// remainder rows of Bt: four rows per wave, lanes across K in 16-byte chunks
+// (16 fp8 or 32 fp4 values, always within one scale block), values decoded
+// to fp32 with their block scale by the gfx950 scaled conversions, fp32 FMAs,
+// and one cross-lane sum per output.
+constexpr int kSkRows = 4, kSkWaves = 4, kSkMaxR = 8;
+
+__device__ __forceinline__ float e8m0_value(int e) {
+  // 2^(e - 127): the bit pattern of a normal float, except e = 0 (2^-127, a
+  // subnormal) and e = 255 (NaN)
+  return e == 0 ? __uint_as_float(0x00400000u) : e == 255 ? __uint_as_float(0x7FC00000u) : __uint_as_float((uint32_t)e << 23);
+}
+
+// two values of word half / byte `sel` of dword w, times scale
+template <int F>
+__device__ __forceinline__ f32x2_s decode2(uint32_t w, float scale, int sel) {
+  if constexpr (F == 0)
+    return sel ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, scale, true)
+               : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, scale, false);
+  else if constexpr (F == 1)
+    return sel ? __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(w, scale, true)
+               : __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(w, scale, false);
+  else
+    return sel == 0   ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 0)
+           : sel == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 1)
+           : sel == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 2)
+                      : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 3);
+}
 
 template <int FA, int FB, int BITS>
-int launch_scaled(const ScaledParams& p, int64_t n_wg, hipStream_t s) {
-  auto k = gemm_scaled_kernel<FA, FB, BITS>;
-  launch_kernel("gemm_scaled", k, dim3((unsigned)n_wg), dim3(kSNT), (uint32_t)kScaledLds, s, p);
-  return check_launch("gemm_scaled");
+__global__ __launch_bounds__(kSkWaves * 64) void gemm_scaled_skinny_kernel(ScaledParams p, int64_t n0, int R) {
+  constexpr int VALS = 16 * 8 / BITS;  // values per 16-byte chunk
+  constexpr int PAIRS = VALS / 2;      // decode steps per chunk
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t m0 = ((int64_t)blockIdx.x * kSkWaves + wave) * kSkRows;
+  const uint8_t* sa = (const uint8_t*)p.sa + p.sa_delta;
+  const uint8_t* sb = (const uint8_t*)p.sb + p.sb_delta;
+  float acc[kSkRows][kSkMaxR];
+#pragma unroll
+  for (int r = 0; r < kSkRows; ++r)
+#pragma unroll
+    for (int c = 0; c < kSkMaxR; ++c) acc[r][c] = 0.f;
+  bool row_ok[kSkRows];
+#pragma unroll
+  for (int r = 0; r < kSkRows; ++r) row_ok[r] = m0 + r < p.M;
+
+  for (int64_t k0 = (int64_t)lane * VALS; k0 < p.K; k0 += 64 * VALS) {
+    const int64_t kb = k0 >> (5 + p.lg_bq);
+    const int64_t byte0 = k0 * BITS / 8;
+    u32x4 a[kSkRows];
+    float as[kSkRows];
+#pragma unroll
+    for (int r = 0; r < kSkRows; ++r) {
+      const int64_t m = row_ok[r] ? m0 + r : 0;  // rows past M read row 0 and are not written
+      a[r] = *(const u32x4*)(p.A + m * p.lda + byte0);
+      as[r] = e8m0_value(sa[m * p.lds_a + kb]);
+    }
+#pragma unroll
+    for (int c = 0; c < kSkMaxR; ++c) {
+      if (c >= R) break;
+      const u32x4 b = *(const u32x4*)(p.B + (n0 + c) * p.ldb + byte0);
+      const float bs = e8m0_value(sb[(n0 + c) * p.lds_b + kb]);
+#pragma unroll
+      for (int q = 0; q < PAIRS; ++q) {
+        const int w = BITS == 8 ? q / 2 : q / 4, sel = BITS == 8 ? q % 2 : q % 4;
+        const f32x2_s bv = decode2<FB>(b[w], bs, sel);
+#pragma unroll
+        for (int r = 0; r < kSkRows; ++r) {
+          const f32x2_s av = decode2<FA>(a[r][w], as[r], sel);
+          acc[r][c] = fmaf(av[0], bv[0], acc[r][c]);
+          acc[r][c] = fmaf(av[1], bv[1], acc[r][c]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kSkRows; ++r)
+#pragma unroll
+    for (int c = 0; c < kSkMaxR; ++c) {
+      if (c >= R) break;
+      float v = acc[r][c];
+      for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+      if (lane == 0 && row_ok[r]) {
+        const int64_t m = m0 + r, n = n0 + c;
+        if (p.acc) v += p.acc[m * p.ldacc + n];
+        p.C[m * p.ldc + n] = v;
+      }
+    }
+}
+
+bool scaled_lds_configured = false;
+
+// main kernel on the first p.N columns; the skinny kernel on columns
+// n_skinny .. n_skinny + r_skinny - 1 (r_skinny = 0: none)
+template <int FA, int FB, int BITS>
+int launch_scaled(const ScaledParams& p, int64_t n_wg, int64_t n_skinny, int r_skinny, hipStream_t s) {
+  if (n_wg > 0) {
+    launch_kernel("gemm_scaled/main", gemm_scaled_kernel<FA, FB, BITS>, dim3((unsigned)n_wg), dim3(kSNT),
+                  (uint32_t)kScaledLds, s, p);
+    if (int rc = check_launch("gemm_scaled/main")) return rc;
+  }
+  if (r_skinny > 0) {
+    const int64_t wg = (p.M + kSkRows * kSkWaves - 1) / (kSkRows * kSkWaves);
+    launch_kernel("gemm_scaled/skinny", gemm_scaled_skinny_kernel<FA, FB, BITS>, dim3((unsigned)wg),
+                  dim3(kSkWaves * 64), 0u, s, p, n_skinny, r_skinny);
+    return check_launch("gemm_scaled/skinny");
+  }
+  return STG_OK;
 }
 
 template <int FA, int FB, int BITS>
@@ -473,15 +578,20 @@ extern "C" int gemm_scaled(const void* A, int32_t a_fmt, int64_t lda, const void
   p.lg_bq = 0;
   while ((int64_t)32 << p.lg_bq < block) ++p.lg_bq;
   p.nkb = (int32_t)(K / block);
+  // a remainder of at most 8 columns past the last whole tile column goes to
+  // the skinny kernel; the main kernel then sees N rounded down
+  const int r_skinny = N % kSBN <= kSkMaxR ? (int)(N % kSBN) : 0;
+  p.N = N - r_skinny;
   p.tiles_m = (int32_t)((M + kSBM - 1) / kSBM);
-  p.tiles_n = (int32_t)((N + kSBN - 1) / kSBN);
+  p.tiles_n = (int32_t)((p.N + kSBN - 1) / kSBN);
   const int64_t n_wg = (int64_t)p.tiles_m * p.tiles_n;
   const hipStream_t s = as_stream(stream);
   const int code_a = a_fmt == STG_LP_E4M3 ? 0 : a_fmt == STG_LP_E5M2 ? 1 : 4;
   const int code_b = b_fmt == STG_LP_E4M3 ? 0 : b_fmt == STG_LP_E5M2 ? 1 : 4;
-  if (bits == 4) return launch_scaled<4, 4, 4>(p, n_wg, s);
-  if (code_a == 0 && code_b == 0) return launch_scaled<0, 0, 8>(p, n_wg, s);
-  if (code_a == 0) return launch_scaled<0, 1, 8>(p, n_wg, s);
-  if (code_b == 0) return launch_scaled<1, 0, 8>(p, n_wg, s);
-  return launch_scaled<1, 1, 8>(p, n_wg, s);
+  const int64_t n_sk = p.N;
+  if (bits == 4) return launch_scaled<4, 4, 4>(p, n_wg, n_sk, r_skinny, s);
+  if (code_a == 0 && code_b == 0) return launch_scaled<0, 0, 8>(p, n_wg, n_sk, r_skinny, s);
+  if (code_a == 0) return launch_scaled<0, 1, 8>(p, n_wg, n_sk, r_skinny, s);
+  if (code_b == 0) return launch_scaled<1, 0, 8>(p, n_wg, n_sk, r_skinny, s);
+  return launch_scaled<1, 1, 8>(p, n_wg, n_sk, r_skinny, s);
 }

@@ -82,9 +82,12 @@ EXACT_CODES = {"e4m3": [0x38, 0x40, 0xB8, 0xC0], "e5m2": [0x3C, 0x40, 0xBC, 0xC0
 @pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e4m3"), ("e5m2", "e5m2"),
                                    ("e2m1", "e2m1")])
 @pytest.mark.parametrize("shape,block", [((96, 96, 64), 32), ((257, 130, 1024), 32), ((33, 300, 512), 64),
-                                         ((130, 70, 768), 256)])
+                                         ((130, 70, 768), 256), ((70, 259, 256), 32), ((33, 8, 96), 32),
+                                         ((260, 513, 128), 64)])
 def test_scaled_exact(stg, orc, fa, fb, shape, block):
-    """Values +-1, +-2 and scales 2^-1 .. 2^2: the result is exact, bit for bit."""
+    """Values +-1, +-2 and scales 2^-1 .. 2^2: the result is exact, bit for bit.
+    N = 259, 8 and 513 leave 3, 8 and 1 columns past the last whole 256-column
+    tile, which go to the skinny kernel (N = 8: it alone)."""
     M, N, K = shape
     rng = np.random.default_rng(M * 7 + N + K + block)
     ca = np.array(EXACT_CODES[fa], np.uint8)[rng.integers(0, 4, (M, K))]
@@ -118,6 +121,14 @@ def test_scaled_shapes(stg, orc, shape, fmt):
 def test_scaled_blocks_acc_and_padding(stg, orc, block, fmt):
     say("gemm_scaled block", block, fmt, "with acc and padded strides")
     run_case(stg, orc, 130, 270, 512, block, fmt, fmt, seed=block, with_acc=True, pad=7)
+
+
+@pytest.mark.parametrize("fa,fb", [("e5m2", "e4m3"), ("e4m3", "e5m2"), ("e2m1", "e2m1")])
+def test_scaled_remainder_columns_random(stg, orc, fa, fb):
+    """Full-range codes, accumulator input and padded strides with 5 columns
+    past the last whole tile (the skinny kernel), scales per 64 values."""
+    say("gemm_scaled remainder columns", fa, fb, "(131, 517, 320) block 64")
+    run_case(stg, orc, 131, 517, 320, 64, fa, fb, seed=517, with_acc=True, pad=3)
 
 
 def test_scaled_extreme_scales(stg, orc):
