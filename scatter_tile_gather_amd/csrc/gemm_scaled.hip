@@ -269,11 +269,21 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
     constexpr int NM = kSFM * kSFN * S;
     constexpr int NW = PH == 3 ? kWDma : 0;  // window instructions this step
     constexpr int ND = NW + kDma;
+    // this step's bookkeeping (descriptors and K bound of stage kt + 4's
+    // DMA, the window's group, the scale caps) is issued after the first
+    // MFMA, which needs only the previous step's registers: with one wave per
+    // SIMD, instructions issued while an MFMA runs cost the matrix core nothing
     u32x4_s rsa, rsb;
-    stage_rsrc(kt + kSNS, rsa, rsb);
-    const int g = (kt + 5) / kSG;
-    const int kbw = NW ? first_block(g * kSG) : 0;
-    const int kl_d = k_left(kt + kSNS);
+    int g = 0, kbw = 0, kl_d = 0;
+    auto cap_of = [&](int s) {
+      return (int)(((uint32_t)kt * (KS / 32) + 2 * s + half) >> p.lg_bq) < p.nkb ? 255 : 127;
+    };
+    auto bookkeeping = [&]() {
+      stage_rsrc(kt + kSNS, rsa, rsb);
+      g = (kt + 5) / kSG;
+      kbw = NW ? first_block(g * kSG) : 0;
+      kl_d = k_left(kt + kSNS);
+    };
     // stage kt + 1 is in ring slot (PH + 1) % 4; its reads go between the
     // MFMAs (fp8: two after each of the first ones; fp4: spread over all but
     // the last two, which leave the last reads time to land before the
@@ -282,16 +292,10 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
     using PN = std::integral_constant<int, 1 - P>;
     using SN = std::integral_constant<int, (PH + 1) % kSNS>;
     // scale bytes of K blocks past K may be anything (NaN included): they
-    // are capped to a finite value, their data being zero; applied here, a
-    // step after the bytes were read, so that no wait holds the MFMAs
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int cap = (int)(((uint32_t)kt * (KS / 32) + 2 * s + half) >> p.lg_bq) < p.nkb ? 255 : 127;
-#pragma unroll
-      for (int i = 0; i < kSFM; ++i) sca[P][i][s] = min(sca[P][i][s], cap);
-#pragma unroll
-      for (int j = 0; j < kSFN; ++j) scb[P][j][s] = min(scb[P][j][s], cap);
-    }
+    // are capped to a finite value, their data being zero; applied a step
+    // after the bytes were read (so that no wait holds the MFMAs), in place,
+    // just before each value's first MFMA
+    int cap = 0;
 #pragma unroll
     for (int s = 0; s < S; ++s)
 #pragma unroll
@@ -309,9 +313,17 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
             av = __builtin_shufflevector(fa[P][i], fa[P][i], 4, 5, 6, 7, -1, -1, -1, -1);
             bv = __builtin_shufflevector(fb[P][j], fb[P][j], 4, 5, 6, 7, -1, -1, -1, -1);
           }
+          if (i == 0 && j == 0) cap = cap_of(s);
+          if (j == 0) sca[P][i][s] = min(sca[P][i][s], cap);
+          if (i == 0) scb[P][j][s] = min(scb[P][j][s], cap);
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               av, bv, acc[i][j], FA, FB, 0, sca[P][i][s], 0, scb[P][j][s]);
           const int m = (s * kSFM + i) * kSFN + j;
+          if (m == 0) {
+            __builtin_amdgcn_sched_barrier(0);
+            bookkeeping();
+            __builtin_amdgcn_sched_barrier(0);
+          }
 #pragma unroll
           for (int q = 0; q < NRD; ++q) {
             if ((BITS == 8 ? q / 2 : (q * (NM - 2)) / NRD) == m) {
