@@ -205,3 +205,22 @@ def test_scaled_output_may_alias_the_accumulator(stg, orc):
     u = 2.0 ** -24
     tol = (K * u / (1 - K * u) + 2.0 ** -10) * mag + np.abs(acc.astype(np.float64)) * u + 1e-30
     assert np.all(np.abs(to_host(inout).astype(np.float64) - want) <= tol)
+
+
+@pytest.mark.parametrize("K,block", [(32, 32), (64, 32), (96, 32), (160, 32), (192, 64), (128, 128)])
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_scaled_small_k_main_kernel(stg, orc, K, block, fmt):
+    """K below, at and between whole stages (64 fp8 / 128 fp4 values) on a
+    shape that runs the main kernel (two tile rows, three tile columns):
+    partial first and last stages, windows of groups past K.  Exact values."""
+    M, N = 300, 600
+    rng = np.random.default_rng(K + block)
+    ca = np.array(EXACT_CODES[fmt], np.uint8)[rng.integers(0, 4, (M, K))]
+    cb = np.array(EXACT_CODES[fmt], np.uint8)[rng.integers(0, 4, (N, K))]
+    sa = rng.integers(126, 130, (M, K // block)).astype(np.uint8)
+    sb = rng.integers(126, 130, (N, K // block)).astype(np.uint8)
+    say("gemm_scaled small K", K, "block", block, fmt)
+    C = to_host(stg.gemm_scaled(to_dev(pack(ca, fmt)), fmt, to_dev(sa), to_dev(pack(cb, fmt)), fmt, to_dev(sb), K,
+                                block))
+    np.testing.assert_array_equal(C.astype(np.float64),
+                                  orc.gemm_scaled_f64(pack(ca, fmt), fmt, sa, pack(cb, fmt), fmt, sb, K, block))
