@@ -203,6 +203,8 @@ def tile_gather_masked(a, indices, mask, tile_shape, offset=None, axis: int = 0,
     if out is None:
         out = torch.empty(_gather_out_shape(tile_shape, n, axis), dtype=a.dtype, device=a.device)
     ad, od = _desc(a, "a"), _desc(out, "out")
+    if mask is not None and mask.numel() != n:
+        raise ValueError("mask must hold one entry per index")
     mp = None if mask is None else _dev_array(mask, torch.uint8, "mask")
     _check(lib.tile_gather_masked(ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"), mp, n,
                                   _i64arr(tile_shape), None if offset is None else _i64arr(offset), axis,
@@ -250,6 +252,8 @@ def tile_scatter_masked(a, indices, mask, tile_shape, tile, offset=None, axis: i
     lib = load_library()
     n = indices.numel()
     ad, td = _desc(a, "a"), _desc(tile, "tile")
+    if mask is not None and mask.numel() != n:
+        raise ValueError("mask must hold one entry per index")
     mp = None if mask is None else _dev_array(mask, torch.uint8, "mask")
     _check(lib.tile_scatter_masked(ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"), mp, n,
                                    _i64arr(tile_shape), None if offset is None else _i64arr(offset), axis,
@@ -361,6 +365,8 @@ def ragged_tile_load(src, middle_dim: int, group: int, BM: int, BN: int, ragged_
         if t.dtype not in (torch.int32, torch.uint32) or not t.is_contiguous():
             raise ValueError(f"{nm} must be a contiguous 32-bit integer tensor")
     _on_gpu(out, "out")
+    if out.dtype != src.dtype or not out.is_contiguous() or out.numel() < n * BM * BN:
+        raise ValueError("out must be a contiguous (n_tiles, BM, BN) tensor of src's dtype")
     _check(lib.ragged_tile_load(src.data_ptr(), _dtype_code(src), src.shape[0], middle_dim, group, src.shape[2], BM,
                                 BN, col0, ragged_idx.data_ptr(), dynamic_dim.data_ptr(), middle_idx.data_ptr(), n,
                                 out.data_ptr(), _stream(stream)))
@@ -433,6 +439,14 @@ def gemm_scaled(A, a_fmt: str, a_scale, Bt, b_fmt: str, b_scale, K: int, block: 
         if t.dtype != torch.uint8 or t.dim() != 2 or (t.stride(1) != 1 and t.shape[1] > 1):
             raise ValueError(f"{nm} must be a 2-D uint8 tensor with unit column stride")
     M, N = A.shape[0], Bt.shape[0]
+    if block < 1 or K < 0 or K % block:
+        raise ValueError("K must be a non-negative multiple of block")
+    bits_a, bits_b = (4 if a_fmt == "e2m1" else 8), (4 if b_fmt == "e2m1" else 8)
+    if A.shape[1] * 8 < K * bits_a or Bt.shape[1] * 8 < K * bits_b:
+        raise ValueError("A and Bt rows must hold K values")
+    if tuple(a_scale.shape[:1]) != (M,) or tuple(b_scale.shape[:1]) != (N,) or \
+            a_scale.shape[1] < K // block or b_scale.shape[1] < K // block:
+        raise ValueError("a_scale must be (M, >= K/block) and b_scale (N, >= K/block)")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=A.device)
     _on_gpu(out, "out")

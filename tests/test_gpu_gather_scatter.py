@@ -242,3 +242,13 @@ def test_scatter_debug_mode_rejects_duplicate_destinations(stg, monkeypatch):
     monkeypatch.setenv("STG_DEBUG", "0")
     stg.tile_scatter_masked(a, idx, to_dev(np.array([1, 1, 1, 1], np.uint8)), (4, 8), vals, None, 0)
     torch.cuda.synchronize()
+
+
+def test_binding_rejects_short_masks(stg):
+    a = torch.zeros((16, 8), dtype=torch.float32, device="cuda:0")
+    idx = to_dev(np.array([1, 2, 3, 4], dtype=np.int32))
+    short = to_dev(np.array([1, 1, 1], np.uint8))
+    with pytest.raises(ValueError, match="one entry per index"):
+        stg.tile_gather_masked(a, idx, short, (4, 8), None, 0, -1.0)
+    with pytest.raises(ValueError, match="one entry per index"):
+        stg.tile_scatter_masked(a, idx, short, (4, 8), torch.ones((4, 8), device="cuda:0"), None, 0)

@@ -224,3 +224,23 @@ def test_scaled_small_k_main_kernel(stg, orc, K, block, fmt):
                                 block))
     np.testing.assert_array_equal(C.astype(np.float64),
                                   orc.gemm_scaled_f64(pack(ca, fmt), fmt, sa, pack(cb, fmt), fmt, sb, K, block))
+
+
+def test_scaled_binding_rejects_undersized_tensors(stg):
+    """The C ABI cannot see allocation sizes; the binding checks that every
+    tensor holds what M, N, K and block ask for before anything is launched."""
+    u8 = lambda *shape: torch.zeros(shape, dtype=torch.uint8, device="cuda:0")
+    A, Bt, sa, sb = u8(64, 128), u8(32, 128), u8(64, 4), u8(32, 4)
+    stg.gemm_scaled(A, "e4m3", sa, Bt, "e4m3", sb, 128, 32)  # consistent: runs
+    torch.cuda.synchronize()
+    with pytest.raises(ValueError, match="hold K"):
+        stg.gemm_scaled(A, "e4m3", sa, Bt, "e4m3", sb, 160, 32)
+    with pytest.raises(ValueError, match="a_scale"):
+        stg.gemm_scaled(A, "e4m3", u8(63, 4), Bt, "e4m3", sb, 128, 32)
+    with pytest.raises(ValueError, match="a_scale"):
+        stg.gemm_scaled(A, "e4m3", sa, Bt, "e4m3", u8(32, 3), 128, 32)
+    with pytest.raises(ValueError, match="multiple of block"):
+        stg.gemm_scaled(A, "e4m3", sa, Bt, "e4m3", sb, 100, 32)
+    # fp4: 128 bytes hold 256 values
+    stg.gemm_scaled(A, "e2m1", u8(64, 8), Bt, "e2m1", u8(32, 8), 256, 32)
+    torch.cuda.synchronize()

@@ -121,3 +121,12 @@ def test_ragged_store_random(stg, orc, seed):
     one = random_bits(rng, (1, BM, BN), dt)
     _store(stg, orc, one, X1, md, group, col0, np.array([total - 1], np.uint32), np.array([bm_seq + 5], np.uint32),
            np.array([0], np.uint32))
+
+
+def test_ragged_load_rejects_a_small_out(stg):
+    X = torch.zeros((40, 8, 128), dtype=torch.bfloat16, device="cuda:0")
+    ri, dyn, mi = stg.ragged_tile_schedule([40], 128, 8)
+    trip = [to_dev(t.astype(np.int32)) for t in (ri, dyn, mi)]
+    small = torch.empty((len(ri), 64, 128), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(ValueError, match="out must be"):
+        stg.ragged_tile_load(X, 8, 1, 128, 128, *trip, out=small)
