@@ -17,9 +17,10 @@
 // block 0 and bytes 16-31 for block 1; fp4 (16 bytes, two values per byte,
 // even element low): all of lane half l / 32.  The order of K inside a block
 // does not matter as long as both operands use the same one, so a lane takes
-// the 16-byte chunks 2p + l / 32 (p = 0, 1) of the step's 64-byte K run: K
-// values 32 p + 16 (l / 32) .. +15 of fp8, 32 p + 16 (l / 32) .. of fp4 at
-// twice the density.  The accumulator layout is the 32x32 MFMA layout.
+// the 16-byte chunks 2p + l / 32 (p = 0, 1) of a stage's 64-byte K run: for
+// fp8 the two halves of the stage's one MFMA step (K values 32 p + 16 (l / 32)
+// .. +15), for fp4 its 16 bytes of MFMA step p (K values 64 p + 32 (l / 32)
+// .. +31).  The accumulator layout is the 32x32 MFMA layout.
 //  * Tiles 256 x 256 on 4 waves, one per SIMD, each with 128 x 128
 //    accumulators: with a SIMD to itself a wave has 512 registers, enough to
 //    hold the next stage's operands while the current ones feed the MFMAs,
@@ -42,6 +43,8 @@
 //    finite value, so a NaN byte beyond the matrix cannot reach the zero data
 //    there.
 //  * Clipped fp32 epilogue adding the optional accumulator input.
+//  * Columns past the last whole 256-column tile, when at most 8, go to a
+//    skinny kernel instead of a tile column of their own.
 #include "gemm_common.h"
 
 #include <type_traits>
@@ -270,9 +273,9 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
     constexpr int NW = PH == 3 ? kWDma : 0;  // window instructions this step
     constexpr int ND = NW + kDma;
     // this step's bookkeeping (descriptors and K bound of stage kt + 4's
-    // DMA, the window's group, the scale caps) is issued after the first
-    // MFMA, which needs only the previous step's registers: with one wave per
-    // SIMD, instructions issued while an MFMA runs cost the matrix core nothing
+    // DMA, the window's group) is issued after the first MFMA, which needs
+    // only the previous step's registers: with one wave per SIMD,
+    // instructions issued while an MFMA runs cost the matrix core nothing
     u32x4_s rsa, rsb;
     int g = 0, kbw = 0, kl_d = 0;
     auto cap_of = [&](int s) {
