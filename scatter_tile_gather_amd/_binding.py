@@ -112,18 +112,17 @@ def _on_gpu(t, name: str):
         raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
 
 
+_I64x4 = ctypes.c_int64 * 4
+
+
 def _desc(t, name: str) -> StgTensor:
     _on_gpu(t, name)
-    if t.dim() < 1 or t.dim() > 4:
+    shape, stride = tuple(t.shape), t.stride()
+    r = len(shape)
+    if r < 1 or r > 4:
         raise ValueError(f"{name}: rank must be 1..4")
-    d = StgTensor()
-    d.data = t.data_ptr()
-    d.dtype = _dtype_code(t)
-    d.rank = t.dim()
-    for i in range(4):
-        d.shape[i] = t.shape[i] if i < t.dim() else 1
-        d.stride[i] = t.stride(i) if i < t.dim() else 0
-    return d
+    pad = 4 - r
+    return StgTensor(t.data_ptr(), _dtype_code(t), r, _I64x4(*shape, *((1,) * pad)), _I64x4(*stride, *((0,) * pad)))
 
 
 def _i64arr(vals):
@@ -133,10 +132,22 @@ def _i64arr(vals):
     return arr
 
 
-def _stream(stream) -> int:
+_RAW_STREAM = None
+
+
+def _stream(stream, like=None) -> int:
+    """The HIP stream to enqueue on: `stream`'s, else the current stream of the
+    device `like` lives on (or of the current device)."""
+    global _RAW_STREAM
+    if stream is not None:
+        return stream.cuda_stream
     torch = _torch()
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+    if _RAW_STREAM is None:
+        # torch's raw-stream accessor skips building a Stream object per call
+        _RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", False)
+    if _RAW_STREAM:
+        return _RAW_STREAM(like.get_device() if like is not None else torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _check(rc: int):
@@ -191,7 +202,7 @@ def tile_gather(a, indices, tile_shape, offset=None, axis: int = 0, out=None, st
         out = torch.empty(_gather_out_shape(tile_shape, n, axis), dtype=a.dtype, device=a.device)
     ad, od = _desc(a, "a"), _desc(out, "out")
     _check(lib.tile_gather(ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"), n, _i64arr(tile_shape),
-                           None if offset is None else _i64arr(offset), axis, ctypes.byref(od), _stream(stream)))
+                           None if offset is None else _i64arr(offset), axis, ctypes.byref(od), _stream(stream, a)))
     return out
 
 
@@ -208,7 +219,7 @@ def tile_gather_masked(a, indices, mask, tile_shape, offset=None, axis: int = 0,
     mp = None if mask is None else _dev_array(mask, torch.uint8, "mask")
     _check(lib.tile_gather_masked(ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"), mp, n,
                                   _i64arr(tile_shape), None if offset is None else _i64arr(offset), axis,
-                                  float(padding_value), ctypes.byref(od), _stream(stream)))
+                                  float(padding_value), ctypes.byref(od), _stream(stream, a)))
     return out
 
 
@@ -243,7 +254,7 @@ def tile_gather_backward(a_grad, indices, tile_shape, grad_out, offset=None, axi
         ws_ptr, ws_n = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     _check(lib.tile_gather_backward(ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"), n,
                                     _i64arr(tile_shape), None if offset is None else _i64arr(offset), axis,
-                                    ctypes.byref(gd), ws_ptr, ws_n, _stream(stream)))
+                                    ctypes.byref(gd), ws_ptr, ws_n, _stream(stream, a_grad)))
     return a_grad
 
 
@@ -257,7 +268,7 @@ def tile_scatter_masked(a, indices, mask, tile_shape, tile, offset=None, axis: i
     mp = None if mask is None else _dev_array(mask, torch.uint8, "mask")
     _check(lib.tile_scatter_masked(ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"), mp, n,
                                    _i64arr(tile_shape), None if offset is None else _i64arr(offset), axis,
-                                   ctypes.byref(td), _stream(stream)))
+                                   ctypes.byref(td), _stream(stream, a)))
     return a
 
 
@@ -276,7 +287,7 @@ def tile_copy_bounded(src, tile_rows: int, tile_cols: int, origin_row: int = 0, 
         raise ValueError("out must be a contiguous tile buffer of the source dtype and grid size")
     sd = _desc(src, "src")
     _check(lib.tile_copy_bounded(ctypes.byref(sd), tile_rows, tile_cols, origin_row, origin_col, out.data_ptr(),
-                                 _stream(stream)))
+                                 _stream(stream, src)))
     return out
 
 
@@ -296,7 +307,7 @@ def tile_copy_windows(src, tile_rows: int, tile_cols: int, step_rows: int, step_
         raise ValueError("out must be a contiguous tile buffer of the source dtype and grid size")
     sd = _desc(src, "src")
     _check(lib.tile_copy_windows(ctypes.byref(sd), tile_rows, tile_cols, step_rows, step_cols, origin_row, origin_col,
-                                 1 if check_bounds else 0, out.data_ptr(), _stream(stream)))
+                                 1 if check_bounds else 0, out.data_ptr(), _stream(stream, src)))
     return out
 
 
@@ -312,7 +323,7 @@ def tile_store_windows(tiles, step_rows: int, step_cols: int, origin_row: int, o
         raise ValueError("tile buffer grid does not match dst, step and origin")
     dd = _desc(dst, "dst")
     _check(lib.tile_store_windows(tiles.data_ptr(), tr, tc, step_rows, step_cols, origin_row, origin_col,
-                                  1 if check_bounds else 0, ctypes.byref(dd), _stream(stream)))
+                                  1 if check_bounds else 0, ctypes.byref(dd), _stream(stream, dst)))
     return dst
 
 
@@ -327,7 +338,7 @@ def tile_store_clipped(tiles, origin_row: int, origin_col: int, dst, stream=None
         raise ValueError("tile buffer grid does not match dst and origin")
     dd = _desc(dst, "dst")
     _check(lib.tile_store_clipped(tiles.data_ptr(), tr, tc, origin_row, origin_col, ctypes.byref(dd),
-                                  _stream(stream)))
+                                  _stream(stream, dst)))
     return dst
 
 
@@ -369,7 +380,7 @@ def ragged_tile_load(src, middle_dim: int, group: int, BM: int, BN: int, ragged_
         raise ValueError("out must be a contiguous (n_tiles, BM, BN) tensor of src's dtype")
     _check(lib.ragged_tile_load(src.data_ptr(), _dtype_code(src), src.shape[0], middle_dim, group, src.shape[2], BM,
                                 BN, col0, ragged_idx.data_ptr(), dynamic_dim.data_ptr(), middle_idx.data_ptr(), n,
-                                out.data_ptr(), _stream(stream)))
+                                out.data_ptr(), _stream(stream, src)))
     return out
 
 
@@ -393,7 +404,7 @@ def ragged_tile_store(tiles, dst, middle_dim: int, group: int, ragged_idx, dynam
             raise ValueError(f"{nm} must be a contiguous 32-bit integer tensor with one entry per tile")
     _check(lib.ragged_tile_store(tiles.data_ptr(), _dtype_code(dst), dst.shape[0], middle_dim, group, dst.shape[2], BM,
                                  BN, col0, ragged_idx.data_ptr(), dynamic_dim.data_ptr(), middle_idx.data_ptr(), n,
-                                 dst.data_ptr(), _stream(stream)))
+                                 dst.data_ptr(), _stream(stream, dst)))
     return dst
 
 
@@ -418,7 +429,7 @@ def gemm_bounded(A, B, out=None, out_dtype=None, stream=None):
         raise ValueError("out must be (M, N) with unit column stride")
     code = _dtype_code(out)
     _check(lib.gemm_bounded(A.data_ptr(), A.stride(0), B.data_ptr(), B.stride(0), out.data_ptr(), out.stride(0), M,
-                            N, K, code, _stream(stream)))
+                            N, K, code, _stream(stream, A)))
     return out
 
 
@@ -461,5 +472,5 @@ def gemm_scaled(A, a_fmt: str, a_scale, Bt, b_fmt: str, b_scale, K: int, block: 
     _check(lib.gemm_scaled(A.data_ptr(), LOWP_FORMATS[a_fmt], A.stride(0), a_scale.data_ptr(), a_scale.stride(0),
                            Bt.data_ptr(), LOWP_FORMATS[b_fmt], Bt.stride(0), b_scale.data_ptr(), b_scale.stride(0),
                            SCALE_FORMATS[scale_fmt], block, accp, ldacc, out.data_ptr(), out.stride(0), M, N, K,
-                           _stream(stream)))
+                           _stream(stream, A)))
     return out
