@@ -304,7 +304,36 @@ def run_gather(stg, inputs, steps, warmup):
     e = op_entry("row gather fp32 (1024,256), 4096 int32 indices in [-64,1087], (64,256) tiles", nbytes, ms, kms)
     e["cold_cache"] = cold_entry(nbytes, fn)
     e["note"] = "about 8 MB per call: bound by launch latency and host call overhead, not by HBM"
+    e["graph_replay"] = graph_replay(fn, nbytes, steps)
     return e
+
+
+def graph_replay(fn, nbytes, steps, calls=64):
+    """Per-call time with `calls` calls captured in one HIP graph and the
+    graph replayed `steps` times: the launch path without the host call."""
+    import torch
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(calls):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    per_call = ev0.elapsed_time(ev1) / (steps * calls)
+    return {"calls_per_graph": calls, "replays": steps, "us_per_call": round(per_call * 1e3, 3),
+            "GBps": round(gbs(nbytes, per_call), 1)}
 
 
 def run_masked(stg, inputs, steps, warmup):

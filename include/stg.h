@@ -123,7 +123,8 @@ int tile_gather_masked(const stg_tensor* a, const int32_t* indices, const uint8_
  * (not checked; with the environment variable STG_DEBUG set to anything but
  * "0", the call first synchronizes `stream`, checks on the host that no two
  * active indices in range along `axis` are equal, and fails with
- * STG_ERR_INVALID if they are).
+ * STG_ERR_INVALID if they are; that synchronization rules the debug mode out
+ * under stream capture).
  * Active rows of each workgroup are compacted with wavefront ballots before
  * the copy, so inactive rows cost neither reads nor writes. */
 int tile_scatter_masked(const stg_tensor* a, const int32_t* indices, const uint8_t* mask,
