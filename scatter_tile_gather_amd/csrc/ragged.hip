@@ -21,16 +21,23 @@
 // returns zeros and a store is dropped, and no storage in front of the pointer
 // is needed.
 //
-// One workgroup per tile; a wavefront moves 64 x 16 bytes per instruction.
-// With group > 1 the `group` heads of one position are adjacent in memory, so
-// each position is a single contiguous run of group * depth elements.
+// Work mapping: a tile is split into slices of kThreads 16-byte vectors, one
+// vector per lane, and each slice is one workgroup (4 KiB; a 128 x 128 bf16
+// tile is eight of them).  Slices are numbered so that consecutive ones --
+// the slices of one tile, and the tiles of neighbouring heads, which share the
+// packed rows -- run on the same XCD.  Measured against one workgroup per
+// tile, this moves the 128 x 128 bf16 tiles 4-13% faster (load and store,
+// group 1 and 4).
+// A wavefront moves 64 x 16 bytes per instruction.  With group > 1 the `group`
+// heads of one position are adjacent in memory, so each position is a single
+// contiguous run of group * depth elements.
 #include "stg_internal.h"
 
 namespace stg {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 8;
+constexpr int kUnroll = 1;  // vectors per lane; a slice is kThreads * kUnroll vectors
 
 struct RaggedParams {
   char* x;      // the packed 3-D array (load: source, store: destination)
@@ -49,7 +56,20 @@ struct RaggedParams {
   int32_t cpr;        // 16-byte chunks per output row
   uint32_t cpr_magic, group_magic;
   int32_t items;      // BM * cpr
+  uint32_t slices;    // workgroups per tile: ceil(items / (kThreads * kUnroll)), at most 256
+  uint32_t slices_magic;  // ceil(2^32 / slices), 0 when slices == 1
 };
+
+// Tile of workgroup `wg` (wg < 2^31): wg / slices by a multiply-high whose
+// estimate is at most one too large (the magic's rounding error times wg is
+// below 1/2), then one correction.  All scalar, so the tile's three schedule
+// words are fetched together right after the kernel arguments.
+__device__ __forceinline__ uint32_t tile_of(const RaggedParams& p, uint32_t wg) {
+  if (p.slices == 1) return wg;
+  uint32_t q = __umulhi(wg, p.slices_magic);
+  if (q * p.slices > wg) --q;
+  return q;
+}
 
 // Tile k's view of the packed array: the positions that exist (below
 // dynamic_dim, inside the array, valid head), the address of its first element
@@ -75,56 +95,56 @@ __device__ __forceinline__ TileView tile_view(const RaggedParams& p, int64_t k) 
 
 // FULL: every output row is whole 16-byte vectors, all backed by source
 // columns (BN * esize a multiple of 16, col0 + BN <= depth), and the tile is
-// a whole number of workgroup passes, so no vector needs the element path or
+// a whole number of slices, so no vector needs the element path or
 // a bounds test and vector `it` of the tile sits at byte 16 * it of its
 // output -- the common case (128 x 128 bf16), and about 5% faster.
 template <int ESIZE, bool FULL>
 __global__ __launch_bounds__(kThreads) void ragged_load_kernel(RaggedParams p) {
   constexpr int V = 16 / ESIZE;
-  const int64_t k = blockIdx.x;
+  const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t k = tile_of(p, wg);
   const TileView tv = tile_view(p, k);
   const int64_t dyn = tv.dyn;
   const char* base = tv.base;
   const __amdgpu_buffer_rsrc_t rs = tv.rs;
   char* out = p.tiles + k * p.tile_b;
-  for (int b0 = 0; b0 < p.items; b0 += kThreads * kUnroll) {
-    u32x4 v[kUnroll];
+  const int b0 = (int)(wg - k * p.slices) * (kThreads * kUnroll);
+  u32x4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int it = b0 + u * kThreads + threadIdx.x;
-      v[u] = (u32x4){0, 0, 0, 0};
-      if (FULL || it < p.items) {
-        const int j = (int)div_small((uint32_t)it, p.cpr_magic);  // tile row = s * group + g
-        const int b = (it - j * p.cpr) * 16;
-        const int s = (int)div_small((uint32_t)j, p.group_magic);
-        const int g = j - s * p.group;
-        const bool row_ok = s < dyn;
-        const uint32_t roff = (uint32_t)(s * p.row_b + g * p.head_b);
-        const bool full = row_ok && (FULL || b + 16 <= p.valid_b);
-        v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, full ? roff + b : kOOB, 0, 0);
-        if (!FULL && row_ok && !full && b < p.valid_b) {
+  for (int u = 0; u < kUnroll; ++u) {
+    const int it = b0 + u * kThreads + threadIdx.x;
+    v[u] = (u32x4){0, 0, 0, 0};
+    if (FULL || it < p.items) {
+      const int j = (int)div_small((uint32_t)it, p.cpr_magic);  // tile row = s * group + g
+      const int b = (it - j * p.cpr) * 16;
+      const int s = (int)div_small((uint32_t)j, p.group_magic);
+      const int g = j - s * p.group;
+      const bool row_ok = s < dyn;
+      const uint32_t roff = (uint32_t)(s * p.row_b + g * p.head_b);
+      const bool full = row_ok && (FULL || b + 16 <= p.valid_b);
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, full ? roff + b : kOOB, 0, 0);
+      if (!FULL && row_ok && !full && b < p.valid_b) {
 #pragma unroll
-          for (int e = 0; e < V; ++e)
-            if (b + e * ESIZE < p.valid_b) vec_set<ESIZE>(v[u], e, load_elem<ESIZE>(base + roff + b + e * ESIZE));
-        }
+        for (int e = 0; e < V; ++e)
+          if (b + e * ESIZE < p.valid_b) vec_set<ESIZE>(v[u], e, load_elem<ESIZE>(base + roff + b + e * ESIZE));
       }
     }
+  }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int it = b0 + u * kThreads + threadIdx.x;
-      if (FULL) {
-        st16(out + (int64_t)it * 16, v[u]);
-      } else if (it < p.items) {
-        const int j = (int)div_small((uint32_t)it, p.cpr_magic);
-        const int b = (it - j * p.cpr) * 16;
-        char* d = out + (int64_t)j * p.out_row_b + b;
-        if (b + 16 <= p.out_row_b) {
-          st16(d, v[u]);
-        } else {
+  for (int u = 0; u < kUnroll; ++u) {
+    const int it = b0 + u * kThreads + threadIdx.x;
+    if (FULL) {
+      st16(out + (int64_t)it * 16, v[u]);
+    } else if (it < p.items) {
+      const int j = (int)div_small((uint32_t)it, p.cpr_magic);
+      const int b = (it - j * p.cpr) * 16;
+      char* d = out + (int64_t)j * p.out_row_b + b;
+      if (b + 16 <= p.out_row_b) {
+        st16(d, v[u]);
+      } else {
 #pragma unroll
-          for (int e = 0; e < V; ++e)
-            if (b + e * ESIZE < p.out_row_b) store_elem<ESIZE>(d + e * ESIZE, vec_get<ESIZE>(v[u], e));
-        }
+        for (int e = 0; e < V; ++e)
+          if (b + e * ESIZE < p.out_row_b) store_elem<ESIZE>(d + e * ESIZE, vec_get<ESIZE>(v[u], e));
       }
     }
   }
@@ -139,47 +159,47 @@ __global__ __launch_bounds__(kThreads) void ragged_load_kernel(RaggedParams p) {
 template <int ESIZE, bool FULL>
 __global__ __launch_bounds__(kThreads) void ragged_store_kernel(RaggedParams p) {
   constexpr int V = 16 / ESIZE;
-  const int64_t k = blockIdx.x;
+  const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t k = tile_of(p, wg);
   const TileView tv = tile_view(p, k);
   const char* in = p.tiles + k * p.tile_b;
-  for (int b0 = 0; b0 < p.items; b0 += kThreads * kUnroll) {
-    u32x4 v[kUnroll];
-    uint32_t off[kUnroll];  // byte offset of the vector in the view, kOOB when it has no place
-    int bb[kUnroll];        // byte of the vector within its row; -1 when nothing is stored
+  const int b0 = (int)(wg - k * p.slices) * (kThreads * kUnroll);
+  u32x4 v[kUnroll];
+  uint32_t off[kUnroll];  // byte offset of the vector in the view, kOOB when it has no place
+  int bb[kUnroll];        // byte of the vector within its row; -1 when nothing is stored
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int it = b0 + u * kThreads + threadIdx.x;
-      off[u] = kOOB;
-      bb[u] = -1;
-      v[u] = (u32x4){0, 0, 0, 0};
-      if (FULL || it < p.items) {
-        const int j = (int)div_small((uint32_t)it, p.cpr_magic);
-        const int b = (it - j * p.cpr) * 16;
-        const int s = (int)div_small((uint32_t)j, p.group_magic);
-        const int g = j - s * p.group;
-        if (s < tv.dyn && b < p.valid_b) {
-          bb[u] = b;
-          off[u] = (uint32_t)(s * p.row_b + g * p.head_b) + b;
-          const char* src = in + (int64_t)j * p.out_row_b + b;
-          if (FULL || b + 16 <= p.out_row_b) {
-            v[u] = ld16(src);
-          } else {
+  for (int u = 0; u < kUnroll; ++u) {
+    const int it = b0 + u * kThreads + threadIdx.x;
+    off[u] = kOOB;
+    bb[u] = -1;
+    v[u] = (u32x4){0, 0, 0, 0};
+    if (FULL || it < p.items) {
+      const int j = (int)div_small((uint32_t)it, p.cpr_magic);
+      const int b = (it - j * p.cpr) * 16;
+      const int s = (int)div_small((uint32_t)j, p.group_magic);
+      const int g = j - s * p.group;
+      if (s < tv.dyn && b < p.valid_b) {
+        bb[u] = b;
+        off[u] = (uint32_t)(s * p.row_b + g * p.head_b) + b;
+        const char* src = in + (int64_t)j * p.out_row_b + b;
+        if (FULL || b + 16 <= p.out_row_b) {
+          v[u] = ld16(src);
+        } else {
 #pragma unroll
-            for (int e = 0; e < V; ++e)
-              if (b + e * ESIZE < p.out_row_b) vec_set<ESIZE>(v[u], e, load_elem<ESIZE>(src + e * ESIZE));
-          }
+          for (int e = 0; e < V; ++e)
+            if (b + e * ESIZE < p.out_row_b) vec_set<ESIZE>(v[u], e, load_elem<ESIZE>(src + e * ESIZE));
         }
       }
     }
+  }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const bool full = bb[u] >= 0 && (FULL || bb[u] + 16 <= p.valid_b);
-      __builtin_amdgcn_raw_buffer_store_b128(v[u], tv.rs, full ? off[u] : kOOB, 0, 0);
-      if (!FULL && bb[u] >= 0 && !full) {
+  for (int u = 0; u < kUnroll; ++u) {
+    const bool full = bb[u] >= 0 && (FULL || bb[u] + 16 <= p.valid_b);
+    __builtin_amdgcn_raw_buffer_store_b128(v[u], tv.rs, full ? off[u] : kOOB, 0, 0);
+    if (!FULL && bb[u] >= 0 && !full) {
 #pragma unroll
-        for (int e = 0; e < V; ++e)
-          if (bb[u] + e * ESIZE < p.valid_b) store_elem<ESIZE>(tv.base + off[u] + e * ESIZE, vec_get<ESIZE>(v[u], e));
-      }
+      for (int e = 0; e < V; ++e)
+        if (bb[u] + e * ESIZE < p.valid_b) store_elem<ESIZE>(tv.base + off[u] + e * ESIZE, vec_get<ESIZE>(v[u], e));
     }
   }
 }
@@ -222,8 +242,10 @@ int ragged_setup(const char* name, const void* x, int32_t dtype, int64_t total_r
     return fail(STG_ERR_RANGE, "%s: tile of %d x %d elements is too large", name, BM, BN);
   if ((int64_t)p.bm_seq * p.row_b + p.out_row_b >= kMaxOffset32)
     return fail(STG_ERR_RANGE, "%s: BM_seq rows span more than 2^31 bytes", name);
-  if (n_tiles > INT32_MAX) return fail(STG_ERR_RANGE, "%s: too many tiles", name);
   p.items = BM * p.cpr;
+  p.slices = (uint32_t)((p.items + kThreads * kUnroll - 1) / (kThreads * kUnroll));
+  p.slices_magic = p.slices == 1 ? 0u : (uint32_t)(((uint64_t(1) << 32) + p.slices - 1) / p.slices);
+  if (n_tiles > INT32_MAX / (int64_t)p.slices) return fail(STG_ERR_RANGE, "%s: too many tiles", name);
   p.cpr_magic = div_magic((uint32_t)p.cpr);
   p.group_magic = div_magic((uint32_t)group);
   return STG_OK;
@@ -250,7 +272,7 @@ extern "C" int ragged_tile_load(const void* src, int32_t dtype, int64_t total_ro
                          dynamic_dim, middle_idx, n_tiles, tiles_out, p, es)) || n_tiles == 0)
     return rc;
   const hipStream_t s = as_stream(stream);
-  const dim3 grid((unsigned)n_tiles), block(kThreads);
+  const dim3 grid((unsigned)(n_tiles * p.slices)), block(kThreads);
   const bool full = ragged_full(p);
 #define STG_RAGGED(K, E) \
   full ? launch_kernel(name, K<E, true>, grid, block, 0, s, p) : launch_kernel(name, K<E, false>, grid, block, 0, s, p)
@@ -275,7 +297,7 @@ extern "C" int ragged_tile_store(const void* tiles_in, int32_t dtype, int64_t to
                          dynamic_dim, middle_idx, n_tiles, tiles_in, p, es)) || n_tiles == 0)
     return rc;
   const hipStream_t s = as_stream(stream);
-  const dim3 grid((unsigned)n_tiles), block(kThreads);
+  const dim3 grid((unsigned)(n_tiles * p.slices)), block(kThreads);
   const bool full = ragged_full(p);
   switch (es) {
     case 1: STG_RAGGED(ragged_store_kernel, 1); break;

@@ -130,3 +130,28 @@ def test_ragged_load_rejects_a_small_out(stg):
     small = torch.empty((len(ri), 64, 128), dtype=torch.bfloat16, device="cuda:0")
     with pytest.raises(ValueError, match="out must be"):
         stg.ragged_tile_load(X, 8, 1, 128, 128, *trip, out=small)
+
+
+# ---- tiles spanning many workgroup slices --------------------------------------
+
+@pytest.mark.parametrize("case", [
+    # dtype, group, md, depth, BM, BN, col0: 4800 vectors = 18 whole slices of 256 and a tail of 192
+    (np.float32, 1, 3, 210, 96, 200, 7),
+    # 16-byte rows of a 1-byte type: one vector per row, 4 whole slices and a tail of 8
+    (np.uint8, 4, 2, 40, 1032, 16, 24),
+    # exactly 2 slices, every row whole vectors (the unchecked-interior instance)
+    (np.uint16, 2, 2, 64, 64, 64, 0),
+])
+def test_ragged_many_slices(stg, orc, case):
+    dt, group, md, depth, BM, BN, col0 = case
+    rng = np.random.default_rng(4242 + BM)
+    bm_seq = BM // group
+    lens = np.array([bm_seq * 2 + 5, 3, bm_seq, 1, bm_seq + 1], dtype=np.int64)
+    total = int(lens.sum())
+    X0 = random_bits(rng, (total, md * group, depth), dt)
+    ri, dyn, mi = stg.ragged_tile_schedule(lens, bm_seq, md)
+    say("ragged many slices", dt.__name__, "group", group, "md", md, "depth", depth, "BM", BM, "BN", BN, "tiles",
+        len(ri))
+    _run(stg, orc, X0, md, group, BM, BN, col0, ri, dyn, mi)
+    tiles = random_bits(rng, (len(ri), BM, BN), dt)
+    _store(stg, orc, tiles, X0, md, group, col0, ri, dyn, mi)
