@@ -28,10 +28,8 @@
 // masked-out scatter rows.  Repeated indices add up in an unspecified order.
 // The chip retires about 77 G lane-wise float atomic adds per second whatever
 // the table size, so with a caller-provided workspace the row layout takes an
-// atomic-free path instead: a histogram of destination rows, a scan into
-// segment offsets, a fill of each term's row id into its destination's
-// segment (the histogram's integer atomics return each term's rank within its
-// row, so the fill is a plain scatter), and a reduction in
+// atomic-free path instead: the terms are grouped by destination row with a
+// two-level counting sort done in LDS (no global atomics), and a reduction in
 // which one group of lanes owns a destination row, adds its terms and writes
 // the row once with plain stores.
 #include "stg_internal.h"
@@ -103,13 +101,16 @@ __device__ __forceinline__ void resolve_row(const RowParams& p, int64_t g, int64
 
 // FULL: the row is whole 16-byte vectors and every column is in bounds
 // (lo_b = 0, hi_b = row_bytes), so no vector takes the element path.
+// Workgroups are numbered XCD by XCD, so that consecutive output rows are
+// written from one L2 (2% faster on the masked-gather workload; the scatter,
+// whose writes land at random rows, gains nothing from it).
 template <int ESIZE, bool FULL>
 __global__ __launch_bounds__(kThreads) void gather_rows_kernel(RowParams p) {
   constexpr int V = 16 / ESIZE;
   __shared__ int64_t s_src[kMaxRowsPerWg];
   __shared__ int64_t s_dst[kMaxRowsPerWg];
   const int tid = threadIdx.x;
-  const int64_t row0 = (int64_t)blockIdx.x * p.rows_per_wg;
+  const int64_t row0 = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * p.rows_per_wg;
   const int nr = (int)min((int64_t)p.rows_per_wg, p.n_rows - row0);
   if (tid < nr) {
     int64_t ao, to;
@@ -299,10 +300,27 @@ __global__ __launch_bounds__(kThreads) void scatter_elem_kernel(ElemParams p) {
 
 // ---- sorted (segmented) backward -------------------------------------------
 //
+// The terms (grad_out rows) are grouped by destination row with a two-level
+// counting sort, every step of it in LDS: destination rows fall into at most
+// 4096 buckets of 2^shift consecutive rows;
+//  1. each workgroup counts the bucket of each of its 4096 terms (LDS
+//     atomics) and writes its counts as one column of a bucket-major table;
+//  2. an exclusive scan of that table gives every (bucket, workgroup) pair
+//     its place, so that each bucket's terms form one contiguous run;
+//  3. each workgroup sorts its terms by bucket in LDS and writes them, as
+//     (row, term) pairs, into those runs -- contiguous stretches, not single
+//     scattered words;
+//  4. one workgroup per bucket counts its terms per row (LDS atomics over a
+//     window of 4096 rows), scans the counts into the rows' segment offsets
+//     and places each term id into its row's segment.
+// The reduce kernel then sums each row's segment.  The order of the terms
+// inside a segment follows the LDS atomics and is unspecified.  Global
+// memory sees no atomics at all; the earlier histogram of returning global
+// atomics took about 0.25 ms of the 0.98 ms of the 4M-term workload.
+//
 // Destination row id of grad_out row g: (sa * p_ext + sp) * q_ext + sq, dense
 // in [0, R) with R = ax_ext * p_ext * q_ext; -1 when the row has no in-range
-// source.  Workspace (int32): count[R] | offs[R + 1] | perm[n_rows] |
-// rank[n_rows] | bsum[nb].
+// source.
 __device__ __forceinline__ int32_t dest_row_id(const RowParams& p, int64_t g, int64_t& t_off) {
   int64_t o_ax, op = 0, oq = 0;
   if (p.rest == 1) {
@@ -322,22 +340,10 @@ __device__ __forceinline__ int32_t dest_row_id(const RowParams& p, int64_t g, in
 
 constexpr int kScanBlock = 1024;  // counts per scan block (256 threads x 4)
 
-__global__ __launch_bounds__(kThreads) void seg_zero_kernel(int32_t* count, int64_t R) {
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < R; i += (int64_t)gridDim.x * kThreads) count[i] = 0;
-}
-
-// count[r] = terms of destination row r; rank[g] = place of term g among them
-__global__ __launch_bounds__(kThreads) void seg_hist_kernel(RowParams p, int32_t* count, int32_t* rank) {
-  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < p.n_rows; g += (int64_t)gridDim.x * kThreads) {
-    int64_t t_off;
-    const int32_t r = dest_row_id(p, g, t_off);
-    if (r >= 0) rank[g] = atomicAdd(count + r, 1);
-  }
-}
-
-// exclusive scan within a workgroup of 256 values (one per thread)
-__device__ __forceinline__ int32_t wg_exclusive_scan(int32_t v, int32_t& total) {
-  __shared__ int32_t s_w[kThreads / 64];
+// exclusive scan within a workgroup of NT values (one per thread)
+template <int NT>
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t& total) {
+  __shared__ int32_t s_w[NT / 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int32_t x = v;
 #pragma unroll
@@ -350,12 +356,15 @@ __device__ __forceinline__ int32_t wg_exclusive_scan(int32_t v, int32_t& total) 
   int32_t before = 0;
   total = 0;
 #pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     before += w < wave ? s_w[w] : 0;
     total += s_w[w];
   }
   __syncthreads();
   return before + x - v;
+}
+__device__ __forceinline__ int32_t wg_exclusive_scan(int32_t v, int32_t& total) {
+  return block_exclusive_scan<kThreads>(v, total);
 }
 
 // block b: sum of count[b*1024 .. b*1024+1023]
@@ -403,18 +412,167 @@ __global__ __launch_bounds__(kThreads) void seg_offs_kernel(int32_t* count, int6
   }
 }
 
-__global__ __launch_bounds__(kThreads) void seg_fill_kernel(RowParams p, const int32_t* rank, const int32_t* offs,
-                                                            int32_t* perm) {
-  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < p.n_rows; g += (int64_t)gridDim.x * kThreads) {
-    int64_t t_off;
-    const int32_t r = dest_row_id(p, g, t_off);
-    if (r >= 0) perm[offs[r] + rank[g]] = (int32_t)g;
+constexpr int kChunk = 4096;                    // terms per workgroup in steps 1 and 3
+constexpr int kChunkPer = kChunk / kThreads;    // 16 per lane
+constexpr int kMaxBuckets = 4096;
+constexpr int kWindow = 4096;                   // destination rows per pass in step 4
+constexpr int kBuildThreads = 1024;
+
+// Step 1: cnt1[b * n_chunks + w] = terms of chunk w whose row is in bucket b.
+__global__ __launch_bounds__(kThreads) void seg_count_kernel(RowParams p, int shift, int nb, int64_t n_chunks,
+                                                             int32_t* cnt1) {
+  __shared__ int32_t lh[kMaxBuckets];
+  const int tid = threadIdx.x;
+  for (int b = tid; b < nb; b += kThreads) lh[b] = 0;
+  __syncthreads();
+  const int64_t g0 = (int64_t)blockIdx.x * kChunk;
+#pragma unroll 4
+  for (int i = 0; i < kChunkPer; ++i) {
+    const int64_t g = g0 + i * kThreads + tid;
+    if (g < p.n_rows) {
+      int64_t t_off;
+      const int32_t r = dest_row_id(p, g, t_off);
+      if (r >= 0) atomicAdd(&lh[r >> shift], 1);
+    }
   }
+  __syncthreads();
+  for (int b = tid; b < nb; b += kThreads) cnt1[(int64_t)b * n_chunks + blockIdx.x] = lh[b];
+}
+
+// Step 3: sort chunk w's terms by bucket in LDS and write each bucket's
+// stretch of (row << 32 | term) pairs at its place pos1[b * n_chunks + w].
+__global__ __launch_bounds__(kThreads) void seg_bucket_kernel(RowParams p, int shift, int nb, int64_t n_chunks,
+                                                              const int32_t* pos1, uint64_t* pairs) {
+  __shared__ int32_t lh[kMaxBuckets];  // counts; chunk-local starts; then place minus local start
+  __shared__ uint64_t srt[kChunk];     // the chunk's pairs in bucket order
+  const int tid = threadIdx.x;
+  const int64_t w = blockIdx.x;
+  for (int b = tid; b < nb; b += kThreads) lh[b] = 0;
+  __syncthreads();
+  const int64_t g0 = w * kChunk;
+  int32_t rr[kChunkPer], rk[kChunkPer];
+#pragma unroll
+  for (int i = 0; i < kChunkPer; ++i) {
+    const int64_t g = g0 + i * kThreads + tid;
+    rr[i] = -1;
+    rk[i] = 0;
+    if (g < p.n_rows) {
+      int64_t t_off;
+      rr[i] = dest_row_id(p, g, t_off);
+      if (rr[i] >= 0) rk[i] = atomicAdd(&lh[rr[i] >> shift], 1);
+    }
+  }
+  __syncthreads();
+  // exclusive scan of lh[0, nb): lane t owns the per consecutive counts from t * per
+  const int per = (nb + kThreads - 1) / kThreads;  // <= 16
+  int32_t sum = 0;
+  for (int e = 0; e < per; ++e) {
+    const int b = tid * per + e;
+    if (b < nb) sum += lh[b];
+  }
+  int32_t total;
+  int32_t run = wg_exclusive_scan(sum, total);
+  for (int e = 0; e < per; ++e) {
+    const int b = tid * per + e;
+    if (b < nb) {
+      const int32_t c = lh[b];
+      lh[b] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kChunkPer; ++i) {
+    if (rr[i] >= 0) {
+      const int64_t g = g0 + i * kThreads + tid;
+      srt[lh[rr[i] >> shift] + rk[i]] = ((uint64_t)(uint32_t)rr[i] << 32) | (uint32_t)g;
+    }
+  }
+  __syncthreads();
+  // pair k of the sorted chunk, in bucket b, goes to pos1[b * n_chunks + w] + (k - local start of b)
+  for (int e = 0; e < per; ++e) {
+    const int b = tid * per + e;
+    if (b < nb) lh[b] = pos1[(int64_t)b * n_chunks + w] - lh[b];
+  }
+  __syncthreads();
+  for (int k = tid; k < total; k += kThreads) {
+    const uint64_t pr = srt[k];
+    pairs[(int64_t)lh[(int)(pr >> 32) >> shift] + k] = pr;
+  }
+}
+
+// Step 4: one workgroup per bucket.  Its pairs are pairs[s0, s1); its rows
+// [b << shift, min((b + 1) << shift, R)) are taken kWindow at a time: count
+// the terms per row, scan the counts into segment offsets (offs), then place
+// each term id at its row's cursor (perm).  offs[R] = number of terms.
+__global__ __launch_bounds__(kBuildThreads) void seg_build_kernel(int64_t R, int shift, int nb, int64_t n_chunks,
+                                                                  const int32_t* pos1, const uint64_t* pairs,
+                                                                  int32_t* offs, int32_t* perm) {
+  __shared__ int32_t cur[kWindow];
+  constexpr int kPer = kWindow / kBuildThreads;  // 4
+  constexpr int kU = 8;                          // pairs in flight per lane
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int64_t s0 = pos1[(int64_t)b * n_chunks], s1 = pos1[(int64_t)(b + 1) * n_chunks];
+  const int64_t row_lo = (int64_t)b << shift;
+  const int64_t row_hi = min(R, (int64_t)(b + 1) << shift);
+  int64_t base = s0;
+  for (int64_t w0 = row_lo; w0 < row_hi; w0 += kWindow) {
+    const int64_t W = min((int64_t)kWindow, row_hi - w0);
+    for (int j = tid; j < kWindow; j += kBuildThreads) cur[j] = 0;
+    __syncthreads();
+    for (int64_t i0 = s0; i0 < s1; i0 += kU * kBuildThreads) {
+      uint64_t pr[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t i = i0 + u * kBuildThreads + tid;
+        pr[u] = i < s1 ? pairs[i] : ~uint64_t(0);
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t d = (int64_t)(pr[u] >> 32) - w0;  // the end marker gives d >= 2^31
+        if (d >= 0 && d < W) atomicAdd(&cur[d], 1);
+      }
+    }
+    __syncthreads();
+    int32_t c[kPer], v = 0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      c[e] = cur[tid * kPer + e];
+      v += c[e];
+    }
+    int32_t total;
+    int32_t run = (int32_t)base + block_exclusive_scan<kBuildThreads>(v, total);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int j = tid * kPer + e;
+      if (j < W) offs[w0 + j] = run;
+      cur[j] = run;
+      run += c[e];
+    }
+    __syncthreads();
+    for (int64_t i0 = s0; i0 < s1; i0 += kU * kBuildThreads) {
+      uint64_t pr[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t i = i0 + u * kBuildThreads + tid;
+        pr[u] = i < s1 ? pairs[i] : ~uint64_t(0);
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t d = (int64_t)(pr[u] >> 32) - w0;
+        if (d >= 0 && d < W) perm[atomicAdd(&cur[d], 1)] = (int32_t)(uint32_t)pr[u];
+      }
+    }
+    base += total;
+    __syncthreads();
+  }
+  if (b == nb - 1 && tid == 0) offs[R] = (int32_t)s1;
 }
 
 // One group of LPR lanes per destination row: each lane owns 16-byte chunks
 // lane, lane + LPR, ... of the row's valid byte window, adds the terms of the
-// row's segment (four grad_out rows in flight) to a.grad's values and stores
+// row's segment (eight grad_out rows in flight) to a.grad's values and stores
 // the row once.  Rows with an empty segment are not touched.
 template <int ESIZE, int LPR>
 __global__ __launch_bounds__(kThreads) void seg_reduce_kernel(RowParams p, int64_t R, const int32_t* offs,
@@ -444,10 +602,10 @@ __global__ __launch_bounds__(kThreads) void seg_reduce_kernel(RowParams p, int64
     float accf[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) accf[e] = (float)acc[e];
-    for (int32_t k = k0; k < k1; k += 4) {
-      u32x4 v[4];
+    for (int32_t k = k0; k < k1; k += 8) {
+      u32x4 v[8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < 8; ++q) {
         v[q] = (u32x4){0, 0, 0, 0};
         if (k + q < k1) {
           int64_t t_off;
@@ -465,7 +623,7 @@ __global__ __launch_bounds__(kThreads) void seg_reduce_kernel(RowParams p, int64
         }
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < 8; ++q) {
         if (k + q >= k1) break;
 #pragma unroll
         for (int e = 0; e < V; ++e) {
@@ -565,47 +723,68 @@ int launch_elems(Op op, int esize, const ElemParams& p, hipStream_t s) {
   return check_launch(op_name(op));
 }
 
-// Shared argument checks and dispatch of the three entry points.  `a` is the
-// indexed array; `t` the dense side (gather output, scatter input).
 // Segmented backward: workspace layout and size (bytes) for R destination
 // rows and n_rows grad_out rows.
 struct SegLayout {
-  int64_t count, offs, perm, rank, bsum, bytes, nb;
+  int shift;                   // bucket = destination row >> shift
+  int64_t nbk, n_chunks, L1;   // buckets, term chunks of kChunk, nbk * n_chunks
+  int64_t nb1;                 // scan blocks over the L1 counts
+  int64_t offs, perm, pairs, cnt1, pos1, bsum, bytes;  // byte offsets in the workspace, total size
 };
 
+// Workspace: offs int32[R + 1] | perm int32[n_rows] | pairs uint64[n_rows] |
+// cnt1 int32[L1] | pos1 int32[L1 + 1] | bsum int32[nb1], each 256-byte aligned.
+// At most 512 buckets while they span at most kWindow rows (R <= 2^21), then
+// up to kMaxBuckets of kWindow rows (R <= 2^24); past that, kMaxBuckets
+// buckets of several windows each.
 SegLayout seg_layout(int64_t R, int64_t n_rows) {
   SegLayout L;
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
-  L.nb = (R + kScanBlock - 1) / kScanBlock;
-  L.count = 0;
-  L.offs = up(L.count + R * 4);
+  int lg = 0;
+  while ((int64_t(1) << lg) < R) ++lg;
+  L.shift = lg > 9 ? lg - 9 : 0;
+  if (L.shift > 12) L.shift = std::max(12, lg - 12);
+  L.nbk = R > 0 ? ((R - 1) >> L.shift) + 1 : 0;
+  L.n_chunks = (n_rows + kChunk - 1) / kChunk;
+  L.L1 = L.nbk * L.n_chunks;
+  L.nb1 = (L.L1 + kScanBlock - 1) / kScanBlock;
+  L.offs = 0;
   L.perm = up(L.offs + (R + 1) * 4);
-  L.rank = up(L.perm + n_rows * 4);
-  L.bsum = up(L.rank + n_rows * 4);
-  L.bytes = up(L.bsum + L.nb * 4);
+  L.pairs = up(L.perm + n_rows * 4);
+  L.cnt1 = up(L.pairs + n_rows * 8);
+  L.pos1 = up(L.cnt1 + L.L1 * 4);
+  L.bsum = up(L.pos1 + (L.L1 + 1) * 4);
+  L.bytes = up(L.bsum + L.nb1 * 4);
   return L;
 }
 
 int launch_segmented(const char* name, int esize, const RowParams& p, int64_t R, char* ws, hipStream_t s) {
   const SegLayout L = seg_layout(R, p.n_rows);
-  int32_t* count = (int32_t*)(ws + L.count);
+  if (L.L1 >= INT32_MAX)
+    return fail(STG_ERR_RANGE, "%s: %lld destination rows with %lld terms exceed the grouped path's tables", name,
+                (long long)R, (long long)p.n_rows);
+  if (p.n_rows == 0) return STG_OK;  // nothing to add
   int32_t* offs = (int32_t*)(ws + L.offs);
   int32_t* perm = (int32_t*)(ws + L.perm);
-  int32_t* rank = (int32_t*)(ws + L.rank);
+  uint64_t* pairs = (uint64_t*)(ws + L.pairs);
+  int32_t* cnt1 = (int32_t*)(ws + L.cnt1);
+  int32_t* pos1 = (int32_t*)(ws + L.pos1);
   int32_t* bsum = (int32_t*)(ws + L.bsum);
-  auto gs = [](int64_t n) { return dim3((unsigned)std::min<int64_t>((n + kThreads - 1) / kThreads, 65536)); };
-  launch_kernel("tile_gather_backward/zero", seg_zero_kernel, gs(R), dim3(kThreads), 0, s, count, R);
-  launch_kernel("tile_gather_backward/hist", seg_hist_kernel, gs(p.n_rows), dim3(kThreads), 0, s, p, count, rank);
-  launch_kernel("tile_gather_backward/bsum", seg_bsum_kernel, dim3((unsigned)L.nb), dim3(kThreads), 0, s,
-                (const int32_t*)count, R, bsum);
-  launch_kernel("tile_gather_backward/bscan", seg_bscan_kernel, dim3(1), dim3(kThreads), 0, s, bsum, L.nb);
-  launch_kernel("tile_gather_backward/offs", seg_offs_kernel, dim3((unsigned)L.nb), dim3(kThreads), 0, s, count, R,
-                (const int32_t*)bsum, offs);
-  launch_kernel("tile_gather_backward/fill", seg_fill_kernel, gs(p.n_rows), dim3(kThreads), 0, s, p,
-                (const int32_t*)rank, (const int32_t*)offs, perm);
+  const int nbk = (int)L.nbk;
+  const dim3 chunks((unsigned)L.n_chunks), blk(kThreads);
+  launch_kernel("tile_gather_backward/count", seg_count_kernel, chunks, blk, 0, s, p, L.shift, nbk, L.n_chunks, cnt1);
+  launch_kernel("tile_gather_backward/bsum", seg_bsum_kernel, dim3((unsigned)L.nb1), blk, 0, s, (const int32_t*)cnt1,
+                L.L1, bsum);
+  launch_kernel("tile_gather_backward/bscan", seg_bscan_kernel, dim3(1), blk, 0, s, bsum, L.nb1);
+  launch_kernel("tile_gather_backward/offs", seg_offs_kernel, dim3((unsigned)L.nb1), blk, 0, s, cnt1, L.L1,
+                (const int32_t*)bsum, pos1);
+  launch_kernel("tile_gather_backward/bucket", seg_bucket_kernel, chunks, blk, 0, s, p, L.shift, nbk, L.n_chunks,
+                (const int32_t*)pos1, pairs);
+  launch_kernel("tile_gather_backward/build", seg_build_kernel, dim3((unsigned)nbk), dim3(kBuildThreads), 0, s, R,
+                L.shift, nbk, L.n_chunks, (const int32_t*)pos1, (const uint64_t*)pairs, offs, perm);
   // lanes per destination row: enough for the row's chunks, at most a wavefront
-  const int chunks = p.n_chunks;
-  const int lpr = chunks <= 8 ? 8 : chunks <= 16 ? 16 : chunks <= 32 ? 32 : 64;
+  const int chunks_per_row = p.n_chunks;
+  const int lpr = chunks_per_row <= 8 ? 8 : chunks_per_row <= 16 ? 16 : chunks_per_row <= 32 ? 32 : 64;
   const dim3 grid((unsigned)((R + kThreads / lpr - 1) / (kThreads / lpr)));
 #define STG_SEG(E, LP) launch_kernel("tile_gather_backward/reduce", seg_reduce_kernel<E, LP>, grid, dim3(kThreads), 0, s, \
                                      p, R, (const int32_t*)offs, (const int32_t*)perm)
@@ -653,6 +832,8 @@ int check_unique_destinations(const char* name, const int32_t* indices, const ui
   return STG_OK;
 }
 
+// Shared argument checks and dispatch of the entry points.  `a` is the
+// indexed array; `t` the dense side (gather output, scatter input).
 int run(Op op, const stg_tensor* a, const int32_t* indices, const uint8_t* mask, int64_t n_indices,
         const int64_t* tile_shape, const int64_t* offset, int32_t axis, double padding_value,
         const stg_tensor* t, void* stream, void* workspace = nullptr, int64_t workspace_bytes = 0) {

@@ -114,3 +114,21 @@ def test_backward_grouped_long_segments(stg, orc):
     a0 = rng.standard_normal((4096, 40)).astype(np.float32)
     say("gather backward grouped: skewed segments")
     run_case(stg, orc, a0, idx, (8, 40), g, ws="auto")
+
+
+@pytest.mark.parametrize("rows,cols,n_tiles", [
+    (3 * 2 ** 20 + 5, 2, 5000),  # more than 2^20 destination rows: 769 buckets of 4096 rows
+    (2 ** 24 + 4099, 1, 4000),   # more than 2^24 rows: buckets of two 4096-row windows
+])
+def test_backward_grouped_large_tables(stg, orc, rows, cols, n_tiles):
+    """Grouped execution on tables past the single-window bucket sizes, with
+    out-of-range indices and one heavy row in the last bucket."""
+    rng = np.random.default_rng(rows % 1000)
+    n = 64 * n_tiles
+    idx = rng.integers(-2, rows + 2, n).astype(np.int32)
+    idx[: n // 8] = rows - 1
+    rng.shuffle(idx)
+    g = rng.standard_normal((n, cols)).astype(np.float32)
+    a0 = rng.standard_normal((rows, cols)).astype(np.float32)
+    say("gather backward grouped: large table", rows, "x", cols, "terms", n)
+    run_case(stg, orc, a0, idx, (64, cols), g, ws="auto")
