@@ -136,15 +136,18 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
     b_kc[q] = c * CHUNK_K;
     b_off[q] = n0 + r < p.N ? (uint32_t)(r * p.ldb + c * 16) : kOOB;
   }
-  // window DMA q of this thread: 16-byte chunk t & 1 of the window of row
-  // t / 2, t = (wave * kWDmaOp + q) * 64 + lane; byte offsets of the rows'
-  // first scales from the 16-byte aligned bases (below 2^31)
+  // window DMA q of this thread: LDS chunk t & 1 of the window of row t / 2,
+  // t = (wave * kWDmaOp + q) * 64 + lane, which holds the window's chunk
+  // (t & 1) ^ bit 3 of the row: the 32 rows whose scale bytes one read
+  // instruction fetches (same byte of each window, windows 32 bytes apart)
+  // then fall on 16 banks instead of 8.  Byte offsets of the rows' first
+  // scales from the 16-byte aligned bases (below 2^31).
   uint32_t sa_row[kWDmaOp], sb_row[kWDmaOp], s_ch[kWDmaOp];
   bool sa_ok[kWDmaOp], sb_ok[kWDmaOp];
 #pragma unroll
   for (int q = 0; q < kWDmaOp; ++q) {
     const int t = (wave * kWDmaOp + q) * 64 + lane, srow = t >> 1;
-    s_ch[q] = 16 * (t & 1);
+    s_ch[q] = 16 * ((t & 1) ^ ((srow >> 3) & 1));
     sa_ok[q] = m0 + srow < p.M;
     sb_ok[q] = n0 + srow < p.N;
     sa_row[q] = sa_ok[q] ? (uint32_t)(p.sa_delta + (m0 + srow) * p.lds_a) : 0u;
@@ -210,6 +213,9 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
   // and B rows; rows 32 i further on keep the swizzle (bits 1-2 of r/2 and
   // r/4 do not change), so the other blocks are at fixed distances
   const int ra0 = wm * 128 + (lane & 31), rb0 = wn * 128 + (lane & 31);
+  // window chunks are swapped in rows with bit 3 set (rows 32 i further on
+  // keep it): a scale byte at window position x sits at x ^ s_swz
+  const int s_swz = 16 * (((lane & 31) >> 3) & 1);
   const int a_l0 = ra0 * kRowB + (a_phys(ra0, half) << 4), a_l1 = ra0 * kRowB + (a_phys(ra0, 2 + half) << 4);
   const int b_l0 = rb0 * kRowB + (a_phys(rb0, half) << 4), b_l1 = rb0 * kRowB + (a_phys(rb0, 2 + half) << 4);
   // Read instruction q of stage kt (ring slot SLOT) into buffer P: q <
@@ -239,9 +245,9 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
       const int kbg = first_block(kt & ~(kSG - 1));
       const int kb = (int)(((uint32_t)kt * (KS / 32) + 2 * s + half) >> p.lg_bq);
       if (w < kSFM)
-        sca[P][w][s] = sas[(ra0 + w * 32) * kSWin + ((a_ph[w] + kbg) & 15) + (kb - kbg)];
+        sca[P][w][s] = sas[(ra0 + w * 32) * kSWin + ((((a_ph[w] + kbg) & 15) + (kb - kbg)) ^ s_swz)];
       else
-        scb[P][w - kSFM][s] = sbs[(rb0 + (w - kSFM) * 32) * kSWin + ((b_ph[w - kSFM] + kbg) & 15) + (kb - kbg)];
+        scb[P][w - kSFM][s] = sbs[(rb0 + (w - kSFM) * 32) * kSWin + ((((b_ph[w - kSFM] + kbg) & 15) + (kb - kbg)) ^ s_swz)];
     }
   };
   auto join = [&](auto p_tag) {
