@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(RowParams p) {
         const int b = (it - r * p.n_chunks) * 16;
         char* d = p.t + s_dst[r] + b;
         if (FULL || b + 16 <= p.row_bytes) {
-          st16(d, v[u]);
+          st16_nt(d, v[u]);
         } else {
 #pragma unroll
           for (int e = 0; e < V; ++e)
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void scatter_rows_kernel(RowParams p) {
           if (ACCUM)
             accum16<ESIZE>(const_cast<char*>(p.a) + s_dst[r] + b, v[u]);
           else
-            st16(const_cast<char*>(p.a) + s_dst[r] + b, v[u]);
+            st16_nt(const_cast<char*>(p.a) + s_dst[r] + b, v[u]);
         } else if (b + 16 > p.lo_b && b < p.hi_b) {
           const char* src = p.t + s_src[r] + b;
           char* dst = const_cast<char*>(p.a) + s_dst[r] + b;
@@ -642,7 +642,7 @@ __global__ __launch_bounds__(kThreads) void seg_reduce_kernel(RowParams p, int64
       vec_set<ESIZE>(out, e, bits);
     }
     if (whole) {
-      st16(arow + b, out);
+      st16_nt(arow + b, out);
     } else {
 #pragma unroll
       for (int e = 0; e < V; ++e) {

@@ -69,6 +69,16 @@ __device__ __forceinline__ u32x4 ld16(const char* p) {
 }
 __device__ __forceinline__ void st16(char* p, u32x4 v) { __builtin_memcpy(p, &v, 16); }
 
+// Non-temporal 16-byte store (global_store_dwordx4 ... nt), any byte alignment.
+// The row gather/scatter kernels write their rows this way: measured back to
+// back, the masked gather runs 18% faster with it (5.8 -> 6.9 TB/s) and the
+// masked scatter to random rows 27% faster (4.9 -> 6.2 TB/s).  It is not a
+// general win: the clipped tile stores into a matrix run about 25% slower
+// with it, and the tile-buffer writes of the copy and ragged kernels gain
+// nothing, so those keep plain stores.
+typedef u32x4 u32x4_unaligned __attribute__((aligned(1)));
+__device__ __forceinline__ void st16_nt(char* p, u32x4 v) { __builtin_nontemporal_store(v, (u32x4_unaligned*)p); }
+
 // Buffer resource over [base, base + bytes) with the gfx9 raw-buffer format
 // word: loads whose offset lies past num_records return zero and stores past
 // it are dropped, which is how invalid vectors are zero-filled or clipped
