@@ -33,7 +33,10 @@
 //  * The scale bytes travel the same way, once per group of 4 stages: per
 //    row the 16-byte aligned 32-byte window that holds the row's (at most
 //    16) scale bytes of the group is DMA'd into one of two window buffers,
-//    and each lane reads its bytes from LDS.  (Per-stage windows would cost
+//    and each lane reads its bytes from LDS: with 32-value blocks and scale
+//    rows that start 16-byte aligned, a whole group's bytes at once, packed
+//    into one register per block row and selected per MFMA with op_sel;
+//    otherwise one byte per MFMA step.  (Per-stage windows would cost
 //    one L2 request per row and stage for a few bytes, doubling the requests
 //    of the whole kernel.)  No load the compiler can see is in flight in the
 //    K loop, so its own waits never force a later stage's DMA to land early;
@@ -92,8 +95,13 @@ static_assert(kWDmaOp * kSNT * 16 == kASc && kASc == kBSc, "whole windows per DM
 static_assert(kScaledLds <= 160 * 1024, "LDS");
 
 // FA / FB: operand format codes of the scaled MFMA (0 e4m3, 1 e5m2, 4 e2m1);
-// BITS: 8 for fp8 operands, 4 for fp4 (both operands of one width)
-template <int FA, int FB, int BITS>
+// BITS: 8 for fp8 operands, 4 for fp4 (both operands of one width).  PK: the
+// packed-scale path, for 32-value blocks whose scale rows start 16-byte
+// aligned (row strides and bases multiples of 16): each lane reads the scale
+// bytes of a whole group of 4 stages with one 8-byte LDS read per block row
+// (fp4: two), gathers its own into one register, and each MFMA selects its
+// byte with op_sel; otherwise one byte is read per MFMA step.
+template <int FA, int FB, int BITS, bool PK>
 __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_scaled_kernel(
     ScaledParams p) {
   constexpr int KS = kRowB * 8 / BITS;    // K values per stage: 64 (fp8) / 128 (fp4)
@@ -209,6 +217,14 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
   // register order the instruction takes; fp4 -- the 16 bytes of MFMA step h.
   i32x8 fa[2][kSFM], fb[2][kSFN];
   int sca[2][kSFM][S], scb[2][kSFN][S];
+  // packed path: byte i of scp[w][h] is the scale of K block kbg + 8 h +
+  // 2 i + half of the current group (kbg: its first block) for block row w
+  // (A rows, then B rows); scr[w]: the 8 raw window bytes just read
+  uint32_t scp[kSFM + kSFN][S];
+  uint64_t scr[kSFM + kSFN];
+  // v_perm selector gathering window bytes half, 2 + half, 4 + half, 6 + half
+  const uint32_t s_sel = (uint32_t)half | (uint32_t)(2 + half) << 8 | (uint32_t)(4 + half) << 16 |
+                         (uint32_t)(6 + half) << 24;
   // LDS byte offsets of this lane's chunks half and 2 + half of its first A
   // and B rows; rows 32 i further on keep the swizzle (bits 1-2 of r/2 and
   // r/4 do not change), so the other blocks are at fixed distances
@@ -225,7 +241,12 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
   // its row's window of group kt / 4 (kbg: the group's first block).  The
   // 16-byte halves land in ta / tb and are joined into fa / fb by join().
   constexpr int NRD_A = 2 * kSFM, NRD_B = 2 * kSFN, NRD_S = (kSFM + kSFN) * S;
-  constexpr int NRD = NRD_A + NRD_B + NRD_S;
+  // reads of the stage in ring slot SLOT: the packed path reads scales only
+  // for a group's first stage (half 0 of its bytes) and, fp4, its third (half 1)
+  auto nrd_of = [](auto slot_tag) {
+    constexpr int SLOT = decltype(slot_tag)::value;
+    return NRD_A + NRD_B + (!PK ? NRD_S : (SLOT == 0 || (BITS == 4 && SLOT == 2)) ? kSFM + kSFN : 0);
+  };
   i32x4 ta[kSFM][2], tb[kSFN][2];
   auto read_one = [&](int kt, int q, auto p_tag, auto slot_tag) {
     constexpr int P = decltype(p_tag)::value;
@@ -238,6 +259,15 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
     } else if (q < NRD_A + NRD_B) {
       const int j = (q - NRD_A) >> 1, h = q & 1;
       tb[j][h] = *(const i32x4*)(bs + (h ? b_l1 : b_l0) + j * 32 * kRowB);
+    } else if constexpr (PK) {
+      // 8 bytes, half H of the row's window bytes of group kt / 4 (window
+      // position (kbg & 15) + 8 H, 8-byte aligned, chunks swapped as written)
+      constexpr int H = SLOT == 2 ? 1 : 0;
+      const char* sas = smem + kSNS * kSlot + ((kt / kSG) & 1) * kScBuf;
+      const int kbg = first_block(kt & ~(kSG - 1));
+      const int w = q - NRD_A - NRD_B;
+      const int row = w < kSFM ? ra0 + w * 32 : kASc / kSWin + rb0 + (w - kSFM) * 32;
+      scr[w] = *(const uint64_t*)(sas + row * kSWin + (((kbg & 15) + 8 * H) ^ s_swz));
     } else {
       const unsigned char* sas = (const unsigned char*)(smem + kSNS * kSlot + ((kt / kSG) & 1) * kScBuf);
       const unsigned char* sbs = sas + kASc;
@@ -257,10 +287,30 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
 #pragma unroll
     for (int j = 0; j < kSFN; ++j) fb[P][j] = __builtin_shufflevector(tb[j][0], tb[j][1], 0, 1, 2, 3, 4, 5, 6, 7);
   };
+  // packed path, after the scale reads of stage kt (ring slot SLOT): gather
+  // each lane's four bytes; bytes of blocks at or past K get a finite scale
+  // (127), since the window may hold anything there (NaN included) and their
+  // data is zero
+  auto pack_scales = [&](int kt, auto slot_tag) {
+    constexpr int SLOT = decltype(slot_tag)::value;
+    if constexpr (PK && (SLOT == 0 || (BITS == 4 && SLOT == 2))) {
+      constexpr int H = SLOT == 2 ? 1 : 0;
+      const int kb0 = first_block(kt & ~(kSG - 1)) + 8 * H + half;
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m |= kb0 + 2 * i >= p.nkb ? 0xFFu << (8 * i) : 0u;
+#pragma unroll
+      for (int w = 0; w < kSFM + kSFN; ++w) {
+        const uint32_t v = __builtin_amdgcn_perm((uint32_t)(scr[w] >> 32), (uint32_t)scr[w], s_sel);
+        scp[w][H] = (v & ~m) | (0x7F7F7F7Fu & m);
+      }
+    }
+  };
   auto read_stage = [&](int kt, auto p_tag, auto slot_tag) {
 #pragma unroll
-    for (int q = 0; q < NRD; ++q) read_one(kt, q, p_tag, slot_tag);
+    for (int q = 0; q < nrd_of(slot_tag); ++q) read_one(kt, q, p_tag, slot_tag);
     join(p_tag);
+    pack_scales(kt, slot_tag);
   };
 
   // one K step on stage kt (kt % 4 == PH), whose operands are in buffer P:
@@ -277,6 +327,7 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
     constexpr int PH = decltype(ph_tag)::value;
     constexpr int NM = kSFM * kSFN * S;
     constexpr int NW = PH == 3 ? kWDma : 0;  // window instructions this step
+    constexpr int NRD = nrd_of(std::integral_constant<int, (PH + 1) % kSNS>());
     constexpr int ND = NW + kDma;
     // this step's bookkeeping (descriptors and K bound of stage kt + 4's
     // DMA, the window's group) is issued after the first MFMA, which needs
@@ -322,11 +373,23 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
             av = __builtin_shufflevector(fa[P][i], fa[P][i], 4, 5, 6, 7, -1, -1, -1, -1);
             bv = __builtin_shufflevector(fb[P][j], fb[P][j], 4, 5, 6, 7, -1, -1, -1, -1);
           }
-          if (i == 0 && j == 0) cap = cap_of(s);
-          if (j == 0) sca[P][i][s] = min(sca[P][i][s], cap);
-          if (i == 0) scb[P][j][s] = min(scb[P][j][s], cap);
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              av, bv, acc[i][j], FA, FB, 0, sca[P][i][s], 0, scb[P][j][s]);
+          if constexpr (PK) {
+            // byte of the packed scales: fp8, stage PH of the group; fp4,
+            // MFMA step s of stage PH, in word PH / 2
+            constexpr int H = BITS == 8 ? 0 : PH >> 1;
+            constexpr int SEL0 = BITS == 8 ? PH : 2 * (PH & 1), SEL1 = SEL0 + 1;
+            const int sa_w = (int)scp[i][H], sb_w = (int)scp[kSFM + j][H];
+            acc[i][j] = s == 0 ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], FA, FB, SEL0,
+                                                                                 sa_w, SEL0, sb_w)
+                               : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], FA, FB, SEL1,
+                                                                                 sa_w, SEL1, sb_w);
+          } else {
+            if (i == 0 && j == 0) cap = cap_of(s);
+            if (j == 0) sca[P][i][s] = min(sca[P][i][s], cap);
+            if (i == 0) scb[P][j][s] = min(scb[P][j][s], cap);
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                av, bv, acc[i][j], FA, FB, 0, sca[P][i][s], 0, scb[P][j][s]);
+          }
           const int m = (s * kSFM + i) * kSFN + j;
           if (m == 0) {
             __builtin_amdgcn_sched_barrier(0);
@@ -356,6 +419,7 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
         }
     __builtin_amdgcn_sched_barrier(0);  // every MFMA is issued before the wait
     join(PN());
+    pack_scales(kt + 1, SN());
     wait_vmcnt(2 * kDma + (PH == 0 || PH == 3 ? kWDma : 0));
     __syncthreads();
   };
@@ -515,10 +579,14 @@ bool scaled_lds_configured = false;
 // main kernel on the first p.N columns; the skinny kernel on columns
 // n_skinny .. n_skinny + r_skinny - 1 (r_skinny = 0: none)
 template <int FA, int FB, int BITS>
-int launch_scaled(const ScaledParams& p, int64_t n_wg, int64_t n_skinny, int r_skinny, hipStream_t s) {
+int launch_scaled(const ScaledParams& p, bool packed, int64_t n_wg, int64_t n_skinny, int r_skinny, hipStream_t s) {
   if (n_wg > 0) {
-    launch_kernel("gemm_scaled/main", gemm_scaled_kernel<FA, FB, BITS>, dim3((unsigned)n_wg), dim3(kSNT),
-                  (uint32_t)kScaledLds, s, p);
+    if (packed)
+      launch_kernel("gemm_scaled/main", gemm_scaled_kernel<FA, FB, BITS, true>, dim3((unsigned)n_wg), dim3(kSNT),
+                    (uint32_t)kScaledLds, s, p);
+    else
+      launch_kernel("gemm_scaled/main", gemm_scaled_kernel<FA, FB, BITS, false>, dim3((unsigned)n_wg), dim3(kSNT),
+                    (uint32_t)kScaledLds, s, p);
     if (int rc = check_launch("gemm_scaled/main")) return rc;
   }
   if (r_skinny > 0) {
@@ -532,7 +600,9 @@ int launch_scaled(const ScaledParams& p, int64_t n_wg, int64_t n_skinny, int r_s
 
 template <int FA, int FB, int BITS>
 bool set_lds() {
-  return hipFuncSetAttribute((const void*)gemm_scaled_kernel<FA, FB, BITS>,
+  return hipFuncSetAttribute((const void*)gemm_scaled_kernel<FA, FB, BITS, false>,
+                             hipFuncAttributeMaxDynamicSharedMemorySize, kScaledLds) == hipSuccess &&
+         hipFuncSetAttribute((const void*)gemm_scaled_kernel<FA, FB, BITS, true>,
                              hipFuncAttributeMaxDynamicSharedMemorySize, kScaledLds) == hipSuccess;
 }
 
@@ -610,9 +680,11 @@ extern "C" int gemm_scaled(const void* A, int32_t a_fmt, int64_t lda, const void
   const int code_a = a_fmt == STG_LP_E4M3 ? 0 : a_fmt == STG_LP_E5M2 ? 1 : 4;
   const int code_b = b_fmt == STG_LP_E4M3 ? 0 : b_fmt == STG_LP_E5M2 ? 1 : 4;
   const int64_t n_sk = p.N;
-  if (bits == 4) return launch_scaled<4, 4, 4>(p, n_wg, n_sk, r_skinny, s);
-  if (code_a == 0 && code_b == 0) return launch_scaled<0, 0, 8>(p, n_wg, n_sk, r_skinny, s);
-  if (code_a == 0) return launch_scaled<0, 1, 8>(p, n_wg, n_sk, r_skinny, s);
-  if (code_b == 0) return launch_scaled<1, 0, 8>(p, n_wg, n_sk, r_skinny, s);
-  return launch_scaled<1, 1, 8>(p, n_wg, n_sk, r_skinny, s);
+  // packed-scale path: 32-value blocks, every scale row starting 16-byte aligned
+  const bool packed = p.lg_bq == 0 && p.sa_delta == 0 && p.sb_delta == 0 && lds_a % 16 == 0 && lds_b % 16 == 0;
+  if (bits == 4) return launch_scaled<4, 4, 4>(p, packed, n_wg, n_sk, r_skinny, s);
+  if (code_a == 0 && code_b == 0) return launch_scaled<0, 0, 8>(p, packed, n_wg, n_sk, r_skinny, s);
+  if (code_a == 0) return launch_scaled<0, 1, 8>(p, packed, n_wg, n_sk, r_skinny, s);
+  if (code_b == 0) return launch_scaled<1, 0, 8>(p, packed, n_wg, n_sk, r_skinny, s);
+  return launch_scaled<1, 1, 8>(p, packed, n_wg, n_sk, r_skinny, s);
 }

@@ -189,6 +189,33 @@ def test_scaled_unaligned_scale_views(stg, orc, base, fmt):
                                   orc.gemm_scaled_f64(pack(ca, fmt), fmt, sa, pack(cb, fmt), fmt, sb, K, block))
 
 
+@pytest.mark.parametrize("K", [96, 160, 544, 640, 1056])
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_scaled_packed_scales_nan_padding(stg, orc, K, fmt):
+    """Scale rows 16-byte aligned (bases and row strides multiples of 16,
+    32-value blocks: the packed-scale path) with every byte past K / 32 set
+    to 0xFF, the e8m0 NaN: the groups of 8 (fp8) or 16 (fp4) blocks that run
+    past K must not let those bytes reach the zero data there.  K = 544 and
+    640 end inside a second group, 1056 inside a third.  Exact values."""
+    M, N, block = 300, 600, 32
+    nkb = K // block
+    lds = (nkb + 15) // 16 * 16 + 16
+    rng = np.random.default_rng(K + (7 if fmt == "e2m1" else 0))
+    ca = np.array(EXACT_CODES[fmt], np.uint8)[rng.integers(0, 4, (M, K))]
+    cb = np.array(EXACT_CODES[fmt], np.uint8)[rng.integers(0, 4, (N, K))]
+    sa_full = np.full((M, lds), 0xFF, np.uint8)
+    sb_full = np.full((N, lds), 0xFF, np.uint8)
+    sa_full[:, :nkb] = rng.integers(126, 130, (M, nkb))
+    sb_full[:, :nkb] = rng.integers(126, 130, (N, nkb))
+    sad, sbd = to_dev(sa_full)[:, :nkb], to_dev(sb_full)[:, :nkb]
+    assert sad.data_ptr() % 16 == 0 and sbd.data_ptr() % 16 == 0 and sad.stride(0) % 16 == 0
+    say("gemm_scaled packed scales, NaN padding, K", K, fmt, "row stride", lds)
+    C = to_host(stg.gemm_scaled(to_dev(pack(ca, fmt)), fmt, sad, to_dev(pack(cb, fmt)), fmt, sbd, K, block))
+    np.testing.assert_array_equal(C.astype(np.float64),
+                                  orc.gemm_scaled_f64(pack(ca, fmt), fmt, sa_full[:, :nkb], pack(cb, fmt), fmt,
+                                                      sb_full[:, :nkb], K, block))
+
+
 def test_scaled_output_may_alias_the_accumulator(stg, orc):
     M, N, K = 140, 300, 256
     rng = np.random.default_rng(77)
