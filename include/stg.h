@@ -306,7 +306,10 @@ int ragged_tile_store(const void* tiles_in, int32_t dtype, int64_t total_rows, i
  * Supported here (else STG_ERR_UNSUPPORTED): e8m0 scales with block 32 times
  * a power of two -- 32 is the scale granularity of the gfx950 scaled MFMA;
  * e4m3 scales are not powers of two and would need a different instruction
- * path.  Errors as for gemm_bounded. */
+ * path.  Errors as for gemm_bounded.
+ * Speed: block 32 with both scale matrices 16-byte aligned and lds_a, lds_b
+ * multiples of 16 takes a faster scale path (fp4 about 6% faster); any other
+ * layout gives the same results on the general path. */
 typedef enum { STG_LP_E4M3 = 0, STG_LP_E5M2 = 1, STG_LP_E2M1 = 2 } stg_lowp_format;
 typedef enum { STG_SC_E8M0 = 0, STG_SC_E4M3 = 1 } stg_scale_format;
 int gemm_scaled(const void* A, int32_t a_fmt, int64_t lda, const void* a_scale, int64_t lds_a,
