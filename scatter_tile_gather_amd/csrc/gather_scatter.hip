@@ -417,12 +417,22 @@ constexpr int kChunkPer = kChunk / kThreads;    // 16 per lane
 constexpr int kMaxBuckets = 4096;
 constexpr int kWindow = 4096;                   // destination rows per pass in step 4
 constexpr int kBuildThreads = 1024;
+constexpr int kSegChunk = 64;                  // terms per reduce group; longer segments are split
+constexpr int kMaxPieces = 4096;               // pieces of one segment at most
+
+// Terms per piece of a segment of c terms: kSegChunk, or longer for a row so
+// hot that kSegChunk-term pieces would number more than kMaxPieces (their
+// partial sums all meet in atomics on that one row).
+__device__ __forceinline__ int32_t seg_piece(int32_t c) {
+  return c <= kSegChunk * kMaxPieces ? kSegChunk : (c + kMaxPieces - 1) / kMaxPieces;
+}
 
 // Step 1: cnt1[b * n_chunks + w] = terms of chunk w whose row is in bucket b.
 __global__ __launch_bounds__(kThreads) void seg_count_kernel(RowParams p, int shift, int nb, int64_t n_chunks,
-                                                             int32_t* cnt1) {
+                                                             int32_t* cnt1, int32_t* n_split) {
   __shared__ int32_t lh[kMaxBuckets];
   const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && tid == 0) *n_split = 0;  // the build appends the long segments' pieces
   for (int b = tid; b < nb; b += kThreads) lh[b] = 0;
   __syncthreads();
   const int64_t g0 = (int64_t)blockIdx.x * kChunk;
@@ -507,7 +517,8 @@ __global__ __launch_bounds__(kThreads) void seg_bucket_kernel(RowParams p, int s
 // each term id at its row's cursor (perm).  offs[R] = number of terms.
 __global__ __launch_bounds__(kBuildThreads) void seg_build_kernel(int64_t R, int shift, int nb, int64_t n_chunks,
                                                                   const int32_t* pos1, const uint64_t* pairs,
-                                                                  int32_t* offs, int32_t* perm) {
+                                                                  int32_t* offs, int32_t* perm,
+                                                                  uint64_t* split_list, int32_t* n_split) {
   __shared__ int32_t cur[kWindow];
   constexpr int kPer = kWindow / kBuildThreads;  // 4
   constexpr int kU = 8;                          // pairs in flight per lane
@@ -549,6 +560,11 @@ __global__ __launch_bounds__(kBuildThreads) void seg_build_kernel(int64_t R, int
       if (j < W) offs[w0 + j] = run;
       cur[j] = run;
       run += c[e];
+      if (c[e] > kSegChunk) {  // a long segment: list its pieces past the first
+        const int extra = (c[e] - 1) / seg_piece(c[e]);
+        const int at = atomicAdd(n_split, extra);
+        for (int q = 0; q < extra; ++q) split_list[at + q] = ((uint64_t)(w0 + j) << 32) | (uint32_t)(q + 1);
+      }
     }
     __syncthreads();
     for (int64_t i0 = s0; i0 < s1; i0 += kU * kBuildThreads) {
@@ -570,22 +586,16 @@ __global__ __launch_bounds__(kBuildThreads) void seg_build_kernel(int64_t R, int
   if (b == nb - 1 && tid == 0) offs[R] = (int32_t)s1;
 }
 
-// One group of LPR lanes per destination row: each lane owns 16-byte chunks
-// lane, lane + LPR, ... of the row's valid byte window, adds the terms of the
-// row's segment (eight grad_out rows in flight) to a.grad's values and stores
-// the row once.  Rows with an empty segment are not touched.
+// Terms [kb, ke) of a destination row's segment, summed by one group of LPR
+// lanes: each lane owns 16-byte chunks sub, sub + LPR, ... of the row's valid
+// byte window and keeps eight grad_out rows in flight.  init: start from
+// a.grad's values and store the row (plain stores); otherwise start from zero
+// and add the partial sums into a.grad with float atomics (the row's segment
+// is split over several groups).
 template <int ESIZE, int LPR>
-__global__ __launch_bounds__(kThreads) void seg_reduce_kernel(RowParams p, int64_t R, const int32_t* offs,
-                                                              const int32_t* perm) {
+__device__ __forceinline__ void seg_sum_terms(const RowParams& p, const int32_t* perm, char* arow, int32_t kb,
+                                              int32_t ke, int sub, bool init) {
   constexpr int V = 16 / ESIZE;
-  const int sub = threadIdx.x % LPR;
-  const int64_t r = (int64_t)blockIdx.x * (kThreads / LPR) + threadIdx.x / LPR;
-  if (r >= R) return;
-  const int32_t k0 = offs[r], k1 = offs[r + 1];
-  if (k0 == k1) return;
-  const int64_t sq = r % p.q_ext, rr = r / p.q_ext;
-  const int64_t sp = rr % p.p_ext, sa = rr / p.p_ext;
-  char* arow = const_cast<char*>(p.a) + sa * p.a_ax_b + sp * p.a_p_b + sq * p.a_q_b + p.a_col_b;
   for (int b = p.lo_b - p.lo_b % 16 + sub * 16; b < p.hi_b; b += LPR * 16) {
     // element e of this chunk is valid when b + e*ESIZE lies in [lo_b, hi_b)
     const bool whole = b >= p.lo_b && b + 16 <= p.hi_b;
@@ -594,7 +604,7 @@ __global__ __launch_bounds__(kThreads) void seg_reduce_kernel(RowParams p, int64
     for (int e = 0; e < V; ++e) {
       const int bb = b + e * ESIZE;
       acc[e] = 0.0;
-      if (bb >= p.lo_b && bb < p.hi_b) {
+      if (init && bb >= p.lo_b && bb < p.hi_b) {
         const uint64_t bits = load_elem<ESIZE>(arow + bb);
         acc[e] = ESIZE == 4 ? (double)__uint_as_float((uint32_t)bits) : __longlong_as_double((long long)bits);
       }
@@ -602,12 +612,12 @@ __global__ __launch_bounds__(kThreads) void seg_reduce_kernel(RowParams p, int64
     float accf[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) accf[e] = (float)acc[e];
-    for (int32_t k = k0; k < k1; k += 8) {
+    for (int32_t k = kb; k < ke; k += 8) {
       u32x4 v[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         v[q] = (u32x4){0, 0, 0, 0};
-        if (k + q < k1) {
+        if (k + q < ke) {
           int64_t t_off;
           dest_row_id(p, perm[k + q], t_off);
           const char* trow = p.t + t_off;
@@ -624,7 +634,7 @@ __global__ __launch_bounds__(kThreads) void seg_reduce_kernel(RowParams p, int64
       }
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        if (k + q >= k1) break;
+        if (k + q >= ke) break;
 #pragma unroll
         for (int e = 0; e < V; ++e) {
           const uint64_t bits = vec_get<ESIZE>(v[q], e);
@@ -641,7 +651,13 @@ __global__ __launch_bounds__(kThreads) void seg_reduce_kernel(RowParams p, int64
       const uint64_t bits = ESIZE == 4 ? (uint64_t)__float_as_uint(accf[e]) : (uint64_t)__double_as_longlong(acc[e]);
       vec_set<ESIZE>(out, e, bits);
     }
-    if (whole) {
+    if (!init) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const int bb = b + e * ESIZE;
+        if (bb >= p.lo_b && bb < p.hi_b) accum_elem<ESIZE>(arow + bb, vec_get<ESIZE>(out, e));
+      }
+    } else if (whole) {
       st16_nt(arow + b, out);
     } else {
 #pragma unroll
@@ -650,6 +666,49 @@ __global__ __launch_bounds__(kThreads) void seg_reduce_kernel(RowParams p, int64
         if (bb >= p.lo_b && bb < p.hi_b) store_elem<ESIZE>(arow + bb, vec_get<ESIZE>(out, e));
       }
     }
+  }
+}
+
+__device__ __forceinline__ char* seg_arow(const RowParams& p, int64_t r) {
+  const int64_t sq = r % p.q_ext, rr = r / p.q_ext;
+  const int64_t sp = rr % p.p_ext, sa = rr / p.p_ext;
+  return const_cast<char*>(p.a) + sa * p.a_ax_b + sp * p.a_p_b + sq * p.a_q_b + p.a_col_b;
+}
+
+// One group of LPR lanes per destination row sums the row's segment onto
+// a.grad's values and stores the row once; a segment longer than kSegChunk
+// terms only has its first piece summed here, added atomically, the other
+// pieces going to seg_split_kernel.  Rows with an empty segment are not
+// touched.
+template <int ESIZE, int LPR>
+__global__ __launch_bounds__(kThreads) void seg_reduce_kernel(RowParams p, int64_t R, const int32_t* offs,
+                                                              const int32_t* perm) {
+  const int sub = threadIdx.x % LPR;
+  const int64_t r = (int64_t)blockIdx.x * (kThreads / LPR) + threadIdx.x / LPR;
+  if (r >= R) return;
+  const int32_t k0 = offs[r], k1 = offs[r + 1];
+  if (k0 == k1) return;
+  const bool split = k1 - k0 > kSegChunk;
+  seg_sum_terms<ESIZE, LPR>(p, perm, seg_arow(p, r), k0, split ? k0 + seg_piece(k1 - k0) : k1, sub, !split);
+}
+
+// The further pieces of long segments, from the list the segment build
+// wrote: entry (row << 32 | piece), piece >= 1; *n_split entries.  Groups
+// stride over the list.
+template <int ESIZE, int LPR>
+__global__ __launch_bounds__(kThreads) void seg_split_kernel(RowParams p, const int32_t* offs, const int32_t* perm,
+                                                             const uint64_t* split_list, const int32_t* n_split) {
+  const int sub = threadIdx.x % LPR;
+  const int n = *n_split;
+  for (int64_t g = (int64_t)blockIdx.x * (kThreads / LPR) + threadIdx.x / LPR; g < n;
+       g += (int64_t)gridDim.x * (kThreads / LPR)) {
+    const uint64_t e = split_list[g];
+    const int64_t r = (int64_t)(e >> 32);
+    const int32_t piece = (int32_t)(uint32_t)e;
+    const int32_t len = seg_piece(offs[r + 1] - offs[r]);
+    const int32_t kb = offs[r] + piece * len;
+    const int32_t ke = min(offs[r + 1], kb + len);
+    seg_sum_terms<ESIZE, LPR>(p, perm, seg_arow(p, r), kb, ke, sub, false);
   }
 }
 
@@ -729,11 +788,13 @@ struct SegLayout {
   int shift;                   // bucket = destination row >> shift
   int64_t nbk, n_chunks, L1;   // buckets, term chunks of kChunk, nbk * n_chunks
   int64_t nb1;                 // scan blocks over the L1 counts
-  int64_t offs, perm, pairs, cnt1, pos1, bsum, bytes;  // byte offsets in the workspace, total size
+  int64_t n_pieces;            // capacity of the long-segment piece list
+  int64_t offs, perm, pairs, cnt1, pos1, bsum, split, n_split, bytes;  // byte offsets, total size
 };
 
 // Workspace: offs int32[R + 1] | perm int32[n_rows] | pairs uint64[n_rows] |
-// cnt1 int32[L1] | pos1 int32[L1 + 1] | bsum int32[nb1], each 256-byte aligned.
+// cnt1 int32[L1] | pos1 int32[L1 + 1] | bsum int32[nb1] | split uint64[n_rows /
+// kSegChunk + 1] | n_split int32, each 256-byte aligned.
 // At most 512 buckets while they span at most kWindow rows (R <= 2^21), then
 // up to kMaxBuckets of kWindow rows (R <= 2^24); past that, kMaxBuckets
 // buckets of several windows each.
@@ -754,7 +815,10 @@ SegLayout seg_layout(int64_t R, int64_t n_rows) {
   L.cnt1 = up(L.pairs + n_rows * 8);
   L.pos1 = up(L.cnt1 + L.L1 * 4);
   L.bsum = up(L.pos1 + (L.L1 + 1) * 4);
-  L.bytes = up(L.bsum + L.nb1 * 4);
+  L.n_pieces = n_rows / kSegChunk + 1;
+  L.split = up(L.bsum + L.nb1 * 4);
+  L.n_split = up(L.split + L.n_pieces * 8);
+  L.bytes = up(L.n_split + 4);
   return L;
 }
 
@@ -770,9 +834,12 @@ int launch_segmented(const char* name, int esize, const RowParams& p, int64_t R,
   int32_t* cnt1 = (int32_t*)(ws + L.cnt1);
   int32_t* pos1 = (int32_t*)(ws + L.pos1);
   int32_t* bsum = (int32_t*)(ws + L.bsum);
+  uint64_t* split = (uint64_t*)(ws + L.split);
+  int32_t* n_split = (int32_t*)(ws + L.n_split);
   const int nbk = (int)L.nbk;
   const dim3 chunks((unsigned)L.n_chunks), blk(kThreads);
-  launch_kernel("tile_gather_backward/count", seg_count_kernel, chunks, blk, 0, s, p, L.shift, nbk, L.n_chunks, cnt1);
+  launch_kernel("tile_gather_backward/count", seg_count_kernel, chunks, blk, 0, s, p, L.shift, nbk, L.n_chunks, cnt1,
+                n_split);
   launch_kernel("tile_gather_backward/bsum", seg_bsum_kernel, dim3((unsigned)L.nb1), blk, 0, s, (const int32_t*)cnt1,
                 L.L1, bsum);
   launch_kernel("tile_gather_backward/bscan", seg_bscan_kernel, dim3(1), blk, 0, s, bsum, L.nb1);
@@ -781,13 +848,22 @@ int launch_segmented(const char* name, int esize, const RowParams& p, int64_t R,
   launch_kernel("tile_gather_backward/bucket", seg_bucket_kernel, chunks, blk, 0, s, p, L.shift, nbk, L.n_chunks,
                 (const int32_t*)pos1, pairs);
   launch_kernel("tile_gather_backward/build", seg_build_kernel, dim3((unsigned)nbk), dim3(kBuildThreads), 0, s, R,
-                L.shift, nbk, L.n_chunks, (const int32_t*)pos1, (const uint64_t*)pairs, offs, perm);
+                L.shift, nbk, L.n_chunks, (const int32_t*)pos1, (const uint64_t*)pairs, offs, perm, split, n_split);
   // lanes per destination row: enough for the row's chunks, at most a wavefront
   const int chunks_per_row = p.n_chunks;
   const int lpr = chunks_per_row <= 8 ? 8 : chunks_per_row <= 16 ? 16 : chunks_per_row <= 32 ? 32 : 64;
   const dim3 grid((unsigned)((R + kThreads / lpr - 1) / (kThreads / lpr)));
-#define STG_SEG(E, LP) launch_kernel("tile_gather_backward/reduce", seg_reduce_kernel<E, LP>, grid, dim3(kThreads), 0, s, \
-                                     p, R, (const int32_t*)offs, (const int32_t*)perm)
+  // groups for the long segments' further pieces: striding over the list
+  // the build wrote (empty unless a row takes more than kSegChunk terms)
+  const int64_t gpw = kThreads / lpr;
+  const dim3 sgrid((unsigned)std::min<int64_t>((L.n_pieces + gpw - 1) / gpw, 1024));
+#define STG_SEG(E, LP)                                                                                               \
+  do {                                                                                                               \
+    launch_kernel("tile_gather_backward/reduce", seg_reduce_kernel<E, LP>, grid, dim3(kThreads), 0, s, p, R,        \
+                  (const int32_t*)offs, (const int32_t*)perm);                                                      \
+    launch_kernel("tile_gather_backward/split", seg_split_kernel<E, LP>, sgrid, dim3(kThreads), 0, s, p,             \
+                  (const int32_t*)offs, (const int32_t*)perm, (const uint64_t*)split, (const int32_t*)n_split);     \
+  } while (0)
   if (esize == 4) {
     if (lpr == 8) STG_SEG(4, 8); else if (lpr == 16) STG_SEG(4, 16); else if (lpr == 32) STG_SEG(4, 32); else STG_SEG(4, 64);
   } else {

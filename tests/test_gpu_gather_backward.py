@@ -132,3 +132,34 @@ def test_backward_grouped_large_tables(stg, orc, rows, cols, n_tiles):
     a0 = rng.standard_normal((rows, cols)).astype(np.float32)
     say("gather backward grouped: large table", rows, "x", cols, "terms", n)
     run_case(stg, orc, a0, idx, (64, cols), g, ws="auto")
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_backward_grouped_segment_pieces(stg, orc, dtype):
+    """Rows whose segments are just under, at and past multiples of the
+    64-term piece a reduce group sums (63, 64, 65, 127, 128, 129, 1000 and
+    7000 terms): longer segments are split over several groups that add
+    their partial sums atomically."""
+    rng = np.random.default_rng(64 + (dtype == np.float64))
+    counts = {3: 63, 10: 64, 17: 65, 40: 127, 41: 128, 42: 129, 77: 1000, 90: 7000}
+    fill = 500 + (-(sum(counts.values()) + 500)) % 8  # other rows' terms, to a whole number of tiles
+    idx = np.concatenate([np.full(c, r) for r, c in counts.items()] + [rng.integers(100, 200, fill)]).astype(np.int32)
+    rng.shuffle(idx)
+    n = idx.size
+    assert n % 8 == 0 and all(int((idx == r).sum()) == c for r, c in counts.items())
+    g = rng.standard_normal((n, 24)).astype(dtype)
+    a0 = rng.standard_normal((200, 24)).astype(dtype)
+    say("gather backward grouped: segment pieces", np.dtype(dtype).name, "terms", n)
+    run_case(stg, orc, a0, idx, (8, 24), g, ws="auto")
+
+
+def test_backward_grouped_hot_row(stg, orc):
+    """One row takes 300,000 terms, more than 4096 pieces of 64: its pieces
+    grow (74 terms) so that at most 4096 partial sums meet on the row."""
+    rng = np.random.default_rng(300)
+    idx = np.concatenate([np.full(300000, 5), rng.integers(0, 1000, 4000)]).astype(np.int32)
+    rng.shuffle(idx)
+    g = rng.standard_normal((idx.size, 3)).astype(np.float32)
+    a0 = rng.standard_normal((1000, 3)).astype(np.float32)
+    say("gather backward grouped: hot row of 300000 terms")
+    run_case(stg, orc, a0, idx, (8, 3), g, ws="auto")
