@@ -224,8 +224,8 @@ def tile_gather_masked(a, indices, mask, tile_shape, offset=None, axis: int = 0,
 
 
 def tile_gather_backward_workspace(a_grad, n_indices: int, tile_shape, axis: int = 0) -> int:
-    """Bytes of workspace the grouped (atomic-free) execution needs; 0 when the
-    layout always runs on atomics."""
+    """Bytes of workspace the grouped execution needs; 0 when the layout always
+    runs on atomics."""
     lib = load_library()
     ad = _desc(a_grad, "a_grad")
     n = int(lib.tile_gather_backward_workspace(ctypes.byref(ad), n_indices, _i64arr(tile_shape), axis))
@@ -240,7 +240,8 @@ def tile_gather_backward(a_grad, indices, tile_shape, grad_out, offset=None, axi
     the output gradient grad_out (fp32 or fp64).  workspace: None (hardware
     float atomics), a device uint8 tensor of at least
     tile_gather_backward_workspace(...) bytes, or "auto" to allocate one here
-    (grouped execution, no float atomics)."""
+    (grouped execution: each row summed and stored once; float atomics only
+    for the pieces of rows with more than 64 terms)."""
     torch = _torch()
     lib = load_library()
     n = indices.numel()
