@@ -422,6 +422,8 @@ constexpr int kWindow = 4096;                   // destination rows per pass in 
 constexpr int kBuildThreads = 1024;
 constexpr int kSegChunk = 64;                  // terms per reduce group; longer segments are split
 constexpr int kMaxPieces = 4096;               // pieces of one segment at most
+constexpr int kHotPairs = 65536;               // a bucket with more terms is built by many workgroups
+constexpr int kSlice = 16384;                  // terms per workgroup of a hot bucket
 
 // Terms per piece of a segment of c terms: kSegChunk, or longer for a row so
 // hot that kSegChunk-term pieces would number more than kMaxPieces (their
@@ -432,10 +434,13 @@ __device__ __forceinline__ int32_t seg_piece(int32_t c) {
 
 // Step 1: cnt1[b * n_chunks + w] = terms of chunk w whose row is in bucket b.
 __global__ __launch_bounds__(kThreads) void seg_count_kernel(RowParams p, int shift, int nb, int64_t n_chunks,
-                                                             int32_t* cnt1, int32_t* n_split) {
+                                                             int32_t* cnt1, int32_t* n_split, int32_t* n_hot) {
   __shared__ int32_t lh[kMaxBuckets];
   const int tid = threadIdx.x;
-  if (blockIdx.x == 0 && tid == 0) *n_split = 0;  // the build appends the long segments' pieces
+  if (blockIdx.x == 0 && tid == 0) {  // the build appends long segments' pieces and hot buckets' slices
+    *n_split = 0;
+    *n_hot = 0;
+  }
   for (int b = tid; b < nb; b += kThreads) lh[b] = 0;
   __syncthreads();
   const int64_t g0 = (int64_t)blockIdx.x * kChunk;
@@ -514,6 +519,41 @@ __global__ __launch_bounds__(kThreads) void seg_bucket_kernel(RowParams p, int s
   }
 }
 
+// After a window's scan: list the pieces past the first of this thread's
+// rows w0 + kPer * tid + e whose segments are long (c[e] > kSegChunk); one
+// global atomic per workgroup reserves the places (long rows can be many in
+// a skewed bucket, and atomics on one counter serialize).
+template <int kPer>
+__device__ __forceinline__ void list_pieces(const int32_t (&c)[kPer], int64_t w0, uint64_t* split_list,
+                                            int32_t* n_split) {
+  __shared__ int32_t s_at;
+  int32_t mine = 0;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e)
+    if (c[e] > kSegChunk) mine += (c[e] - 1) / seg_piece(c[e]);
+  int32_t total;
+  int32_t at = block_exclusive_scan<kBuildThreads>(mine, total);
+  if (total == 0) return;  // uniform: the same total in every thread
+  if (threadIdx.x == 0) s_at = atomicAdd(n_split, total);
+  __syncthreads();
+  at += s_at;
+  __syncthreads();  // s_at is read before the next window may set it
+  // the entries are written by whole wavefronts, one long row at a time (a
+  // hot row has up to kMaxPieces - 1 of them)
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int extra = c[e] > kSegChunk ? (c[e] - 1) / seg_piece(c[e]) : 0;
+    for (uint64_t pend = __ballot(extra > 0); pend; pend &= pend - 1) {
+      const int L = __builtin_ctzll(pend);
+      const int n_e = __shfl(extra, L), at_e = __shfl(at, L);
+      const int64_t row = w0 + (int64_t)((threadIdx.x & ~63) + L) * kPer + e;
+      for (int q = lane; q < n_e; q += 64) split_list[at_e + q] = ((uint64_t)row << 32) | (uint32_t)(q + 1);
+    }
+    at += extra;
+  }
+}
+
 // Step 4: one workgroup per bucket.  Its pairs are pairs[s0, s1); its rows
 // [b << shift, min((b + 1) << shift, R)) are taken kWindow at a time: count
 // the terms per row, scan the counts into segment offsets (offs), then place
@@ -521,7 +561,9 @@ __global__ __launch_bounds__(kThreads) void seg_bucket_kernel(RowParams p, int s
 __global__ __launch_bounds__(kBuildThreads) void seg_build_kernel(int64_t R, int shift, int nb, int64_t n_chunks,
                                                                   const int32_t* pos1, const uint64_t* pairs,
                                                                   int32_t* offs, int32_t* perm,
-                                                                  uint64_t* split_list, int32_t* n_split) {
+                                                                  uint64_t* split_list, int32_t* n_split,
+                                                                  int32_t* gcur, int32_t* hot, uint64_t* hot_list,
+                                                                  int32_t* n_hot) {
   __shared__ int32_t cur[kWindow];
   constexpr int kPer = kWindow / kBuildThreads;  // 4
   constexpr int kU = 8;                          // pairs in flight per lane
@@ -530,6 +572,21 @@ __global__ __launch_bounds__(kBuildThreads) void seg_build_kernel(int64_t R, int
   const int64_t s0 = pos1[(int64_t)b * n_chunks], s1 = pos1[(int64_t)(b + 1) * n_chunks];
   const int64_t row_lo = (int64_t)b << shift;
   const int64_t row_hi = min(R, (int64_t)(b + 1) << shift);
+  if (b == nb - 1 && tid == 0) offs[R] = (int32_t)s1;
+  if (s1 - s0 > kHotPairs) {
+    // a hot bucket: one workgroup would stream all its terms alone; the
+    // seg_hot_* kernels build it with one workgroup per kSlice terms.  Zero
+    // its rows' counters and list its slices.
+    for (int64_t r = row_lo + tid; r < row_hi; r += kBuildThreads) gcur[r] = 0;
+    if (tid == 0) {
+      hot[b] = 1;
+      const int ns = (int)((s1 - s0 + kSlice - 1) / kSlice);
+      const int at = atomicAdd(n_hot, ns);
+      for (int g = 0; g < ns; ++g) hot_list[at + g] = ((uint64_t)b << 32) | (uint32_t)g;
+    }
+    return;
+  }
+  if (tid == 0) hot[b] = 0;
   int64_t base = s0;
   for (int64_t w0 = row_lo; w0 < row_hi; w0 += kWindow) {
     const int64_t W = min((int64_t)kWindow, row_hi - w0);
@@ -563,12 +620,8 @@ __global__ __launch_bounds__(kBuildThreads) void seg_build_kernel(int64_t R, int
       if (j < W) offs[w0 + j] = run;
       cur[j] = run;
       run += c[e];
-      if (c[e] > kSegChunk) {  // a long segment: list its pieces past the first
-        const int extra = (c[e] - 1) / seg_piece(c[e]);
-        const int at = atomicAdd(n_split, extra);
-        for (int q = 0; q < extra; ++q) split_list[at + q] = ((uint64_t)(w0 + j) << 32) | (uint32_t)(q + 1);
-      }
     }
+    list_pieces(c, w0, split_list, n_split);
     __syncthreads();
     for (int64_t i0 = s0; i0 < s1; i0 += kU * kBuildThreads) {
       uint64_t pr[kU];
@@ -586,7 +639,140 @@ __global__ __launch_bounds__(kBuildThreads) void seg_build_kernel(int64_t R, int
     base += total;
     __syncthreads();
   }
-  if (b == nb - 1 && tid == 0) offs[R] = (int32_t)s1;
+}
+
+// Hot buckets, step 4 spread over workgroups: (a) each slice of kSlice terms
+// counts its terms per row (LDS) and adds the counts into gcur (global
+// atomics, one per row and slice); (b) one workgroup per hot bucket scans
+// the counts into segment offsets, sets gcur to them and lists long
+// segments' pieces; (c) each slice counts again, reserves its place in each
+// row's segment with one global atomic per row, and places its term ids.
+// Slices are entries (bucket << 32 | slice) of hot_list; workgroups stride
+// over the *n_hot entries.
+struct HotSlice {
+  int64_t p0, p1, row_lo, row_hi;
+};
+__device__ __forceinline__ HotSlice hot_slice(uint64_t e, int64_t R, int shift, int64_t n_chunks, const int32_t* pos1) {
+  const int b = (int)(e >> 32), g = (int)(uint32_t)e;
+  const int64_t s0 = pos1[(int64_t)b * n_chunks], s1 = pos1[(int64_t)(b + 1) * n_chunks];
+  HotSlice h;
+  h.p0 = s0 + (int64_t)g * kSlice;
+  h.p1 = min(s1, h.p0 + kSlice);
+  h.row_lo = (int64_t)b << shift;
+  h.row_hi = min(R, (int64_t)(b + 1) << shift);
+  return h;
+}
+
+// LDS counts of the slice's terms with rows in [w0, w0 + W)
+__device__ __forceinline__ void hot_window_count(const uint64_t* pairs, int64_t p0, int64_t p1, int64_t w0, int64_t W,
+                                                 int32_t* cnt) {
+  constexpr int kU = 8;
+  const int tid = threadIdx.x;
+  for (int j = tid; j < kWindow; j += kBuildThreads) cnt[j] = 0;
+  __syncthreads();
+  for (int64_t i0 = p0; i0 < p1; i0 += kU * kBuildThreads) {
+    uint64_t pr[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t i = i0 + u * kBuildThreads + tid;
+      pr[u] = i < p1 ? pairs[i] : ~uint64_t(0);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t d = (int64_t)(pr[u] >> 32) - w0;
+      if (d >= 0 && d < W) atomicAdd(&cnt[d], 1);
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kBuildThreads) void seg_hot_count_kernel(int64_t R, int shift, int64_t n_chunks,
+                                                                      const int32_t* pos1, const uint64_t* pairs,
+                                                                      const uint64_t* hot_list, const int32_t* n_hot,
+                                                                      int32_t* gcur) {
+  __shared__ int32_t cnt[kWindow];
+  const int nh = *n_hot;
+  for (int e = blockIdx.x; e < nh; e += gridDim.x) {
+    const HotSlice h = hot_slice(hot_list[e], R, shift, n_chunks, pos1);
+    for (int64_t w0 = h.row_lo; w0 < h.row_hi; w0 += kWindow) {
+      const int64_t W = min((int64_t)kWindow, h.row_hi - w0);
+      hot_window_count(pairs, h.p0, h.p1, w0, W, cnt);
+      for (int j = threadIdx.x; j < W; j += kBuildThreads)
+        if (cnt[j]) atomicAdd(&gcur[w0 + j], cnt[j]);
+      __syncthreads();
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBuildThreads) void seg_hot_scan_kernel(int64_t R, int shift, int64_t n_chunks,
+                                                                     const int32_t* pos1, const int32_t* hot,
+                                                                     int32_t* offs, int32_t* gcur,
+                                                                     uint64_t* split_list, int32_t* n_split) {
+  constexpr int kPer = kWindow / kBuildThreads;  // 4
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  if (!hot[b]) return;
+  const int64_t s0 = pos1[(int64_t)b * n_chunks];
+  const int64_t row_lo = (int64_t)b << shift;
+  const int64_t row_hi = min(R, (int64_t)(b + 1) << shift);
+  int64_t base = s0;
+  for (int64_t w0 = row_lo; w0 < row_hi; w0 += kWindow) {
+    const int64_t W = min((int64_t)kWindow, row_hi - w0);
+    int32_t c[kPer], v = 0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int j = tid * kPer + e;
+      c[e] = j < W ? gcur[w0 + j] : 0;
+      v += c[e];
+    }
+    int32_t total;
+    int32_t run = (int32_t)base + block_exclusive_scan<kBuildThreads>(v, total);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int j = tid * kPer + e;
+      if (j < W) {
+        offs[w0 + j] = run;
+        gcur[w0 + j] = run;
+      }
+      run += c[e];
+    }
+    list_pieces(c, w0, split_list, n_split);
+    base += total;
+  }
+}
+
+__global__ __launch_bounds__(kBuildThreads) void seg_hot_place_kernel(int64_t R, int shift, int64_t n_chunks,
+                                                                      const int32_t* pos1, const uint64_t* pairs,
+                                                                      const uint64_t* hot_list, const int32_t* n_hot,
+                                                                      int32_t* gcur, int32_t* perm) {
+  __shared__ int32_t cnt[kWindow];
+  constexpr int kU = 8;
+  const int tid = threadIdx.x;
+  const int nh = *n_hot;
+  for (int e = blockIdx.x; e < nh; e += gridDim.x) {
+    const HotSlice h = hot_slice(hot_list[e], R, shift, n_chunks, pos1);
+    for (int64_t w0 = h.row_lo; w0 < h.row_hi; w0 += kWindow) {
+      const int64_t W = min((int64_t)kWindow, h.row_hi - w0);
+      hot_window_count(pairs, h.p0, h.p1, w0, W, cnt);
+      for (int j = tid; j < W; j += kBuildThreads)
+        if (cnt[j]) cnt[j] = atomicAdd(&gcur[w0 + j], cnt[j]);  // this slice's place in the row's segment
+      __syncthreads();
+      for (int64_t i0 = h.p0; i0 < h.p1; i0 += kU * kBuildThreads) {
+        uint64_t pr[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int64_t i = i0 + u * kBuildThreads + tid;
+          pr[u] = i < h.p1 ? pairs[i] : ~uint64_t(0);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int64_t d = (int64_t)(pr[u] >> 32) - w0;
+          if (d >= 0 && d < W) perm[atomicAdd(&cnt[d], 1)] = (int32_t)(uint32_t)pr[u];
+        }
+      }
+      __syncthreads();
+    }
+  }
 }
 
 // Terms [kb, ke) of a destination row's segment, summed by one group of LPR
@@ -792,12 +978,15 @@ struct SegLayout {
   int64_t nbk, n_chunks, L1;   // buckets, term chunks of kChunk, nbk * n_chunks
   int64_t nb1;                 // scan blocks over the L1 counts
   int64_t n_pieces;            // capacity of the long-segment piece list
-  int64_t offs, perm, pairs, cnt1, pos1, bsum, split, n_split, bytes;  // byte offsets, total size
+  int64_t n_slices;            // capacity of the hot-bucket slice list
+  int64_t offs, perm, pairs, cnt1, pos1, bsum, split, n_split, gcur, hot, hot_list, n_hot, bytes;  // byte offsets
 };
 
 // Workspace: offs int32[R + 1] | perm int32[n_rows] | pairs uint64[n_rows] |
 // cnt1 int32[L1] | pos1 int32[L1 + 1] | bsum int32[nb1] | split uint64[n_rows /
-// kSegChunk + 1] | n_split int32, each 256-byte aligned.
+// kSegChunk + 1] | n_split int32 | gcur int32[R] | hot int32[nbk] | hot_list
+// uint64[n_rows / kSlice + n_rows / kHotPairs + 1] | n_hot int32, each 256-byte
+// aligned.
 // At most 512 buckets while they span at most kWindow rows (R <= 2^21), then
 // up to kMaxBuckets of kWindow rows (R <= 2^24); past that, kMaxBuckets
 // buckets of several windows each.
@@ -819,9 +1008,14 @@ SegLayout seg_layout(int64_t R, int64_t n_rows) {
   L.pos1 = up(L.cnt1 + L.L1 * 4);
   L.bsum = up(L.pos1 + (L.L1 + 1) * 4);
   L.n_pieces = n_rows / kSegChunk + 1;
+  L.n_slices = n_rows / kSlice + n_rows / kHotPairs + 1;
   L.split = up(L.bsum + L.nb1 * 4);
   L.n_split = up(L.split + L.n_pieces * 8);
-  L.bytes = up(L.n_split + 4);
+  L.gcur = up(L.n_split + 4);
+  L.hot = up(L.gcur + R * 4);
+  L.hot_list = up(L.hot + L.nbk * 4);
+  L.n_hot = up(L.hot_list + L.n_slices * 8);
+  L.bytes = up(L.n_hot + 4);
   return L;
 }
 
@@ -839,10 +1033,14 @@ int launch_segmented(const char* name, int esize, const RowParams& p, int64_t R,
   int32_t* bsum = (int32_t*)(ws + L.bsum);
   uint64_t* split = (uint64_t*)(ws + L.split);
   int32_t* n_split = (int32_t*)(ws + L.n_split);
+  int32_t* gcur = (int32_t*)(ws + L.gcur);
+  int32_t* hot = (int32_t*)(ws + L.hot);
+  uint64_t* hot_list = (uint64_t*)(ws + L.hot_list);
+  int32_t* n_hot = (int32_t*)(ws + L.n_hot);
   const int nbk = (int)L.nbk;
   const dim3 chunks((unsigned)L.n_chunks), blk(kThreads);
   launch_kernel("tile_gather_backward/count", seg_count_kernel, chunks, blk, 0, s, p, L.shift, nbk, L.n_chunks, cnt1,
-                n_split);
+                n_split, n_hot);
   launch_kernel("tile_gather_backward/bsum", seg_bsum_kernel, dim3((unsigned)L.nb1), blk, 0, s, (const int32_t*)cnt1,
                 L.L1, bsum);
   launch_kernel("tile_gather_backward/bscan", seg_bscan_kernel, dim3(1), blk, 0, s, bsum, L.nb1);
@@ -851,7 +1049,18 @@ int launch_segmented(const char* name, int esize, const RowParams& p, int64_t R,
   launch_kernel("tile_gather_backward/bucket", seg_bucket_kernel, chunks, blk, 0, s, p, L.shift, nbk, L.n_chunks,
                 (const int32_t*)pos1, pairs);
   launch_kernel("tile_gather_backward/build", seg_build_kernel, dim3((unsigned)nbk), dim3(kBuildThreads), 0, s, R,
-                L.shift, nbk, L.n_chunks, (const int32_t*)pos1, (const uint64_t*)pairs, offs, perm, split, n_split);
+                L.shift, nbk, L.n_chunks, (const int32_t*)pos1, (const uint64_t*)pairs, offs, perm, split, n_split,
+                gcur, hot, hot_list, n_hot);
+  // hot buckets (more than kHotPairs terms): many workgroups each; the
+  // slice kernels stride over the list the build wrote (usually empty)
+  const dim3 hgrid(256), hblk(kBuildThreads);
+  launch_kernel("tile_gather_backward/hot_count", seg_hot_count_kernel, hgrid, hblk, 0, s, R, L.shift, L.n_chunks,
+                (const int32_t*)pos1, (const uint64_t*)pairs, (const uint64_t*)hot_list, (const int32_t*)n_hot, gcur);
+  launch_kernel("tile_gather_backward/hot_scan", seg_hot_scan_kernel, dim3((unsigned)nbk), hblk, 0, s, R, L.shift,
+                L.n_chunks, (const int32_t*)pos1, (const int32_t*)hot, offs, gcur, split, n_split);
+  launch_kernel("tile_gather_backward/hot_place", seg_hot_place_kernel, hgrid, hblk, 0, s, R, L.shift, L.n_chunks,
+                (const int32_t*)pos1, (const uint64_t*)pairs, (const uint64_t*)hot_list, (const int32_t*)n_hot, gcur,
+                perm);
   // lanes per destination row: enough for the row's chunks, at most a wavefront
   const int chunks_per_row = p.n_chunks;
   const int lpr = chunks_per_row <= 8 ? 8 : chunks_per_row <= 16 ? 16 : chunks_per_row <= 32 ? 32 : 64;

@@ -163,3 +163,19 @@ def test_backward_grouped_hot_row(stg, orc):
     a0 = rng.standard_normal((1000, 3)).astype(np.float32)
     say("gather backward grouped: hot row of 300000 terms")
     run_case(stg, orc, a0, idx, (8, 3), g, ws="auto")
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_backward_grouped_hot_buckets(stg, orc, dtype):
+    """Skewed indices that make buckets of more than 65536 terms, which many
+    workgroups build slice by slice: Zipf-distributed rows over a (70000, 20)
+    table (row 0 alone takes about a third of the 300,000 terms), plus a block
+    of rows hit uniformly."""
+    rng = np.random.default_rng(1100 + (dtype == np.float64))
+    idx = np.concatenate([np.minimum(rng.zipf(1.3, 240000) - 1, 69999), rng.integers(40000, 70000, 60000)])
+    idx = idx.astype(np.int32)
+    rng.shuffle(idx)
+    g = rng.standard_normal((idx.size, 20)).astype(dtype)
+    a0 = rng.standard_normal((70000, 20)).astype(dtype)
+    say("gather backward grouped: hot buckets", np.dtype(dtype).name, "max count", int(np.bincount(idx).max()))
+    run_case(stg, orc, a0, idx, (8, 20), g, ws="auto")
