@@ -157,7 +157,7 @@ int tile_scatter_masked(const stg_tensor* a, const int32_t* indices, const uint8
  *    and added with the same hardware float atomics (STG_ERR_INVALID if the buffer is
  *    too small; STG_ERR_RANGE with 2^31 or more destination rows or terms, or
  *    when the per-4096-term bucket-count table would reach 2^31 entries).  The
- *    buffer holds about 4 bytes per destination row and 12 per term.  For
+ *    buffer holds about 8 bytes per destination row and 12 per term.  For
  *    any other layout the workspace is not used. */
 int tile_gather_backward(const stg_tensor* a_grad, const int32_t* indices, int64_t n_indices,
                          const int64_t* tile_shape, const int64_t* offset, int32_t axis,
