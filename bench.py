@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default="all",
-                    help="comma list of: copy,full,gather,masked,backward,ragged,gemm,scaled,calib (rocprof runs); 'all' for the "
+                    help="comma list of: copy,full,gather,masked,backward,zipf,ragged,gemm,scaled,calib (rocprof runs); 'all' for the "
                          "full report")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU time budget of the oracle baseline")
@@ -400,6 +400,33 @@ def run_gather_backward(stg, inputs, steps, warmup):
     return res
 
 
+def run_gather_backward_zipf(stg, inputs, steps, warmup):
+    """The grouped backward of the workload above on skewed indices: Zipf,
+    a = 1.1 (the hottest row takes about a quarter of the 4,194,304 terms)."""
+    import torch
+
+    w = inputs.masked()
+    rows, cols = w["table"].shape
+    zidx_h = inputs.zipf_indices(rows=rows, n=w["indices"].size)
+    zidx = _dev(zidx_h)
+    g = torch.Generator(device="cuda:0").manual_seed(1007)
+    grad_out = torch.randn((zidx.numel(), cols), generator=g, dtype=torch.float32, device="cuda:0")
+    a_grad = torch.zeros((rows, cols), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(stg.tile_gather_backward_workspace(a_grad, zidx.numel(), (64, cols), 0), dtype=torch.uint8,
+                     device="cuda:0")
+    touched = int(np.unique(zidx_h).size)
+    nbytes = zidx.numel() * 4 + zidx.numel() * cols * 4 + 2 * touched * cols * 4
+    fn = lambda: stg.tile_gather_backward(a_grad, zidx, (64, cols), grad_out, workspace=ws)
+    ms = time_fn(fn, steps, warmup)
+    kms = traced_kernel_ms(stg, fn, steps)
+    e = op_entry("gather backward (grouped by destination row), Zipf(1.1) indices: a.grad fp32 (1048576,128), "
+                 "4194304 indices, (64,128) tiles", nbytes, ms, kms)
+    e["note"] = ("algorithmic bytes as for the uniform indices; rows past 64 terms are split into pieces added with "
+                 "float atomics")
+    e["max_terms_per_row"] = int(np.bincount(zidx_h).max())
+    return e
+
+
 def run_ragged(stg, inputs, steps, warmup):
     import torch
 
@@ -576,8 +603,8 @@ def main():
     from scatter_tile_gather_amd import inputs
 
     stg.load_library()
-    only = set(args.only.split(",")) if args.only != "all" else {"copy", "full", "gather", "masked", "backward", "ragged",
-                                                                             "gemm", "scaled"}
+    only = set(args.only.split(",")) if args.only != "all" else {"copy", "full", "gather", "masked", "backward", "zipf",
+                                                                             "ragged", "gemm", "scaled"}
     ops = {}
     head = None
     if "calib" in only:
@@ -599,6 +626,10 @@ def main():
         ops["gather_backward_grouped"], ops["gather_backward_atomic"] = run_gather_backward(stg, inputs, args.steps,
                                                                                             args.warmup)
         print("[bench] gather backward done", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+    if "zipf" in only:
+        ops["gather_backward_grouped_zipf"] = run_gather_backward_zipf(stg, inputs, args.steps, args.warmup)
+        print("[bench] gather backward, Zipf indices, done", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
     if "ragged" in only:
         (ops["ragged_group1"], ops["ragged_store_group1"], ops["ragged_group4"],

@@ -42,6 +42,7 @@ SEED_MASKED = 1003
 SEED_RAGGED = 1004
 SEED_GEMM = 1005
 SEED_SCALED_GEMM = 1006
+SEED_ZIPF = 1007
 
 # A bf16 bit pattern that a N(0,1) draw never produces (a signalling-NaN-like
 # payload); it marks padding columns and untouched destination elements.
@@ -108,6 +109,14 @@ def masked(seed: int = SEED_MASKED, rows: int = 1048576, cols: int = 128, n_gath
     smask = (rs.random(n_scatter) < p_scatter).astype(np.uint8)
     return {"table": table, "indices": idx, "gmask": gmask, "padding_value": padding_value,
             "vals": vals, "perm": perm, "smask": smask}
+
+
+def zipf_indices(seed: int = SEED_ZIPF, rows: int = 1048576, n: int = 4194304, a: float = 1.1) -> np.ndarray:
+    """Skewed gather indices: row k drawn with probability proportional to
+    (k + 1)^-a (numpy's Zipf sampler, values past the table folded onto the
+    last row), int32.  At a = 1.1 row 0 takes about a quarter of the terms."""
+    (rz,) = _rngs(seed, 1)
+    return np.minimum(rz.zipf(a, n) - 1, rows - 1).astype(np.int32)
 
 
 # ---- ragged varlen 3-D tiles ------------------------------------------------
