@@ -402,7 +402,8 @@ def run_gather_backward(stg, inputs, steps, warmup):
 
 def run_gather_backward_zipf(stg, inputs, steps, warmup):
     """The grouped backward of the workload above on skewed indices: Zipf,
-    a = 1.1 (the hottest row takes about a quarter of the 4,194,304 terms)."""
+    a = 1.1 truncated to the table (the hottest row takes about 12% of the
+    4,194,304 terms)."""
     import torch
 
     w = inputs.masked()

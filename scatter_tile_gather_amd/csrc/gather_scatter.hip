@@ -775,134 +775,73 @@ __global__ __launch_bounds__(kBuildThreads) void seg_hot_place_kernel(int64_t R,
   }
 }
 
-// Terms [kb, ke) of a destination row's segment, summed by one group of LPR
-// lanes: each lane owns 16-byte chunks sub, sub + LPR, ... of the row's valid
-// byte window and keeps eight grad_out rows in flight.  init: start from
-// a.grad's values and store the row (plain stores); otherwise start from zero
-// and add the partial sums into a.grad with float atomics.  (The reduce
-// kernel runs this fused form, measured 5% faster there than the chunk
-// routines below, which the split kernel combines across groups.)
-template <int ESIZE, int LPR>
-__device__ __forceinline__ void seg_sum_terms(const RowParams& p, const int32_t* perm, char* arow, int32_t kb,
-                                              int32_t ke, int sub, bool init) {
-  constexpr int V = 16 / ESIZE;
-  for (int b = p.lo_b - p.lo_b % 16 + sub * 16; b < p.hi_b; b += LPR * 16) {
-    // element e of this chunk is valid when b + e*ESIZE lies in [lo_b, hi_b)
-    const bool whole = b >= p.lo_b && b + 16 <= p.hi_b;
-    double acc[V];
-#pragma unroll
-    for (int e = 0; e < V; ++e) {
-      const int bb = b + e * ESIZE;
-      acc[e] = 0.0;
-      if (init && bb >= p.lo_b && bb < p.hi_b) {
-        const uint64_t bits = load_elem<ESIZE>(arow + bb);
-        acc[e] = ESIZE == 4 ? (double)__uint_as_float((uint32_t)bits) : __longlong_as_double((long long)bits);
-      }
-    }
-    float accf[V];
-#pragma unroll
-    for (int e = 0; e < V; ++e) accf[e] = (float)acc[e];
-    for (int32_t k = kb; k < ke; k += 8) {
-      u32x4 v[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        v[q] = (u32x4){0, 0, 0, 0};
-        if (k + q < ke) {
-          int64_t t_off;
-          dest_row_id(p, perm[k + q], t_off);
-          const char* trow = p.t + t_off;
-          if (whole) {
-            v[q] = ld16(trow + b);
-          } else {
-#pragma unroll
-            for (int e = 0; e < V; ++e) {
-              const int bb = b + e * ESIZE;
-              if (bb >= p.lo_b && bb < p.hi_b) vec_set<ESIZE>(v[q], e, load_elem<ESIZE>(trow + bb));
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (k + q >= ke) break;
-#pragma unroll
-        for (int e = 0; e < V; ++e) {
-          const uint64_t bits = vec_get<ESIZE>(v[q], e);
-          if (ESIZE == 4)
-            accf[e] += __uint_as_float((uint32_t)bits);
-          else
-            acc[e] += __longlong_as_double((long long)bits);
-        }
-      }
-    }
-    u32x4 out = {0, 0, 0, 0};
-#pragma unroll
-    for (int e = 0; e < V; ++e) {
-      const uint64_t bits = ESIZE == 4 ? (uint64_t)__float_as_uint(accf[e]) : (uint64_t)__double_as_longlong(acc[e]);
-      vec_set<ESIZE>(out, e, bits);
-    }
-    if (!init) {
-#pragma unroll
-      for (int e = 0; e < V; ++e) {
-        const int bb = b + e * ESIZE;
-        if (bb >= p.lo_b && bb < p.hi_b) accum_elem<ESIZE>(arow + bb, vec_get<ESIZE>(out, e));
-      }
-    } else if (whole) {
-      st16_nt(arow + b, out);
-    } else {
-#pragma unroll
-      for (int e = 0; e < V; ++e) {
-        const int bb = b + e * ESIZE;
-        if (bb >= p.lo_b && bb < p.hi_b) store_elem<ESIZE>(arow + bb, vec_get<ESIZE>(out, e));
-      }
-    }
-  }
+// Byte offset in grad_out of the tile row g (dest_row_id's t_off, without
+// the index lookup).
+__device__ __forceinline__ int64_t grad_row_off(const RowParams& p, int64_t g) {
+  if (p.rest == 1) return g * p.t_ax_b;
+  const int64_t o_ax = g / p.rest, rr = g - o_ax * p.rest;
+  const int64_t op = rr / p.q_n, oq = rr - op * p.q_n;
+  return o_ax * p.t_ax_b + op * p.t_p_b + oq * p.t_q_b;
 }
 
-// Sum of terms [kb, ke) of a destination row's segment over the 16-byte
-// chunk at byte b of the row's valid window (element e valid when b + e *
-// ESIZE lies in [lo_b, hi_b)), eight grad_out rows in flight; init: start
-// from a.grad's values (arow) instead of zero.  Returns the sum's bits.
-template <int ESIZE>
-__device__ __forceinline__ u32x4 seg_chunk_sum(const RowParams& p, const int32_t* perm, const char* arow, int32_t kb,
-                                               int32_t ke, int b, bool init) {
+constexpr int kSegBatch = 4;  // grad_out rows in flight per lane in a segment sum
+
+// grad_out rows of segment terms k .. k+kSegBatch-1, read from perm;
+// positions at or past ke repeat term ke - 1 (the caller has kb <= ke - 1),
+// so the reads stay inside the segment and need no branch.
+__device__ __forceinline__ void seg_batch_perm(const int32_t* perm, int32_t k, int32_t ke, int32_t (&g)[kSegBatch]) {
+#pragma unroll
+  for (int q = 0; q < kSegBatch; ++q) g[q] = perm[min(k + q, ke - 1)];
+}
+
+// The 16-byte chunk at byte b of a row, restricted to the valid byte window
+// [lo_b, hi_b): one 16-byte read for a chunk inside the window (every chunk,
+// when ALIGNED: both window edges are multiples of 16), element reads for a
+// chunk on its edge, elements outside the window reading as 0.
+template <int ESIZE, bool ALIGNED>
+__device__ __forceinline__ u32x4 seg_ld_chunk(const RowParams& p, const char* row, int b) {
   constexpr int V = 16 / ESIZE;
-  const bool whole = b >= p.lo_b && b + 16 <= p.hi_b;
-  double acc[V];
+  if (ALIGNED || (b >= p.lo_b && b + 16 <= p.hi_b)) return ld16(row + b);
+  u32x4 v = {0, 0, 0, 0};
 #pragma unroll
   for (int e = 0; e < V; ++e) {
     const int bb = b + e * ESIZE;
-    acc[e] = 0.0;
-    if (init && bb >= p.lo_b && bb < p.hi_b) {
-      const uint64_t bits = load_elem<ESIZE>(arow + bb);
-      acc[e] = ESIZE == 4 ? (double)__uint_as_float((uint32_t)bits) : __longlong_as_double((long long)bits);
-    }
+    if (bb >= p.lo_b && bb < p.hi_b) vec_set<ESIZE>(v, e, load_elem<ESIZE>(row + bb));
   }
+  return v;
+}
+
+// Sum of terms [kb, ke) of a destination row's segment (kb < ke) over the
+// 16-byte chunk at byte b of the row's window, in term order, starting from
+// a.grad's values (arow) when init, else from zero; returns the sum's bits.
+// kSegBatch grad_out rows are in flight at once and the next kSegBatch perm
+// entries are read while they are, so the loop waits on one memory latency
+// per batch.  (Reading a perm entry and its row one term at a time made each
+// term wait for two latencies in a row: vector memory reads complete in
+// order, and each perm read queued behind the previous term's row read.)
+template <int ESIZE, bool ALIGNED>
+__device__ __forceinline__ u32x4 seg_chunk_sum_w(const RowParams& p, const int32_t* perm, const char* arow, int32_t kb,
+                                                 int32_t ke, int b, bool init) {
+  constexpr int V = 16 / ESIZE;
+  u32x4 a0 = {0, 0, 0, 0};
+  if (init) a0 = seg_ld_chunk<ESIZE, ALIGNED>(p, arow, b);
+  int32_t g[kSegBatch];
+  seg_batch_perm(perm, kb, ke, g);
   float accf[V];
+  double acc[V];
 #pragma unroll
-  for (int e = 0; e < V; ++e) accf[e] = (float)acc[e];
-  for (int32_t k = kb; k < ke; k += 8) {
-    u32x4 v[8];
+  for (int e = 0; e < V; ++e) {
+    accf[e] = __uint_as_float((uint32_t)vec_get<ESIZE>(a0, e));
+    acc[e] = __longlong_as_double((long long)vec_get<ESIZE>(a0, e));
+  }
+  for (int32_t k = kb; k < ke; k += kSegBatch) {
+    u32x4 v[kSegBatch];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      v[q] = (u32x4){0, 0, 0, 0};
-      if (k + q < ke) {
-        int64_t t_off;
-        dest_row_id(p, perm[k + q], t_off);
-        const char* trow = p.t + t_off;
-        if (whole) {
-          v[q] = ld16(trow + b);
-        } else {
+    for (int q = 0; q < kSegBatch; ++q)
+      v[q] = k + q < ke ? seg_ld_chunk<ESIZE, ALIGNED>(p, p.t + grad_row_off(p, g[q]), b) : (u32x4){0, 0, 0, 0};
+    seg_batch_perm(perm, k + kSegBatch, ke, g);
 #pragma unroll
-          for (int e = 0; e < V; ++e) {
-            const int bb = b + e * ESIZE;
-            if (bb >= p.lo_b && bb < p.hi_b) vec_set<ESIZE>(v[q], e, load_elem<ESIZE>(trow + bb));
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < kSegBatch; ++q) {
       if (k + q >= ke) break;
 #pragma unroll
       for (int e = 0; e < V; ++e) {
@@ -916,11 +855,16 @@ __device__ __forceinline__ u32x4 seg_chunk_sum(const RowParams& p, const int32_t
   }
   u32x4 out = {0, 0, 0, 0};
 #pragma unroll
-  for (int e = 0; e < V; ++e) {
-    const uint64_t bits = ESIZE == 4 ? (uint64_t)__float_as_uint(accf[e]) : (uint64_t)__double_as_longlong(acc[e]);
-    vec_set<ESIZE>(out, e, bits);
-  }
+  for (int e = 0; e < V; ++e)
+    vec_set<ESIZE>(out, e, ESIZE == 4 ? (uint64_t)__float_as_uint(accf[e]) : (uint64_t)__double_as_longlong(acc[e]));
   return out;
+}
+
+template <int ESIZE>
+__device__ __forceinline__ u32x4 seg_chunk_sum(const RowParams& p, const int32_t* perm, const char* arow, int32_t kb,
+                                               int32_t ke, int b, bool init) {
+  return ((p.lo_b | p.hi_b) & 15) == 0 ? seg_chunk_sum_w<ESIZE, true>(p, perm, arow, kb, ke, b, init)
+                                       : seg_chunk_sum_w<ESIZE, false>(p, perm, arow, kb, ke, b, init);
 }
 
 // Write a chunk sum into a.grad: plain stores (store) or float atomics adding
@@ -948,6 +892,17 @@ __device__ __forceinline__ void seg_chunk_out(const RowParams& p, char* arow, in
 // First 16-byte chunk of lane `sub` of a group of LPR lanes; the lane then
 // takes every LPR-th chunk of the row's valid window.
 __device__ __forceinline__ int seg_first_b(const RowParams& p, int sub) { return p.lo_b - p.lo_b % 16 + sub * 16; }
+
+// Terms [kb, ke) of a destination row's segment, summed by one group of LPR
+// lanes, each lane over its chunks of the row.  init: start from a.grad's
+// values and store the row (plain stores); otherwise start from zero and add
+// the partial sums into a.grad with float atomics.
+template <int ESIZE, int LPR>
+__device__ __forceinline__ void seg_sum_terms(const RowParams& p, const int32_t* perm, char* arow, int32_t kb,
+                                              int32_t ke, int sub, bool init) {
+  for (int b = seg_first_b(p, sub); b < p.hi_b; b += LPR * 16)
+    seg_chunk_out<ESIZE>(p, arow, b, seg_chunk_sum<ESIZE>(p, perm, arow, kb, ke, b, init), init);
+}
 
 __device__ __forceinline__ char* seg_arow(const RowParams& p, int64_t r) {
   const int64_t sq = r % p.q_ext, rr = r / p.q_ext;

@@ -112,11 +112,15 @@ def masked(seed: int = SEED_MASKED, rows: int = 1048576, cols: int = 128, n_gath
 
 
 def zipf_indices(seed: int = SEED_ZIPF, rows: int = 1048576, n: int = 4194304, a: float = 1.1) -> np.ndarray:
-    """Skewed gather indices: row k drawn with probability proportional to
-    (k + 1)^-a (numpy's Zipf sampler, values past the table folded onto the
-    last row), int32.  At a = 1.1 row 0 takes about a quarter of the terms."""
+    """Skewed gather indices, int32: a Zipf law truncated to the table, row k
+    drawn with probability proportional to (k + 1)^-a, k < rows (inverse CDF
+    of uniform draws).  At a = 1.1 over 1,048,576 rows, row 0 takes about 12%
+    of the terms and about 3,600 rows take more than 64 each."""
     (rz,) = _rngs(seed, 1)
-    return np.minimum(rz.zipf(a, n) - 1, rows - 1).astype(np.int32)
+    w = np.arange(1, rows + 1, dtype=np.float64) ** -a
+    cdf = np.cumsum(w)
+    cdf /= cdf[-1]
+    return np.minimum(np.searchsorted(cdf, rz.random(n), side="right"), rows - 1).astype(np.int32)
 
 
 # ---- ragged varlen 3-D tiles ------------------------------------------------
