@@ -29,9 +29,9 @@
 // The chip retires about 77 G lane-wise float atomic adds per second whatever
 // the table size, so with a caller-provided workspace the row layout takes an
 // atomic-free path instead: the terms are grouped by destination row with a
-// two-level counting sort done in LDS (no global atomics), and a reduction in
-// which one group of lanes owns a destination row, adds its terms and writes
-// the row once with plain stores.
+// two-level counting sort done in LDS, and a reduction in which one group of
+// lanes owns four consecutive destination rows, adds their terms and writes
+// each row once with plain stores (rows with more than 64 terms excepted).
 #include "stg_internal.h"
 
 #include <algorithm>
@@ -314,10 +314,11 @@ __global__ __launch_bounds__(kThreads) void scatter_elem_kernel(ElemParams p) {
 //     window of 4096 rows), scans the counts into the rows' segment offsets
 //     and places each term id into its row's segment.
 // The reduce kernel then sums each row's segment.  The order of the terms
-// inside a segment follows the LDS atomics and is unspecified.  The sort
-// itself uses no global atomics but one per long segment (to list its
-// pieces); the sums of long segments (more than 64 terms) are split into
-// pieces added with float atomics, all other rows are stored once.  (A
+// inside a segment follows the LDS atomics and is unspecified.  The sort's
+// only global atomics reserve list places for long segments' pieces (one per
+// workgroup and window) and, for buckets of more than 65,536 terms, count and
+// place their terms; the sums of long segments (more than 64 terms) are split
+// into pieces added with float atomics, all other rows are stored once.  (A
 // histogram of returning global atomics took 0.25 ms of the 4M-term
 // workload; the four steps take 0.09 ms.)
 //
@@ -519,8 +520,8 @@ __global__ __launch_bounds__(kThreads) void seg_bucket_kernel(RowParams p, int s
   }
 }
 
-// After a window's scan: list the pieces past the first of this thread's
-// rows w0 + kPer * tid + e whose segments are long (c[e] > kSegChunk); one
+// After a window's scan: list the pieces of this thread's rows
+// w0 + kPer * tid + e whose segments are long (c[e] > kSegChunk); one
 // global atomic per workgroup reserves the places (long rows can be many in
 // a skewed bucket, and atomics on one counter serialize).
 template <int kPer>
@@ -530,7 +531,7 @@ __device__ __forceinline__ void list_pieces(const int32_t (&c)[kPer], int64_t w0
   int32_t mine = 0;
 #pragma unroll
   for (int e = 0; e < kPer; ++e)
-    if (c[e] > kSegChunk) mine += (c[e] - 1) / seg_piece(c[e]);
+    if (c[e] > kSegChunk) mine += (c[e] + seg_piece(c[e]) - 1) / seg_piece(c[e]);
   int32_t total;
   int32_t at = block_exclusive_scan<kBuildThreads>(mine, total);
   if (total == 0) return;  // uniform: the same total in every thread
@@ -539,16 +540,16 @@ __device__ __forceinline__ void list_pieces(const int32_t (&c)[kPer], int64_t w0
   at += s_at;
   __syncthreads();  // s_at is read before the next window may set it
   // the entries are written by whole wavefronts, one long row at a time (a
-  // hot row has up to kMaxPieces - 1 of them)
+  // hot row has up to kMaxPieces of them)
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
-    const int extra = c[e] > kSegChunk ? (c[e] - 1) / seg_piece(c[e]) : 0;
+    const int extra = c[e] > kSegChunk ? (c[e] + seg_piece(c[e]) - 1) / seg_piece(c[e]) : 0;
     for (uint64_t pend = __ballot(extra > 0); pend; pend &= pend - 1) {
       const int L = __builtin_ctzll(pend);
       const int n_e = __shfl(extra, L), at_e = __shfl(at, L);
       const int64_t row = w0 + (int64_t)((threadIdx.x & ~63) + L) * kPer + e;
-      for (int q = lane; q < n_e; q += 64) split_list[at_e + q] = ((uint64_t)row << 32) | (uint32_t)(q + 1);
+      for (int q = lane; q < n_e; q += 64) split_list[at_e + q] = ((uint64_t)row << 32) | (uint32_t)q;
     }
     at += extra;
   }
@@ -905,30 +906,143 @@ __device__ __forceinline__ void seg_sum_terms(const RowParams& p, const int32_t*
 }
 
 __device__ __forceinline__ char* seg_arow(const RowParams& p, int64_t r) {
+  if (p.q_ext == 1 && p.p_ext == 1) return const_cast<char*>(p.a) + r * p.a_ax_b + p.a_col_b;
   const int64_t sq = r % p.q_ext, rr = r / p.q_ext;
   const int64_t sp = rr % p.p_ext, sa = rr / p.p_ext;
   return const_cast<char*>(p.a) + sa * p.a_ax_b + sp * p.a_p_b + sq * p.a_q_b + p.a_col_b;
 }
 
-// One group of LPR lanes per destination row sums the row's segment onto
-// a.grad's values and stores the row once; a segment longer than kSegChunk
-// terms only has its first piece summed here, added atomically, the other
-// pieces going to seg_split_kernel.  Rows with an empty segment are not
-// touched.
+constexpr int kRowsPerGroup = 4;  // consecutive destination rows per group in the reduce (a Four<>)
+
+// Four values picked by a lane-varying index with selects: a register array
+// indexed that way is placed in scratch memory.
+template <class T>
+struct Four {
+  T x0, x1, x2, x3;
+  __device__ __forceinline__ T pick(int i) const { return i == 0 ? x0 : i == 1 ? x1 : i == 2 ? x2 : x3; }
+};
+
+// Row (0 .. kRowsPerGroup - 1) of term kk of a group's stream.
+__device__ __forceinline__ int seg_row_of(const int32_t (&o)[kRowsPerGroup + 1], int32_t kk) {
+  int jj = 0;
+#pragma unroll
+  for (int m = 1; m < kRowsPerGroup; ++m) jj += kk >= o[m];
+  return jj;
+}
+
+template <int ESIZE>
+__device__ __forceinline__ void seg_acc_start(const u32x4& a0, float (&accf)[16 / ESIZE], double (&acc)[16 / ESIZE]) {
+#pragma unroll
+  for (int e = 0; e < 16 / ESIZE; ++e) {
+    accf[e] = __uint_as_float((uint32_t)vec_get<ESIZE>(a0, e));
+    acc[e] = __longlong_as_double((long long)vec_get<ESIZE>(a0, e));
+  }
+}
+
+template <int ESIZE>
+__device__ __forceinline__ u32x4 seg_acc_bits(const float (&accf)[16 / ESIZE], const double (&acc)[16 / ESIZE]) {
+  u32x4 out = {0, 0, 0, 0};
+#pragma unroll
+  for (int e = 0; e < 16 / ESIZE; ++e)
+    vec_set<ESIZE>(out, e, ESIZE == 4 ? (uint64_t)__float_as_uint(accf[e]) : (uint64_t)__double_as_longlong(acc[e]));
+  return out;
+}
+
+// The segments of kRowsPerGroup consecutive destination rows lie back to
+// back in perm, [o[0], o[kRowsPerGroup]), and are summed here as one stream
+// of terms over the 16-byte chunk at byte b: batches of grad_out rows stay in
+// flight across row boundaries, and each row, once its last term is added,
+// is stored from a.grad's value plus its terms in term order.  Rows with an
+// empty segment are not touched.  (One row per group left the rows' reads
+// idle while the group waited on the row's offsets and then its perm
+// entries.)
+template <int ESIZE, bool ALIGNED>
+__device__ __forceinline__ void seg_stream_chunk(const RowParams& p, const int32_t* perm,
+                                                 const int32_t (&o)[kRowsPerGroup + 1],
+                                                 const Four<char*>& arow, int b) {
+  constexpr int V = 16 / ESIZE;
+  const int32_t kb = o[0], ke = o[kRowsPerGroup];
+  if (kb >= ke) return;
+  const u32x4 z = {0, 0, 0, 0};
+  const Four<u32x4> init = {o[1] > o[0] ? seg_ld_chunk<ESIZE, ALIGNED>(p, arow.x0, b) : z,
+                            o[2] > o[1] ? seg_ld_chunk<ESIZE, ALIGNED>(p, arow.x1, b) : z,
+                            o[3] > o[2] ? seg_ld_chunk<ESIZE, ALIGNED>(p, arow.x2, b) : z,
+                            o[4] > o[3] ? seg_ld_chunk<ESIZE, ALIGNED>(p, arow.x3, b) : z};
+  int32_t g[kSegBatch];
+  seg_batch_perm(perm, kb, ke, g);
+  float accf[V];
+  double acc[V];
+  int cur = seg_row_of(o, kb);
+  seg_acc_start<ESIZE>(init.pick(cur), accf, acc);
+  for (int32_t k = kb; k < ke; k += kSegBatch) {
+    u32x4 v[kSegBatch];
+#pragma unroll
+    for (int q = 0; q < kSegBatch; ++q)
+      v[q] = k + q < ke ? seg_ld_chunk<ESIZE, ALIGNED>(p, p.t + grad_row_off(p, g[q]), b) : (u32x4){0, 0, 0, 0};
+    seg_batch_perm(perm, k + kSegBatch, ke, g);
+#pragma unroll
+    for (int q = 0; q < kSegBatch; ++q) {
+      if (k + q >= ke) break;
+      const int jj = seg_row_of(o, k + q);
+      if (jj != cur) {
+        seg_chunk_out<ESIZE>(p, arow.pick(cur), b, seg_acc_bits<ESIZE>(accf, acc), true);
+        cur = jj;
+        seg_acc_start<ESIZE>(init.pick(cur), accf, acc);
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const uint64_t bits = vec_get<ESIZE>(v[q], e);
+        if (ESIZE == 4)
+          accf[e] += __uint_as_float((uint32_t)bits);
+        else
+          acc[e] += __longlong_as_double((long long)bits);
+      }
+    }
+  }
+  seg_chunk_out<ESIZE>(p, arow.pick(cur), b, seg_acc_bits<ESIZE>(accf, acc), true);
+}
+
+// One group of LPR lanes per kRowsPerGroup consecutive destination rows sums
+// each row's segment onto a.grad's values and stores the row once.  A
+// segment longer than kSegChunk terms is left to seg_split_kernel, which adds
+// its pieces onto a.grad with float atomics; a group holding such a row takes
+// its other rows one at a time.  Rows with an empty segment are not touched.
 template <int ESIZE, int LPR>
 __global__ __launch_bounds__(kThreads) void seg_reduce_kernel(RowParams p, int64_t R, const int32_t* offs,
                                                               const int32_t* perm) {
   const int sub = threadIdx.x % LPR;
-  const int64_t r = (int64_t)blockIdx.x * (kThreads / LPR) + threadIdx.x / LPR;
-  if (r >= R) return;
-  const int32_t k0 = offs[r], k1 = offs[r + 1];
-  if (k0 == k1) return;
-  const bool split = k1 - k0 > kSegChunk;
-  seg_sum_terms<ESIZE, LPR>(p, perm, seg_arow(p, r), k0, split ? k0 + seg_piece(k1 - k0) : k1, sub, !split);
+  const int64_t r0 = ((int64_t)blockIdx.x * (kThreads / LPR) + threadIdx.x / LPR) * kRowsPerGroup;
+  if (r0 >= R) return;
+  int32_t o[kRowsPerGroup + 1];
+#pragma unroll
+  for (int j = 0; j <= kRowsPerGroup; ++j) o[j] = offs[min(r0 + j, R)];
+  if (o[0] == o[kRowsPerGroup]) return;  // no terms
+  bool longseg = false;
+#pragma unroll
+  for (int j = 0; j < kRowsPerGroup; ++j) longseg = longseg || o[j + 1] - o[j] > kSegChunk;
+  // rows past R have empty segments and are never read or written
+  const Four<char*> arow = {seg_arow(p, r0), seg_arow(p, min(r0 + 1, R - 1)), seg_arow(p, min(r0 + 2, R - 1)),
+                            seg_arow(p, min(r0 + 3, R - 1))};
+  if (longseg) {
+#pragma unroll
+    for (int j = 0; j < kRowsPerGroup; ++j) {
+      const int32_t k0 = o[j], k1 = o[j + 1];
+      if (k0 == k1 || k1 - k0 > kSegChunk) continue;
+      seg_sum_terms<ESIZE, LPR>(p, perm, arow.pick(j), k0, k1, sub, true);
+    }
+    return;
+  }
+  const bool aligned = ((p.lo_b | p.hi_b) & 15) == 0;
+  for (int b = seg_first_b(p, sub); b < p.hi_b; b += LPR * 16) {
+    if (aligned)
+      seg_stream_chunk<ESIZE, true>(p, perm, o, arow, b);
+    else
+      seg_stream_chunk<ESIZE, false>(p, perm, o, arow, b);
+  }
 }
 
-// The further pieces of long segments, from the list the segment build
-// wrote: entry (row << 32 | piece), piece >= 1; *n_split entries, a row's
+// The pieces of long segments, from the list the segment build
+// wrote: entry (row << 32 | piece), piece >= 0; *n_split entries, a row's
 // pieces consecutive.  A workgroup takes kThreads / LPR consecutive entries,
 // one per group; when they all belong to one row (the common case for a hot
 // row), the groups' partial sums are added together in LDS and go out in one
@@ -1076,8 +1190,8 @@ struct SegLayout {
 };
 
 // Workspace: offs int32[R + 1] | perm int32[n_rows] | pairs uint64[n_rows] |
-// cnt1 int32[L1] | pos1 int32[L1 + 1] | bsum int32[nb1] | split uint64[n_rows /
-// kSegChunk + 1] | n_split int32 | gcur int32[R] | hot int32[nbk] | hot_list
+// cnt1 int32[L1] | pos1 int32[L1 + 1] | bsum int32[nb1] | split uint64[2 * n_rows
+// / kSegChunk + 1] | n_split int32 | gcur int32[R] | hot int32[nbk] | hot_list
 // uint64[n_rows / kSlice + n_rows / kHotPairs + 1] | n_hot int32, each 256-byte
 // aligned.
 // At most 512 buckets while they span at most kWindow rows (R <= 2^21), then
@@ -1100,7 +1214,7 @@ SegLayout seg_layout(int64_t R, int64_t n_rows) {
   L.cnt1 = up(L.pairs + n_rows * 8);
   L.pos1 = up(L.cnt1 + L.L1 * 4);
   L.bsum = up(L.pos1 + (L.L1 + 1) * 4);
-  L.n_pieces = n_rows / kSegChunk + 1;
+  L.n_pieces = 2 * n_rows / kSegChunk + 1;  // ceil(c / piece) < 2 c / kSegChunk for c > kSegChunk
   L.n_slices = n_rows / kSlice + n_rows / kHotPairs + 1;
   L.split = up(L.bsum + L.nb1 * 4);
   L.n_split = up(L.split + L.n_pieces * 8);
@@ -1157,7 +1271,8 @@ int launch_segmented(const char* name, int esize, const RowParams& p, int64_t R,
   // lanes per destination row: enough for the row's chunks, at most a wavefront
   const int chunks_per_row = p.n_chunks;
   const int lpr = chunks_per_row <= 8 ? 8 : chunks_per_row <= 16 ? 16 : chunks_per_row <= 32 ? 32 : 64;
-  const dim3 grid((unsigned)((R + kThreads / lpr - 1) / (kThreads / lpr)));
+  const int64_t rows_per_wg = (int64_t)(kThreads / lpr) * kRowsPerGroup;
+  const dim3 grid((unsigned)((R + rows_per_wg - 1) / rows_per_wg));
   // groups for the long segments' further pieces: striding over the list
   // the build wrote (empty unless a row takes more than kSegChunk terms)
   const int64_t gpw = kThreads / lpr;
