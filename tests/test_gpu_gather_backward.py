@@ -153,6 +153,29 @@ def test_backward_grouped_segment_pieces(stg, orc, dtype):
     run_case(stg, orc, a0, idx, (8, 24), g, ws="auto")
 
 
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+@pytest.mark.parametrize("cols,col_off", [(24, 0), (37, 3), (40, -5)])
+def test_backward_grouped_row_groups(stg, orc, dtype, cols, col_off):
+    """The reduce sums four consecutive destination rows per group as one run
+    of terms.  Terms per row, group by group: runs that cross empty rows,
+    groups that mix short segments with long ones (left to the pieces),
+    segments of exactly 64 and 65 terms, an empty group, and a last group cut
+    short by the table's end (35 rows); column windows that start inside a
+    16-byte chunk or are clipped on the left, so element reads at the edges."""
+    rng = np.random.default_rng(4000 + cols + (dtype == np.float64))
+    pattern = [0, 1, 63, 64, 65, 0, 2, 200, 1, 1, 1, 1, 0, 0, 0, 0, 300, 5, 0, 64, 0, 3, 0, 0, 7, 0, 0, 9,
+               64, 65, 64, 65, 2, 0, 4]
+    R = len(pattern)
+    idx = np.concatenate([np.full(c, r) for r, c in enumerate(pattern) if c]).astype(np.int32)
+    rng.shuffle(idx)
+    assert R % 4 == 3 and all(int((idx == r).sum()) == c for r, c in enumerate(pattern))
+    g = rng.standard_normal((idx.size, cols)).astype(dtype)
+    a0 = rng.standard_normal((R, 41)).astype(dtype)
+    say("gather backward grouped: row groups", np.dtype(dtype).name, "cols", cols, "col_off", col_off)
+    _, count = run_case(stg, orc, a0, idx, (1, cols), g, off=[0, col_off], ws="auto")
+    assert count.max() >= 300
+
+
 def test_backward_grouped_hot_row(stg, orc):
     """One row takes 300,000 terms, more than 4096 pieces of 64: its pieces
     grow (74 terms) so that at most 4096 partial sums meet on the row."""
