@@ -155,7 +155,7 @@ int tile_scatter_masked(const stg_tensor* a, const int32_t* indices, const uint8
  *    written once, without float atomics -- except for rows that take more
  *    than 64 terms, whose segment is split into pieces summed in parallel
  *    and added with the same hardware float atomics (STG_ERR_INVALID if the buffer is
- *    too small; STG_ERR_RANGE with 2^31 or more destination rows or terms, or
+ *    too small; STG_ERR_RANGE with 2^31 - 2^20 or more destination rows or terms, or
  *    when the per-4096-term bucket-count table would reach 2^31 entries).  The
  *    buffer holds about 8 bytes per destination row and 12 per term.  For
  *    any other layout the workspace is not used. */

@@ -1427,8 +1427,11 @@ int run(Op op, const stg_tensor* a, const int32_t* indices, const uint8_t* mask,
     if (grid > INT32_MAX) return fail(STG_ERR_RANGE, "%s: too many rows", name);
     if (op == Op::GatherBackward && workspace) {
       const int64_t R = p.ax_ext * p.p_ext * p.q_ext;
-      if (R >= INT32_MAX || p.n_rows >= INT32_MAX)
-        return fail(STG_ERR_RANGE, "%s: the segmented path needs fewer than 2^31 rows and terms", name);
+      // int32 term and row positions, with headroom for the kernels' strides
+      // past the last one (term batches, chunks, windows, slices)
+      constexpr int64_t kSegLimit = INT32_MAX - (int64_t(1) << 20);
+      if (R >= kSegLimit || p.n_rows >= kSegLimit)
+        return fail(STG_ERR_RANGE, "%s: the segmented path needs fewer than 2^31 - 2^20 rows and terms", name);
       if (workspace_bytes < seg_layout(R, p.n_rows).bytes)
         return fail(STG_ERR_INVALID, "%s: workspace of %lld bytes, %lld needed", name, (long long)workspace_bytes,
                     (long long)seg_layout(R, p.n_rows).bytes);
