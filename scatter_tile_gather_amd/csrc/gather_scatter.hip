@@ -521,11 +521,13 @@ __global__ __launch_bounds__(kThreads) void seg_bucket_kernel(RowParams p, int s
 }
 
 // After a window's scan: list the pieces of this thread's rows
-// w0 + kPer * tid + e whose segments are long (c[e] > kSegChunk); one
-// global atomic per workgroup reserves the places (long rows can be many in
-// a skewed bucket, and atomics on one counter serialize).
+// w0 + kPer * tid + e whose segments are long (c[e] > kSegChunk), a row's
+// pieces consecutive and in order; one global atomic per workgroup reserves
+// the places (long rows can be many in a skewed bucket, and atomics on one
+// counter serialize).  Each wavefront writes the entries of its own long
+// rows: the form for buckets with few long rows.
 template <int kPer>
-__device__ __forceinline__ void list_pieces(const int32_t (&c)[kPer], int64_t w0, uint64_t* split_list,
+__device__ __forceinline__ void list_pieces_waves(const int32_t (&c)[kPer], int64_t w0, uint64_t* split_list,
                                             int32_t* n_split) {
   __shared__ int32_t s_at;
   int32_t mine = 0;
@@ -553,6 +555,47 @@ __device__ __forceinline__ void list_pieces(const int32_t (&c)[kPer], int64_t w0
     }
     at += extra;
   }
+}
+
+// The same list for a hot bucket, whose rows can have up to kMaxPieces
+// entries each, too many for one wavefront to write: the rows' first places
+// go to LDS, and every thread of the workgroup writes entries, finding an
+// entry's row by binary search.  (In the other buckets the extra LDS and
+// barriers cost more than they save.)
+template <int kPer>
+__device__ __forceinline__ void list_pieces_wg(const int32_t (&c)[kPer], int64_t w0, uint64_t* split_list,
+                                               int32_t* n_split) {
+  constexpr int kRows = kPer * kBuildThreads;
+  static_assert(kRows == 1 << 12, "the binary search below takes 12 steps");
+  __shared__ int32_t s_at;
+  __shared__ int32_t s_first[kRows];  // first place of each row's pieces, relative to s_at
+  int32_t mine = 0;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e)
+    if (c[e] > kSegChunk) mine += (c[e] + seg_piece(c[e]) - 1) / seg_piece(c[e]);
+  int32_t total;
+  int32_t at = block_exclusive_scan<kBuildThreads>(mine, total);
+  if (total == 0) return;  // uniform: the same total in every thread
+  if (threadIdx.x == 0) s_at = atomicAdd(n_split, total);
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    s_first[threadIdx.x * kPer + e] = at;
+    if (c[e] > kSegChunk) at += (c[e] + seg_piece(c[e]) - 1) / seg_piece(c[e]);
+  }
+  __syncthreads();
+  const int32_t base = s_at;
+  for (int32_t q = threadIdx.x; q < total; q += kBuildThreads) {
+    // the entry's row: the last row whose first place is at or before q
+    // (rows without pieces have an empty range and are passed over)
+    int lo = 0, hi = kRows - 1;
+#pragma unroll
+    for (int step = 0; step < 12; ++step) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_first[mid] <= q) lo = mid; else hi = mid - 1;
+    }
+    split_list[(int64_t)base + q] = ((uint64_t)(w0 + lo) << 32) | (uint32_t)(q - s_first[lo]);
+  }
+  __syncthreads();  // s_at and s_first are rewritten by the next window
 }
 
 // Step 4: one workgroup per bucket.  Its pairs are pairs[s0, s1); its rows
@@ -622,7 +665,7 @@ __global__ __launch_bounds__(kBuildThreads) void seg_build_kernel(int64_t R, int
       cur[j] = run;
       run += c[e];
     }
-    list_pieces(c, w0, split_list, n_split);
+    list_pieces_waves(c, w0, split_list, n_split);
     __syncthreads();
     for (int64_t i0 = s0; i0 < s1; i0 += kU * kBuildThreads) {
       uint64_t pr[kU];
@@ -737,7 +780,7 @@ __global__ __launch_bounds__(kBuildThreads) void seg_hot_scan_kernel(int64_t R, 
       }
       run += c[e];
     }
-    list_pieces(c, w0, split_list, n_split);
+    list_pieces_wg(c, w0, split_list, n_split);
     base += total;
   }
 }
