@@ -425,6 +425,7 @@ def run_gather_backward_zipf(stg, inputs, steps, warmup):
     e["note"] = ("algorithmic bytes as for the uniform indices; rows past 64 terms are split into pieces added with "
                  "float atomics")
     e["max_terms_per_row"] = int(np.bincount(zidx_h).max())
+    e["cold_cache"] = cold_entry(nbytes, fn)
     return e
 
 
