@@ -154,14 +154,15 @@ def test_backward_grouped_segment_pieces(stg, orc, dtype):
 
 
 @pytest.mark.parametrize("dtype", [np.float32, np.float64])
-@pytest.mark.parametrize("cols,col_off", [(24, 0), (37, 3), (40, -5)])
+@pytest.mark.parametrize("cols,col_off", [(24, 0), (37, 3), (40, -5), (600, 0), (601, 3)])
 def test_backward_grouped_row_groups(stg, orc, dtype, cols, col_off):
     """The reduce sums four consecutive destination rows per group as one run
     of terms.  Terms per row, group by group: runs that cross empty rows,
     groups that mix short segments with long ones (left to the pieces),
     segments of exactly 64 and 65 terms, an empty group, and a last group cut
     short by the table's end (35 rows); column windows that start inside a
-    16-byte chunk or are clipped on the left, so element reads at the edges."""
+    16-byte chunk or are clipped on the left, so element reads at the edges,
+    and rows wider than a wavefront's 64 chunks, so several chunks per lane."""
     rng = np.random.default_rng(4000 + cols + (dtype == np.float64))
     pattern = [0, 1, 63, 64, 65, 0, 2, 200, 1, 1, 1, 1, 0, 0, 0, 0, 300, 5, 0, 64, 0, 3, 0, 0, 7, 0, 0, 9,
                64, 65, 64, 65, 2, 0, 4]
@@ -170,7 +171,7 @@ def test_backward_grouped_row_groups(stg, orc, dtype, cols, col_off):
     rng.shuffle(idx)
     assert R % 4 == 3 and all(int((idx == r).sum()) == c for r, c in enumerate(pattern))
     g = rng.standard_normal((idx.size, cols)).astype(dtype)
-    a0 = rng.standard_normal((R, 41)).astype(dtype)
+    a0 = rng.standard_normal((R, cols + 4)).astype(dtype)
     say("gather backward grouped: row groups", np.dtype(dtype).name, "cols", cols, "col_off", col_off)
     _, count = run_case(stg, orc, a0, idx, (1, cols), g, off=[0, col_off], ws="auto")
     assert count.max() >= 300
