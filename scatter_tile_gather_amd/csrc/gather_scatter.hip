@@ -839,13 +839,13 @@ __device__ __forceinline__ void seg_batch_perm(const int32_t* perm, int32_t k, i
 }
 
 // The 16-byte chunk at byte b of a row, restricted to the valid byte window
-// [lo_b, hi_b): one 16-byte read for a chunk inside the window (every chunk,
-// when ALIGNED: both window edges are multiples of 16), element reads for a
-// chunk on its edge, elements outside the window reading as 0.
+// [lo_b, hi_b): one non-temporal 16-byte read for a chunk inside the window
+// (every chunk, when ALIGNED: both window edges are multiples of 16), element
+// reads for a chunk on its edge, elements outside the window reading as 0.
 template <int ESIZE, bool ALIGNED>
 __device__ __forceinline__ u32x4 seg_ld_chunk(const RowParams& p, const char* row, int b) {
   constexpr int V = 16 / ESIZE;
-  if (ALIGNED || (b >= p.lo_b && b + 16 <= p.hi_b)) return ld16(row + b);
+  if (ALIGNED || (b >= p.lo_b && b + 16 <= p.hi_b)) return ld16_nt(row + b);
   u32x4 v = {0, 0, 0, 0};
 #pragma unroll
   for (int e = 0; e < V; ++e) {
