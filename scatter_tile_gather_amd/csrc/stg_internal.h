@@ -83,6 +83,9 @@ __device__ __forceinline__ void st16_nt(char* p, u32x4 v) { __builtin_nontempora
 // The grouped gather backward reads its grad_out rows (each once, in random
 // order) and a.grad's chunks this way: the uniform 4M-term workload runs 7%
 // faster (reduce 0.597 -> 0.550 ms) and the pieces of hot rows 10% faster.
+// The forward row kernels keep plain loads: with this one the masked gather,
+// whose table rows are read about four times each, drops from 6.9 to 5.6
+// TB/s, and the masked scatter, reading contiguous tile rows, from 6.2 to 5.1.
 __device__ __forceinline__ u32x4 ld16_nt(const char* p) {
   return __builtin_nontemporal_load((const u32x4_unaligned*)p);
 }
