@@ -131,9 +131,9 @@ int tile_scatter_masked(const stg_tensor* a, const int32_t* indices, const uint8
                         int64_t n_indices, const int64_t* tile_shape, const int64_t* offset,
                         int32_t axis, const stg_tensor* tile, void* stream);
 
-/* Backward of tile_gather (Warp, warp.tile_load_indexed: the function is
- * differentiable; in a backward pass the adjoint of the returned tile is
- * accumulated atomically into a.grad at the same gathered locations).
+/* Backward of tile_gather (Warp, warp.tile_load_indexed, description: the
+ * load is differentiable, and its backward adds the output gradient into
+ * a.grad at each location the forward read, with atomic adds).
  * grad_out has the shape of tile_gather's `out` for the same indices,
  * tile_shape, offset and axis; for every coordinate o of grad_out whose source
  * coordinate s (as in tile_gather) is in range:

@@ -224,7 +224,7 @@ void orc_tile_store_clipped(const void* tiles_in, int32_t esize, int64_t tm, int
     }
 }
 
-/* ---- ragged varlen 3-D tiles ------------------------------------------ */
+/* ---- gather backward (adjoint of the gather) -------------------------- */
 
 void orc_tile_gather_backward(const orc_array* grad_out, const int32_t* indices, int64_t n_indices,
                               const int64_t* tile_shape, const int64_t* offset, int32_t axis,
@@ -266,6 +266,8 @@ void orc_tile_gather_backward(const orc_array* grad_out, const int32_t* indices,
             count[lin] += 1;
           }
 }
+
+/* ---- tile windows with a step ----------------------------------------- */
 
 void orc_tile_copy_windows(const orc_array* src, int64_t tm, int64_t tn, int64_t step_rows,
                            int64_t step_cols, int64_t origin_row, int64_t origin_col, void* tiles_out) {
@@ -312,6 +314,8 @@ void orc_tile_store_windows(const void* tiles_in, int32_t esize, int64_t tm, int
     }
 }
 
+/* ---- ragged varlen 3-D tiles ------------------------------------------ */
+
 int64_t orc_ragged_schedule(const int64_t* seq_lens, int64_t n_seqs, int32_t bm_seq,
                             int32_t middle_dim, uint32_t* ragged_idx, uint32_t* dynamic_dim,
                             uint32_t* middle_idx) {
@@ -357,7 +361,7 @@ void orc_ragged_tile_load(const void* X, int32_t esize, int64_t total_rows, int3
   }
 }
 
-/* ---- bounded GEMM reference ------------------------------------------- */
+/* ---- ragged varlen 3-D store ------------------------------------------ */
 
 void orc_ragged_tile_store(const void* tiles_in, int32_t esize, int64_t total_rows, int32_t middle_dim,
                            int32_t group, int32_t depth, int32_t BM, int32_t BN, int32_t col0,
@@ -379,6 +383,8 @@ void orc_ragged_tile_store(const void* tiles_in, int32_t esize, int64_t total_ro
         }
   }
 }
+
+/* ---- block-scaled GEMM reference -------------------------------------- */
 
 double orc_decode_lowp(uint8_t code, int32_t fmt) {
   int s, e, m, ebits, mbits, bias;
@@ -429,6 +435,8 @@ void orc_gemm_scaled(const uint8_t* A, int32_t a_fmt, int64_t lda_bytes, const u
       C[m * N + n] = sum;
     }
 }
+
+/* ---- bounded GEMM reference ------------------------------------------- */
 
 double orc_bf16_to_f64(uint16_t h) {
   uint32_t bits = (uint32_t)h << 16;

@@ -103,10 +103,9 @@ void orc_tile_copy_bounded(const orc_array* src, int64_t tm, int64_t tn, int64_t
 void orc_tile_store_clipped(const void* tiles_in, int32_t esize, int64_t tm, int64_t tn,
                             int64_t origin_row, int64_t origin_col, orc_array* dst);
 
-/* Backward of the indexed gather (Warp, warp.tile_load_indexed: the
- * function is differentiable, and in a backward pass the adjoint of the
- * returned tile is accumulated atomically into a.grad at the same gathered
- * locations).  For every coordinate o of grad_out (the gather's output
+/* Backward of the indexed gather (Warp, warp.tile_load_indexed,
+ * description: the load is differentiable; its backward adds the output
+ * gradient into a.grad at each location the forward read, atomically).  For every coordinate o of grad_out (the gather's output
  * shape) whose source coordinate s -- as in orc_tile_gather -- is in range:
  *   acc[s] += grad_out[o];  abs_sum[s] += |grad_out[o]|;  count[s] += 1
  * Out-of-range sources contribute nothing; repeated indices add up.

@@ -248,7 +248,13 @@ def tile_gather_backward(a_grad, indices, tile_shape, grad_out, offset=None, axi
     ad, gd = _desc(a_grad, "a_grad"), _desc(grad_out, "grad_out")
     if isinstance(workspace, str) and workspace == "auto":
         nb = tile_gather_backward_workspace(a_grad, n, tile_shape, axis)
-        workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=a_grad.device) if nb else None
+        workspace = None
+        if nb:
+            # allocated on the stream the kernels run on: when this function
+            # returns, the caching allocator hands the block out again only to
+            # work queued on that stream after them
+            with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream(a_grad.device)):
+                workspace = torch.empty(nb, dtype=torch.uint8, device=a_grad.device)
     ws_ptr, ws_n = None, 0
     if workspace is not None:
         _on_gpu(workspace, "workspace")

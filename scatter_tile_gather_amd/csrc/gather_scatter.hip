@@ -20,9 +20,9 @@
 //  * element path -- anything else (gather along the innermost axis, strided
 //    innermost dimension): one element per lane.
 //
-// Backward of the gather (Warp, warp.tile_load_indexed: differentiable; in a
-// backward pass the adjoint of the returned tile is accumulated atomically
-// into a.grad at the same gathered locations): the scatter kernels with every
+// Backward of the gather (Warp, warp.tile_load_indexed, description: the load
+// is differentiable; its backward adds the output gradient into a.grad at
+// each location the forward read, atomically): the scatter kernels with every
 // store replaced by a hardware float atomic add (fp32 or fp64, relaxed, device
 // scope), unmasked; rows whose source is out of range are compacted away like
 // masked-out scatter rows.  Repeated indices add up in an unspecified order.

@@ -480,7 +480,17 @@ int launch(const char* name, GemmParams p, int64_t cols, hipStream_t s) {
   return check_launch("gemm_bounded");
 }
 
-bool lds_configured = false;
+// Raises the kernels' dynamic LDS limit once per process; a function-local
+// static is initialised exactly once even when the first calls come from
+// several host threads at the same time.
+bool lds_configured() {
+  static const bool ok =
+      hipFuncSetAttribute((const void*)gemm_kernel<MainCfg>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          MainCfg::LDS_B) == hipSuccess &&
+      hipFuncSetAttribute((const void*)gemm_kernel<EdgeCfg>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          EdgeCfg::LDS_B) == hipSuccess;
+  return ok;
+}
 
 }  // namespace
 }  // namespace stg
@@ -502,14 +512,8 @@ extern "C" int gemm_bounded(const void* A, int64_t lda, const void* B, int64_t l
   // 32-bit buffer offsets within one stage: BM rows of A, BK rows of B
   if ((int64_t)MainCfg::BM * lda * 2 + 256 >= kMaxOffset32 || (int64_t)BK * ldb * 2 + 512 >= kMaxOffset32)
     return fail(STG_ERR_RANGE, "%s: a stage of A or B spans more than 2^31 bytes", name);
-  if (!lds_configured) {
-    if (hipFuncSetAttribute((const void*)gemm_kernel<MainCfg>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            MainCfg::LDS_B) != hipSuccess ||
-        hipFuncSetAttribute((const void*)gemm_kernel<EdgeCfg>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            EdgeCfg::LDS_B) != hipSuccess)
-      return fail(STG_ERR_LAUNCH, "%s: cannot reserve LDS: %s", name, hipGetErrorString(hipGetLastError()));
-    lds_configured = true;
-  }
+  if (!lds_configured())
+    return fail(STG_ERR_LAUNCH, "%s: cannot reserve LDS for the GEMM kernels", name);
   GemmParams p{};
   p.A = (const char*)A;
   p.B = (const char*)B;

@@ -574,7 +574,6 @@ __global__ __launch_bounds__(kSkWaves * 64) void gemm_scaled_skinny_kernel(Scale
     }
 }
 
-bool scaled_lds_configured = false;
 
 // main kernel on the first p.N columns; the skinny kernel on columns
 // n_skinny .. n_skinny + r_skinny - 1 (r_skinny = 0: none)
@@ -642,12 +641,11 @@ extern "C" int gemm_scaled(const void* A, int32_t a_fmt, int64_t lda, const void
       (M - 1) * lds_a + K / block + 64 >= kMaxOffset32 || (N - 1) * lds_b + K / block + 64 >= kMaxOffset32)
     return fail(STG_ERR_RANGE, "%s: a stage or a scale matrix spans more than 2^31 bytes, or a size is too large",
                 name);
-  if (!scaled_lds_configured) {
-    if (!set_lds<0, 0, 8>() || !set_lds<0, 1, 8>() || !set_lds<1, 0, 8>() || !set_lds<1, 1, 8>() ||
-        !set_lds<4, 4, 4>())
-      return fail(STG_ERR_LAUNCH, "%s: cannot reserve LDS: %s", name, hipGetErrorString(hipGetLastError()));
-    scaled_lds_configured = true;
-  }
+  // once per process; a function-local static is initialised exactly once
+  // even when the first calls come from several host threads
+  static const bool lds_ok = set_lds<0, 0, 8>() && set_lds<0, 1, 8>() && set_lds<1, 0, 8>() &&
+                             set_lds<1, 1, 8>() && set_lds<4, 4, 4>();
+  if (!lds_ok) return fail(STG_ERR_LAUNCH, "%s: cannot reserve LDS for the scaled GEMM kernels", name);
   ScaledParams p{};
   p.A = (const char*)A;
   p.B = (const char*)Bt;

@@ -55,6 +55,20 @@ def test_ragged_schedule_matches_oracle(stg, orc, seed):
             np.testing.assert_array_equal(g, w)
 
 
+def test_ragged_schedule_workload_matches_oracle(stg, orc):
+    """The ragged workload's own 64 lengths, at both group settings: the
+    product's schedule (which the ragged parity tests take their triples
+    from) equals the oracle's, entry by entry."""
+    lens = stg_pkg.inputs.ragged()["seq_lens"]
+    assert len(lens) == 64
+    for bm_seq, md in [(128, 8), (32, 2)]:
+        got = stg.ragged_tile_schedule(lens, bm_seq, md)
+        want = orc.ragged_schedule(lens, bm_seq, md)
+        assert len(got[0]) == len(want[0]) > 0
+        for g, w in zip(got, want):
+            np.testing.assert_array_equal(np.asarray(g, dtype=np.uint32), w)
+
+
 def test_ragged_schedule_workload_count(stg):
     lens = stg_pkg.inputs.ragged()["seq_lens"]
     for bm_seq, md in [(128, 8), (32, 2)]:

@@ -203,3 +203,27 @@ def test_backward_grouped_hot_buckets(stg, orc, dtype):
     a0 = rng.standard_normal((70000, 20)).astype(dtype)
     say("gather backward grouped: hot buckets", np.dtype(dtype).name, "max count", int(np.bincount(idx).max()))
     run_case(stg, orc, a0, idx, (8, 20), g, ws="auto")
+
+
+def test_backward_auto_workspace_on_side_stream(stg, orc):
+    """workspace="auto" with the kernels on a side stream: the workspace is
+    released when the call returns, while its kernels may still run there.
+    Tensors allocated and filled on the default stream right after must not
+    receive that block; the gradient still matches the oracle."""
+    rng = np.random.default_rng(31)
+    rows, cols, n = 1 << 16, 64, 1 << 20
+    idx = rng.integers(0, rows, n).astype(np.int32)
+    g = rng.standard_normal((n, cols)).astype(np.float32)
+    a0 = np.zeros((rows, cols), np.float32)
+    a_dev, i_dev, g_dev = to_dev(a0), to_dev(idx), to_dev(g)
+    nb = stg.tile_gather_backward_workspace(a_dev, n, (64, cols), 0)
+    assert nb > 0
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    say("gather backward, auto workspace on a side stream, then default-stream allocations of the same size")
+    stg.tile_gather_backward(a_dev, i_dev, (64, cols), g_dev, None, 0, workspace="auto", stream=side)
+    fills = [torch.full((nb,), 0xFF, dtype=torch.uint8, device="cuda:0") for _ in range(4)]
+    torch.cuda.synchronize()
+    assert all(int(f.min()) == 0xFF for f in fills)
+    acc, abs_sum, count = orc.tile_gather_backward(a0, idx, (64, cols), g, None, 0)
+    check_backward(to_host(a_dev), a0, acc, abs_sum, count)

@@ -117,6 +117,129 @@ def test_gemm_strided_operands_and_clipped_epilogue(stg, orc):
             assert np.all(pad == 0x40E0)  # bf16 7.0: the padding is never written
 
 
+def abs_bits(X):
+    """bf16 bit patterns with the sign cleared: |X| exactly."""
+    return (X & np.uint16(0x7FFF)).astype(np.uint16)
+
+
+def gamma(K):
+    """gamma_K = K u / (1 - K u), u = 2^-24: the bound on the relative error of
+    a K-term fp32 sum in any order (Higham, Accuracy and Stability, 3.1)."""
+    u = 2.0 ** -24
+    return K * u / (1 - K * u)
+
+
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_gemm_literal_input_scaling(stg, orc, out_f32):
+    """The workload text read literally: A and B both ~N(0,1)/sqrt(K), so
+    C ~ N(0, 1/K).  The 1e-2 bound holds trivially there, so the fp32 output
+    is also held to the summation bound gamma_K * sum|a||b| (exact products,
+    fp32 accumulation), and the bf16 output to that plus half a bf16 ulp."""
+    g = inputs.gemm(65, 97, 73, scale_a=True)
+    say("gemm 65x97x73, both operands / sqrt(K)", "f32" if out_f32 else "bf16")
+    C, _ = run(stg, g["A"], g["B"], out_f32)
+    C64 = orc.gemm_f64(g["A"], g["B"])
+    check(C, C64, out_f32)
+    bound = gamma(73) * orc.gemm_f64(abs_bits(g["A"]), abs_bits(g["B"]))
+    if not out_f32:
+        bound = bound + bf16_ulp(C64) / 2
+    assert np.all(np.abs(C - C64) <= bound)
+    assert np.std(C64) < 0.3  # the literal reading really gives the narrow output
+
+
+def test_gemm_literal_input_scaling_large_sampled(stg, orc):
+    M, N, K = 8191, 8193, 4097
+    g = inputs.gemm(M, N, K, scale_a=True)
+    say("gemm 8191x8193x4097, both operands / sqrt(K), fp32 out, sampled")
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+    stg.gemm_bounded(to_dev(g["A"]), to_dev(g["B"]), out=C)
+    torch.cuda.synchronize()
+    r, c = _sample_coords(M, N)
+    got = to_host(C[torch.from_numpy(r).cuda(), torch.from_numpy(c).cuda()]).astype(np.float64)
+    want = orc.gemm_sample_f64(g["A"], g["B"], r, c)
+    check(got, want, True)
+    mag = orc.gemm_sample_f64(abs_bits(g["A"]), abs_bits(g["B"]), r, c)
+    assert np.all(np.abs(got - want) <= gamma(K) * mag)
+
+
+def _tie_operands(M, N, K, seed):
+    """Operands whose every output is the exact sum of two bf16 values of one
+    column scale 2^e_n: a 'head' 1.m (eight significant bits) and a 'tail'
+    from {+-2^-8, +-2^-9, +-3*2^-9, +-5*2^-10}.  The sums need up to ten
+    significant bits, so they are exact in fp32 and in any fp32 accumulation
+    order, and many fall exactly halfway between two bf16 values (head +-
+    2^-8, with the head's last significand bit 0 or 1)."""
+    rng = np.random.default_rng(seed)
+    half = K // 2
+    e = rng.integers(-3, 4, N).astype(np.float64)
+    head = (1 + rng.integers(0, 128, (half, N)) / 128.0) * rng.choice([-1.0, 1.0], (half, N))
+    tails = np.array([2.0 ** -8, -2.0 ** -8, 2.0 ** -9, -2.0 ** -9, 3 * 2.0 ** -9, -3 * 2.0 ** -9, 5 * 2.0 ** -10])
+    tail = rng.choice(tails, (K - half, N), p=[0.3, 0.3, 0.08, 0.08, 0.08, 0.08, 0.08])
+    Bv = np.concatenate([head, tail]) * 2.0 ** e
+    B = inputs.f32_to_bf16_bits(Bv.astype(np.float32))
+    assert np.array_equal(inputs.bf16_bits_to_f32(B).astype(np.float64), Bv)  # every value exact in bf16
+    A = np.zeros((M, K), dtype=np.uint16)
+    A[np.arange(M), rng.integers(0, half, M)] = 0x3F80
+    A[np.arange(M), half + rng.integers(0, K - half, M)] = 0x3F80
+    return A, B
+
+
+@pytest.mark.parametrize("shape", [(65, 97, 73), (300, 520, 200), (257, 1000, 4097)])
+def test_gemm_bf16_epilogue_rounds_to_nearest_even(stg, orc, shape):
+    """The bf16 epilogue pinned bit for bit, ties included: every output is an
+    exact fp32 sum (both outputs equal the fp64 oracle exactly), and the bf16
+    output is the oracle's nearest-even rounding of it.  About half the
+    outputs are exact ties, with both parities of the last kept bit, so
+    truncation, round-half-up and round-half-away all fail."""
+    M, N, K = shape
+    A, B = _tie_operands(M, N, K, seed=M + N)
+    say("gemm bf16 epilogue ties", shape)
+    C32, _ = run(stg, A, B, True)
+    C64 = orc.gemm_f64(A, B)
+    np.testing.assert_array_equal(C32, C64)
+    _, full16 = run(stg, A, B, False)
+    want = orc.f64_to_bf16_bits(C64)
+    ties = np.abs(C64 - inputs.bf16_bits_to_f32(want).astype(np.float64)) == bf16_ulp(C64) / 2
+    assert ties.mean() > 0.3
+    np.testing.assert_array_equal(full16[:, :N], want)
+
+
+def test_gemm_bf16_output_is_rne_of_f32_output(stg, orc):
+    """On normal operands the bf16 output of the kernel equals the
+    nearest-even rounding (oracle) of the same kernel's fp32 output, bit for
+    bit: in full at 65x97x73 and, at 8191x8193x4097, on the edge rows and
+    columns plus 65,536 seeded interior samples."""
+    g = inputs.gemm(65, 97, 73)
+    say("gemm bf16 == rne(f32), 65x97x73")
+    C32, _ = run(stg, g["A"], g["B"], True)
+    _, full16 = run(stg, g["A"], g["B"], False)
+    np.testing.assert_array_equal(full16, orc.f64_to_bf16_bits(C32))
+    M, N, K = 8191, 8193, 4097
+    g = inputs.gemm(M, N, K)
+    say("gemm bf16 == rne(f32), 8191x8193x4097 sampled")
+    Ad, Bd = to_dev(g["A"]), to_dev(g["B"])
+    C32 = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+    stg.gemm_bounded(Ad, Bd, out=C32)
+    C16 = stg.gemm_bounded(Ad, Bd)
+    torch.cuda.synchronize()
+    r, c = _sample_coords(M, N)
+    rt, ct = torch.from_numpy(r).cuda(), torch.from_numpy(c).cuda()
+    got16 = to_host(C16[rt, ct])
+    got32 = to_host(C32[rt, ct]).astype(np.float64)
+    np.testing.assert_array_equal(got16, orc.f64_to_bf16_bits(got32))
+
+
+def _sample_coords(M, N):
+    """The last row, the first row of the last 256-row tile, the last column,
+    the first column past the last whole 256-column tile, plus 65,536 seeded
+    interior samples."""
+    rng = np.random.default_rng(99)
+    lr, lc = (M - 1) // 256 * 256, (N - 1) // 256 * 256
+    rows = [np.full(N, M - 1), np.full(N, lr), np.arange(M), np.arange(M), rng.integers(0, M, 65536)]
+    cols = [np.arange(N), np.arange(N), np.full(M, N - 1), np.full(M, lc - 1), rng.integers(0, N, 65536)]
+    return np.concatenate(rows).astype(np.int64), np.concatenate(cols).astype(np.int64)
+
+
 def test_gemm_large_shape_sampled(stg, orc):
     M, N, K = 8191, 8193, 4097
     g = inputs.gemm(M, N, K)
