@@ -171,6 +171,24 @@ int tile_gather_backward(const stg_tensor* a_grad, const int32_t* indices, int64
 int64_t tile_gather_backward_workspace(const stg_tensor* a_grad, int64_t n_indices,
                                        const int64_t* tile_shape, int32_t axis);
 
+/* tile_gather_backward without a caller workspace, for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, semantics and errors as
+ * tile_gather_backward with a workspace, except that the grouped execution's
+ * scratch lives in a static device array of the library holding
+ * STG_STATIC_SCRATCH_BYTES (64 MiB) on each GPU it runs on, kept until the
+ * process ends; a call needing more (tile_gather_backward_workspace(...) >
+ * STG_STATIC_SCRATCH_BYTES, about 4M terms onto 1M rows) returns
+ * STG_ERR_RANGE and enqueues nothing.  Layouts that take no workspace run on
+ * float atomics as in tile_gather_backward.  The call allocates and frees
+ * nothing.  All calls on one GPU share its array: calls that overlap in time
+ * on one GPU (two streams, or two host threads without ordering) race and
+ * give undefined results; `stream` must belong to the current device. */
+#define STG_STATIC_SCRATCH_BYTES (64ll << 20)
+int tile_gather_backward_static(const stg_tensor* a_grad, const int32_t* indices, int64_t n_indices,
+                                const int64_t* tile_shape, const int64_t* offset, int32_t axis,
+                                const stg_tensor* grad_out, void* stream);
+
 /* Boundary-tile copy with zero fill (Tylo.jl Boundary tiles: opening section,
  * "A concrete edge"; cuTile.jl Memory, "Bounds checking": loads pad).
  * src is rank 2, logical (M, N), any strides (leading stride need not be

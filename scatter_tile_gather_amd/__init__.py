@@ -7,6 +7,7 @@ input generators used by the tests and the benchmark.
 from . import inputs  # noqa: F401
 from ._binding import (  # noqa: F401
     LIB_PATH,
+    STATIC_SCRATCH_BYTES,
     StgError,
     exported_names,
     gemm_bounded,
@@ -23,6 +24,7 @@ from ._binding import (  # noqa: F401
     tile_copy_windows,
     tile_gather,
     tile_gather_backward,
+    tile_gather_backward_static,
     tile_gather_backward_workspace,
     tile_gather_masked,
     tile_scatter_masked,

@@ -49,6 +49,7 @@ _SIGNATURES = {
     "tile_scatter_masked": (ctypes.c_int, [_TP, _P, _P, _I64, _I64P, _I64P, _I32, _TP, _P]),
     "tile_gather_backward": (ctypes.c_int, [_TP, _P, _I64, _I64P, _I64P, _I32, _TP, _P, _I64, _P]),
     "tile_gather_backward_workspace": (_I64, [_TP, _I64, _I64P, _I32]),
+    "tile_gather_backward_static": (ctypes.c_int, [_TP, _P, _I64, _I64P, _I64P, _I32, _TP, _P]),
     "tile_copy_bounded": (ctypes.c_int, [_TP, _I64, _I64, _I64, _I64, _P, _P]),
     "tile_store_clipped": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _TP, _P]),
     "tile_copy_windows": (ctypes.c_int, [_TP, _I64, _I64, _I64, _I64, _I64, _I64, _I32, _P, _P]),
@@ -262,6 +263,25 @@ def tile_gather_backward(a_grad, indices, tile_shape, grad_out, offset=None, axi
     _check(lib.tile_gather_backward(ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"), n,
                                     _i64arr(tile_shape), None if offset is None else _i64arr(offset), axis,
                                     ctypes.byref(gd), ws_ptr, ws_n, _stream(stream, a_grad)))
+    return a_grad
+
+
+# bytes of the library's static scratch array (STG_STATIC_SCRATCH_BYTES in stg.h)
+STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def tile_gather_backward_static(a_grad, indices, tile_shape, grad_out, offset=None, axis: int = 0, stream=None):
+    """tile_gather_backward's grouped execution with its scratch in the
+    library's static device array instead of a workspace: nothing is
+    allocated.  Calls needing more than STATIC_SCRATCH_BYTES raise StgError
+    (STG_ERR_RANGE); calls that overlap in time on one GPU race."""
+    torch = _torch()
+    lib = load_library()
+    ad, gd = _desc(a_grad, "a_grad"), _desc(grad_out, "grad_out")
+    _check(lib.tile_gather_backward_static(ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"),
+                                           indices.numel(), _i64arr(tile_shape),
+                                           None if offset is None else _i64arr(offset), axis, ctypes.byref(gd),
+                                           _stream(stream, a_grad)))
     return a_grad
 
 

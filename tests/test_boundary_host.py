@@ -281,3 +281,17 @@ def test_gemm_scaled_argument_errors(stg):
     assert call(C=None) == 1
     assert call(M=-1) == 1
     assert call(M=0) == 0  # nothing to do
+
+
+def test_static_scratch_size_and_oversized_rejection(stg):
+    """The static scratch size is the one stg.h declares, and a call needing
+    more scratch than that fails with STG_ERR_RANGE in the host checks, before
+    any HIP call (fake device pointers are never touched)."""
+    m = re.search(r"#define\s+STG_STATIC_SCRATCH_BYTES\s+\((\d+)ll\s*<<\s*(\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == stg_pkg.STATIC_SCRATCH_BYTES
+    lib = stg.load_library()
+    a = _t([1 << 22, 128])
+    g = _t([1 << 24, 128], data=0x2000)
+    rc = lib.tile_gather_backward_static(ctypes.byref(a), ctypes.c_void_p(0x3000), 1 << 24, _i64([64, 128]), None, 0,
+                                         ctypes.byref(g), None)
+    assert rc == 3 and b"static array" in lib.stg_last_error()
