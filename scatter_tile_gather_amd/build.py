@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libstg.so")
-SOURCES = ["common.hip", "gather_scatter.hip", "copy.hip", "ragged.hip", "gemm.hip", "gemm_scaled.hip", "gather_backward_static.hip"]
+SOURCES = ["common.hip", "gather_scatter.hip", "copy.hip", "ragged.hip", "gemm.hip", "gemm_scaled.hip", "gemm_scaled_general.hip", "gather_backward_static.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -618,24 +618,25 @@ extern "C" int gemm_scaled(const void* A, int32_t a_fmt, int64_t lda, const void
   const char* name = "gemm_scaled";
   auto known = [](int32_t f) { return f == STG_LP_E4M3 || f == STG_LP_E5M2 || f == STG_LP_E2M1; };
   if (!known(a_fmt) || !known(b_fmt)) return fail(STG_ERR_UNSUPPORTED, "%s: unknown operand format", name);
-  if ((a_fmt == STG_LP_E2M1) != (b_fmt == STG_LP_E2M1))
-    return fail(STG_ERR_UNSUPPORTED, "%s: fp4 operands pair only with fp4 operands here", name);
   if (scale_fmt != STG_SC_E8M0 && scale_fmt != STG_SC_E4M3)
     return fail(STG_ERR_UNSUPPORTED, "%s: unknown scale format", name);
-  if (scale_fmt == STG_SC_E4M3)
-    return fail(STG_ERR_UNSUPPORTED, "%s: e4m3 scales are not powers of two; the scaled MFMA takes e8m0 only", name);
   if (M < 0 || N < 0 || K < 0) return fail(STG_ERR_INVALID, "%s: negative size", name);
-  if (block < 32 || (block & (block - 1)))
-    return fail(STG_ERR_UNSUPPORTED, "%s: block must be 32 times a power of two", name);
+  if (block < 1) return fail(STG_ERR_INVALID, "%s: block must be >= 1", name);
   if (K % block) return fail(STG_ERR_INVALID, "%s: K %lld is not a multiple of the block %lld", name, (long long)K,
                              (long long)block);
-  const int bits = a_fmt == STG_LP_E2M1 ? 4 : 8;
-  const int64_t row_bytes = K * bits / 8;
-  if (lda < row_bytes || ldb < row_bytes || lds_a < K / block || lds_b < K / block || ldc < N ||
+  const int bits = a_fmt == STG_LP_E2M1 ? 4 : 8, bits_b = b_fmt == STG_LP_E2M1 ? 4 : 8;
+  if (lda < (K * bits + 7) / 8 || ldb < (K * bits_b + 7) / 8 || lds_a < K / block || lds_b < K / block || ldc < N ||
       (acc && ldacc < N))
     return fail(STG_ERR_INVALID, "%s: row strides must cover the rows", name);
   if (M == 0 || N == 0) return STG_OK;
   if (!C || (K > 0 && (!A || !Bt || !a_scale || !b_scale))) return fail(STG_ERR_INVALID, "%s: null operand", name);
+  // the scaled MFMA takes e8m0 scales per 32 K values of two operands of one
+  // width; every other case goes to the general path (values scaled while
+  // staged, bf16 MFMA)
+  const bool mfma_path = scale_fmt == STG_SC_E8M0 && block >= 32 && (block & (block - 1)) == 0 && bits == bits_b;
+  if (!mfma_path)
+    return gemm_scaled_general(A, a_fmt, lda, a_scale, lds_a, Bt, b_fmt, ldb, b_scale, lds_b, scale_fmt, block, acc,
+                               ldacc, C, ldc, M, N, K, as_stream(stream));
   if ((int64_t)kSBM * lda + 256 >= kMaxOffset32 || (int64_t)kSBN * ldb + 256 >= kMaxOffset32 ||
       M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2 ||
       (M - 1) * lds_a + K / block + 64 >= kMaxOffset32 || (N - 1) * lds_b + K / block + 64 >= kMaxOffset32)

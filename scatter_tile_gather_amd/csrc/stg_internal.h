@@ -164,4 +164,12 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t w, uint32_t total) {
 __device__ __forceinline__ uint32_t div_small(uint32_t n, uint32_t magic) { return __umulhi(n << 1, magic); }
 inline uint32_t div_magic(uint32_t d) { return (uint32_t)(((uint64_t(1) << 31) + d - 1) / d); }
 
+// Block-scaled GEMM for the operand pairs, scale formats and blocks the
+// scaled MFMA does not take (gemm_scaled_general.hip); arguments as
+// gemm_scaled's, already checked by it.
+int gemm_scaled_general(const void* A, int32_t a_fmt, int64_t lda, const void* a_scale, int64_t lds_a,
+                        const void* Bt, int32_t b_fmt, int64_t ldb, const void* b_scale, int64_t lds_b,
+                        int32_t scale_fmt, int64_t block, const float* acc, int64_t ldacc, float* C, int64_t ldc,
+                        int64_t M, int64_t N, int64_t K, hipStream_t s);
+
 }  // namespace stg

@@ -1,21 +1,27 @@
 """GPU parity of gemm_scaled against the fp64 CPU oracle.
 
-Tolerances, from the arithmetic and from a measured property of the scaled
-MFMA:
- * fp4 (e2m1) operands: every product of two decoded values and two e8m0
-   scales is exact in fp32, so the fp32 sum of K terms in any order is within
-   gamma_K * sum|terms| (gamma_K = K u / (1 - K u), u = 2^-24) of the exact
-   sum; one more rounding covers the accumulator input.
- * fp8 operands: v_mfma_scale_f32_32x32x64_f8f6f4 does not sum fp8 products
-   at fp32 precision.  Over full-range random codes (64 <= K <= 2048, uniform
-   and random scales) its error reached 2^-11.8 of sum|terms|, independent of
-   K, i.e. it arises inside one 64-value instruction.  The bound used is
-   (2^-10 + gamma_K) * sum|terms|: 4x that measurement, and still 64 times
-   below the half-ulp (2^-4) that rounding an input to e4m3 costs.
- * Operands whose every partial sum is exact in 14 bits (values +-1, +-2,
-   scales 2^-1 .. 2^2) must come out bit-exact in every format: that pins the
+Tolerances, from the arithmetic of each path:
+ * General path (e4m3 scales, blocks that are not 32 x 2^n, fp4 x fp8 pairs):
+   values are scaled exactly while staged and the bf16 MFMA sums their exact
+   products in fp32, so the error is within gamma_K * sum|terms| (gamma_K =
+   K u / (1 - K u), u = 2^-24), plus one rounding of the accumulator input.
+ * Scaled-MFMA path (e8m0 scales per 32 x 2^n values, fp8 x fp8 or fp4 x
+   fp4): v_mfma_scale_f32_32x32x64_f8f6f4 does not add products at fp32
+   precision.  Its rule, pinned by test_scaled_mfma_group_rule below: the
+   products of each group of 8 consecutive K values are cut (toward zero) to
+   the grid 2^(E - 13), E the exponent of the group's largest product, and
+   summed exactly; the group sums are then accumulated in fp32.  A product
+   has at most 8 significant bits, so the group's largest product is exact and
+   each of the other 7 loses less than 2^(E - 13) <= 2^-13 max|product|.  The
+   bound is therefore sum over groups of 7 * 2^-13 * max|product of the group|
+   plus gamma_K * sum|terms| (the group sums' fp32 accumulation), at most
+   (7 * 2^-13 + gamma_K) * sum|terms|.  fp4 products span at most a factor
+   144 < 2^13 inside a group (scales are constant over 32 values), so for fp4
+   the first term is zero.
+ * Exact cases: operands whose products are exact on every group's grid and
+   whose sums fit 24 bits come out bit-exact (both paths); they pin the
    operand layout and which scale meets which K block.
-sum|terms| comes from the oracle applied to the sign-cleared codes.
+sum|terms| and the group maxima come from the oracle's decoded values.
 """
 import numpy as np
 import pytest
@@ -41,34 +47,86 @@ def codes(rng, shape, fmt):
 
 
 def pack(c, fmt):
-    return (c[:, 0::2] & 0xF) | ((c[:, 1::2] & 0xF) << 4) if fmt == "e2m1" else c
+    if fmt != "e2m1":
+        return c
+    if c.shape[1] % 2:  # odd K: the last byte's high nibble is padding
+        c = np.concatenate([c, np.zeros((c.shape[0], 1), np.uint8)], axis=1)
+    return (c[:, 0::2] & 0xF) | ((c[:, 1::2] & 0xF) << 4)
+
+
+def mfma_path(fa, fb, block, scale_fmt):
+    """True when gemm_scaled runs on the scaled MFMA (e8m0 scales, blocks of
+    32 times a power of two, operands of one width); else the general path."""
+    return scale_fmt == "e8m0" and block >= 32 and block & (block - 1) == 0 and (fa == "e2m1") == (fb == "e2m1")
+
+
+def scale_codes(rng, shape, scale_fmt, lo=118, hi=136):
+    """e8m0 bytes in [lo, hi); e4m3 codes 2^-2 .. 2^2 x (1 + m/8), no NaN."""
+    if scale_fmt == "e8m0":
+        return rng.integers(lo, hi, shape).astype(np.uint8)
+    return rng.integers(0x28, 0x48, shape).astype(np.uint8)
 
 
 def unsign(c, fmt):
     return c & (0x7 if fmt == "e2m1" else 0x7F)
 
 
-def run_case(stg, orc, M, N, K, block, fa, fb, seed, with_acc=False, pad=0, scale_lo=118, scale_hi=136):
+def unsign_scale(s, scale_fmt):
+    return s & 0x7F if scale_fmt == "e4m3" else s
+
+
+_LUT = {}
+
+
+def values(orc, codes_, fmt, is_scale=False):
+    """Exact values of operand codes (one code per element, e2m1 unpacked) or
+    of scale bytes, from the oracle's decoders."""
+    key = (fmt, is_scale)
+    if key not in _LUT:
+        dec = orc.decode_scale if is_scale else orc.decode_lowp
+        _LUT[key] = dec(np.arange(256 if (is_scale or fmt != "e2m1") else 16, dtype=np.uint8), fmt)
+    return _LUT[key][codes_]
+
+
+def group_bound(orc, ca, fa, sa, cb, fb, sb, block, s_fmt="e8m0"):
+    """sum over groups of 8 consecutive K values of 7 * 2^-13 * max|product|,
+    (M, N): the scaled MFMA's cut of small products (module docstring)."""
+    K = ca.shape[1]
+    A = values(orc, ca, fa) * np.repeat(values(orc, sa, s_fmt, True), block, axis=1)
+    B = values(orc, cb, fb) * np.repeat(values(orc, sb, s_fmt, True), block, axis=1)
+    G = K // 8
+    out = np.zeros((A.shape[0], B.shape[0]))
+    for g in range(G):
+        prod = np.abs(A[:, None, 8 * g:8 * g + 8] * B[None, :, 8 * g:8 * g + 8])
+        out += prod.max(axis=2)
+    return 7 * 2.0 ** -13 * out
+
+
+def run_case(stg, orc, M, N, K, block, fa, fb, seed, with_acc=False, pad=0, scale_lo=118, scale_hi=136,
+             scale_fmt="e8m0"):
     rng = np.random.default_rng(seed)
     ca, cb = codes(rng, (M, K), fa), codes(rng, (N, K), fb)
     A, Bt = pack(ca, fa), pack(cb, fb)
-    sa = rng.integers(scale_lo, scale_hi, (M, K // block)).astype(np.uint8)
-    sb = rng.integers(scale_lo, scale_hi, (N, K // block)).astype(np.uint8)
+    sa = scale_codes(rng, (M, K // block), scale_fmt, scale_lo, scale_hi)
+    sb = scale_codes(rng, (N, K // block), scale_fmt, scale_lo, scale_hi)
     acc = rng.standard_normal((M, N)).astype(np.float32) if with_acc else None
     # padded operand rows (strides beyond the row), sentinel-filled output padding
     Ad = to_dev(np.pad(A, ((0, 0), (0, pad)), constant_values=0x5A))[:, :A.shape[1]]
     Bd = to_dev(np.pad(Bt, ((0, 0), (0, pad)), constant_values=0x5A))[:, :Bt.shape[1]]
     store = torch.full((M, N + pad), 7.0, dtype=torch.float32, device="cuda:0")
-    stg.gemm_scaled(Ad, fa, to_dev(sa), Bd, fb, to_dev(sb), K, block,
+    stg.gemm_scaled(Ad, fa, to_dev(sa), Bd, fb, to_dev(sb), K, block, scale_fmt=scale_fmt,
                     acc=None if acc is None else to_dev(acc), out=store[:, :N])
     torch.cuda.synchronize()
     full = to_host(store)
     got = full[:, :N].astype(np.float64)
-    want = orc.gemm_scaled_f64(A, fa, sa, Bt, fb, sb, K, block, acc=acc)
-    mag = orc.gemm_scaled_f64(pack(unsign(ca, fa), fa), fa, sa, pack(unsign(cb, fb), fb), fb, sb, K, block)
+    want = orc.gemm_scaled_f64(A, fa, sa, Bt, fb, sb, K, block, s_fmt=scale_fmt, acc=acc)
+    mag = orc.gemm_scaled_f64(pack(unsign(ca, fa), fa), fa, unsign_scale(sa, scale_fmt), pack(unsign(cb, fb), fb), fb,
+                              unsign_scale(sb, scale_fmt), K, block, s_fmt=scale_fmt)
     u = 2.0 ** -24
-    gk = K * u / (1 - K * u) + (0.0 if fa == "e2m1" else 2.0 ** -10)
+    gk = K * u / (1 - K * u)
     tol = gk * mag + (np.abs(acc.astype(np.float64)) * u if acc is not None else 0) + 1e-30
+    if mfma_path(fa, fb, block, scale_fmt):
+        tol = tol + group_bound(orc, ca, fa, sa, cb, fb, sb, block, scale_fmt)
     err = np.abs(got - want)
     assert np.all(err <= tol), (float((err - tol).max()), float(err.max()))
     if pad:
@@ -162,9 +220,14 @@ def test_scaled_large_sampled(stg, orc):
     cols = np.concatenate([np.arange(0, 64), np.arange(N - 64, N), rng.integers(0, N, 64)])
     want = orc.gemm_scaled_f64(ca[rows], "e4m3", sa[rows], cb[cols], "e4m3", sb[cols], K, 32)
     mag = orc.gemm_scaled_f64(ca[rows] & 0x7F, "e4m3", sa[rows], cb[cols] & 0x7F, "e4m3", sb[cols], K, 32)
-    tol = (K * 2.0 ** -24 / (1 - K * 2.0 ** -24) + 2.0 ** -10) * mag + 1e-30
+    tol = (K * 2.0 ** -24 / (1 - K * 2.0 ** -24) + 7 * 2.0 ** -13) * mag + 1e-30
     err = np.abs(C[np.ix_(rows, cols)].astype(np.float64) - want)
     assert np.all(err <= tol), float((err - tol).max())
+    # the per-group bound on a corner of the sample
+    r, c = rows[:32], cols[:32]
+    tight = K * 2.0 ** -24 / (1 - K * 2.0 ** -24) * mag[:32, :32] + group_bound(orc, ca[r], "e4m3", sa[r], cb[c], "e4m3",
+                                                                                sb[c], 32) + 1e-30
+    assert np.all(err[:32, :32] <= tight), float((err[:32, :32] - tight).max())
 
 
 @pytest.mark.parametrize("base", [1, 3, 8, 15])
@@ -230,7 +293,8 @@ def test_scaled_output_may_alias_the_accumulator(stg, orc):
     want = orc.gemm_scaled_f64(ca, "e5m2", sa, cb, "e5m2", sb, K, 64, acc=acc)
     mag = orc.gemm_scaled_f64(ca & 0x7F, "e5m2", sa, cb & 0x7F, "e5m2", sb, K, 64)
     u = 2.0 ** -24
-    tol = (K * u / (1 - K * u) + 2.0 ** -10) * mag + np.abs(acc.astype(np.float64)) * u + 1e-30
+    tol = K * u / (1 - K * u) * mag + np.abs(acc.astype(np.float64)) * u + 1e-30
+    tol = tol + group_bound(orc, ca, "e5m2", sa, cb, "e5m2", sb, 64)
     assert np.all(np.abs(to_host(inout).astype(np.float64) - want) <= tol)
 
 
@@ -271,3 +335,135 @@ def test_scaled_binding_rejects_undersized_tensors(stg):
     # fp4: 128 bytes hold 256 values
     stg.gemm_scaled(A, "e2m1", u8(64, 8), Bt, "e2m1", u8(32, 8), 256, 32)
     torch.cuda.synchronize()
+
+
+# ---- general path: e4m3 scales, any block dividing K, fp4 x fp8 pairs ------
+#
+# Values are scaled exactly while staged and summed by the bf16 MFMA in fp32,
+# so the bound is gamma_K * sum|terms| (plus one rounding of the accumulator
+# input) for every format pair: no term for reduced internal precision.
+
+EXACT_SCALES = {"e8m0": [126, 127, 128, 129], "e4m3": [0x30, 0x38, 0x3C, 0x40]}  # 0.5, 1, 1.5, 2
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e2m1"), ("e2m1", "e5m2"), ("e4m3", "e4m3"), ("e5m2", "e2m1"),
+                                   ("e2m1", "e2m1")])
+@pytest.mark.parametrize("scale_fmt,block,shape", [("e4m3", 32, (300, 520, 256)), ("e4m3", 16, (257, 259, 96)),
+                                                   ("e8m0", 16, (65, 97, 128)), ("e4m3", 1, (33, 70, 40)),
+                                                   ("e4m3", 3, (130, 300, 99)), ("e8m0", 48, (260, 513, 144)),
+                                                   ("e4m3", 96, (70, 40, 192))])
+def test_scaled_general_exact(stg, orc, fa, fb, scale_fmt, block, shape):
+    """Values +-1, +-2 and scales 0.5, 1, 1.5, 2: every partial sum is exact
+    in fp32, so the general path must match the oracle bit for bit.  This pins
+    which scale meets which value (blocks of 1, 3, 16, 48, 96 that do not
+    split into 32-value groups), the FP4 nibble order next to fp8 bytes, and
+    the ragged M, N and K tails (K = 99 and 40 end inside a 32-value step;
+    fp4 with K = 99 has an odd row length)."""
+    M, N, K = shape
+    if mfma_path(fa, fb, block, scale_fmt):
+        pytest.skip("runs on the scaled MFMA (covered above)")
+    rng = np.random.default_rng(M + N + K + block)
+    ca = np.array(EXACT_CODES[fa], np.uint8)[rng.integers(0, 4, (M, K))]
+    cb = np.array(EXACT_CODES[fb], np.uint8)[rng.integers(0, 4, (N, K))]
+    sa = np.array(EXACT_SCALES[scale_fmt], np.uint8)[rng.integers(0, 4, (M, K // block))]
+    sb = np.array(EXACT_SCALES[scale_fmt], np.uint8)[rng.integers(0, 4, (N, K // block))]
+    say("gemm_scaled general exact", fa, fb, scale_fmt, "block", block, shape)
+    C = to_host(stg.gemm_scaled(to_dev(pack(ca, fa)), fa, to_dev(sa), to_dev(pack(cb, fb)), fb, to_dev(sb), K, block,
+                                scale_fmt=scale_fmt))
+    np.testing.assert_array_equal(C.astype(np.float64),
+                                  orc.gemm_scaled_f64(pack(ca, fa), fa, sa, pack(cb, fb), fb, sb, K, block,
+                                                      s_fmt=scale_fmt))
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e2m1", "e4m3"), ("e5m2", "e2m1"),
+                                   ("e2m1", "e2m1")])
+@pytest.mark.parametrize("scale_fmt,block", [("e4m3", 16), ("e4m3", 32), ("e8m0", 16), ("e4m3", 5)])
+def test_scaled_general_random(stg, orc, fa, fb, scale_fmt, block):
+    """Full-range codes, an accumulator input and padded strides, on a shape
+    with ragged tails in M, N and K: within gamma_K * sum|terms|."""
+    K = 320 if block != 5 else 325
+    if mfma_path(fa, fb, block, scale_fmt):
+        pytest.skip("runs on the scaled MFMA (covered above)")
+    say("gemm_scaled general random", fa, fb, scale_fmt, "block", block)
+    run_case(stg, orc, 131, 517, K, block, fa, fb, seed=block + len(fa + fb), with_acc=True, pad=3,
+             scale_fmt=scale_fmt)
+
+
+def test_scaled_general_large_sampled(stg, orc):
+    """(2048, 2304, 4096) e4m3 x e4m3 with e4m3 scales per 16 values (a
+    layout the scaled MFMA cannot take): sampled rows and columns including
+    the last tile's, within gamma_K * sum|terms|."""
+    M, N, K, block = 2048, 2304, 4096, 16
+    rng = np.random.default_rng(13)
+    ca, cb = codes(rng, (M, K), "e4m3"), codes(rng, (N, K), "e4m3")
+    sa, sb = scale_codes(rng, (M, K // block), "e4m3"), scale_codes(rng, (N, K // block), "e4m3")
+    say("gemm_scaled general large (2048,2304,4096) e4m3, e4m3 scales per 16, sampled")
+    C = to_host(stg.gemm_scaled(to_dev(ca), "e4m3", to_dev(sa), to_dev(cb), "e4m3", to_dev(sb), K, block,
+                                scale_fmt="e4m3"))
+    rows = np.concatenate([np.arange(0, 32), np.arange(M - 32, M), rng.integers(0, M, 32)])
+    cols = np.concatenate([np.arange(0, 32), np.arange(N - 32, N), rng.integers(0, N, 32)])
+    want = orc.gemm_scaled_f64(ca[rows], "e4m3", sa[rows], cb[cols], "e4m3", sb[cols], K, block, s_fmt="e4m3")
+    mag = orc.gemm_scaled_f64(ca[rows] & 0x7F, "e4m3", sa[rows] & 0x7F, cb[cols] & 0x7F, "e4m3", sb[cols] & 0x7F, K,
+                              block, s_fmt="e4m3")
+    tol = K * 2.0 ** -24 / (1 - K * 2.0 ** -24) * mag + 1e-30
+    err = np.abs(C[np.ix_(rows, cols)].astype(np.float64) - want)
+    assert np.all(err <= tol), float((err - tol).max())
+
+
+# ---- the scaled MFMA's summation rule --------------------------------------
+
+def _e4m3(e, m=0):
+    """e4m3 code of (1 + m/8) 2^e (normal) or 2^e (subnormal, e >= -9)."""
+    return (1 << (e + 9)) if e < -6 else ((e + 7) << 3) | m
+
+
+@pytest.mark.parametrize("label,terms,expect", [
+    # one product of 1 at K position 0; products of other sizes at other positions
+    ("2^-13 in the group is kept", {0: (0, 0, 0), 1: (-4, 0, -9)}, 1 + 2.0 ** -13),
+    ("2^-14 in the group is cut", {0: (0, 0, 0), 1: (-5, 0, -9)}, 1.0),
+    ("3 x 2^-14 in the group cuts to 2^-13", {0: (0, 0, 0), 1: (-4, 4, -9)}, 1 + 2.0 ** -13),
+    ("-2^-14 in the group cuts toward zero", {0: (0, 0, 0), 1: (-5, 0x10, -9)}, 1.0),
+    ("2^-14 in the next group is kept", {0: (0, 0, 0), 8: (-5, 0, -9)}, 1 + 2.0 ** -14),
+    ("groups are K 0..7, 8..15: position 7 and 8", {7: (0, 0, 0), 8: (-5, 0, -9)}, 1 + 2.0 ** -14),
+    ("two 2^-14 are cut one by one", {0: (-5, 0, -9), 1: (-5, 0, -9), 2: (0, 0, 0)}, 1.0),
+    ("eight 2^-14 of their own group add up", {0: (0, 0, 0), **{j: (-5, 0, -9) for j in range(8, 16)}}, 1 + 2.0 ** -11),
+])
+def test_scaled_mfma_group_rule(stg, label, terms, expect):
+    """The rule the fp8 tolerance is derived from (module docstring), pinned on
+    products with one nonzero row and column: A[0, k] = (1 + m/8) 2^e times
+    B[0, k] = 2^eb, unit e8m0 scales, K = 64 (one MFMA step).  A term is
+    (e, m_bits_or_sign, eb); m 0x10 marks a negative A value."""
+    K = 64
+    A = np.zeros((32, K), np.uint8)
+    Bt = np.zeros((32, K), np.uint8)
+    for k, (e, m, eb) in terms.items():
+        A[0, k] = _e4m3(e, m & 7) | (0x80 if m & 0x10 else 0)
+        Bt[0, k] = _e4m3(eb)
+    ones = np.full((32, K // 32), 127, np.uint8)
+    say("scaled MFMA summation rule:", label)
+    C = to_host(stg.gemm_scaled(to_dev(A), "e4m3", to_dev(ones), to_dev(Bt), "e4m3", to_dev(ones), K, 32))
+    assert float(C[0, 0]) == expect
+    assert not C[1:].any() and not C[0, 1:].any()
+
+
+def test_scaled_mfma_exact_at_the_group_boundary(stg, orc):
+    """fp8 e4m3 operands with exponents -2 .. 1 and every mantissa: a product
+    (1 + m/8)(1 + n/8) 2^(a+b) has its last bit at 2^(a+b-6), and a group's
+    largest product is below 2^4, so every product lies on its group's grid
+    2^(E - 13) exactly when E - (a + b) <= 7 -- which holds here with
+    equality at the extremes.  Scales 2^0 and 2^1 keep all sums within 24
+    bits (last bit 2^-10, |sum| < 2^14), so the result must be bit-exact: a
+    coarser in-group sum than the rule above would show here."""
+    M, N, K = 300, 280, 512
+    rng = np.random.default_rng(21)
+
+    def cds(shape):
+        return ((rng.integers(5, 9, shape) << 3) | rng.integers(0, 8, shape) | (rng.integers(0, 2, shape) << 7)).astype(
+            np.uint8)
+
+    ca, cb = cds((M, K)), cds((N, K))
+    sa = rng.integers(127, 129, (M, K // 32)).astype(np.uint8)
+    sb = np.full((N, K // 32), 127, np.uint8)
+    say("scaled MFMA exact at the group boundary (300, 280, 512) e4m3")
+    C = to_host(stg.gemm_scaled(to_dev(ca), "e4m3", to_dev(sa), to_dev(cb), "e4m3", to_dev(sb), K, 32))
+    np.testing.assert_array_equal(C.astype(np.float64), orc.gemm_scaled_f64(ca, "e4m3", sa, cb, "e4m3", sb, K, 32))
