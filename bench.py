@@ -674,6 +674,26 @@ def run_gemm_scaled(stg, inputs, steps, warmup):
                 "TFLOP/s", f"one {pr}-row panel of the {M}-row output (fp64 sums of decoded values), extrapolated "
                            f"to the whole GEMM as a rate")
         del A, Bt, sa, sb, C
+    # the general path: e4m3 scales per 16 values (no scaled-MFMA layout),
+    # values scaled while staged, bf16 MFMA
+    g = inputs.scaled_gemm(M, N, K, "e4m3", block=16)
+    rng = np.random.default_rng(1016)
+    sa_h = rng.integers(0x28, 0x48, g["sa"].shape).astype(np.uint8)  # e4m3 scales 2^-2 .. 2^2 x (1 + m/8)
+    sb_h = rng.integers(0x28, 0x48, g["sb"].shape).astype(np.uint8)
+    A, Bt, sa, sb = _dev(g["A"]), _dev(g["Bt"]), _dev(sa_h), _dev(sb_h)
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+    fn = lambda: stg.gemm_scaled(A, "e4m3", sa, Bt, "e4m3", sb, K, 16, scale_fmt="e4m3", out=C)
+    fn()
+    ms = time_fn(fn, steps, warmup)
+    kern = traced_kernel_ms(stg, fn, steps)
+    flop = 2.0 * M * N * K
+    tf = flop / (ms * 1e-3) / 1e12
+    out["gemm_scaled_general_fp8_e4m3scales"] = {
+        "workload": "block-scaled GEMM e4m3 x e4m3 with e4m3 scales per 16 K values (general path: values scaled "
+                    "while staged, bf16 MFMA), A(8191,4096) Bt(8193,4096), fp32 clipped output",
+        "value": round(tf, 1), "unit": "TFLOP/s", "ms": round(ms, 4), "flop": flop,
+        "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4), "kernel_ms": kern}
+    del A, Bt, sa, sb, C
     return out
 
 

@@ -39,11 +39,14 @@
 //  * Clipped fp32 epilogue adding the optional accumulator input.
 #include "gemm_common.h"
 
+#include <type_traits>
+
 namespace stg {
 namespace {
 
 typedef __bf16 bf16x8_g __attribute__((ext_vector_type(8)));
 typedef float f32x16_g __attribute__((ext_vector_type(16)));
+typedef float f32x2_g __attribute__((ext_vector_type(2)));
 
 constexpr int kGBM = 256, kGBN = 256, kGBK = 32;
 constexpr int kGWM = 2, kGWN = 4, kGNT = kGWM * kGWN * 64;
@@ -95,14 +98,43 @@ __device__ __forceinline__ float decode_scale(uint32_t b, int sf) {
   return b ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
 }
 
-// Codes of one lane's 16 K values of one row: 16 bytes (fp8) or 8 (fp4).
+// 16 codes of one format times one scale, as 16 bf16 values.  The gfx950
+// conversions (v_cvt_scalef32_pk_f32_fp8 / _bf8 / _fp4) decode two codes
+// exactly and multiply them by 2^(exponent of their f32 scale operand) --
+// only the exponent is used -- so `pow2` carries the scale's power of two
+// and `mult` the rest (an e4m3 scale's significand and sign, a zero or NaN
+// scale), applied by an exact fp32 multiply before the bf16 rounding.
+template <int FMT, int E>
+__device__ __forceinline__ uint32_t decode2(const u32x4& w, float pow2, float mult) {
+  f32x2_g f;
+  if constexpr (FMT == STG_LP_E4M3)
+    f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[E >> 2], pow2, ((E >> 1) & 1) != 0);
+  else if constexpr (FMT == STG_LP_E5M2)
+    f = __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(w[E >> 2], pow2, ((E >> 1) & 1) != 0);
+  else
+    f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[E >> 3], pow2, (E >> 1) & 3);
+  const __bf16 b0 = (__bf16)(f[0] * mult), b1 = (__bf16)(f[1] * mult);
+  return (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+}
+template <int FMT>
+__device__ __forceinline__ void decode16(const u32x4& w, float pow2, float mult, u32x4 out[2]) {
+  out[0] = (u32x4){decode2<FMT, 0>(w, pow2, mult), decode2<FMT, 2>(w, pow2, mult), decode2<FMT, 4>(w, pow2, mult),
+                   decode2<FMT, 6>(w, pow2, mult)};
+  out[1] = (u32x4){decode2<FMT, 8>(w, pow2, mult), decode2<FMT, 10>(w, pow2, mult), decode2<FMT, 12>(w, pow2, mult),
+                   decode2<FMT, 14>(w, pow2, mult)};
+}
+
+// Codes of one lane's 16 K values of one row (16 bytes of fp8 or 8 of fp4)
+// and the scale byte they share (blocks that are multiples of 16).
 struct Codes {
   u32x4 w;
-  uint32_t s0, s1;  // scale bytes of the first and the last of the 16 values (blocks of 16 or more)
+  uint32_t s;
 };
 
+template <int FA, int FB, bool BLK16>
 __global__ __launch_bounds__(kGNT) void gemm_scaled_general_kernel(GeneralParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int BA = FA == STG_LP_E2M1 ? 4 : 8, BB = FB == STG_LP_E2M1 ? 4 : 8;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / kGWN, wn = wave % kGWN;
   int tm, tn;
@@ -113,84 +145,113 @@ __global__ __launch_bounds__(kGNT) void gemm_scaled_general_kernel(GeneralParams
   // this lane's staging rows: row r of the A tile and of the Bt tile, K
   // values 16h .. 16h+15 of each step
   const int r = tid >> 1, h = tid & 1;
-  const int bits_a = p.fa == STG_LP_E2M1 ? 4 : 8, bits_b = p.fb == STG_LP_E2M1 ? 4 : 8;
-  const int64_t ra = m0 + r, rb = n0 + r;
-  // buffer resources over each operand's rows of this tile (zero past the
-  // matrix) and over the scale matrices
+  // buffer resources over each operand's rows of this tile and over the
+  // scale matrices: offsets past the matrix read as zero
   auto rsrc_rows = [](const char* base, int64_t row0, int64_t rows, int64_t ld, int64_t row_bytes) {
     const int64_t avail = rows > row0 ? (rows - 1 - row0) * ld + row_bytes : 0;
     return make_rsrc(base + (rows > row0 ? row0 * ld : 0), (uint32_t)(avail < (int64_t)kOOB ? avail : kOOB - 1));
   };
-  const int64_t rba = (p.K * bits_a + 7) / 8, rbb = (p.K * bits_b + 7) / 8;
   const int64_t nkb = p.K / p.block;
-  const __amdgpu_buffer_rsrc_t rs_a = rsrc_rows(p.A, m0, p.M, p.lda, rba);
-  const __amdgpu_buffer_rsrc_t rs_b = rsrc_rows(p.B, n0, p.N, p.ldb, rbb);
+  const __amdgpu_buffer_rsrc_t rs_a = rsrc_rows(p.A, m0, p.M, p.lda, (p.K * BA + 7) / 8);
+  const __amdgpu_buffer_rsrc_t rs_b = rsrc_rows(p.B, n0, p.N, p.ldb, (p.K * BB + 7) / 8);
   const __amdgpu_buffer_rsrc_t rs_sa = rsrc_rows(p.sa, m0, p.M, p.lds_a, nkb);
   const __amdgpu_buffer_rsrc_t rs_sb = rsrc_rows(p.sb, n0, p.N, p.lds_b, nkb);
-  const bool in_a = ra < p.M, in_b = rb < p.N;
+  const bool in_a = m0 + r < p.M, in_b = n0 + r < p.N;
   const uint32_t row_a = in_a ? (uint32_t)(r * p.lda) : kOOB, row_b = in_b ? (uint32_t)(r * p.ldb) : kOOB;
   const uint32_t srow_a = in_a ? (uint32_t)(r * p.lds_a) : kOOB, srow_b = in_b ? (uint32_t)(r * p.lds_b) : kOOB;
-  const bool blk16 = p.block % 16 == 0;  // the 16 values of a lane share one scale
 
-  auto load_codes = [&](int kt, const __amdgpu_buffer_rsrc_t& rs, uint32_t row_off, int bits,
-                        const __amdgpu_buffer_rsrc_t& rss, uint32_t srow) {
+  // codes of step kt.  All but the last step lie inside K: one vector load
+  // each.  In the last step the row may end inside a lane's 16 values, and a
+  // vector load there could reach past the matrix's last byte: byte loads up
+  // to the row's end instead (bytes past it read as zero).
+  auto load_codes = [&](auto bits_c, int kt, const __amdgpu_buffer_rsrc_t& rs, uint32_t row_off,
+                        const __amdgpu_buffer_rsrc_t& rss, uint32_t srow, bool last) {
+    constexpr int bits = decltype(bits_c)::value;
     Codes c;
-    const int64_t k = (int64_t)kt * kGBK + 16 * h;
-    const uint32_t off = row_off == kOOB ? kOOB : row_off + (uint32_t)(k * bits / 8);
+    const uint32_t k = (uint32_t)kt * kGBK + 16 * h;
+    const uint32_t off = row_off == kOOB ? kOOB : row_off + k * bits / 8;
     c.w = (u32x4){0, 0, 0, 0};
-    if (k + 16 <= p.K) {
-      if (bits == 8) {
+    if (!last || (int64_t)k + 16 <= p.K) {
+      if constexpr (bits == 8) {
         c.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
       } else {
         const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
         c.w = (u32x4){v[0], v[1], 0, 0};
       }
-    } else if (k < p.K && row_off != kOOB) {
-      // the row ends inside these 16 values: byte loads up to the row's last
-      // byte, so no load reaches past the matrix
+    } else if ((int64_t)k < p.K && row_off != kOOB) {
       const int nb = (int)(((p.K - k) * bits + 7) / 8);
+      uint32_t by[16];
 #pragma unroll
-      for (int b = 0; b < 16; ++b)
-        if (b < nb) c.w[b >> 2] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, off + b, 0, 0) << (8 * (b & 3));
+      for (int b = 0; b < 16; ++b) by[b] = __builtin_amdgcn_raw_buffer_load_b8(rs, b < nb ? off + b : kOOB, 0, 0);
+#pragma unroll
+      for (int b = 0; b < 16; ++b) c.w[b >> 2] |= by[b] << (8 * (b & 3));
+      // fp4 with an odd number of values left: the last byte's high nibble
+      // is past K
+      if (bits == 4 && ((p.K - k) & 1)) c.w[(nb - 1) >> 2] &= ~(0xF0u << (8 * ((nb - 1) & 3)));
     }
-    c.s0 = c.s1 = 0;
-    if (blk16 && k < p.K && srow != kOOB)
-      c.s0 = c.s1 = __builtin_amdgcn_raw_buffer_load_b8(rss, srow + (uint32_t)k / (uint32_t)p.block, 0, 0);
+    c.s = 0;
+    if constexpr (BLK16)
+      c.s = __builtin_amdgcn_raw_buffer_load_b8(
+          rss, (srow == kOOB || (int64_t)k >= p.K) ? kOOB : srow + k / (uint32_t)p.block, 0, 0);
     return c;
   };
-  // scaled bf16 values of one lane's 16 K values into LDS row `row` of the
-  // operand region at `region` (zero at K and beyond)
-  auto decode_store = [&](int kt, const Codes& c, int fmt, int bits, const __amdgpu_buffer_rsrc_t& rss,
-                          uint32_t srow, char* region) {
-    const int64_t k0 = (int64_t)kt * kGBK + 16 * h;
+
+  // scaled bf16 values of one lane's 16 K values into LDS row r of the
+  // operand region (zero at K and beyond)
+  auto decode_store = [&](auto fmt_c, int kt, const Codes& c, const __amdgpu_buffer_rsrc_t& rss, uint32_t srow,
+                          char* region) {
+    constexpr int fmt = decltype(fmt_c)::value;
     u32x4 out[2];
-    float sc = decode_scale(c.s0, p.sf);
-    int64_t sidx = -1, next = 0;  // general blocks: scale index of the current value, first K of the next block
-    if (!blk16 && k0 < p.K) {
-      sidx = (uint32_t)k0 / (uint32_t)p.block;
-      next = (sidx + 1) * p.block;
-      sc = decode_scale(srow == kOOB ? 0u : __builtin_amdgcn_raw_buffer_load_b8(rss, srow + (uint32_t)sidx, 0, 0),
-                        p.sf);
-    }
-#pragma unroll
-    for (int e = 0; e < 16; e += 2) {
-      float v[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int ee = e + u;
-        const uint32_t code = bits == 8 ? (c.w[ee >> 2] >> (8 * (ee & 3))) & 0xFF : (c.w[ee >> 3] >> (4 * (ee & 7))) & 0xF;
-        const int64_t k = k0 + ee;
-        if (!blk16 && k < p.K && k >= next) {  // k == next: the next block starts here
-          sidx += 1;
-          next += p.block;
-          sc = decode_scale(srow == kOOB ? 0u : __builtin_amdgcn_raw_buffer_load_b8(rss, srow + (uint32_t)sidx, 0, 0),
-                            p.sf);
-        }
-        v[u] = k < p.K ? decode_code(code, fmt) * sc : 0.f;
+    if constexpr (BLK16) {
+      // one scale for the 16 values; codes past K were loaded as zero
+      float pow2, mult;
+      if (p.sf == STG_SC_E8M0) {
+        // 2^(b-127); b = 0 as 2^-126 * 0.5 (an exponent field of 0 is not a
+        // power of two for the conversion), 0xFF as NaN
+        pow2 = c.s ? __uint_as_float(c.s << 23) : 0x1p-126f;
+        mult = c.s == 0xFF ? __uint_as_float(0x7FC00000u) : c.s ? 1.f : 0.5f;
+      } else {
+        const float sc = decode_scale(c.s, STG_SC_E4M3);  // normal f32, zero or NaN
+        pow2 = __uint_as_float(__float_as_uint(sc) & 0x7F800000u);
+        mult = __uint_as_float((__float_as_uint(sc) & 0x807FFFFFu) | 0x3F800000u);
+        if (sc == 0.f) pow2 = 1.f, mult = 0.f;
+        if (sc != sc) pow2 = 1.f, mult = sc;
       }
-      const __bf16 b0 = (__bf16)v[0], b1 = (__bf16)v[1];
-      out[e >> 3][(e >> 1) & 3] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
-                                  ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+      decode16<fmt>(c.w, pow2, mult, out);
+    } else {
+      // blocks that do not hold whole 16-value runs: each value finds its
+      // scale (the block boundaries inside the run, at most 16)
+      constexpr int bits = fmt == STG_LP_E2M1 ? 4 : 8;
+      const int64_t k0 = (int64_t)kt * kGBK + 16 * h;
+      float sc = 0.f;
+      int64_t sidx = -1, next = 0;  // scale index of the current value, first K of the next block
+      if (k0 < p.K) {
+        sidx = (uint32_t)k0 / (uint32_t)p.block;
+        next = (sidx + 1) * p.block;
+        sc = decode_scale(srow == kOOB ? 0u : __builtin_amdgcn_raw_buffer_load_b8(rss, srow + (uint32_t)sidx, 0, 0),
+                          p.sf);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        float v[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int ee = e + u;
+          const uint32_t code =
+              bits == 8 ? (c.w[ee >> 2] >> (8 * (ee & 3))) & 0xFF : (c.w[ee >> 3] >> (4 * (ee & 7))) & 0xF;
+          const int64_t k = k0 + ee;
+          if (k < p.K && k >= next) {  // k == next: the next block starts here
+            sidx += 1;
+            next += p.block;
+            sc = decode_scale(
+                srow == kOOB ? 0u : __builtin_amdgcn_raw_buffer_load_b8(rss, srow + (uint32_t)sidx, 0, 0), p.sf);
+          }
+          v[u] = k < p.K ? decode_code(code, fmt) * sc : 0.f;
+        }
+        const __bf16 b0 = (__bf16)v[0], b1 = (__bf16)v[1];
+        out[e >> 3][(e >> 1) & 3] =
+            (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+      }
     }
     *(u32x4*)(region + r * 64 + (a_phys(r, 2 * h) << 4)) = out[0];
     *(u32x4*)(region + r * 64 + (a_phys(r, 2 * h + 1) << 4)) = out[1];
@@ -206,21 +267,24 @@ __global__ __launch_bounds__(kGNT) void gemm_scaled_general_kernel(GeneralParams
 
   auto stage_a = [&](int kt) { return smem + (kt & 1) * kGStage; };
   auto stage_b = [&](int kt) { return smem + (kt & 1) * kGStage + kGBM * 64; };
+  using IA = std::integral_constant<int, FA>;
+  using IB = std::integral_constant<int, FB>;
+  using BitsA = std::integral_constant<int, BA>;
+  using BitsB = std::integral_constant<int, BB>;
 
-  if (nk > 0) {
-    const Codes ca = load_codes(0, rs_a, row_a, bits_a, rs_sa, srow_a);
-    const Codes cb = load_codes(0, rs_b, row_b, bits_b, rs_sb, srow_b);
-    decode_store(0, ca, p.fa, bits_a, rs_sa, srow_a, stage_a(0));
-    decode_store(0, cb, p.fb, bits_b, rs_sb, srow_b, stage_b(0));
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    Codes ca, cb;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      ca = load_codes(kt + 1, rs_a, row_a, bits_a, rs_sa, srow_a);
-      cb = load_codes(kt + 1, rs_b, row_b, bits_b, rs_sb, srow_b);
-    }
+  // codes are loaded two steps ahead (one global round trip is longer than
+  // a step), into two register sets used alternately
+  Codes qa0, qb0, qa1, qb1;
+  auto load_both = [&](int kt, Codes& qa, Codes& qb) {
+    const bool last = kt == nk - 1;
+    qa = load_codes(BitsA{}, kt, rs_a, row_a, rs_sa, srow_a, last);
+    qb = load_codes(BitsB{}, kt, rs_b, row_b, rs_sb, srow_b, last);
+  };
+  auto decode_both = [&](int kt, const Codes& qa, const Codes& qb) {
+    decode_store(IA{}, kt, qa, rs_sa, srow_a, stage_a(kt));
+    decode_store(IB{}, kt, qb, rs_sb, srow_b, stage_b(kt));
+  };
+  auto mfma_step = [&](int kt) {
     const char* as = stage_a(kt);
     const char* bs = stage_b(kt);
 #pragma unroll
@@ -242,13 +306,44 @@ __global__ __launch_bounds__(kGNT) void gemm_scaled_general_kernel(GeneralParams
         for (int j = 0; j < kGFN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
-    if (more) {
-      // stage (kt + 1) & 1 was last read in step kt - 1, before its barrier
-      decode_store(kt + 1, ca, p.fa, bits_a, rs_sa, srow_a, stage_a(kt + 1));
-      decode_store(kt + 1, cb, p.fb, bits_b, rs_sb, srow_b, stage_b(kt + 1));
-    }
+  };
+  // step kt: load the codes of step kt + 2 into (qa_later, qb_later) -- that
+  // set's codes, of step kt, were decoded in step kt - 1 -- then the MFMAs of
+  // stage kt, then the decode of step kt + 1 from (qa_next, qb_next) into the
+  // other stage, last read in step kt - 1 before its barrier
+  auto step = [&](int kt, Codes& qa_next, Codes& qb_next, Codes& qa_later, Codes& qb_later) {
+    if (kt + 2 < nk) load_both(kt + 2, qa_later, qb_later);
+    mfma_step(kt);
+    if (kt + 1 < nk) decode_both(kt + 1, qa_next, qb_next);
     __syncthreads();
+  };
+  // the same with only whole-vector loads and no end tests, for the steps
+  // whose loads and decodes all lie before the last step
+  auto inner_step = [&](int kt, Codes& qa_next, Codes& qb_next, Codes& qa_later, Codes& qb_later) {
+    qa_later = load_codes(BitsA{}, kt + 2, rs_a, row_a, rs_sa, srow_a, false);
+    qb_later = load_codes(BitsB{}, kt + 2, rs_b, row_b, rs_sb, srow_b, false);
+    mfma_step(kt);
+    decode_both(kt + 1, qa_next, qb_next);
+    __syncthreads();
+  };
+
+  if (nk > 0) {
+    load_both(0, qa0, qb0);
+    if (nk > 1) load_both(1, qa1, qb1);
+    decode_both(0, qa0, qb0);
   }
+  __syncthreads();
+  int kt = 0;
+  // inner steps while kt + 2 < nk - 1, two at a time (the register sets swap)
+  for (; kt + 4 < nk; kt += 2) {
+    inner_step(kt, qa1, qb1, qa0, qb0);
+    inner_step(kt + 1, qa0, qb0, qa1, qb1);
+  }
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, qa1, qb1, qa0, qb0);
+    step(kt + 1, qa0, qb0, qa1, qb1);
+  }
+  if (kt < nk) step(kt, qa1, qb1, qa0, qb0);
 
   // clipped epilogue: lane l, accumulator q of block (i, j) is row
   // 8(q/4) + 4(l/32) + q%4, column l%32 of that 32 x 32 block
@@ -268,6 +363,32 @@ __global__ __launch_bounds__(kGNT) void gemm_scaled_general_kernel(GeneralParams
     }
 }
 
+template <int FA, int FB>
+int launch_general(const GeneralParams& p, int64_t n_wg, hipStream_t s) {
+  static const bool lds_ok =
+      hipFuncSetAttribute((const void*)gemm_scaled_general_kernel<FA, FB, true>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kGStage) == hipSuccess &&
+      hipFuncSetAttribute((const void*)gemm_scaled_general_kernel<FA, FB, false>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kGStage) == hipSuccess;
+  if (!lds_ok) return fail(STG_ERR_LAUNCH, "gemm_scaled: cannot reserve LDS for the general scaled GEMM kernel");
+  if (p.block % 16 == 0)
+    launch_kernel("gemm_scaled/general", gemm_scaled_general_kernel<FA, FB, true>, dim3((unsigned)n_wg), dim3(kGNT),
+                  (uint32_t)(2 * kGStage), s, p);
+  else
+    launch_kernel("gemm_scaled/general", gemm_scaled_general_kernel<FA, FB, false>, dim3((unsigned)n_wg), dim3(kGNT),
+                  (uint32_t)(2 * kGStage), s, p);
+  return check_launch("gemm_scaled");
+}
+
+template <int FA>
+int launch_general_a(const GeneralParams& p, int64_t n_wg, hipStream_t s) {
+  switch (p.fb) {
+    case STG_LP_E4M3: return launch_general<FA, STG_LP_E4M3>(p, n_wg, s);
+    case STG_LP_E5M2: return launch_general<FA, STG_LP_E5M2>(p, n_wg, s);
+    default: return launch_general<FA, STG_LP_E2M1>(p, n_wg, s);
+  }
+}
+
 }  // namespace
 
 int gemm_scaled_general(const void* A, int32_t a_fmt, int64_t lda, const void* a_scale, int64_t lds_a,
@@ -280,10 +401,6 @@ int gemm_scaled_general(const void* A, int32_t a_fmt, int64_t lda, const void* a
       (int64_t)kGBM * lds_a + 64 >= kMaxOffset32 || (int64_t)kGBN * lds_b + 64 >= kMaxOffset32 ||
       M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2 || block > INT32_MAX)
     return fail(STG_ERR_RANGE, "%s: a tile's rows span more than 2^31 bytes, or a size is too large", name);
-  static const bool lds_ok = hipFuncSetAttribute((const void*)gemm_scaled_general_kernel,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 2 * kGStage) == hipSuccess;
-  if (!lds_ok) return fail(STG_ERR_LAUNCH, "%s: cannot reserve LDS for the general scaled GEMM kernel", name);
   GeneralParams p{};
   p.A = (const char*)A;
   p.B = (const char*)Bt;
@@ -299,9 +416,11 @@ int gemm_scaled_general(const void* A, int32_t a_fmt, int64_t lda, const void* a
   p.tiles_n = (int32_t)((N + kGBN - 1) / kGBN);
   const int64_t n_wg = (int64_t)p.tiles_m * p.tiles_n;
   if (n_wg == 0) return STG_OK;
-  launch_kernel("gemm_scaled/general", gemm_scaled_general_kernel, dim3((unsigned)n_wg), dim3(kGNT),
-                (uint32_t)(2 * kGStage), s, p);
-  return check_launch(name);
+  switch (a_fmt) {
+    case STG_LP_E4M3: return launch_general_a<STG_LP_E4M3>(p, n_wg, s);
+    case STG_LP_E5M2: return launch_general_a<STG_LP_E5M2>(p, n_wg, s);
+    default: return launch_general_a<STG_LP_E2M1>(p, n_wg, s);
+  }
 }
 
 }  // namespace stg
