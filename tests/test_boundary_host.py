@@ -270,12 +270,12 @@ def test_gemm_scaled_argument_errors(stg):
                                a["lds_b"], a["sf"], a["block"], a["acc"], a["ldacc"], a["C"], a["ldc"], a["M"], a["N"],
                                a["K"], None)
 
-    assert call(sf=1) == 2  # e4m3 scales: not on the scaled MFMA
-    assert b"e8m0" in lib.stg_last_error()
-    assert call(block=16) == 2
-    assert call(block=96, K=96) == 2  # not 32 times a power of two
-    assert call(fa=2) == 2  # fp4 with fp8
-    assert call(fa=7) == 2
+    # e4m3 scales, blocks such as 16 or 96 and fp4 x fp8 pairs are supported
+    # (general path); what remains an error fails in the host checks
+    assert call(fa=7) == 2  # unknown operand format
+    assert call(sf=5) == 2  # unknown scale format
+    assert call(block=0) == 1
+    assert call(fa=2, lda=31) == 1  # fp4 rows of 64 values need 32 bytes
     assert call(K=96, block=64) == 1  # K not a multiple of the block
     assert call(lda=32) == 1  # row stride shorter than the row
     assert call(C=None) == 1
