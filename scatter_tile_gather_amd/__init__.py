@@ -7,12 +7,14 @@ input generators used by the tests and the benchmark.
 from . import inputs  # noqa: F401
 from ._binding import (  # noqa: F401
     LIB_PATH,
+    Prepared,
     STATIC_SCRATCH_BYTES,
     StgError,
     exported_names,
     gemm_bounded,
     gemm_scaled,
     load_library,
+    prepare,
     ragged_tile_load,
     ragged_tile_store,
     ragged_tile_schedule,

@@ -136,9 +136,9 @@ def _i64arr(vals):
 _RAW_STREAM = None
 
 
-def _stream(stream, like=None) -> int:
+def _stream(stream, like=None, device=None) -> int:
     """The HIP stream to enqueue on: `stream`'s, else the current stream of the
-    device `like` lives on (or of the current device)."""
+    device `like` lives on (or of `device`, or of the current device)."""
     global _RAW_STREAM
     if stream is not None:
         return stream.cuda_stream
@@ -146,9 +146,73 @@ def _stream(stream, like=None) -> int:
     if _RAW_STREAM is None:
         # torch's raw-stream accessor skips building a Stream object per call
         _RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", False)
+    dev = like.get_device() if like is not None else device if device is not None else torch.cuda.current_device()
     if _RAW_STREAM:
-        return _RAW_STREAM(like.get_device() if like is not None else torch.cuda.current_device())
-    return torch.cuda.current_stream().cuda_stream
+        return _RAW_STREAM(dev)
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+_CAPTURE = None  # list of recorded (C function, arguments) while a call is prepared
+
+
+def _call(name: str, *args):
+    """Invoke the C entry point `name` (its last argument is the stream) and
+    raise on failure -- or, while prepare() runs, record the call instead."""
+    fn = getattr(load_library(), name)
+    if _CAPTURE is not None:
+        _CAPTURE.append((name, fn, args))
+        return
+    _check(fn(*args))
+
+
+class Prepared:
+    """An entry-point call whose argument marshalling (tensor descriptors,
+    shape and offset arrays, checks, output allocation) was done once by
+    prepare(); calling it enqueues the same operation again, on the stream
+    given at preparation or else on the current stream of the device the
+    operands live on.  It holds references to every tensor involved, so they
+    stay allocated.  The tensors' contents may change between calls; their
+    storage, shapes and strides must not."""
+
+    __slots__ = ("calls", "result", "keep", "stream", "device")
+
+    def __init__(self, calls, result, keep, stream, device):
+        self.calls = calls
+        self.result = result
+        self.keep = keep
+        self.stream = stream
+        self.device = device
+
+    def __call__(self):
+        s = self.stream.cuda_stream if self.stream is not None else _stream(None, None, self.device)
+        for name, fn, args in self.calls:
+            rc = fn(*args[:-1], s)
+            if rc != 0:
+                raise StgError(rc, load_library().stg_last_error().decode())
+        return self.result
+
+
+def prepare(op, *args, **kwargs):
+    """Prepare `op(*args, **kwargs)` (one of this module's entry points, with
+    the same arguments) for repeated calls: marshalling and checks run now and
+    the C call is recorded, not made; the returned Prepared object enqueues it
+    each time it is called and returns what `op` returns.  For latency-bound
+    callers (small gathers) this removes the per-call argument marshalling."""
+    global _CAPTURE
+    torch = _torch()
+    if _CAPTURE is not None:
+        raise RuntimeError("prepare() does not nest")
+    _CAPTURE = []
+    try:
+        result = op(*args, **kwargs)
+        calls = _CAPTURE
+    finally:
+        _CAPTURE = None
+    if not calls:
+        raise ValueError(f"{getattr(op, '__name__', op)} makes no device call with these arguments")
+    tensors = [x for x in list(args) + list(kwargs.values()) if isinstance(x, torch.Tensor)]
+    device = next((t.get_device() for t in tensors if t.is_cuda), torch.cuda.current_device())
+    return Prepared(calls, result, (args, kwargs, result), kwargs.get("stream"), device)
 
 
 def _check(rc: int):
@@ -202,8 +266,8 @@ def tile_gather(a, indices, tile_shape, offset=None, axis: int = 0, out=None, st
     if out is None:
         out = torch.empty(_gather_out_shape(tile_shape, n, axis), dtype=a.dtype, device=a.device)
     ad, od = _desc(a, "a"), _desc(out, "out")
-    _check(lib.tile_gather(ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"), n, _i64arr(tile_shape),
-                           None if offset is None else _i64arr(offset), axis, ctypes.byref(od), _stream(stream, a)))
+    _call("tile_gather", ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"), n, _i64arr(tile_shape),
+                           None if offset is None else _i64arr(offset), axis, ctypes.byref(od), _stream(stream, a))
     return out
 
 
@@ -218,9 +282,9 @@ def tile_gather_masked(a, indices, mask, tile_shape, offset=None, axis: int = 0,
     if mask is not None and mask.numel() != n:
         raise ValueError("mask must hold one entry per index")
     mp = None if mask is None else _dev_array(mask, torch.uint8, "mask")
-    _check(lib.tile_gather_masked(ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"), mp, n,
+    _call("tile_gather_masked", ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"), mp, n,
                                   _i64arr(tile_shape), None if offset is None else _i64arr(offset), axis,
-                                  float(padding_value), ctypes.byref(od), _stream(stream, a)))
+                                  float(padding_value), ctypes.byref(od), _stream(stream, a))
     return out
 
 
@@ -254,15 +318,17 @@ def tile_gather_backward(a_grad, indices, tile_shape, grad_out, offset=None, axi
             # allocated on the stream the kernels run on: when this function
             # returns, the caching allocator hands the block out again only to
             # work queued on that stream after them
+            if _CAPTURE is not None:
+                raise ValueError("prepare(): pass a workspace tensor instead of \"auto\"")
             with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream(a_grad.device)):
                 workspace = torch.empty(nb, dtype=torch.uint8, device=a_grad.device)
     ws_ptr, ws_n = None, 0
     if workspace is not None:
         _on_gpu(workspace, "workspace")
         ws_ptr, ws_n = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    _check(lib.tile_gather_backward(ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"), n,
+    _call("tile_gather_backward", ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"), n,
                                     _i64arr(tile_shape), None if offset is None else _i64arr(offset), axis,
-                                    ctypes.byref(gd), ws_ptr, ws_n, _stream(stream, a_grad)))
+                                    ctypes.byref(gd), ws_ptr, ws_n, _stream(stream, a_grad))
     return a_grad
 
 
@@ -278,10 +344,10 @@ def tile_gather_backward_static(a_grad, indices, tile_shape, grad_out, offset=No
     torch = _torch()
     lib = load_library()
     ad, gd = _desc(a_grad, "a_grad"), _desc(grad_out, "grad_out")
-    _check(lib.tile_gather_backward_static(ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"),
+    _call("tile_gather_backward_static", ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"),
                                            indices.numel(), _i64arr(tile_shape),
                                            None if offset is None else _i64arr(offset), axis, ctypes.byref(gd),
-                                           _stream(stream, a_grad)))
+                                           _stream(stream, a_grad))
     return a_grad
 
 
@@ -293,9 +359,9 @@ def tile_scatter_masked(a, indices, mask, tile_shape, tile, offset=None, axis: i
     if mask is not None and mask.numel() != n:
         raise ValueError("mask must hold one entry per index")
     mp = None if mask is None else _dev_array(mask, torch.uint8, "mask")
-    _check(lib.tile_scatter_masked(ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"), mp, n,
+    _call("tile_scatter_masked", ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"), mp, n,
                                    _i64arr(tile_shape), None if offset is None else _i64arr(offset), axis,
-                                   ctypes.byref(td), _stream(stream, a)))
+                                   ctypes.byref(td), _stream(stream, a))
     return a
 
 
@@ -313,8 +379,8 @@ def tile_copy_bounded(src, tile_rows: int, tile_cols: int, origin_row: int = 0, 
     if out.dtype != src.dtype or not out.is_contiguous() or out.numel() < max(gr, 0) * max(gc, 0) * tile_rows * tile_cols:
         raise ValueError("out must be a contiguous tile buffer of the source dtype and grid size")
     sd = _desc(src, "src")
-    _check(lib.tile_copy_bounded(ctypes.byref(sd), tile_rows, tile_cols, origin_row, origin_col, out.data_ptr(),
-                                 _stream(stream, src)))
+    _call("tile_copy_bounded", ctypes.byref(sd), tile_rows, tile_cols, origin_row, origin_col, out.data_ptr(),
+                                 _stream(stream, src))
     return out
 
 
@@ -333,8 +399,8 @@ def tile_copy_windows(src, tile_rows: int, tile_cols: int, step_rows: int, step_
     if out.dtype != src.dtype or not out.is_contiguous() or out.numel() < max(gr, 0) * max(gc, 0) * tile_rows * tile_cols:
         raise ValueError("out must be a contiguous tile buffer of the source dtype and grid size")
     sd = _desc(src, "src")
-    _check(lib.tile_copy_windows(ctypes.byref(sd), tile_rows, tile_cols, step_rows, step_cols, origin_row, origin_col,
-                                 1 if check_bounds else 0, out.data_ptr(), _stream(stream, src)))
+    _call("tile_copy_windows", ctypes.byref(sd), tile_rows, tile_cols, step_rows, step_cols, origin_row, origin_col,
+                                 1 if check_bounds else 0, out.data_ptr(), _stream(stream, src))
     return out
 
 
@@ -349,8 +415,8 @@ def tile_store_windows(tiles, step_rows: int, step_cols: int, origin_row: int, o
                                             stg_tile_grid(dst.shape[1], origin_col, step_cols)):
         raise ValueError("tile buffer grid does not match dst, step and origin")
     dd = _desc(dst, "dst")
-    _check(lib.tile_store_windows(tiles.data_ptr(), tr, tc, step_rows, step_cols, origin_row, origin_col,
-                                  1 if check_bounds else 0, ctypes.byref(dd), _stream(stream, dst)))
+    _call("tile_store_windows", tiles.data_ptr(), tr, tc, step_rows, step_cols, origin_row, origin_col,
+                                  1 if check_bounds else 0, ctypes.byref(dd), _stream(stream, dst))
     return dst
 
 
@@ -364,8 +430,8 @@ def tile_store_clipped(tiles, origin_row: int, origin_col: int, dst, stream=None
                                             stg_tile_grid(dst.shape[1], origin_col, tc)):
         raise ValueError("tile buffer grid does not match dst and origin")
     dd = _desc(dst, "dst")
-    _check(lib.tile_store_clipped(tiles.data_ptr(), tr, tc, origin_row, origin_col, ctypes.byref(dd),
-                                  _stream(stream, dst)))
+    _call("tile_store_clipped", tiles.data_ptr(), tr, tc, origin_row, origin_col, ctypes.byref(dd),
+                                  _stream(stream, dst))
     return dst
 
 
@@ -405,9 +471,9 @@ def ragged_tile_load(src, middle_dim: int, group: int, BM: int, BN: int, ragged_
     _on_gpu(out, "out")
     if out.dtype != src.dtype or not out.is_contiguous() or out.numel() < n * BM * BN:
         raise ValueError("out must be a contiguous (n_tiles, BM, BN) tensor of src's dtype")
-    _check(lib.ragged_tile_load(src.data_ptr(), _dtype_code(src), src.shape[0], middle_dim, group, src.shape[2], BM,
+    _call("ragged_tile_load", src.data_ptr(), _dtype_code(src), src.shape[0], middle_dim, group, src.shape[2], BM,
                                 BN, col0, ragged_idx.data_ptr(), dynamic_dim.data_ptr(), middle_idx.data_ptr(), n,
-                                out.data_ptr(), _stream(stream, src)))
+                                out.data_ptr(), _stream(stream, src))
     return out
 
 
@@ -429,9 +495,9 @@ def ragged_tile_store(tiles, dst, middle_dim: int, group: int, ragged_idx, dynam
         _on_gpu(t, nm)
         if t.dtype not in (torch.int32, torch.uint32) or not t.is_contiguous() or t.numel() != n:
             raise ValueError(f"{nm} must be a contiguous 32-bit integer tensor with one entry per tile")
-    _check(lib.ragged_tile_store(tiles.data_ptr(), _dtype_code(dst), dst.shape[0], middle_dim, group, dst.shape[2], BM,
+    _call("ragged_tile_store", tiles.data_ptr(), _dtype_code(dst), dst.shape[0], middle_dim, group, dst.shape[2], BM,
                                  BN, col0, ragged_idx.data_ptr(), dynamic_dim.data_ptr(), middle_idx.data_ptr(), n,
-                                 dst.data_ptr(), _stream(stream, dst)))
+                                 dst.data_ptr(), _stream(stream, dst))
     return dst
 
 
@@ -455,8 +521,8 @@ def gemm_bounded(A, B, out=None, out_dtype=None, stream=None):
     if out.dim() != 2 or tuple(out.shape) != (M, N) or (out.stride(1) != 1 and N > 1):
         raise ValueError("out must be (M, N) with unit column stride")
     code = _dtype_code(out)
-    _check(lib.gemm_bounded(A.data_ptr(), A.stride(0), B.data_ptr(), B.stride(0), out.data_ptr(), out.stride(0), M,
-                            N, K, code, _stream(stream, A)))
+    _call("gemm_bounded", A.data_ptr(), A.stride(0), B.data_ptr(), B.stride(0), out.data_ptr(), out.stride(0), M,
+                            N, K, code, _stream(stream, A))
     return out
 
 
@@ -496,8 +562,8 @@ def gemm_scaled(A, a_fmt: str, a_scale, Bt, b_fmt: str, b_scale, K: int, block: 
         if acc.dtype != torch.float32 or tuple(acc.shape) != (M, N) or (acc.stride(1) != 1 and N > 1):
             raise ValueError("acc must be float32 (M, N) with unit column stride")
         accp, ldacc = acc.data_ptr(), acc.stride(0)
-    _check(lib.gemm_scaled(A.data_ptr(), LOWP_FORMATS[a_fmt], A.stride(0), a_scale.data_ptr(), a_scale.stride(0),
+    _call("gemm_scaled", A.data_ptr(), LOWP_FORMATS[a_fmt], A.stride(0), a_scale.data_ptr(), a_scale.stride(0),
                            Bt.data_ptr(), LOWP_FORMATS[b_fmt], Bt.stride(0), b_scale.data_ptr(), b_scale.stride(0),
                            SCALE_FORMATS[scale_fmt], block, accp, ldacc, out.data_ptr(), out.stride(0), M, N, K,
-                           _stream(stream, A)))
+                           _stream(stream, A))
     return out
