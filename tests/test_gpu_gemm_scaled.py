@@ -467,3 +467,27 @@ def test_scaled_mfma_exact_at_the_group_boundary(stg, orc):
     say("scaled MFMA exact at the group boundary (300, 280, 512) e4m3")
     C = to_host(stg.gemm_scaled(to_dev(ca), "e4m3", to_dev(sa), to_dev(cb), "e4m3", to_dev(sb), K, 32))
     np.testing.assert_array_equal(C.astype(np.float64), orc.gemm_scaled_f64(ca, "e4m3", sa, cb, "e4m3", sb, K, 32))
+
+
+def test_scaled_general_special_scales(stg, orc):
+    """General path, special scale values: an e4m3 scale of 0 (that block's
+    products are 0), and NaN scales (e4m3 0x7F, e8m0 0xFF) -- every output of
+    that column is NaN, as in the oracle; everything else exact."""
+    M, N, K = 40, 50, 64
+    rng = np.random.default_rng(4)
+    ca = np.array(EXACT_CODES["e4m3"], np.uint8)[rng.integers(0, 4, (M, K))]
+    cb = np.array(EXACT_CODES["e4m3"], np.uint8)[rng.integers(0, 4, (N, K))]
+    for s_fmt, zero, nan in (("e4m3", 0x00, 0x7F), ("e8m0", None, 0xFF)):
+        sa = np.array(EXACT_SCALES[s_fmt], np.uint8)[rng.integers(0, 4, (M, K // 16))]
+        sb = np.array(EXACT_SCALES[s_fmt], np.uint8)[rng.integers(0, 4, (N, K // 16))]
+        if zero is not None:
+            sa[3, 1] = zero  # row 3, block 1: those products are 0
+        sb[7, 2] = nan  # column 7, block 2: NaN
+        say("gemm_scaled general special scales", s_fmt)
+        C = to_host(stg.gemm_scaled(to_dev(ca), "e4m3", to_dev(sa), to_dev(cb), "e4m3", to_dev(sb), K, 16,
+                                    scale_fmt=s_fmt)).astype(np.float64)
+        want = orc.gemm_scaled_f64(ca, "e4m3", sa, cb, "e4m3", sb, K, 16, s_fmt=s_fmt)
+        assert np.all(np.isnan(C[:, 7])) and np.all(np.isnan(want[:, 7]))
+        keep = np.ones(N, bool)
+        keep[7] = False
+        np.testing.assert_array_equal(C[:, keep], want[:, keep])
