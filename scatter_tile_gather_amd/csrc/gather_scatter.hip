@@ -423,8 +423,10 @@ constexpr int kWindow = 4096;                   // destination rows per pass in 
 constexpr int kBuildThreads = 1024;
 constexpr int kSegChunk = 64;                  // terms per reduce group; longer segments are split
 constexpr int kMaxPieces = 4096;               // pieces of one segment at most
-constexpr int kHotPairs = 65536;               // a bucket with more terms is built by many workgroups
+constexpr int kHotPairs = 16384;               // a bucket with more terms is built by many workgroups
+                                               // (one workgroup takes ~50 us over 60,000 terms)
 constexpr int kSlice = 16384;                  // terms per workgroup of a hot bucket
+constexpr int kSplitWorkgroups = 1024;         // workgroups on the long segments' pieces, at most
 
 // Terms per piece of a segment of c terms: kSegChunk, or longer for a row so
 // hot that kSegChunk-term pieces would number more than kMaxPieces (their
@@ -1047,14 +1049,14 @@ __device__ __forceinline__ void seg_stream_chunk(const RowParams& p, const int32
 
 // One group of LPR lanes per kRowsPerGroup consecutive destination rows sums
 // each row's segment onto a.grad's values and stores the row once.  A
-// segment longer than kSegChunk terms is left to seg_split_kernel, which adds
+// segment longer than kSegChunk terms is left to seg_split_wg, which adds
 // its pieces onto a.grad with float atomics; a group holding such a row takes
 // its other rows one at a time.  Rows with an empty segment are not touched.
 template <int ESIZE, int LPR>
-__global__ __launch_bounds__(kThreads) void seg_reduce_kernel(RowParams p, int64_t R, const int32_t* offs,
-                                                              const int32_t* perm) {
+__device__ __forceinline__ void seg_reduce_wg(const RowParams& p, int64_t R, const int32_t* offs, const int32_t* perm,
+                                              int64_t wg) {
   const int sub = threadIdx.x % LPR;
-  const int64_t r0 = ((int64_t)blockIdx.x * (kThreads / LPR) + threadIdx.x / LPR) * kRowsPerGroup;
+  const int64_t r0 = (wg * (kThreads / LPR) + threadIdx.x / LPR) * kRowsPerGroup;
   if (r0 >= R) return;
   int32_t o[kRowsPerGroup + 1];
 #pragma unroll
@@ -1092,15 +1094,16 @@ __global__ __launch_bounds__(kThreads) void seg_reduce_kernel(RowParams p, int64
 // set of atomics, which divides the atomics meeting on that row's elements by
 // the number of groups.
 template <int ESIZE, int LPR>
-__global__ __launch_bounds__(kThreads) void seg_split_kernel(RowParams p, const int32_t* offs, const int32_t* perm,
-                                                             const uint64_t* split_list, const int32_t* n_split) {
+__device__ __forceinline__ void seg_split_wg(const RowParams& p, const int32_t* offs, const int32_t* perm,
+                                             const uint64_t* split_list, const int32_t* n_split, int64_t wg,
+                                             int64_t n_wg) {
   constexpr int G = kThreads / LPR;  // groups per workgroup
   constexpr int V = 16 / ESIZE;
   __shared__ u32x4 part[G][LPR];
   __shared__ int64_t s_row[G];
   const int sub = threadIdx.x % LPR, grp = threadIdx.x / LPR;
   const int n = *n_split;
-  for (int64_t e0 = (int64_t)blockIdx.x * G; e0 < n; e0 += (int64_t)gridDim.x * G) {
+  for (int64_t e0 = wg * G; e0 < n; e0 += n_wg * G) {
     const int64_t g = e0 + grp;
     int64_t r = -1;
     int32_t kb = 0, ke = 0;
@@ -1114,8 +1117,10 @@ __global__ __launch_bounds__(kThreads) void seg_split_kernel(RowParams p, const 
     }
     if (sub == 0) s_row[grp] = r;
     __syncthreads();
+    // partly unrolled here and in the sum below: with 32 groups (LPR 8) a
+    // full unroll holds every group's value in registers at once
     bool one_row = true;
-#pragma unroll
+#pragma unroll 4
     for (int q = 1; q < G; ++q) one_row = one_row && s_row[q] == s_row[0];
     if (one_row) {  // every entry valid and of one row
       char* arow = seg_arow(p, r);
@@ -1127,7 +1132,7 @@ __global__ __launch_bounds__(kThreads) void seg_split_kernel(RowParams p, const 
         __syncthreads();
         if (grp == 0 && b < p.hi_b) {
           u32x4 sum = part[0][sub];
-#pragma unroll
+#pragma unroll 4
           for (int q = 1; q < G; ++q) {
             const u32x4 x = part[q][sub];
 #pragma unroll
@@ -1149,6 +1154,22 @@ __global__ __launch_bounds__(kThreads) void seg_split_kernel(RowParams p, const 
     }
     __syncthreads();  // s_row is rewritten by the next round
   }
+}
+
+// Both sums in one launch: workgroups [0, n_split_wg) take the pieces of the
+// long segments (grid-striding over the list), the rest take the short
+// segments, kThreads / LPR groups of kRowsPerGroup rows each.  The two touch
+// disjoint destination rows (a row's segment is either short or split), so
+// nothing orders them, and the short segments' groups fill the slots the
+// pieces leave free instead of waiting for the last piece.
+template <int ESIZE, int LPR>
+__global__ __launch_bounds__(kThreads) void seg_sum_kernel(RowParams p, int64_t R, const int32_t* offs,
+                                                           const int32_t* perm, const uint64_t* split_list,
+                                                           const int32_t* n_split, int n_split_wg) {
+  if ((int)blockIdx.x < n_split_wg)
+    seg_split_wg<ESIZE, LPR>(p, offs, perm, split_list, n_split, blockIdx.x, n_split_wg);
+  else
+    seg_reduce_wg<ESIZE, LPR>(p, R, offs, perm, (int64_t)blockIdx.x - n_split_wg);
 }
 
 // ---- host side -------------------------------------------------------------
@@ -1315,18 +1336,20 @@ int launch_segmented(const char* name, int esize, const RowParams& p, int64_t R,
   const int chunks_per_row = p.n_chunks;
   const int lpr = chunks_per_row <= 8 ? 8 : chunks_per_row <= 16 ? 16 : chunks_per_row <= 32 ? 32 : 64;
   const int64_t rows_per_wg = (int64_t)(kThreads / lpr) * kRowsPerGroup;
-  const dim3 grid((unsigned)((R + rows_per_wg - 1) / rows_per_wg));
-  // groups for the long segments' further pieces: striding over the list
-  // the build wrote (empty unless a row takes more than kSegChunk terms)
+  // workgroups for the long segments' pieces, striding over the list the
+  // build wrote (empty unless a row takes more than kSegChunk terms); they
+  // come first in the grid, so the long-running ones start first
   const int64_t gpw = kThreads / lpr;
-  const dim3 sgrid((unsigned)std::min<int64_t>((L.n_pieces + gpw - 1) / gpw, 1024));
+  const int n_split_wg = (int)std::min<int64_t>((L.n_pieces + gpw - 1) / gpw, kSplitWorkgroups);
+  const int64_t reduce_wg = (R + rows_per_wg - 1) / rows_per_wg;
+  if (n_split_wg + reduce_wg > INT32_MAX)
+    return fail(STG_ERR_RANGE, "%s: %lld destination rows need more workgroups than one launch holds", name,
+                (long long)R);
+  const dim3 sgrid((unsigned)(n_split_wg + reduce_wg));
 #define STG_SEG(E, LP)                                                                                               \
-  do {                                                                                                               \
-    launch_kernel("tile_gather_backward/reduce", seg_reduce_kernel<E, LP>, grid, dim3(kThreads), 0, s, p, R,        \
-                  (const int32_t*)offs, (const int32_t*)perm);                                                      \
-    launch_kernel("tile_gather_backward/split", seg_split_kernel<E, LP>, sgrid, dim3(kThreads), 0, s, p,             \
-                  (const int32_t*)offs, (const int32_t*)perm, (const uint64_t*)split, (const int32_t*)n_split);     \
-  } while (0)
+  launch_kernel("tile_gather_backward/sum", seg_sum_kernel<E, LP>, sgrid, dim3(kThreads), 0, s, p, R,                \
+                (const int32_t*)offs, (const int32_t*)perm, (const uint64_t*)split, (const int32_t*)n_split,        \
+                n_split_wg)
   if (esize == 4) {
     if (lpr == 8) STG_SEG(4, 8); else if (lpr == 16) STG_SEG(4, 16); else if (lpr == 32) STG_SEG(4, 32); else STG_SEG(4, 64);
   } else {

@@ -243,7 +243,7 @@ def test_gather_backward_workspace_query_and_errors(stg):
     # table int32[L1] and its scan int32[L1 + 1], scan block sums, the list
     # of long segments' pieces uint64[n / 32 + 1] and its length, per-row
     # counters int32[R], hot-bucket flags int32[buckets], the hot slices'
-    # list uint64[n / 16384 + n / 65536 + 1] and its length; R = 1024 rows
+    # list uint64[n / 16384 + n / 16384 + 1] and its length; R = 1024 rows
     # make 512 buckets of 2 rows, n = 4096 terms one chunk, so L1 = 512
     nbytes = lib.tile_gather_backward_workspace(B(g), 4096, ts, 0)
     assert nbytes == 4352 + 16384 + 32768 + 2048 + 2304 + 256 + 1280 + 256 + 4096 + 2048 + 256 + 256

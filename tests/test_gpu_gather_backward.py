@@ -191,7 +191,7 @@ def test_backward_grouped_hot_row(stg, orc):
 
 @pytest.mark.parametrize("dtype", [np.float32, np.float64])
 def test_backward_grouped_hot_buckets(stg, orc, dtype):
-    """Skewed indices that make buckets of more than 65536 terms, which many
+    """Skewed indices that make buckets of more than 16384 terms, which many
     workgroups build slice by slice: Zipf-distributed rows over a (70000, 20)
     table (row 0 alone takes about a third of the 300,000 terms), plus a block
     of rows hit uniformly."""
