@@ -334,9 +334,11 @@ int ragged_tile_store(const void* tiles_in, int32_t dtype, int64_t total_rows, i
  *    16, a faster scale path is taken (fp4 about 6% faster).
  *  - every other case (e4m3 scales, blocks such as 16 or 48, fp4 x fp8 pairs)
  *    multiplies each value by its scale while staging -- exact in bf16 for
- *    e4m3 scales, and for e8m0 scales while 2^(e-127) times the value stays
- *    within bf16's range [2^-133, 2^128) -- and sums with the bf16 MFMA in
- *    fp32: the result is within fp32 accumulation rounding of the exact sum.
+ *    e4m3 scales, and for e8m0 scales while value x 2^(e-127) is a multiple
+ *    of 2^-133 (bf16's subnormal step) below 2^128: scale bytes 3..246 with
+ *    e4m3 operands, 10..239 with e5m2, 0..252 with e2m1 -- and sums with the
+ *    bf16 MFMA (which keeps subnormal inputs) in fp32: the result is within
+ *    fp32 accumulation rounding of the exact sum.
  */
 typedef enum { STG_LP_E4M3 = 0, STG_LP_E5M2 = 1, STG_LP_E2M1 = 2 } stg_lowp_format;
 typedef enum { STG_SC_E8M0 = 0, STG_SC_E4M3 = 1 } stg_scale_format;

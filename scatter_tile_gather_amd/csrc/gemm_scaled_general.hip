@@ -17,11 +17,12 @@
 // accumulation.  The scaling is exact: an operand value has at most 4
 // significant bits (e4m3: 4, e5m2: 3, e2m1: 2) and a scale at most 4 (e4m3)
 // or 1 (e8m0), so value x scale has at most 8 and is a bf16 number whenever
-// its exponent lies in bf16's range -- always with e4m3 scales (the products
-// lie in [2^-18, 2^25]); with e8m0 scales whenever 2^(e-127) times the
-// operand value neither overflows nor falls below 2^-133.  The bf16 products
-// of two such values are exact in fp32, so the result differs from the exact
-// sum only by fp32 accumulation rounding.
+// it is a multiple of 2^-133 (bf16's subnormal step) below 2^128 -- always
+// with e4m3 scales (the products lie in [2^-25, 2^25]); with e8m0 scale
+// bytes 3..246 for e4m3 operands, 10..239 for e5m2 and 0..252 for e2m1.  The
+// bf16 MFMA keeps subnormal inputs, and the bf16 products of two such values
+// are exact in fp32, so the result differs from the exact sum only by fp32
+// accumulation rounding.
 //
 //  * Tiles 256 x 256 on 8 waves (2 x 4), each wave 128 x 64 accumulators of
 //    v_mfma_f32_32x32x16_bf16; K steps of 32.

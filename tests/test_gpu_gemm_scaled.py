@@ -491,3 +491,66 @@ def test_scaled_general_special_scales(stg, orc):
         keep = np.ones(N, bool)
         keep[7] = False
         np.testing.assert_array_equal(C[:, keep], want[:, keep])
+
+
+# Scaled values at the ends of the range where the general path is exact:
+# (code, e8m0 scale byte) pairs whose product code x 2^(b - 127) is a multiple
+# of 2^-133 (bf16's subnormal step) and below 2^128 -- the smallest subnormal
+# codes at the lowest such byte, the largest finite codes at the highest.
+GENERAL_EXACT_EDGES = {
+    "e4m3": ([0x01, 0x0F, 0x7E, 0x81], [3, 4, 127, 246]),
+    "e5m2": ([0x01, 0x03, 0x7B, 0x81], [10, 11, 127, 239]),
+    "e2m1": ([0x1, 0x7, 0x9, 0xF], [0, 1, 127, 252]),
+}
+UNIT_CODE = {"e4m3": 0x38, "e5m2": 0x3C, "e2m1": 0x2}
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2", "e2m1"])
+def test_scaled_general_exact_at_the_range_ends(stg, orc, fmt):
+    """General path (blocks of 16), one nonzero term per output: each output
+    is a single scaled product, so it must equal the fp64 oracle bit for bit
+    wherever the scaled value is a bf16 number -- down to bf16 subnormals
+    (e4m3 from scale byte 3, e5m2 from 10, e2m1 from 0; the bf16 MFMA keeps
+    subnormal inputs) and up to the largest finite codes just below 2^128
+    (bytes 246, 239, 252)."""
+    cs, bs = GENERAL_EXACT_EDGES[fmt]
+    pairs = [(c, b) for c in cs for b in bs]
+    M, N, K, block = len(pairs), 8, 32, 16
+    ca = np.zeros((M, K), np.uint8)
+    sa = np.full((M, K // block), 127, np.uint8)
+    for i, (c, b) in enumerate(pairs):
+        k = (5 * i) % K
+        ca[i, k] = c
+        sa[i, k // block] = b
+    cb = np.full((N, K), UNIT_CODE[fmt], np.uint8)
+    sb = np.full((N, K // block), 127, np.uint8)
+    say("gemm_scaled general path, exact range ends", fmt)
+    C = to_host(stg.gemm_scaled(to_dev(pack(ca, fmt)), fmt, to_dev(sa), to_dev(pack(cb, fmt)), fmt, to_dev(sb), K,
+                                block)).astype(np.float64)
+    want = orc.gemm_scaled_f64(pack(ca, fmt), fmt, sa, pack(cb, fmt), fmt, sb, K, block)
+    assert np.all(want != 0) and np.all(np.isfinite(want))
+    np.testing.assert_array_equal(C, want)
+
+
+def test_scaled_general_exact_e4m3_scale_extremes(stg, orc):
+    """e4m3 scales always give bf16 numbers: the smallest subnormal and the
+    largest finite scale on the smallest and largest codes of both fp8
+    formats, single-term outputs, bit-exact."""
+    rows = [(fmt, c, s) for fmt, cs in (("e4m3", (0x01, 0x7E)), ("e5m2", (0x01, 0x7B)))
+            for c in cs for s in (0x01, 0x7E, 0x81)]
+    for fmt in ("e4m3", "e5m2"):
+        sel = [(c, s) for f, c, s in rows if f == fmt]
+        M, N, K, block = len(sel), 8, 32, 16
+        ca = np.zeros((M, K), np.uint8)
+        sa = np.full((M, K // block), 0x38, np.uint8)
+        for i, (c, s) in enumerate(sel):
+            ca[i, 3 * i % K] = c
+            sa[i, (3 * i % K) // block] = s
+        cb = np.full((N, K), UNIT_CODE[fmt], np.uint8)
+        sb = np.full((N, K // block), 0x38, np.uint8)
+        say("gemm_scaled general path, e4m3 scale extremes", fmt)
+        C = to_host(stg.gemm_scaled(to_dev(ca), fmt, to_dev(sa), to_dev(cb), fmt, to_dev(sb), K, block,
+                                    scale_fmt="e4m3")).astype(np.float64)
+        want = orc.gemm_scaled_f64(ca, fmt, sa, cb, fmt, sb, K, block, s_fmt="e4m3")
+        assert np.all(want != 0)
+        np.testing.assert_array_equal(C, want)
