@@ -183,7 +183,8 @@ int64_t tile_gather_backward_workspace(const stg_tensor* a_grad, int64_t n_indic
  * float atomics as in tile_gather_backward.  The call allocates and frees
  * nothing.  All calls on one GPU share its array: calls that overlap in time
  * on one GPU (two streams, or two host threads without ordering) race and
- * give undefined results; `stream` must belong to the current device. */
+ * give undefined results.  `stream` must belong to the current device
+ * (STG_ERR_INVALID otherwise, before anything is enqueued). */
 #define STG_STATIC_SCRATCH_BYTES (64ll << 20)
 int tile_gather_backward_static(const stg_tensor* a_grad, const int32_t* indices, int64_t n_indices,
                                 const int64_t* tile_shape, const int64_t* offset, int32_t axis,

@@ -344,10 +344,11 @@ def tile_gather_backward_static(a_grad, indices, tile_shape, grad_out, offset=No
     torch = _torch()
     lib = load_library()
     ad, gd = _desc(a_grad, "a_grad"), _desc(grad_out, "grad_out")
-    _call("tile_gather_backward_static", ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"),
-                                           indices.numel(), _i64arr(tile_shape),
-                                           None if offset is None else _i64arr(offset), axis, ctypes.byref(gd),
-                                           _stream(stream, a_grad))
+    # the library takes the current device's static array: make it a_grad's
+    with torch.cuda.device(a_grad.device):
+        _call("tile_gather_backward_static", ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"),
+              indices.numel(), _i64arr(tile_shape), None if offset is None else _i64arr(offset), axis,
+              ctypes.byref(gd), _stream(stream, a_grad))
     return a_grad
 
 

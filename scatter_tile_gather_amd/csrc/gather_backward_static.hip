@@ -64,8 +64,20 @@ extern "C" int tile_gather_backward_static(const stg_tensor* a_grad, const int32
     return stg::fail(STG_ERR_RANGE, "%s: %lld bytes of scratch needed, the static array holds %lld", name,
                      (long long)need, (long long)STG_STATIC_SCRATCH_BYTES);
   void* ws = nullptr;
-  int rc;
-  if (need > 0 && (rc = scratch_address(name, &ws))) return rc;
+  if (need > 0) {
+    // the array looked up is the current device's: a stream of another
+    // device would run the kernels against an address that is not theirs
+    if (stream) {
+      int cur = -1, sdev = -1;
+      hipError_t e = hipGetDevice(&cur);
+      if (e == hipSuccess) e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+      if (e != hipSuccess) return stg::fail(STG_ERR_LAUNCH, "%s: stream device: %s", name, hipGetErrorString(e));
+      if (sdev != cur)
+        return stg::fail(STG_ERR_INVALID, "%s: the stream is on device %d, the current device is %d", name, sdev, cur);
+    }
+    const int rc = scratch_address(name, &ws);
+    if (rc) return rc;
+  }
   return tile_gather_backward(a_grad, indices, n_indices, tile_shape, offset, axis, grad_out, ws,
                               need > 0 ? STG_STATIC_SCRATCH_BYTES : 0, stream);
 }
