@@ -497,16 +497,15 @@ int launch(const char* name, GemmParams p, int64_t cols, hipStream_t s) {
   return check_launch("gemm_bounded");
 }
 
-// Raises the kernels' dynamic LDS limit once per process; a function-local
-// static is initialised exactly once even when the first calls come from
-// several host threads at the same time.
+// Raises the kernels' dynamic LDS limit once on each device.
 bool lds_configured() {
-  static const bool ok =
-      hipFuncSetAttribute((const void*)gemm_kernel<MainCfg>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          MainCfg::LDS_B) == hipSuccess &&
-      hipFuncSetAttribute((const void*)gemm_kernel<EdgeCfg>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          EdgeCfg::LDS_B) == hipSuccess;
-  return ok;
+  static OncePerDevice once;
+  return once.run([] {
+    return hipFuncSetAttribute((const void*)gemm_kernel<MainCfg>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               MainCfg::LDS_B) == hipSuccess &&
+           hipFuncSetAttribute((const void*)gemm_kernel<EdgeCfg>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               EdgeCfg::LDS_B) == hipSuccess;
+  });
 }
 
 }  // namespace

@@ -642,10 +642,12 @@ extern "C" int gemm_scaled(const void* A, int32_t a_fmt, int64_t lda, const void
       (M - 1) * lds_a + K / block + 64 >= kMaxOffset32 || (N - 1) * lds_b + K / block + 64 >= kMaxOffset32)
     return fail(STG_ERR_RANGE, "%s: a stage or a scale matrix spans more than 2^31 bytes, or a size is too large",
                 name);
-  // once per process; a function-local static is initialised exactly once
-  // even when the first calls come from several host threads
-  static const bool lds_ok = set_lds<0, 0, 8>() && set_lds<0, 1, 8>() && set_lds<1, 0, 8>() &&
-                             set_lds<1, 1, 8>() && set_lds<4, 4, 4>();
+  // once on each device
+  static OncePerDevice once;
+  const bool lds_ok = once.run([] {
+    return set_lds<0, 0, 8>() && set_lds<0, 1, 8>() && set_lds<1, 0, 8>() && set_lds<1, 1, 8>() &&
+           set_lds<4, 4, 4>();
+  });
   if (!lds_ok) return fail(STG_ERR_LAUNCH, "%s: cannot reserve LDS for the scaled GEMM kernels", name);
   ScaledParams p{};
   p.A = (const char*)A;

@@ -366,11 +366,13 @@ __global__ __launch_bounds__(kGNT) void gemm_scaled_general_kernel(GeneralParams
 
 template <int FA, int FB>
 int launch_general(const GeneralParams& p, int64_t n_wg, hipStream_t s) {
-  static const bool lds_ok =
-      hipFuncSetAttribute((const void*)gemm_scaled_general_kernel<FA, FB, true>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kGStage) == hipSuccess &&
-      hipFuncSetAttribute((const void*)gemm_scaled_general_kernel<FA, FB, false>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kGStage) == hipSuccess;
+  static OncePerDevice once;  // the kernels' dynamic LDS limit, once on each device
+  const bool lds_ok = once.run([] {
+    return hipFuncSetAttribute((const void*)gemm_scaled_general_kernel<FA, FB, true>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kGStage) == hipSuccess &&
+           hipFuncSetAttribute((const void*)gemm_scaled_general_kernel<FA, FB, false>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kGStage) == hipSuccess;
+  });
   if (!lds_ok) return fail(STG_ERR_LAUNCH, "gemm_scaled: cannot reserve LDS for the general scaled GEMM kernel");
   if (p.block % 16 == 0)
     launch_kernel("gemm_scaled/general", gemm_scaled_general_kernel<FA, FB, true>, dim3((unsigned)n_wg), dim3(kGNT),

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/stg.h"
 
 namespace stg {
@@ -30,6 +32,27 @@ int dtype_size(int32_t dtype);
 int fill_pattern(double v, int32_t dtype, uint32_t fill[4]);
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Runs f (returning bool) once per device -- the one current at the call --
+// and returns its result on every later call on that device, also when the
+// first calls come from several host threads.  Kernel attributes such as the
+// dynamic LDS limit belong to each device's copy of a kernel, so they are set
+// once on every device the library launches on.
+class OncePerDevice {
+ public:
+  template <class F>
+  bool run(F&& f) {
+    int d = -1;
+    if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= kDevices) return false;
+    std::call_once(flag_[d], [&] { ok_[d] = f(); });
+    return ok_[d];
+  }
+
+ private:
+  static constexpr int kDevices = 64;
+  std::once_flag flag_[kDevices];
+  bool ok_[kDevices] = {};
+};
 
 // Validate a tensor descriptor: non-null, rank in [1,4], known dtype,
 // non-negative shape and stride.  Returns STG_OK or a failure code.
