@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import threading
 
 import numpy as np
 
@@ -152,15 +153,24 @@ def _stream(stream, like=None, device=None) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
 
-_CAPTURE = None  # list of recorded (C function, arguments) while a call is prepared
+# per host thread: the list of recorded (name, C function, arguments) while
+# prepare() runs on that thread, else None; calls from other threads meanwhile
+# run as usual
+_TLS = threading.local()
+
+
+def _capturing():
+    return getattr(_TLS, "capture", None)
 
 
 def _call(name: str, *args):
     """Invoke the C entry point `name` (its last argument is the stream) and
-    raise on failure -- or, while prepare() runs, record the call instead."""
+    raise on failure -- or, while prepare() runs on this thread, record the
+    call instead."""
     fn = getattr(load_library(), name)
-    if _CAPTURE is not None:
-        _CAPTURE.append((name, fn, args))
+    cap = _capturing()
+    if cap is not None:
+        cap.append((name, fn, args))
         return
     _check(fn(*args))
 
@@ -198,16 +208,15 @@ def prepare(op, *args, **kwargs):
     the C call is recorded, not made; the returned Prepared object enqueues it
     each time it is called and returns what `op` returns.  For latency-bound
     callers (small gathers) this removes the per-call argument marshalling."""
-    global _CAPTURE
     torch = _torch()
-    if _CAPTURE is not None:
+    if _capturing() is not None:
         raise RuntimeError("prepare() does not nest")
-    _CAPTURE = []
+    _TLS.capture = []
     try:
         result = op(*args, **kwargs)
-        calls = _CAPTURE
+        calls = _TLS.capture
     finally:
-        _CAPTURE = None
+        _TLS.capture = None
     if not calls:
         raise ValueError(f"{getattr(op, '__name__', op)} makes no device call with these arguments")
     tensors = [x for x in list(args) + list(kwargs.values()) if isinstance(x, torch.Tensor)]
@@ -318,7 +327,7 @@ def tile_gather_backward(a_grad, indices, tile_shape, grad_out, offset=None, axi
             # allocated on the stream the kernels run on: when this function
             # returns, the caching allocator hands the block out again only to
             # work queued on that stream after them
-            if _CAPTURE is not None:
+            if _capturing() is not None:
                 raise ValueError("prepare(): pass a workspace tensor instead of \"auto\"")
             with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream(a_grad.device)):
                 workspace = torch.empty(nb, dtype=torch.uint8, device=a_grad.device)

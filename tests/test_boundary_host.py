@@ -295,3 +295,36 @@ def test_static_scratch_size_and_oversized_rejection(stg):
     rc = lib.tile_gather_backward_static(ctypes.byref(a), ctypes.c_void_p(0x3000), 1 << 24, _i64([64, 128]), None, 0,
                                          ctypes.byref(g), None)
     assert rc == 3 and b"static array" in lib.stg_last_error()
+
+
+def test_prepare_capture_is_per_thread(stg):
+    """prepare() records the entry-point calls made on its own thread only: a
+    call from another host thread meanwhile is made, not recorded.  The
+    recording is driven directly with a library function that needs no GPU
+    (stg_tile_grid), so the check runs on the host."""
+    import threading
+    from scatter_tile_gather_amd import _binding as b
+
+    b.load_library()
+    seen = {}
+
+    def other():
+        seen["capture"] = b._capturing()
+        try:  # made, not recorded: a non-zero return is raised as an error
+            b._call("stg_tile_grid", 100, 0, 10)
+            seen["made"] = False
+        except b.StgError:
+            seen["made"] = True
+
+    b._TLS.capture = []
+    try:
+        t = threading.Thread(target=other)
+        t.start()
+        t.join()
+        b._call("stg_tile_grid", 100, 0, 10)  # recorded here
+        mine = list(b._TLS.capture)
+    finally:
+        b._TLS.capture = None
+    assert seen == {"capture": None, "made": True}
+    assert [name for name, _, _ in mine] == ["stg_tile_grid"]
+    assert b._capturing() is None
