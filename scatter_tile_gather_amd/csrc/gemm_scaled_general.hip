@@ -48,6 +48,14 @@ namespace {
 typedef __bf16 bf16x8_g __attribute__((ext_vector_type(8)));
 typedef float f32x16_g __attribute__((ext_vector_type(16)));
 typedef float f32x2_g __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_g __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to bf16 (nearest even) and packed, element 0 in the
+// low half: one v_cvt_pk_bf16_f32 (converting each value on its own left two
+// conversions plus a shift and an or per pair).
+__device__ __forceinline__ uint32_t pack_bf16x2(f32x2_g v) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_g));
+}
 
 constexpr int kGBM = 256, kGBN = 256, kGBK = 32;
 constexpr int kGWM = 2, kGWN = 4, kGNT = kGWM * kGWN * 64;
@@ -114,8 +122,7 @@ __device__ __forceinline__ uint32_t decode2(const u32x4& w, float pow2, float mu
     f = __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(w[E >> 2], pow2, ((E >> 1) & 1) != 0);
   else
     f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[E >> 3], pow2, (E >> 1) & 3);
-  const __bf16 b0 = (__bf16)(f[0] * mult), b1 = (__bf16)(f[1] * mult);
-  return (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+  return pack_bf16x2(f * mult);
 }
 template <int FMT>
 __device__ __forceinline__ void decode16(const u32x4& w, float pow2, float mult, u32x4 out[2]) {
@@ -166,7 +173,7 @@ __global__ __launch_bounds__(kGNT) void gemm_scaled_general_kernel(GeneralParams
   // vector load there could reach past the matrix's last byte: byte loads up
   // to the row's end instead (bytes past it read as zero).
   auto load_codes = [&](auto bits_c, int kt, const __amdgpu_buffer_rsrc_t& rs, uint32_t row_off,
-                        const __amdgpu_buffer_rsrc_t& rss, uint32_t srow, bool last) {
+                        const __amdgpu_buffer_rsrc_t& rss, uint32_t srow, bool last, uint32_t sq) {
     constexpr int bits = decltype(bits_c)::value;
     Codes c;
     const uint32_t k = (uint32_t)kt * kGBK + 16 * h;
@@ -193,7 +200,7 @@ __global__ __launch_bounds__(kGNT) void gemm_scaled_general_kernel(GeneralParams
     c.s = 0;
     if constexpr (BLK16)
       c.s = __builtin_amdgcn_raw_buffer_load_b8(
-          rss, (srow == kOOB || (int64_t)k >= p.K) ? kOOB : srow + k / (uint32_t)p.block, 0, 0);
+          rss, (srow == kOOB || (int64_t)k >= p.K) ? kOOB : srow + sq, 0, 0);
     return c;
   };
 
@@ -205,19 +212,20 @@ __global__ __launch_bounds__(kGNT) void gemm_scaled_general_kernel(GeneralParams
     u32x4 out[2];
     if constexpr (BLK16) {
       // one scale for the 16 values; codes past K were loaded as zero
-      float pow2, mult;
-      if (p.sf == STG_SC_E8M0) {
-        // 2^(b-127); b = 0 as 2^-126 * 0.5 (an exponent field of 0 is not a
-        // power of two for the conversion), 0xFF as NaN
-        pow2 = c.s ? __uint_as_float(c.s << 23) : 0x1p-126f;
-        mult = c.s == 0xFF ? __uint_as_float(0x7FC00000u) : c.s ? 1.f : 0.5f;
-      } else {
-        const float sc = decode_scale(c.s, STG_SC_E4M3);  // normal f32, zero or NaN
-        pow2 = __uint_as_float(__float_as_uint(sc) & 0x7F800000u);
-        mult = __uint_as_float((__float_as_uint(sc) & 0x807FFFFFu) | 0x3F800000u);
-        if (sc == 0.f) pow2 = 1.f, mult = 0.f;
-        if (sc != sc) pow2 = 1.f, mult = sc;
-      }
+      // both readings of the byte, selected without a branch (a branch here
+      // would cut the step into blocks the scheduler cannot interleave):
+      // e8m0, 2^(b-127), b = 0 as 2^-126 * 0.5 (an exponent field of 0 is
+      // not a power of two for the conversion), 0xFF NaN; e4m3, its value
+      // (normal f32, zero or NaN) decoded by the hardware conversion with a
+      // unit scale, split into its power of two and the rest
+      const float p8 = c.s ? __uint_as_float(c.s << 23) : 0x1p-126f;
+      const float m8 = c.s == 0xFF ? __uint_as_float(0x7FC00000u) : c.s ? 1.f : 0.5f;
+      const float sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c.s, 1.0f, false)[0];
+      const bool zero = sc == 0.f, nan = sc != sc;
+      const float p4 = zero || nan ? 1.f : __uint_as_float(__float_as_uint(sc) & 0x7F800000u);
+      const float m4 = zero ? 0.f : nan ? sc : __uint_as_float((__float_as_uint(sc) & 0x807FFFFFu) | 0x3F800000u);
+      const bool e8 = p.sf == STG_SC_E8M0;
+      const float pow2 = e8 ? p8 : p4, mult = e8 ? m8 : m4;
       decode16<fmt>(c.w, pow2, mult, out);
     } else {
       // blocks that do not hold whole 16-value runs: each value finds its
@@ -249,9 +257,7 @@ __global__ __launch_bounds__(kGNT) void gemm_scaled_general_kernel(GeneralParams
           }
           v[u] = k < p.K ? decode_code(code, fmt) * sc : 0.f;
         }
-        const __bf16 b0 = (__bf16)v[0], b1 = (__bf16)v[1];
-        out[e >> 3][(e >> 1) & 3] =
-            (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+        out[e >> 3][(e >> 1) & 3] = pack_bf16x2((f32x2_g){v[0], v[1]});
       }
     }
     *(u32x4*)(region + r * 64 + (a_phys(r, 2 * h) << 4)) = out[0];
@@ -276,10 +282,30 @@ __global__ __launch_bounds__(kGNT) void gemm_scaled_general_kernel(GeneralParams
   // codes are loaded two steps ahead (one global round trip is longer than
   // a step), into two register sets used alternately
   Codes qa0, qb0, qa1, qb1;
+  // scale block of this lane's 16 values in the next step loaded, as a
+  // running quotient and remainder of 32 kt + 16 h by the block (loads go
+  // step by step, 0, 1, 2, ...; a block of 16 or more advances at most twice
+  // per step), instead of a division per load
+  uint32_t s_q = 0, s_r = 0;
+  if constexpr (BLK16) {
+    s_q = 16u * h / (uint32_t)p.block;
+    s_r = 16u * h % (uint32_t)p.block;
+  }
+  auto next_scale = [&]() {
+    const uint32_t q = s_q;
+    if constexpr (BLK16) {
+      const uint32_t blk = (uint32_t)p.block;
+      s_r += kGBK;
+      if (s_r >= blk) s_r -= blk, ++s_q;
+      if (s_r >= blk) s_r -= blk, ++s_q;
+    }
+    return q;
+  };
   auto load_both = [&](int kt, Codes& qa, Codes& qb) {
     const bool last = kt == nk - 1;
-    qa = load_codes(BitsA{}, kt, rs_a, row_a, rs_sa, srow_a, last);
-    qb = load_codes(BitsB{}, kt, rs_b, row_b, rs_sb, srow_b, last);
+    const uint32_t sq = next_scale();
+    qa = load_codes(BitsA{}, kt, rs_a, row_a, rs_sa, srow_a, last, sq);
+    qb = load_codes(BitsB{}, kt, rs_b, row_b, rs_sb, srow_b, last, sq);
   };
   auto decode_both = [&](int kt, const Codes& qa, const Codes& qb) {
     decode_store(IA{}, kt, qa, rs_sa, srow_a, stage_a(kt));
@@ -321,10 +347,21 @@ __global__ __launch_bounds__(kGNT) void gemm_scaled_general_kernel(GeneralParams
   // the same with only whole-vector loads and no end tests, for the steps
   // whose loads and decodes all lie before the last step
   auto inner_step = [&](int kt, Codes& qa_next, Codes& qb_next, Codes& qa_later, Codes& qb_later) {
-    qa_later = load_codes(BitsA{}, kt + 2, rs_a, row_a, rs_sa, srow_a, false);
-    qb_later = load_codes(BitsB{}, kt + 2, rs_b, row_b, rs_sb, srow_b, false);
+    const uint32_t sq = next_scale();
+    qa_later = load_codes(BitsA{}, kt + 2, rs_a, row_a, rs_sa, srow_a, false, sq);
+    qb_later = load_codes(BitsB{}, kt + 2, rs_b, row_b, rs_sb, srow_b, false, sq);
     mfma_step(kt);
     decode_both(kt + 1, qa_next, qb_next);
+    // the decode's VALU work between the MFMAs of the same wave: left to
+    // itself the scheduler issues all 16 MFMAs and then the decode, and the
+    // per-step barrier keeps a SIMD's two waves in that same phase, so the
+    // matrix core idled through both waves' decodes
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the first operand reads
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+    }
     __syncthreads();
   };
 
