@@ -685,35 +685,39 @@ def run_gemm_scaled(stg, inputs, steps, warmup):
                            f"to the whole GEMM as a rate")
         del A, Bt, sa, sb, C
     # the general path: e4m3 scales per 16 values (no scaled-MFMA layout),
-    # values scaled while staged, bf16 MFMA
-    g = inputs.scaled_gemm(M, N, K, "e4m3", block=16)
-    rng = np.random.default_rng(1016)
-    sa_h = rng.integers(0x28, 0x48, g["sa"].shape).astype(np.uint8)  # e4m3 scales 2^-2 .. 2^2 x (1 + m/8)
-    sb_h = rng.integers(0x28, 0x48, g["sb"].shape).astype(np.uint8)
-    A, Bt, sa, sb = _dev(g["A"]), _dev(g["Bt"]), _dev(sa_h), _dev(sb_h)
-    C = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
-    fn = lambda: stg.gemm_scaled(A, "e4m3", sa, Bt, "e4m3", sb, K, 16, scale_fmt="e4m3", out=C)
-    fn()
-    ms = time_fn(fn, steps, warmup)
-    kern = traced_kernel_ms(stg, fn, steps)
-    flop = 2.0 * M * N * K
-    tf = flop / (ms * 1e-3) / 1e12
-    out["gemm_scaled_general_fp8_e4m3scales"] = {
-        "workload": "block-scaled GEMM e4m3 x e4m3 with e4m3 scales per 16 K values (general path: values scaled "
-                    "while staged, bf16 MFMA), A(8191,4096) Bt(8193,4096), fp32 clipped output",
-        "value": round(tf, 1), "unit": "TFLOP/s", "ms": round(ms, 4), "flop": flop,
-        "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4), "kernel_ms": kern,
-        "cold_cache": cold_entry(stg, 0, fn, flop=flop)}
-    if ORACLE_OPS:
-        import oracle
+    # values scaled while staged, bf16 MFMA; fp8 e4m3 values, and fp4 e2m1
+    # values (two per byte) -- e2m1 with e4m3 scales per 16 is the layout of
+    # the 4-bit formats that scale every 16 values
+    for fmt, key, what in (("e4m3", "gemm_scaled_general_fp8_e4m3scales", "e4m3 x e4m3"),
+                           ("e2m1", "gemm_scaled_general_fp4_e4m3scales", "e2m1 x e2m1 (two per byte)")):
+        g = inputs.scaled_gemm(M, N, K, fmt, block=16)
+        rng = np.random.default_rng(1016)
+        sa_h = rng.integers(0x28, 0x48, g["sa"].shape).astype(np.uint8)  # e4m3 scales 2^-2 .. 2^2 x (1 + m/8)
+        sb_h = rng.integers(0x28, 0x48, g["sb"].shape).astype(np.uint8)
+        A, Bt, sa, sb = _dev(g["A"]), _dev(g["Bt"]), _dev(sa_h), _dev(sb_h)
+        C = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+        fn = lambda: stg.gemm_scaled(A, fmt, sa, Bt, fmt, sb, K, 16, scale_fmt="e4m3", out=C)
+        fn()
+        ms = time_fn(fn, steps, warmup)
+        kern = traced_kernel_ms(stg, fn, steps)
+        flop = 2.0 * M * N * K
+        tf = flop / (ms * 1e-3) / 1e12
+        out[key] = {
+            "workload": f"block-scaled GEMM {what} with e4m3 scales per 16 K values (general path: values scaled "
+                        "while staged, bf16 MFMA), A(8191,4096) Bt(8193,4096), fp32 clipped output",
+            "value": round(tf, 1), "unit": "TFLOP/s", "ms": round(ms, 4), "flop": flop,
+            "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4), "kernel_ms": kern,
+            "cold_cache": cold_entry(stg, 0, fn, flop=flop)}
+        if ORACLE_OPS:
+            import oracle
 
-        pr = 2
-        Ap, sap = np.ascontiguousarray(g["A"][:pr]), np.ascontiguousarray(sa_h[:pr])
-        out["gemm_scaled_general_fp8_e4m3scales"]["cpu_baseline"] = oracle_leg(
-            lambda: oracle.gemm_scaled_f64(Ap, "e4m3", sap, g["Bt"], "e4m3", sb_h, K, 16, s_fmt="e4m3"),
-            2.0 * pr * N * K, "TFLOP/s", f"one {pr}-row panel of the {M}-row output, extrapolated to the whole GEMM "
-                                         f"as a rate")
-    del A, Bt, sa, sb, C
+            pr = 2
+            Ap, sap = np.ascontiguousarray(g["A"][:pr]), np.ascontiguousarray(sa_h[:pr])
+            out[key]["cpu_baseline"] = oracle_leg(
+                lambda: oracle.gemm_scaled_f64(Ap, fmt, sap, g["Bt"], fmt, sb_h, K, 16, s_fmt="e4m3"),
+                2.0 * pr * N * K, "TFLOP/s", f"one {pr}-row panel of the {M}-row output, extrapolated to the whole "
+                                             f"GEMM as a rate")
+        del A, Bt, sa, sb, C
     return out
 
 
