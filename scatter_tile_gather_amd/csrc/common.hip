@@ -126,7 +126,12 @@ int check_tensor(const stg_tensor* t, const char* name) {
   for (int d = 0; d < t->rank; ++d) {
     if (t->shape[d] < 0) return fail(STG_ERR_INVALID, "%s: negative shape[%d]", name, d);
     if (t->stride[d] < 0) return fail(STG_ERR_INVALID, "%s: negative stride[%d]", name, d);
-    numel *= t->shape[d];
+    // extents and element counts stay far from int64 overflow, which the
+    // size and offset arithmetic downstream relies on
+    if (t->shape[d] > (int64_t(1) << 40) || t->stride[d] > (int64_t(1) << 40))
+      return fail(STG_ERR_RANGE, "%s: shape[%d] or stride[%d] exceeds 2^40", name, d, d);
+    if (__builtin_mul_overflow(numel, t->shape[d], &numel) || numel > (int64_t(1) << 48))
+      return fail(STG_ERR_RANGE, "%s: more than 2^48 elements", name);
   }
   if (numel > 0 && !t->data) return fail(STG_ERR_INVALID, "%s: null data pointer", name);
   return STG_OK;

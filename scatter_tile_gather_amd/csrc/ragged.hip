@@ -216,6 +216,13 @@ int ragged_setup(const char* name, const void* x, int32_t dtype, int64_t total_r
     return fail(STG_ERR_INVALID, "%s: middle_dim, group, depth, BM and BN must be >= 1", name);
   if (BM % group) return fail(STG_ERR_INVALID, "%s: BM %d is not a multiple of group %d", name, BM, group);
   if (col0 < 0 || col0 >= depth) return fail(STG_ERR_INVALID, "%s: col0 %d not in [0, depth)", name, col0);
+  // a packed row (middle_dim x group x depth elements) must fit the 32-bit
+  // offsets of one tile's rows; checked factor by factor so that the product
+  // cannot overflow first
+  if ((int64_t)depth * es >= kMaxOffset32 || (int64_t)middle_dim * group >= kMaxOffset32 / ((int64_t)depth * es) ||
+      total_rows > (int64_t(1) << 40))
+    return fail(STG_ERR_RANGE, "%s: packed rows of %d x %d x %d elements, or %lld rows, too large", name,
+                middle_dim, group, depth, (long long)total_rows);
   if (n_tiles == 0) return STG_OK;
   if (!tiles || !ragged_idx || !dynamic_dim || !middle_idx)
     return fail(STG_ERR_INVALID, "%s: null tile buffer or tile triples", name);

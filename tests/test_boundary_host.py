@@ -118,6 +118,12 @@ def test_gather_argument_errors(stg):
     neg = _t([16, 8], stride=[-8, 1])
     assert lib.tile_gather(B(neg), 0x10, 8, ts, None, 0, B(out), None) == 1
     assert lib.tile_gather(B(a), 0x10, 8, ts, _i64([1 << 50, 0]), 0, B(out), None) == 3  # offset range
+    # extents whose product would overflow int64 (4 x 2^20 extents = 2^80
+    # elements), and a single extent past 2^40: range errors, nothing launched
+    huge = _t([1 << 20, 1 << 20, 1 << 20, 1 << 20], stride=[0, 0, 0, 1])
+    assert lib.tile_gather(B(huge), 0x10, 8, _i64([4, 1, 1, 8]), None, 0, B(_t([8, 1, 1, 8])), None) == 3
+    assert b"2^48" in lib.stg_last_error()
+    assert lib.tile_gather(B(_t([1 << 41, 8], stride=[8, 1])), 0x10, 8, ts, None, 0, B(out), None) == 3
     # padding value not representable in the element type
     ai, oi = _t([16, 8], dtype=4), _t([8, 8], dtype=4)
     assert lib.tile_gather_masked(B(ai), 0x10, None, 8, ts, None, 0, 300.0, B(oi), None) == 1
@@ -157,6 +163,11 @@ def test_ragged_argument_errors(stg):
     assert call(out=None) == 1
     assert call(middle_dim=0) == 1
     assert call(n=0, out=None) == 0  # nothing to do
+    # packed rows too large for 32-bit tile offsets, factor products that
+    # would overflow, and more than 2^40 rows: range errors
+    assert call(middle_dim=1 << 20, group=1 << 10, BM=1 << 10) == 3
+    assert call(middle_dim=(1 << 31) - 1, group=(1 << 14), depth=(1 << 31) - 1, BM=1 << 14) == 3
+    assert call(total_rows=(1 << 41)) == 3
     n = ctypes.c_int64()
     assert lib.ragged_tile_schedule(None, 3, 4, 1, None, None, None, ctypes.byref(n)) == 1
     lens = np.array([3, -1], dtype=np.int64)
