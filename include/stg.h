@@ -57,7 +57,8 @@ typedef enum {
 
 /* A strided device array: the logical extent `shape` of a (possibly larger)
  * allocation.  rank is 1..4; entries past rank are ignored.  Strides are in
- * elements and must be >= 0. */
+ * elements and must be >= 0.  Every entry point rejects with STG_ERR_RANGE a
+ * descriptor with an extent or stride above 2^40 or more than 2^48 elements. */
 typedef struct {
   void* data;
   int32_t dtype; /* stg_dtype */
