@@ -238,6 +238,10 @@ int launch(const char* name, const stg_tensor* mat, int64_t tm, int64_t tn, int6
   const int64_t M = mat->shape[0], N = mat->shape[1];
   const int64_t G_r = stg_tile_grid(M, r0, sr), G_c = stg_tile_grid(N, c0, sc);
   if (G_r == 0 || G_c == 0) return STG_OK;
+  int64_t n_elems;  // tile-buffer elements, bounded like a descriptor's
+  if (__builtin_mul_overflow(G_r, G_c, &n_elems) || __builtin_mul_overflow(n_elems, tm * tn, &n_elems) ||
+      n_elems > (int64_t(1) << 48))
+    return fail(STG_ERR_RANGE, "%s: the tile buffer would hold more than 2^48 elements", name);
   // every window inside the logical extent: the unchecked instance applies
   const bool inside = r0 >= 0 && c0 >= 0 && r0 + (G_r - 1) * sr + tm <= M && c0 + (G_c - 1) * sc + tn <= N;
   if (!check_bounds && !inside)

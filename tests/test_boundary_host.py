@@ -142,6 +142,11 @@ def test_copy_argument_errors(stg):
     assert lib.tile_store_clipped(0x10, 2, 2, 0, 0, None, None) == 1
     # grids that are empty are a successful no-op without touching the GPU
     assert lib.tile_copy_bounded(B(_t([8, 8])), 2, 2, 8, 0, None, None) == 0
+    # a grid whose tile buffer would exceed 2^48 elements: range error
+    # (the array itself is within the descriptor limit of 2^48 elements)
+    big = _t([1 << 24, 1 << 24], stride=[1 << 24, 1])
+    assert lib.tile_copy_bounded(B(big), 1, 1, -(1 << 20), -(1 << 20), 0x10, None) == 3
+    assert b"tile buffer" in lib.stg_last_error()
 
 
 def test_ragged_argument_errors(stg):
