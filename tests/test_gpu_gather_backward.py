@@ -104,6 +104,25 @@ def test_backward_embedding_scale(stg, orc, ws):
     run_case(stg, orc, a0, idx, (64, 128), g, ws=ws)
 
 
+@pytest.mark.parametrize("dist", ["uniform", "zipf"])
+def test_backward_grouped_workload_full(stg, orc, dist):
+    """The timed gather-backward workloads at full size, in the grouped
+    execution the benchmark runs: a (1048576, 128) fp32 gradient, 4,194,304
+    indices in (64, 128) tiles, drawn uniformly or from Zipf(1.1) truncated to
+    the table (the hottest row takes 519,112 terms: its pieces, the
+    many-workgroup build of the hot buckets and the one-launch sums at the
+    sizes they run at), every element against the fp64 oracle."""
+    rows, n = 1 << 20, 1 << 22
+    rng = np.random.default_rng(4242 + (dist == "zipf"))
+    idx = inputs.zipf_indices(rows=rows, n=n) if dist == "zipf" else rng.integers(0, rows, n).astype(np.int32)
+    g = rng.standard_normal((n, 128), dtype=np.float32)
+    a0 = rng.standard_normal((rows, 128), dtype=np.float32)
+    say("gather backward grouped: full workload", dist)
+    _, count = run_case(stg, orc, a0, idx, (64, 128), g, ws="auto")
+    if dist == "zipf":
+        assert int(count.max()) == 519112  # terms onto each element of the hottest row
+
+
 def test_backward_grouped_long_segments(stg, orc):
     """Grouped execution with a skewed index list: one row takes 5000 terms,
     a few others hundreds, most none."""
