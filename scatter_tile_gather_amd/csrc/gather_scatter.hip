@@ -1482,11 +1482,14 @@ int run(Op op, const stg_tensor* a, const int32_t* indices, const uint8_t* mask,
     p.lo_b = (int32_t)(lo * es);
     p.hi_b = (int32_t)(hi * es);
     for (int i = 0; i < 4; ++i) p.fill[i] = fill[i];
-    // about eight 16-byte vectors per lane, but keep enough workgroups in
-    // flight to cover all 256 CUs several times over
+    // about eight 16-byte vectors per lane, but keep at least 512 workgroups
+    // (two per CU) while rows allow: on the 4096-row, 1 KiB-row gather a
+    // kernel of 512 workgroups of 8 rows takes 3.9 us, of 2048 of 2 rows 5.0
+    // (more workgroups only add dispatch and index resolution to a launch
+    // that is two dependent memory round trips long), of 64 of 64 rows 6.6
     int64_t rows = (kThreads * kUnroll) / p.n_chunks;
     rows = rows < 1 ? 1 : rows > kMaxRowsPerWg ? kMaxRowsPerWg : rows;
-    while (rows > 1 && (p.n_rows + rows - 1) / rows < 2048) rows /= 2;
+    while (rows > 1 && (p.n_rows + rows - 1) / rows < 512) rows /= 2;
     if (rows * p.n_chunks > 65535) rows = 65535 / p.n_chunks;
     p.rows_per_wg = (int32_t)rows;
     const int64_t grid = (p.n_rows + rows - 1) / rows;
