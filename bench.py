@@ -382,7 +382,9 @@ def run_gather(stg, inputs, steps, warmup):
 
     out = torch.empty((idx.numel(), w["a"].shape[1]), dtype=torch.float32, device="cuda:0")
     fn = lambda: stg.tile_gather(a, idx, w["tile_shape"], w["offset"], w["axis"], out=out)
-    ms = time_fn(fn, steps, warmup)
+    # a call is a few microseconds: time at least 200, so that one hiccup of
+    # the host or the driver does not dominate the mean
+    ms = time_fn(fn, max(steps, 200), warmup)
     kms = traced_kernel_ms(stg, fn, steps)
     n_valid = int(((w["indices"] >= 0) & (w["indices"] < w["a"].shape[0])).sum())
     row_b = w["a"].shape[1] * 4
