@@ -427,6 +427,12 @@ constexpr int kHotPairs = 16384;               // a bucket with more terms is bu
                                                // (one workgroup takes ~50 us over 60,000 terms)
 constexpr int kSlice = 16384;                  // terms per workgroup of a hot bucket
 constexpr int kSplitWorkgroups = 1024;         // workgroups on the long segments' pieces, at most
+// Consecutive rounds of list entries per block of such a workgroup.  A block
+// puts that many of a hot row's pieces (the longest ones) one after another
+// on one workgroup, so more rounds save atomics but lengthen the slowest
+// workgroup: Zipf(1.1) over 4M terms, pieces 642 us with one round per block,
+// 619 / 608 / 619 with 2 / 3 / 4, 700 with 8, 929 with 16.
+constexpr int kSplitRounds = 3;
 
 // Terms per piece of a segment of c terms: kSegChunk, or longer for a row so
 // hot that kSegChunk-term pieces would number more than kMaxPieces (their
@@ -1086,74 +1092,106 @@ __device__ __forceinline__ void seg_reduce_wg(const RowParams& p, int64_t R, con
   }
 }
 
-// The pieces of long segments, from the list the segment build
-// wrote: entry (row << 32 | piece), piece >= 0; *n_split entries, a row's
-// pieces consecutive.  A workgroup takes kThreads / LPR consecutive entries,
-// one per group; when they all belong to one row (the common case for a hot
-// row), the groups' partial sums are added together in LDS and go out in one
-// set of atomics, which divides the atomics meeting on that row's elements by
-// the number of groups.
+// Elementwise sum of two chunk sums.
+template <int ESIZE>
+__device__ __forceinline__ u32x4 seg_add(u32x4 a, const u32x4& x) {
+#pragma unroll
+  for (int el = 0; el < 16 / ESIZE; ++el) {
+    if (ESIZE == 4)
+      vec_set<4>(a, el, __float_as_uint(__uint_as_float((uint32_t)vec_get<4>(a, el)) +
+                                        __uint_as_float((uint32_t)vec_get<4>(x, el))));
+    else
+      vec_set<8>(a, el, (uint64_t)__double_as_longlong(__longlong_as_double((long long)vec_get<8>(a, el)) +
+                                                       __longlong_as_double((long long)vec_get<8>(x, el))));
+  }
+  return a;
+}
+
+// The pieces of long segments, from the list the segment build wrote:
+// entry (row << 32 | piece), piece >= 0; *n_split entries, a row's pieces
+// consecutive.  A workgroup takes blocks of kSplitRounds rounds of
+// kThreads / LPR consecutive entries, one entry per group and round, the
+// blocks strided over the workgroups.  When a round's entries all belong to
+// one row (the common case for a hot row), the groups' partial sums are added
+// together in LDS; for rows one pass of a group's lanes covers, that sum is
+// also carried from round to round while the row stays the same, and goes out
+// in one set of atomics when it changes.  A hot row's elements then meet one
+// set of atomics per workgroup and block instead of one per round (the
+// hottest rows' 4096 pieces had met in 512 atomic sets on each element).
 template <int ESIZE, int LPR>
 __device__ __forceinline__ void seg_split_wg(const RowParams& p, const int32_t* offs, const int32_t* perm,
                                              const uint64_t* split_list, const int32_t* n_split, int64_t wg,
                                              int64_t n_wg) {
   constexpr int G = kThreads / LPR;  // groups per workgroup
-  constexpr int V = 16 / ESIZE;
+  constexpr int B = kSplitRounds * G;  // entries per block
   __shared__ u32x4 part[G][LPR];
   __shared__ int64_t s_row[G];
   const int sub = threadIdx.x % LPR, grp = threadIdx.x / LPR;
   const int n = *n_split;
-  for (int64_t e0 = wg * G; e0 < n; e0 += n_wg * G) {
-    const int64_t g = e0 + grp;
-    int64_t r = -1;
-    int32_t kb = 0, ke = 0;
-    if (g < n) {
-      const uint64_t e = split_list[g];
-      r = (int64_t)(e >> 32);
-      const int32_t piece = (int32_t)(uint32_t)e;
-      const int32_t len = seg_piece(offs[r + 1] - offs[r]);
-      kb = offs[r] + piece * len;
-      ke = min(offs[r + 1], kb + len);
-    }
-    if (sub == 0) s_row[grp] = r;
-    __syncthreads();
-    // partly unrolled here and in the sum below: with 32 groups (LPR 8) a
-    // full unroll holds every group's value in registers at once
-    bool one_row = true;
+  const bool single_b = p.hi_b <= seg_first_b(p, 0) + LPR * 16;
+  const int bc = seg_first_b(p, 0) + sub * 16;  // this lane's chunk when single_b
+  int64_t carry_row = -1;                       // row of the carried sum (group 0's lanes hold it)
+  u32x4 carry = {0, 0, 0, 0};
+  for (int64_t blk = wg * B; blk < n; blk += n_wg * B) {
+    for (int64_t e0 = blk; e0 < blk + B && e0 < n; e0 += G) {
+      const int64_t g = e0 + grp;
+      int64_t r = -1;
+      int32_t kb = 0, ke = 0;
+      if (g < n) {
+        const uint64_t e = split_list[g];
+        r = (int64_t)(e >> 32);
+        const int32_t piece = (int32_t)(uint32_t)e;
+        const int32_t len = seg_piece(offs[r + 1] - offs[r]);
+        kb = offs[r] + piece * len;
+        ke = min(offs[r + 1], kb + len);
+      }
+      if (sub == 0) s_row[grp] = r;
+      __syncthreads();
+      // partly unrolled here and in the sums below: with 32 groups (LPR 8) a
+      // full unroll holds every group's value in registers at once
+      bool one_row = true;
 #pragma unroll 4
-    for (int q = 1; q < G; ++q) one_row = one_row && s_row[q] == s_row[0];
-    if (one_row) {  // every entry valid and of one row
-      char* arow = seg_arow(p, r);
-      // the same trip count in every lane (barriers inside): lanes whose
-      // chunk lies past the window add zeros and write nothing
-      for (int b0 = seg_first_b(p, 0); b0 < p.hi_b; b0 += LPR * 16) {
-        const int b = b0 + sub * 16;
-        part[grp][sub] = b < p.hi_b ? seg_chunk_sum<ESIZE>(p, perm, arow, kb, ke, b, false) : (u32x4){0, 0, 0, 0};
+      for (int q = 1; q < G; ++q) one_row = one_row && s_row[q] == s_row[0];
+      if (one_row && single_b) {  // every entry valid and of one row, one chunk per lane
+        part[grp][sub] = bc < p.hi_b ? seg_chunk_sum<ESIZE>(p, perm, seg_arow(p, r), kb, ke, bc, false)
+                                     : (u32x4){0, 0, 0, 0};
         __syncthreads();
-        if (grp == 0 && b < p.hi_b) {
+        if (grp == 0) {
           u32x4 sum = part[0][sub];
 #pragma unroll 4
-          for (int q = 1; q < G; ++q) {
-            const u32x4 x = part[q][sub];
-#pragma unroll
-            for (int el = 0; el < V; ++el) {
-              if (ESIZE == 4)
-                vec_set<4>(sum, el, __float_as_uint(__uint_as_float((uint32_t)vec_get<4>(sum, el)) +
-                                                    __uint_as_float((uint32_t)vec_get<4>(x, el))));
-              else
-                vec_set<8>(sum, el, (uint64_t)__double_as_longlong(__longlong_as_double((long long)vec_get<8>(sum, el)) +
-                                                                   __longlong_as_double((long long)vec_get<8>(x, el))));
-            }
+          for (int q = 1; q < G; ++q) sum = seg_add<ESIZE>(sum, part[q][sub]);
+          if (r == carry_row) {
+            carry = seg_add<ESIZE>(carry, sum);
+          } else {
+            if (carry_row >= 0 && bc < p.hi_b) seg_chunk_out<ESIZE>(p, seg_arow(p, carry_row), bc, carry, false);
+            carry = sum;
           }
-          seg_chunk_out<ESIZE>(p, arow, b, sum, false);
         }
-        __syncthreads();
+        carry_row = r;  // the same in every lane
+      } else if (one_row) {
+        char* arow = seg_arow(p, r);
+        // the same trip count in every lane (barriers inside): lanes whose
+        // chunk lies past the window add zeros and write nothing
+        for (int b0 = seg_first_b(p, 0); b0 < p.hi_b; b0 += LPR * 16) {
+          const int b = b0 + sub * 16;
+          part[grp][sub] = b < p.hi_b ? seg_chunk_sum<ESIZE>(p, perm, arow, kb, ke, b, false) : (u32x4){0, 0, 0, 0};
+          __syncthreads();
+          if (grp == 0 && b < p.hi_b) {
+            u32x4 sum = part[0][sub];
+#pragma unroll 4
+            for (int q = 1; q < G; ++q) sum = seg_add<ESIZE>(sum, part[q][sub]);
+            seg_chunk_out<ESIZE>(p, arow, b, sum, false);
+          }
+          __syncthreads();
+        }
+      } else if (r >= 0) {
+        seg_sum_terms<ESIZE, LPR>(p, perm, seg_arow(p, r), kb, ke, sub, false);
       }
-    } else if (r >= 0) {
-      seg_sum_terms<ESIZE, LPR>(p, perm, seg_arow(p, r), kb, ke, sub, false);
+      __syncthreads();  // s_row and part are rewritten by the next round
     }
-    __syncthreads();  // s_row is rewritten by the next round
   }
+  // the last carried sum (atomics commute with the ones issued meanwhile)
+  if (grp == 0 && carry_row >= 0 && bc < p.hi_b) seg_chunk_out<ESIZE>(p, seg_arow(p, carry_row), bc, carry, false);
 }
 
 // Both sums in one launch: workgroups [0, n_split_wg) take the pieces of the
