@@ -25,18 +25,20 @@
 // accumulation rounding.
 //
 //  * Tiles 256 x 256 on 8 waves (2 x 4), each wave 128 x 64 accumulators of
-//    v_mfma_f32_32x32x16_bf16; K steps of 32.
-//  * Staging: each lane owns 16 consecutive K values of one row of A and of
-//    one row of Bt per step.  It loads their codes with one buffer load (16
-//    bytes of fp8, 8 of fp4) through a range-checked buffer resource (rows
-//    past M or N and bytes past the matrix read as zero codes), finds each
-//    value's scale byte, decodes code and scale from their bit fields,
-//    multiplies, rounds to bf16 (exact, above) and writes the 16 bf16 values
-//    to an LDS stage of 64-byte rows with the bf16 GEMM's conflict-free chunk
-//    swizzle; values at K and beyond are written as zero.  Both operands are
-//    K-contiguous rows, so both MFMA operands are plain ds_read_b128 reads.
-//  * Two LDS stages: the codes of step k+1 are loaded before step k's MFMAs
-//    and decoded into the other stage after them; one barrier per step.
+//    v_mfma_f32_32x32x16_bf16; K steps of 64.
+//  * Staging: four lanes share a row, each owning 16 consecutive K values of
+//    two rows of A and of two rows of Bt per step.  A lane loads their codes
+//    with one buffer load per row (16 bytes of fp8, 8 of fp4) through a
+//    range-checked buffer resource (rows past M or N and bytes past the
+//    matrix read as zero codes), finds the values' scale byte, decodes code
+//    and scale from their bit fields, multiplies, rounds to bf16 (exact,
+//    above) and writes the 16 bf16 values to an LDS stage of 128-byte rows
+//    under a conflict-free chunk swizzle; values at K and beyond are written
+//    as zero.  Both operands are K-contiguous rows, so both MFMA operands are
+//    plain ds_read_b128 reads.
+//  * Codes are loaded two steps ahead into two register sets; two LDS
+//    stages: step k's MFMAs, then the decode of step k+1 into the other
+//    stage, interleaved by the scheduler; one barrier per step.
 //  * Clipped fp32 epilogue adding the optional accumulator input.
 #include "gemm_common.h"
 
@@ -57,10 +59,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(f32x2_g v) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_g));
 }
 
-constexpr int kGBM = 256, kGBN = 256, kGBK = 32;
+constexpr int kGBM = 256, kGBN = 256, kGBK = 64;
 constexpr int kGWM = 2, kGWN = 4, kGNT = kGWM * kGWN * 64;
 constexpr int kGFM = kGBM / kGWM / 32, kGFN = kGBN / kGWN / 32;  // 4 x 2 blocks of 32 x 32 per wave
-constexpr int kGStage = (kGBM + kGBN) * kGBK * 2;                 // 32 KiB: A rows then B rows, 64 bytes each
+constexpr int kGRowB = kGBK * 2;                                   // bytes per staged bf16 row
+constexpr int kGStage = (kGBM + kGBN) * kGRowB;                    // 64 KiB: A rows then B rows, 128 bytes each
+
+// Physical 16-byte chunk of logical chunk c (0..7) in staged row r: the 16
+// consecutive rows one ds_read_b128 phase reads (one logical chunk each) fall
+// on 16 distinct 16-byte bank groups of the 256-byte bank sweep -- rows of
+// one parity share a half of the sweep and (r >> 1) & 7 spreads them over it.
+__device__ __forceinline__ int g_phys(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 struct GeneralParams {
   const char* A;
@@ -150,9 +159,14 @@ __global__ __launch_bounds__(kGNT) void gemm_scaled_general_kernel(GeneralParams
   const int64_t m0 = (int64_t)tm * kGBM, n0 = (int64_t)tn * kGBN;
   const int nk = (int)((p.K + kGBK - 1) / kGBK);
 
-  // this lane's staging rows: row r of the A tile and of the Bt tile, K
-  // values 16h .. 16h+15 of each step
-  const int r = tid >> 1, h = tid & 1;
+  // this lane's staging: K values 16q .. 16q+15 of each step in rows r and
+  // r + 128 of the A tile and of the Bt tile.  Four lanes cover a row's 64
+  // K values, so one load instruction reads 16 rows x 64 contiguous bytes of
+  // codes (fp8): 16 cache lines per KiB where two lanes per row, 32 K values
+  // a step, touched 32 (and the kernel spent about a third of its time on
+  // those requests)
+  const int r = tid >> 2, q = tid & 3;
+  constexpr int kRP = kGBM / (kGNT / 4);  // row passes: 2
   // buffer resources over each operand's rows of this tile and over the
   // scale matrices: offsets past the matrix read as zero
   auto rsrc_rows = [](const char* base, int64_t row0, int64_t rows, int64_t ld, int64_t row_bytes) {
@@ -164,9 +178,16 @@ __global__ __launch_bounds__(kGNT) void gemm_scaled_general_kernel(GeneralParams
   const __amdgpu_buffer_rsrc_t rs_b = rsrc_rows(p.B, n0, p.N, p.ldb, (p.K * BB + 7) / 8);
   const __amdgpu_buffer_rsrc_t rs_sa = rsrc_rows(p.sa, m0, p.M, p.lds_a, nkb);
   const __amdgpu_buffer_rsrc_t rs_sb = rsrc_rows(p.sb, n0, p.N, p.lds_b, nkb);
-  const bool in_a = m0 + r < p.M, in_b = n0 + r < p.N;
-  const uint32_t row_a = in_a ? (uint32_t)(r * p.lda) : kOOB, row_b = in_b ? (uint32_t)(r * p.ldb) : kOOB;
-  const uint32_t srow_a = in_a ? (uint32_t)(r * p.lds_a) : kOOB, srow_b = in_b ? (uint32_t)(r * p.lds_b) : kOOB;
+  uint32_t row_a[kRP], row_b[kRP], srow_a[kRP], srow_b[kRP];
+#pragma unroll
+  for (int t = 0; t < kRP; ++t) {
+    const int rt = r + t * (kGNT / 4);
+    const bool in_a = m0 + rt < p.M, in_b = n0 + rt < p.N;
+    row_a[t] = in_a ? (uint32_t)(rt * p.lda) : kOOB;
+    row_b[t] = in_b ? (uint32_t)(rt * p.ldb) : kOOB;
+    srow_a[t] = in_a ? (uint32_t)(rt * p.lds_a) : kOOB;
+    srow_b[t] = in_b ? (uint32_t)(rt * p.lds_b) : kOOB;
+  }
 
   // codes of step kt.  All but the last step lie inside K: one vector load
   // each.  In the last step the row may end inside a lane's 16 values, and a
@@ -176,7 +197,7 @@ __global__ __launch_bounds__(kGNT) void gemm_scaled_general_kernel(GeneralParams
                         const __amdgpu_buffer_rsrc_t& rss, uint32_t srow, bool last, uint32_t sq) {
     constexpr int bits = decltype(bits_c)::value;
     Codes c;
-    const uint32_t k = (uint32_t)kt * kGBK + 16 * h;
+    const uint32_t k = (uint32_t)kt * kGBK + 16 * q;
     const uint32_t off = row_off == kOOB ? kOOB : row_off + k * bits / 8;
     c.w = (u32x4){0, 0, 0, 0};
     if (!last || (int64_t)k + 16 <= p.K) {
@@ -204,10 +225,10 @@ __global__ __launch_bounds__(kGNT) void gemm_scaled_general_kernel(GeneralParams
     return c;
   };
 
-  // scaled bf16 values of one lane's 16 K values into LDS row r of the
+  // scaled bf16 values of one lane's 16 K values into LDS row rw of the
   // operand region (zero at K and beyond)
   auto decode_store = [&](auto fmt_c, int kt, const Codes& c, const __amdgpu_buffer_rsrc_t& rss, uint32_t srow,
-                          char* region) {
+                          char* region, int rw) {
     constexpr int fmt = decltype(fmt_c)::value;
     u32x4 out[2];
     if constexpr (BLK16) {
@@ -231,7 +252,7 @@ __global__ __launch_bounds__(kGNT) void gemm_scaled_general_kernel(GeneralParams
       // blocks that do not hold whole 16-value runs: each value finds its
       // scale (the block boundaries inside the run, at most 16)
       constexpr int bits = fmt == STG_LP_E2M1 ? 4 : 8;
-      const int64_t k0 = (int64_t)kt * kGBK + 16 * h;
+      const int64_t k0 = (int64_t)kt * kGBK + 16 * q;
       float sc = 0.f;
       int64_t sidx = -1, next = 0;  // scale index of the current value, first K of the next block
       if (k0 < p.K) {
@@ -260,8 +281,8 @@ __global__ __launch_bounds__(kGNT) void gemm_scaled_general_kernel(GeneralParams
         out[e >> 3][(e >> 1) & 3] = pack_bf16x2((f32x2_g){v[0], v[1]});
       }
     }
-    *(u32x4*)(region + r * 64 + (a_phys(r, 2 * h) << 4)) = out[0];
-    *(u32x4*)(region + r * 64 + (a_phys(r, 2 * h + 1) << 4)) = out[1];
+    *(u32x4*)(region + rw * kGRowB + (g_phys(rw, 2 * q) << 4)) = out[0];
+    *(u32x4*)(region + rw * kGRowB + (g_phys(rw, 2 * q + 1) << 4)) = out[1];
   };
 
   f32x16_g acc[kGFM][kGFN];
@@ -270,62 +291,72 @@ __global__ __launch_bounds__(kGNT) void gemm_scaled_general_kernel(GeneralParams
 #pragma unroll
     for (int j = 0; j < kGFN; ++j)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   auto stage_a = [&](int kt) { return smem + (kt & 1) * kGStage; };
-  auto stage_b = [&](int kt) { return smem + (kt & 1) * kGStage + kGBM * 64; };
+  auto stage_b = [&](int kt) { return smem + (kt & 1) * kGStage + kGBM * kGRowB; };
   using IA = std::integral_constant<int, FA>;
   using IB = std::integral_constant<int, FB>;
   using BitsA = std::integral_constant<int, BA>;
   using BitsB = std::integral_constant<int, BB>;
 
   // codes are loaded two steps ahead (one global round trip is longer than
-  // a step), into two register sets used alternately
-  Codes qa0, qb0, qa1, qb1;
+  // a step), into two register sets used alternately, each holding this
+  // lane's 16 values in each of its rows of A and of Bt
+  struct CodeSet {
+    Codes a[kRP], b[kRP];
+  };
+  CodeSet set0, set1;
   // scale block of this lane's 16 values in the next step loaded, as a
-  // running quotient and remainder of 32 kt + 16 h by the block (loads go
-  // step by step, 0, 1, 2, ...; a block of 16 or more advances at most twice
-  // per step), instead of a division per load
+  // running quotient and remainder of 64 kt + 16 q by the block (loads go
+  // step by step, 0, 1, 2, ...; a block of 16 or more advances at most four
+  // times per step), instead of a division per load
   uint32_t s_q = 0, s_r = 0;
   if constexpr (BLK16) {
-    s_q = 16u * h / (uint32_t)p.block;
-    s_r = 16u * h % (uint32_t)p.block;
+    s_q = 16u * q / (uint32_t)p.block;
+    s_r = 16u * q % (uint32_t)p.block;
   }
   auto next_scale = [&]() {
-    const uint32_t q = s_q;
+    const uint32_t sq = s_q;
     if constexpr (BLK16) {
       const uint32_t blk = (uint32_t)p.block;
       s_r += kGBK;
-      if (s_r >= blk) s_r -= blk, ++s_q;
-      if (s_r >= blk) s_r -= blk, ++s_q;
+#pragma unroll
+      for (int u = 0; u < kGBK / 16; ++u)
+        if (s_r >= blk) s_r -= blk, ++s_q;
     }
-    return q;
+    return sq;
   };
-  auto load_both = [&](int kt, Codes& qa, Codes& qb) {
-    const bool last = kt == nk - 1;
+  auto load_set = [&](int kt, CodeSet& cs, bool last) {
     const uint32_t sq = next_scale();
-    qa = load_codes(BitsA{}, kt, rs_a, row_a, rs_sa, srow_a, last, sq);
-    qb = load_codes(BitsB{}, kt, rs_b, row_b, rs_sb, srow_b, last, sq);
+#pragma unroll
+    for (int t = 0; t < kRP; ++t) {
+      cs.a[t] = load_codes(BitsA{}, kt, rs_a, row_a[t], rs_sa, srow_a[t], last, sq);
+      cs.b[t] = load_codes(BitsB{}, kt, rs_b, row_b[t], rs_sb, srow_b[t], last, sq);
+    }
   };
-  auto decode_both = [&](int kt, const Codes& qa, const Codes& qb) {
-    decode_store(IA{}, kt, qa, rs_sa, srow_a, stage_a(kt));
-    decode_store(IB{}, kt, qb, rs_sb, srow_b, stage_b(kt));
+  auto decode_set = [&](int kt, const CodeSet& cs) {
+#pragma unroll
+    for (int t = 0; t < kRP; ++t) {
+      decode_store(IA{}, kt, cs.a[t], rs_sa, srow_a[t], stage_a(kt), r + t * (kGNT / 4));
+      decode_store(IB{}, kt, cs.b[t], rs_sb, srow_b[t], stage_b(kt), r + t * (kGNT / 4));
+    }
   };
   auto mfma_step = [&](int kt) {
     const char* as = stage_a(kt);
     const char* bs = stage_b(kt);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < kGBK / 16; ++ks) {
       bf16x8_g fa[kGFM], fb[kGFN];
 #pragma unroll
       for (int i = 0; i < kGFM; ++i) {
         const int rr = wm * (kGBM / kGWM) + i * 32 + (lane & 31);
-        fa[i] = *(const bf16x8_g*)(as + rr * 64 + (a_phys(rr, 2 * ks + (lane >> 5)) << 4));
+        fa[i] = *(const bf16x8_g*)(as + rr * kGRowB + (g_phys(rr, 2 * ks + (lane >> 5)) << 4));
       }
 #pragma unroll
       for (int j = 0; j < kGFN; ++j) {
         const int rr = wn * (kGBN / kGWN) + j * 32 + (lane & 31);
-        fb[j] = *(const bf16x8_g*)(bs + rr * 64 + (a_phys(rr, 2 * ks + (lane >> 5)) << 4));
+        fb[j] = *(const bf16x8_g*)(bs + rr * kGRowB + (g_phys(rr, 2 * ks + (lane >> 5)) << 4));
       }
 #pragma unroll
       for (int i = 0; i < kGFM; ++i)
@@ -334,57 +365,56 @@ __global__ __launch_bounds__(kGNT) void gemm_scaled_general_kernel(GeneralParams
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
   };
-  // step kt: load the codes of step kt + 2 into (qa_later, qb_later) -- that
-  // set's codes, of step kt, were decoded in step kt - 1 -- then the MFMAs of
-  // stage kt, then the decode of step kt + 1 from (qa_next, qb_next) into the
-  // other stage, last read in step kt - 1 before its barrier
-  auto step = [&](int kt, Codes& qa_next, Codes& qb_next, Codes& qa_later, Codes& qb_later) {
-    if (kt + 2 < nk) load_both(kt + 2, qa_later, qb_later);
+  // step kt: load the codes of step kt + 2 into `later` -- that set's codes,
+  // of step kt, were decoded in step kt - 1 -- then the MFMAs of stage kt,
+  // then the decode of step kt + 1 from `next` into the other stage, last
+  // read in step kt - 1 before its barrier
+  auto step = [&](int kt, CodeSet& next, CodeSet& later) {
+    if (kt + 2 < nk) load_set(kt + 2, later, kt + 2 == nk - 1);
     mfma_step(kt);
-    if (kt + 1 < nk) decode_both(kt + 1, qa_next, qb_next);
+    if (kt + 1 < nk) decode_set(kt + 1, next);
     __syncthreads();
   };
   // the same with only whole-vector loads and no end tests, for the steps
   // whose loads and decodes all lie before the last step
-  auto inner_step = [&](int kt, Codes& qa_next, Codes& qb_next, Codes& qa_later, Codes& qb_later) {
-    const uint32_t sq = next_scale();
-    qa_later = load_codes(BitsA{}, kt + 2, rs_a, row_a, rs_sa, srow_a, false, sq);
-    qb_later = load_codes(BitsB{}, kt + 2, rs_b, row_b, rs_sb, srow_b, false, sq);
+  constexpr int kMfmas = kGFM * kGFN * (kGBK / 16);  // per wave and step
+  auto inner_step = [&](int kt, CodeSet& next, CodeSet& later) {
+    load_set(kt + 2, later, false);
     mfma_step(kt);
-    decode_both(kt + 1, qa_next, qb_next);
+    decode_set(kt + 1, next);
     // the decode's VALU work between the MFMAs of the same wave: left to
-    // itself the scheduler issues all 16 MFMAs and then the decode, and the
+    // itself the scheduler issues all the MFMAs and then the decode, and the
     // per-step barrier keeps a SIMD's two waves in that same phase, so the
     // matrix core idled through both waves' decodes
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the first operand reads
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // the first operand reads
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < kMfmas; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // five VALU
     }
     __syncthreads();
   };
 
   if (nk > 0) {
-    load_both(0, qa0, qb0);
-    if (nk > 1) load_both(1, qa1, qb1);
-    decode_both(0, qa0, qb0);
+    load_set(0, set0, nk == 1);
+    if (nk > 1) load_set(1, set1, nk == 2);
+    decode_set(0, set0);
   }
   __syncthreads();
   int kt = 0;
   // inner steps while kt + 2 < nk - 1, two at a time (the register sets swap)
   for (; kt + 4 < nk; kt += 2) {
-    inner_step(kt, qa1, qb1, qa0, qb0);
-    inner_step(kt + 1, qa0, qb0, qa1, qb1);
+    inner_step(kt, set1, set0);
+    inner_step(kt + 1, set0, set1);
   }
   for (; kt + 1 < nk; kt += 2) {
-    step(kt, qa1, qb1, qa0, qb0);
-    step(kt + 1, qa0, qb0, qa1, qb1);
+    step(kt, set1, set0);
+    step(kt + 1, set0, set1);
   }
-  if (kt < nk) step(kt, qa1, qb1, qa0, qb0);
+  if (kt < nk) step(kt, set1, set0);
 
-  // clipped epilogue: lane l, accumulator q of block (i, j) is row
-  // 8(q/4) + 4(l/32) + q%4, column l%32 of that 32 x 32 block
+  // clipped epilogue: lane l, accumulator v of block (i, j) is row
+  // 8(v/4) + 4(l/32) + v%4, column l%32 of that 32 x 32 block
 #pragma unroll
   for (int i = 0; i < kGFM; ++i)
 #pragma unroll
@@ -392,11 +422,11 @@ __global__ __launch_bounds__(kGNT) void gemm_scaled_general_kernel(GeneralParams
       const int64_t col = n0 + wn * (kGBN / kGWN) + j * 32 + (lane & 31);
       if (col >= p.N) continue;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int64_t row = m0 + wm * (kGBM / kGWM) + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = m0 + wm * (kGBM / kGWM) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (row >= p.M) continue;
         const float a = p.acc ? p.acc[row * p.ldacc + col] : 0.f;
-        p.C[row * p.ldc + col] = a + acc[i][j][q];
+        p.C[row * p.ldc + col] = a + acc[i][j][v];
       }
     }
 }

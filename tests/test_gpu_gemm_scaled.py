@@ -357,7 +357,7 @@ def test_scaled_general_exact(stg, orc, fa, fb, scale_fmt, block, shape):
     in fp32, so the general path must match the oracle bit for bit.  This pins
     which scale meets which value (blocks of 1, 3, 16, 48, 96 that do not
     split into 32-value groups), the FP4 nibble order next to fp8 bytes, and
-    the ragged M, N and K tails (K = 99 and 40 end inside a 32-value step;
+    the ragged M, N and K tails (K = 99 and 40 end inside a 64-value step;
     fp4 with K = 99 has an odd row length)."""
     M, N, K = shape
     if mfma_path(fa, fb, block, scale_fmt):
