@@ -39,19 +39,23 @@ class StgTensor(ctypes.Structure):
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
-_TP = ctypes.POINTER(StgTensor)
+# const stg_tensor* and const int64_t[4] arguments: passed as the bytes of
+# the structure or array (ctypes hands the C side a pointer to them), which
+# converts faster than a typed pointer; byref() of a StgTensor is accepted too
+_TP = ctypes.c_void_p
+_C64 = ctypes.c_void_p
 _I64P = ctypes.POINTER(ctypes.c_int64)
 
 _SIGNATURES = {
     "stg_version": (ctypes.c_int, []),
     "stg_last_error": (ctypes.c_char_p, []),
     "stg_tile_grid": (_I64, [_I64, _I64, _I64]),
-    "tile_gather": (ctypes.c_int, [_TP, _P, _I64, _I64P, _I64P, _I32, _TP, _P]),
-    "tile_gather_masked": (ctypes.c_int, [_TP, _P, _P, _I64, _I64P, _I64P, _I32, ctypes.c_double, _TP, _P]),
-    "tile_scatter_masked": (ctypes.c_int, [_TP, _P, _P, _I64, _I64P, _I64P, _I32, _TP, _P]),
-    "tile_gather_backward": (ctypes.c_int, [_TP, _P, _I64, _I64P, _I64P, _I32, _TP, _P, _I64, _P]),
-    "tile_gather_backward_workspace": (_I64, [_TP, _I64, _I64P, _I32]),
-    "tile_gather_backward_static": (ctypes.c_int, [_TP, _P, _I64, _I64P, _I64P, _I32, _TP, _P]),
+    "tile_gather": (ctypes.c_int, [_TP, _P, _I64, _C64, _C64, _I32, _TP, _P]),
+    "tile_gather_masked": (ctypes.c_int, [_TP, _P, _P, _I64, _C64, _C64, _I32, ctypes.c_double, _TP, _P]),
+    "tile_scatter_masked": (ctypes.c_int, [_TP, _P, _P, _I64, _C64, _C64, _I32, _TP, _P]),
+    "tile_gather_backward": (ctypes.c_int, [_TP, _P, _I64, _C64, _C64, _I32, _TP, _P, _I64, _P]),
+    "tile_gather_backward_workspace": (_I64, [_TP, _I64, _C64, _I32]),
+    "tile_gather_backward_static": (ctypes.c_int, [_TP, _P, _I64, _C64, _C64, _I32, _TP, _P]),
     "tile_copy_bounded": (ctypes.c_int, [_TP, _I64, _I64, _I64, _I64, _P, _P]),
     "tile_store_clipped": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _TP, _P]),
     "tile_copy_windows": (ctypes.c_int, [_TP, _I64, _I64, _I64, _I64, _I64, _I64, _I32, _P, _P]),
@@ -88,10 +92,16 @@ def exported_names():
     return list(_SIGNATURES)
 
 
-def _torch():
-    import torch
+_TORCH = None
 
-    return torch
+
+def _torch():
+    global _TORCH
+    if _TORCH is None:
+        import torch
+
+        _TORCH = torch
+    return _TORCH
 
 
 _DTYPES = None  # torch dtype -> stg_dtype, built on first use
@@ -121,29 +131,44 @@ def _on_gpu(t, name: str):
         raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
 
 
-_I64x4 = ctypes.c_int64 * 4
 # stg_tensor's bytes: data, dtype, rank, shape[4], stride[4] (no padding);
-# packing them and copying the bytes in once is about 4x faster than
-# building the structure field by field, which small latency-bound calls feel
+# packing them in one call is several times faster than building the
+# structure field by field, which small latency-bound calls feel
 _DESC = struct.Struct("<Qii4q4q")
 assert _DESC.size == ctypes.sizeof(StgTensor)
 _ONES = ((), (1,), (1, 1), (1, 1, 1))
 _ZEROS = ((), (0,), (0, 0), (0, 0, 0))
 
 
-def _desc(t, name: str) -> StgTensor:
+def _desc(t, name: str) -> bytes:
+    """The stg_tensor of GPU tensor `t`, as the structure's bytes."""
     _on_gpu(t, name)
     shape = t.shape
     r = len(shape)
     if r < 1 or r > 4:
         raise ValueError(f"{name}: rank must be 1..4")
     pad = 4 - r
-    return StgTensor.from_buffer_copy(_DESC.pack(t.data_ptr(), _dtype_code(t), r, *shape, *_ONES[pad], *t.stride(),
-                                                 *_ZEROS[pad]))
+    return _DESC.pack(t.data_ptr(), _dtype_code(t), r, *shape, *_ONES[pad], *t.stride(), *_ZEROS[pad])
 
 
-def _i64arr(vals):
-    return _I64x4(*(int(v) for v in vals))
+_I64x4 = struct.Struct("<4q")
+_I64_CACHE = {}
+
+
+def _i64arr(vals) -> bytes:
+    """A tile shape or offset as the bytes of an int64_t[4] (zero-padded).
+    The C side only reads these arrays, so one immutable copy per distinct
+    value is kept and reused: a repeated call skips the packing."""
+    key = vals if type(vals) is tuple else tuple(vals)
+    b = _I64_CACHE.get(key)
+    if b is None:
+        if len(key) > 4:
+            raise ValueError("a tile shape or offset has at most 4 entries")
+        b = _I64x4.pack(*(int(v) for v in key), *(0,) * (4 - len(key)))
+        if len(_I64_CACHE) >= 4096:
+            _I64_CACHE.clear()
+        _I64_CACHE[key] = b
+    return b
 
 
 _RAW_STREAM = None
@@ -282,13 +307,12 @@ def _gather_out_shape(tile_shape, n, axis):
 
 def tile_gather(a, indices, tile_shape, offset=None, axis: int = 0, out=None, stream=None):
     torch = _torch()
-    lib = load_library()
     n = indices.numel()
     if out is None:
         out = torch.empty(_gather_out_shape(tile_shape, n, axis), dtype=a.dtype, device=a.device)
     ad, od = _desc(a, "a"), _desc(out, "out")
-    _call("tile_gather", ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"), n, _i64arr(tile_shape),
-                           None if offset is None else _i64arr(offset), axis, ctypes.byref(od), _stream(stream, a))
+    _call("tile_gather", ad, _dev_array(indices, torch.int32, "indices"), n, _i64arr(tile_shape),
+                           None if offset is None else _i64arr(offset), axis, od, _stream(stream, a))
     return out
 
 
@@ -303,9 +327,9 @@ def tile_gather_masked(a, indices, mask, tile_shape, offset=None, axis: int = 0,
     if mask is not None and mask.numel() != n:
         raise ValueError("mask must hold one entry per index")
     mp = None if mask is None else _dev_array(mask, torch.uint8, "mask")
-    _call("tile_gather_masked", ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"), mp, n,
+    _call("tile_gather_masked", ad, _dev_array(indices, torch.int32, "indices"), mp, n,
                                   _i64arr(tile_shape), None if offset is None else _i64arr(offset), axis,
-                                  float(padding_value), ctypes.byref(od), _stream(stream, a))
+                                  float(padding_value), od, _stream(stream, a))
     return out
 
 
@@ -314,7 +338,7 @@ def tile_gather_backward_workspace(a_grad, n_indices: int, tile_shape, axis: int
     runs on atomics."""
     lib = load_library()
     ad = _desc(a_grad, "a_grad")
-    n = int(lib.tile_gather_backward_workspace(ctypes.byref(ad), n_indices, _i64arr(tile_shape), axis))
+    n = int(lib.tile_gather_backward_workspace(ad, n_indices, _i64arr(tile_shape), axis))
     if n < 0:
         raise StgError(-n, lib.stg_last_error().decode())
     return n
@@ -347,9 +371,9 @@ def tile_gather_backward(a_grad, indices, tile_shape, grad_out, offset=None, axi
     if workspace is not None:
         _on_gpu(workspace, "workspace")
         ws_ptr, ws_n = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    _call("tile_gather_backward", ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"), n,
+    _call("tile_gather_backward", ad, _dev_array(indices, torch.int32, "indices"), n,
                                     _i64arr(tile_shape), None if offset is None else _i64arr(offset), axis,
-                                    ctypes.byref(gd), ws_ptr, ws_n, _stream(stream, a_grad))
+                                    gd, ws_ptr, ws_n, _stream(stream, a_grad))
     return a_grad
 
 
@@ -367,9 +391,9 @@ def tile_gather_backward_static(a_grad, indices, tile_shape, grad_out, offset=No
     ad, gd = _desc(a_grad, "a_grad"), _desc(grad_out, "grad_out")
     # the library takes the current device's static array: make it a_grad's
     with torch.cuda.device(a_grad.device):
-        _call("tile_gather_backward_static", ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"),
+        _call("tile_gather_backward_static", ad, _dev_array(indices, torch.int32, "indices"),
               indices.numel(), _i64arr(tile_shape), None if offset is None else _i64arr(offset), axis,
-              ctypes.byref(gd), _stream(stream, a_grad))
+              gd, _stream(stream, a_grad))
     return a_grad
 
 
@@ -381,9 +405,9 @@ def tile_scatter_masked(a, indices, mask, tile_shape, tile, offset=None, axis: i
     if mask is not None and mask.numel() != n:
         raise ValueError("mask must hold one entry per index")
     mp = None if mask is None else _dev_array(mask, torch.uint8, "mask")
-    _call("tile_scatter_masked", ctypes.byref(ad), _dev_array(indices, torch.int32, "indices"), mp, n,
+    _call("tile_scatter_masked", ad, _dev_array(indices, torch.int32, "indices"), mp, n,
                                    _i64arr(tile_shape), None if offset is None else _i64arr(offset), axis,
-                                   ctypes.byref(td), _stream(stream, a))
+                                   td, _stream(stream, a))
     return a
 
 
@@ -401,7 +425,7 @@ def tile_copy_bounded(src, tile_rows: int, tile_cols: int, origin_row: int = 0, 
     if out.dtype != src.dtype or not out.is_contiguous() or out.numel() < max(gr, 0) * max(gc, 0) * tile_rows * tile_cols:
         raise ValueError("out must be a contiguous tile buffer of the source dtype and grid size")
     sd = _desc(src, "src")
-    _call("tile_copy_bounded", ctypes.byref(sd), tile_rows, tile_cols, origin_row, origin_col, out.data_ptr(),
+    _call("tile_copy_bounded", sd, tile_rows, tile_cols, origin_row, origin_col, out.data_ptr(),
                                  _stream(stream, src))
     return out
 
@@ -421,7 +445,7 @@ def tile_copy_windows(src, tile_rows: int, tile_cols: int, step_rows: int, step_
     if out.dtype != src.dtype or not out.is_contiguous() or out.numel() < max(gr, 0) * max(gc, 0) * tile_rows * tile_cols:
         raise ValueError("out must be a contiguous tile buffer of the source dtype and grid size")
     sd = _desc(src, "src")
-    _call("tile_copy_windows", ctypes.byref(sd), tile_rows, tile_cols, step_rows, step_cols, origin_row, origin_col,
+    _call("tile_copy_windows", sd, tile_rows, tile_cols, step_rows, step_cols, origin_row, origin_col,
                                  1 if check_bounds else 0, out.data_ptr(), _stream(stream, src))
     return out
 
@@ -438,7 +462,7 @@ def tile_store_windows(tiles, step_rows: int, step_cols: int, origin_row: int, o
         raise ValueError("tile buffer grid does not match dst, step and origin")
     dd = _desc(dst, "dst")
     _call("tile_store_windows", tiles.data_ptr(), tr, tc, step_rows, step_cols, origin_row, origin_col,
-                                  1 if check_bounds else 0, ctypes.byref(dd), _stream(stream, dst))
+                                  1 if check_bounds else 0, dd, _stream(stream, dst))
     return dst
 
 
@@ -452,7 +476,7 @@ def tile_store_clipped(tiles, origin_row: int, origin_col: int, dst, stream=None
                                             stg_tile_grid(dst.shape[1], origin_col, tc)):
         raise ValueError("tile buffer grid does not match dst and origin")
     dd = _desc(dst, "dst")
-    _call("tile_store_clipped", tiles.data_ptr(), tr, tc, origin_row, origin_col, ctypes.byref(dd),
+    _call("tile_store_clipped", tiles.data_ptr(), tr, tc, origin_row, origin_col, dd,
                                   _stream(stream, dst))
     return dst
 

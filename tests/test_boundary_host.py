@@ -344,3 +344,27 @@ def test_prepare_capture_is_per_thread(stg):
     assert seen == {"capture": None, "made": True}
     assert [name for name, _, _ in mine] == ["stg_tile_grid"]
     assert b._capturing() is None
+
+
+def test_packed_descriptor_and_array_bytes(stg):
+    """The binding passes stg_tensor and int64_t[4] arguments as packed bytes:
+    the packing matches the structure's fields, the C side reads it (its
+    argument checks see the packed rank, dtype and shape), and the cached
+    shape arrays are zero-padded copies keyed by value."""
+    from scatter_tile_gather_amd import _binding as b
+
+    raw = b._DESC.pack(0x1000, 0, 2, 16, 8, 1, 1, 8, 1, 0, 0)
+    d = StgTensor.from_buffer_copy(raw)
+    assert (d.data, d.dtype, d.rank) == (0x1000, 0, 2)
+    assert list(d.shape) == [16, 8, 1, 1] and list(d.stride) == [8, 1, 0, 0]
+    lib = stg.load_library()
+    out = b._DESC.pack(0x2000, 0, 2, 8, 8, 1, 1, 8, 1, 0, 0)
+    ts = b._i64arr((4, 8))
+    assert ts == (4).to_bytes(8, "little") + (8).to_bytes(8, "little") + bytes(16)
+    assert b._i64arr([4, 8]) is ts and b._i64arr((np.int64(4), np.int64(8))) is ts
+    with pytest.raises(ValueError):
+        b._i64arr((1, 2, 3, 4, 5))
+    assert lib.tile_gather(raw, 0x10, 12, ts, None, 0, out, None) == 1  # out rows != 12
+    assert lib.tile_gather(b._DESC.pack(0x1000, 0, 5, 16, 8, 1, 1, 8, 1, 0, 0), 0x10, 8, ts, None, 0, out, None) == 1
+    assert lib.tile_gather(b._DESC.pack(0x1000, 9, 2, 16, 8, 1, 1, 8, 1, 0, 0), 0x10, 8, ts, None, 0, out, None) == 2
+    assert lib.tile_gather(raw, 0x10, 8, ts, b._i64arr((1 << 50, 0)), 0, out, None) == 3  # offset range
