@@ -565,45 +565,51 @@ __device__ __forceinline__ void list_pieces_waves(const int32_t (&c)[kPer], int6
   }
 }
 
-// The same list for a hot bucket, whose rows can have up to kMaxPieces
-// entries each, too many for one wavefront to write: the rows' first places
-// go to LDS, and every thread of the workgroup writes entries, finding an
-// entry's row by binary search.  (In the other buckets the extra LDS and
-// barriers cost more than they save.)
+// Pieces of a segment of c terms in the long-segment list (0 for a short one).
+__device__ __forceinline__ int32_t seg_n_pieces(int32_t c) {
+  return c > kSegChunk ? (c + seg_piece(c) - 1) / seg_piece(c) : 0;
+}
+
+// The same list for the window [w0, w0 + kWindow) of a hot bucket, whose
+// rows can have up to kMaxPieces entries each, too many for one wavefront to
+// write: c holds the terms of this thread's rows, the window's entries go to
+// split_list[base ..), and this workgroup writes entries [share_lo,
+// share_hi) of them -- a hot bucket's entries are shared out among its slice
+// workgroups -- each thread finding an entry's row by binary search over the
+// rows' first places in LDS.  Returns the window's number of entries (the
+// same in every thread).
 template <int kPer>
-__device__ __forceinline__ void list_pieces_wg(const int32_t (&c)[kPer], int64_t w0, uint64_t* split_list,
-                                               int32_t* n_split) {
+__device__ __forceinline__ int32_t list_pieces_share(const int32_t (&c)[kPer], int64_t w0, uint64_t* split_list,
+                                                     int64_t base, int64_t share_num, int64_t share_den) {
   constexpr int kRows = kPer * kBuildThreads;
   static_assert(kRows == 1 << 12, "the binary search below takes 12 steps");
-  __shared__ int32_t s_at;
-  __shared__ int32_t s_first[kRows];  // first place of each row's pieces, relative to s_at
+  __shared__ int32_t s_first[kRows];  // first place of each row's pieces, relative to base
   int32_t mine = 0;
 #pragma unroll
-  for (int e = 0; e < kPer; ++e)
-    if (c[e] > kSegChunk) mine += (c[e] + seg_piece(c[e]) - 1) / seg_piece(c[e]);
+  for (int e = 0; e < kPer; ++e) mine += seg_n_pieces(c[e]);
   int32_t total;
   int32_t at = block_exclusive_scan<kBuildThreads>(mine, total);
-  if (total == 0) return;  // uniform: the same total in every thread
-  if (threadIdx.x == 0) s_at = atomicAdd(n_split, total);
+  if (total == 0) return 0;  // uniform: the same total in every thread
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
     s_first[threadIdx.x * kPer + e] = at;
-    if (c[e] > kSegChunk) at += (c[e] + seg_piece(c[e]) - 1) / seg_piece(c[e]);
+    at += seg_n_pieces(c[e]);
   }
   __syncthreads();
-  const int32_t base = s_at;
-  for (int32_t q = threadIdx.x; q < total; q += kBuildThreads) {
+  const int32_t lo = (int32_t)(total * share_num / share_den), hi = (int32_t)(total * (share_num + 1) / share_den);
+  for (int32_t q = lo + (int32_t)threadIdx.x; q < hi; q += kBuildThreads) {
     // the entry's row: the last row whose first place is at or before q
     // (rows without pieces have an empty range and are passed over)
-    int lo = 0, hi = kRows - 1;
+    int r0 = 0, r1 = kRows - 1;
 #pragma unroll
     for (int step = 0; step < 12; ++step) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_first[mid] <= q) lo = mid; else hi = mid - 1;
+      const int mid = (r0 + r1 + 1) >> 1;
+      if (s_first[mid] <= q) r0 = mid; else r1 = mid - 1;
     }
-    split_list[(int64_t)base + q] = ((uint64_t)(w0 + lo) << 32) | (uint32_t)(q - s_first[lo]);
+    split_list[base + q] = ((uint64_t)(w0 + r0) << 32) | (uint32_t)(q - s_first[r0]);
   }
-  __syncthreads();  // s_at and s_first are rewritten by the next window
+  __syncthreads();  // s_first is rewritten by the next window
+  return total;
 }
 
 // Step 4: one workgroup per bucket.  Its pairs are pairs[s0, s1); its rows
@@ -757,9 +763,8 @@ __global__ __launch_bounds__(kBuildThreads) void seg_hot_count_kernel(int64_t R,
 }
 
 __global__ __launch_bounds__(kBuildThreads) void seg_hot_scan_kernel(int64_t R, int shift, int64_t n_chunks,
-                                                                     const int32_t* pos1, const int32_t* hot,
-                                                                     int32_t* offs, int32_t* gcur,
-                                                                     uint64_t* split_list, int32_t* n_split) {
+                                                                     const int32_t* pos1, int32_t* hot,
+                                                                     int32_t* offs, int32_t* gcur, int32_t* n_split) {
   constexpr int kPer = kWindow / kBuildThreads;  // 4
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
@@ -768,6 +773,7 @@ __global__ __launch_bounds__(kBuildThreads) void seg_hot_scan_kernel(int64_t R, 
   const int64_t row_lo = (int64_t)b << shift;
   const int64_t row_hi = min(R, (int64_t)(b + 1) << shift);
   int64_t base = s0;
+  int32_t pieces = 0;  // the bucket's long-segment pieces (this thread's rows)
   for (int64_t w0 = row_lo; w0 < row_hi; w0 += kWindow) {
     const int64_t W = min((int64_t)kWindow, row_hi - w0);
     int32_t c[kPer], v = 0;
@@ -776,6 +782,7 @@ __global__ __launch_bounds__(kBuildThreads) void seg_hot_scan_kernel(int64_t R, 
       const int j = tid * kPer + e;
       c[e] = j < W ? gcur[w0 + j] : 0;
       v += c[e];
+      pieces += seg_n_pieces(c[e]);
     }
     int32_t total;
     int32_t run = (int32_t)base + block_exclusive_scan<kBuildThreads>(v, total);
@@ -788,21 +795,48 @@ __global__ __launch_bounds__(kBuildThreads) void seg_hot_scan_kernel(int64_t R, 
       }
       run += c[e];
     }
-    list_pieces_wg(c, w0, split_list, n_split);
     base += total;
   }
+  // one place in the piece list for all of the bucket's entries; the slice
+  // workgroups of seg_hot_place write them.  hot[b] keeps that place + 1.
+  int32_t n_pieces;
+  block_exclusive_scan<kBuildThreads>(pieces, n_pieces);
+  if (tid == 0) hot[b] = 1 + (n_pieces ? atomicAdd(n_split, n_pieces) : 0);
 }
 
 __global__ __launch_bounds__(kBuildThreads) void seg_hot_place_kernel(int64_t R, int shift, int64_t n_chunks,
                                                                       const int32_t* pos1, const uint64_t* pairs,
                                                                       const uint64_t* hot_list, const int32_t* n_hot,
-                                                                      int32_t* gcur, int32_t* perm) {
+                                                                      const int32_t* hot, const int32_t* offs,
+                                                                      int32_t* gcur, int32_t* perm,
+                                                                      uint64_t* split_list) {
   __shared__ int32_t cnt[kWindow];
   constexpr int kU = 8;
+  constexpr int kPer = kWindow / kBuildThreads;  // 4
   const int tid = threadIdx.x;
   const int nh = *n_hot;
   for (int e = blockIdx.x; e < nh; e += gridDim.x) {
     const HotSlice h = hot_slice(hot_list[e], R, shift, n_chunks, pos1);
+    // this slice's share of the bucket's long-segment piece list: segment
+    // lengths from the offsets the scan wrote, entries from the place it
+    // reserved (one share per slice, so a bucket of many slices -- the
+    // hottest rows' thousands of pieces -- is listed by as many workgroups)
+    {
+      const int b = (int)(hot_list[e] >> 32), g = (int)(uint32_t)hot_list[e];
+      const int64_t s0 = pos1[(int64_t)b * n_chunks], s1 = pos1[(int64_t)(b + 1) * n_chunks];
+      const int64_t ns = (s1 - s0 + kSlice - 1) / kSlice;
+      int64_t base = hot[b] - 1;
+      for (int64_t w0 = h.row_lo; w0 < h.row_hi; w0 += kWindow) {
+        const int64_t W = min((int64_t)kWindow, h.row_hi - w0);
+        int32_t c[kPer];
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+          const int j = tid * kPer + q;
+          c[q] = j < W ? offs[w0 + j + 1] - offs[w0 + j] : 0;
+        }
+        base += list_pieces_share(c, w0, split_list, base, g, ns);
+      }
+    }
     for (int64_t w0 = h.row_lo; w0 < h.row_hi; w0 += kWindow) {
       const int64_t W = min((int64_t)kWindow, h.row_hi - w0);
       hot_window_count(pairs, h.p0, h.p1, w0, W, cnt);
@@ -1366,10 +1400,10 @@ int launch_segmented(const char* name, int esize, const RowParams& p, int64_t R,
   launch_kernel("tile_gather_backward/hot_count", seg_hot_count_kernel, hgrid, hblk, 0, s, R, L.shift, L.n_chunks,
                 (const int32_t*)pos1, (const uint64_t*)pairs, (const uint64_t*)hot_list, (const int32_t*)n_hot, gcur);
   launch_kernel("tile_gather_backward/hot_scan", seg_hot_scan_kernel, dim3((unsigned)nbk), hblk, 0, s, R, L.shift,
-                L.n_chunks, (const int32_t*)pos1, (const int32_t*)hot, offs, gcur, split, n_split);
+                L.n_chunks, (const int32_t*)pos1, hot, offs, gcur, n_split);
   launch_kernel("tile_gather_backward/hot_place", seg_hot_place_kernel, hgrid, hblk, 0, s, R, L.shift, L.n_chunks,
-                (const int32_t*)pos1, (const uint64_t*)pairs, (const uint64_t*)hot_list, (const int32_t*)n_hot, gcur,
-                perm);
+                (const int32_t*)pos1, (const uint64_t*)pairs, (const uint64_t*)hot_list, (const int32_t*)n_hot,
+                (const int32_t*)hot, (const int32_t*)offs, gcur, perm, split);
   // lanes per destination row: enough for the row's chunks, at most a wavefront
   const int chunks_per_row = p.n_chunks;
   const int lpr = chunks_per_row <= 8 ? 8 : chunks_per_row <= 16 ? 16 : chunks_per_row <= 32 ? 32 : 64;
