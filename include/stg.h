@@ -349,6 +349,33 @@ int gemm_scaled(const void* A, int32_t a_fmt, int64_t lda, const void* a_scale, 
                 int32_t scale_fmt, int64_t block, const float* acc, int64_t ldacc, float* C,
                 int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream);
 
+/* gemm_scaled with a caller-owned workspace (the same product, cuTile.jl
+ * Operations, muladd_scaled).  Where the second execution above applies and
+ * gemm_scaled_workspace returns n > 0 bytes, a workspace of at least n bytes
+ * (device memory, 256-byte aligned, owned by the caller, unused once the
+ * stream has run the call) makes the call decode each operand once into
+ * bf16 matrices there -- the same exact scaled values -- and multiply them
+ * with the bf16 GEMM of gemm_bounded in fp32: the result is again within fp32
+ * accumulation rounding of the exact sum (the summation order differs).
+ * Without a workspace (NULL, or where the query returns 0) this is
+ * gemm_scaled.  STG_ERR_INVALID for a workspace smaller than the query's
+ * bytes or not 256-byte aligned; otherwise errors as for gemm_scaled.  Calls
+ * that share a workspace and overlap in time race on it. */
+int gemm_scaled_ws(const void* A, int32_t a_fmt, int64_t lda, const void* a_scale, int64_t lds_a,
+                   const void* Bt, int32_t b_fmt, int64_t ldb, const void* b_scale, int64_t lds_b,
+                   int32_t scale_fmt, int64_t block, const float* acc, int64_t ldacc, float* C,
+                   int64_t ldc, int64_t M, int64_t N, int64_t K, void* workspace,
+                   int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes for gemm_scaled_ws: 0 where the call takes the scaled MFMA
+ * or decoding first does not pay (M or N at most 256, K = 0, or sizes past
+ * the bf16 GEMM's limits); otherwise the bytes of the decoded operands, bf16
+ * (M, ceil(K/16)*16) and (K, ceil(N/8)*8), each rounded up to 256.  A
+ * negative value is minus an error code (unknown formats: STG_ERR_UNSUPPORTED;
+ * negative sizes, block < 1, K not a multiple of block: STG_ERR_INVALID). */
+int64_t gemm_scaled_workspace(int32_t a_fmt, int32_t b_fmt, int32_t scale_fmt, int64_t block, int64_t M,
+                              int64_t N, int64_t K);
+
 /* Bounded-edge GEMM C = A . B (cuTile.jl Operations, muladd: bf16 operands
  * accumulate in f32; Tylo.jl Boundary tiles, "Accumulator stores and GEMM":
  * ceiling-division output grid and K loop, zero-filled edge stages, and an

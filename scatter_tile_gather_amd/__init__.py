@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     exported_names,
     gemm_bounded,
     gemm_scaled,
+    gemm_scaled_workspace,
     load_library,
     prepare,
     ragged_tile_load,

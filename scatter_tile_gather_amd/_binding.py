@@ -66,6 +66,9 @@ _SIGNATURES = {
     "gemm_bounded": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _I32, _P]),
     "gemm_scaled": (ctypes.c_int, [_P, _I32, _I64, _P, _I64, _P, _I32, _I64, _P, _I64, _I32, _I64, _P, _I64, _P, _I64,
                                    _I64, _I64, _I64, _P]),
+    "gemm_scaled_ws": (ctypes.c_int, [_P, _I32, _I64, _P, _I64, _P, _I32, _I64, _P, _I64, _I32, _I64, _P, _I64, _P,
+                                      _I64, _I64, _I64, _I64, _P, _I64, _P]),
+    "gemm_scaled_workspace": (_I64, [_I32, _I32, _I32, _I64, _I64, _I64, _I64]),
     "stg_trace_enable": (ctypes.c_int, [ctypes.c_int]),
     "stg_trace_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float)]),
 }
@@ -192,12 +195,26 @@ def _stream(stream, like=None, device=None) -> int:
 
 # per host thread: the list of recorded (name, C function, arguments) while
 # prepare() runs on that thread, else None; calls from other threads meanwhile
-# run as usual
+# run as usual.  _TLS.keep: tensors an entry point allocated for itself while
+# being prepared (an "auto" workspace), held by the Prepared object.
 _TLS = threading.local()
 
 
 def _capturing():
     return getattr(_TLS, "capture", None)
+
+
+def _workspace(nbytes: int, device, stream):
+    """An "auto" workspace of nbytes: allocated on the stream the kernels run
+    on, so that once the caller drops it the caching allocator hands the
+    block out again only to work queued on that stream after them; while
+    prepare() records the call, kept for the prepared call's lifetime."""
+    torch = _torch()
+    with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream(device)):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if _capturing() is not None:
+        _TLS.keep.append(ws)
+    return ws
 
 
 def _call(name: str, *args):
@@ -248,17 +265,17 @@ def prepare(op, *args, **kwargs):
     torch = _torch()
     if _capturing() is not None:
         raise RuntimeError("prepare() does not nest")
-    _TLS.capture = []
+    _TLS.capture, _TLS.keep = [], []
     try:
         result = op(*args, **kwargs)
-        calls = _TLS.capture
+        calls, kept = _TLS.capture, _TLS.keep
     finally:
-        _TLS.capture = None
+        _TLS.capture, _TLS.keep = None, None
     if not calls:
         raise ValueError(f"{getattr(op, '__name__', op)} makes no device call with these arguments")
     tensors = [x for x in list(args) + list(kwargs.values()) if isinstance(x, torch.Tensor)]
     device = next((t.get_device() for t in tensors if t.is_cuda), torch.cuda.current_device())
-    return Prepared(calls, result, (args, kwargs, result), kwargs.get("stream"), device)
+    return Prepared(calls, result, (args, kwargs, result, kept), kwargs.get("stream"), device)
 
 
 def _check(rc: int):
@@ -358,15 +375,7 @@ def tile_gather_backward(a_grad, indices, tile_shape, grad_out, offset=None, axi
     ad, gd = _desc(a_grad, "a_grad"), _desc(grad_out, "grad_out")
     if isinstance(workspace, str) and workspace == "auto":
         nb = tile_gather_backward_workspace(a_grad, n, tile_shape, axis)
-        workspace = None
-        if nb:
-            # allocated on the stream the kernels run on: when this function
-            # returns, the caching allocator hands the block out again only to
-            # work queued on that stream after them
-            if _capturing() is not None:
-                raise ValueError("prepare(): pass a workspace tensor instead of \"auto\"")
-            with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream(a_grad.device)):
-                workspace = torch.empty(nb, dtype=torch.uint8, device=a_grad.device)
+        workspace = _workspace(nb, a_grad.device, stream) if nb else None
     ws_ptr, ws_n = None, 0
     if workspace is not None:
         _on_gpu(workspace, "workspace")
@@ -576,12 +585,24 @@ LOWP_FORMATS = {"e4m3": 0, "e5m2": 1, "e2m1": 2}
 SCALE_FORMATS = {"e8m0": 0, "e4m3": 1}
 
 
+def gemm_scaled_workspace(a_fmt: str, b_fmt: str, scale_fmt: str, block: int, M: int, N: int, K: int) -> int:
+    n = int(load_library().gemm_scaled_workspace(LOWP_FORMATS[a_fmt], LOWP_FORMATS[b_fmt], SCALE_FORMATS[scale_fmt],
+                                                 block, M, N, K))
+    if n < 0:
+        raise StgError(-n, load_library().stg_last_error().decode())
+    return n
+
+
 def gemm_scaled(A, a_fmt: str, a_scale, Bt, b_fmt: str, b_scale, K: int, block: int, scale_fmt: str = "e8m0",
-                acc=None, out=None, stream=None):
+                acc=None, out=None, workspace="auto", stream=None):
     """C = (A . a_scale)(B . b_scale) + acc, fp32.  A: uint8 (M, >= K*bits/8)
     operand codes (e2m1: two per byte, even element low); Bt: uint8 (N, ...)
     = B K-major; scales uint8 (M, >= K/block) and (N, >= K/block); acc / out
-    float32 (M, N)."""
+    float32 (M, N).  workspace: "auto" (allocated here where
+    gemm_scaled_workspace asks for one: the general path then decodes each
+    operand once to bf16 before the bf16 GEMM), a device uint8 tensor of at
+    least that many bytes, or None (no workspace: values decoded inside the
+    GEMM kernel)."""
     torch = _torch()
     lib = load_library()
     for t, nm in ((A, "A"), (Bt, "Bt"), (a_scale, "a_scale"), (b_scale, "b_scale")):
@@ -608,8 +629,15 @@ def gemm_scaled(A, a_fmt: str, a_scale, Bt, b_fmt: str, b_scale, K: int, block: 
         if acc.dtype != torch.float32 or tuple(acc.shape) != (M, N) or (acc.stride(1) != 1 and N > 1):
             raise ValueError("acc must be float32 (M, N) with unit column stride")
         accp, ldacc = acc.data_ptr(), acc.stride(0)
-    _call("gemm_scaled", A.data_ptr(), LOWP_FORMATS[a_fmt], A.stride(0), a_scale.data_ptr(), a_scale.stride(0),
-                           Bt.data_ptr(), LOWP_FORMATS[b_fmt], Bt.stride(0), b_scale.data_ptr(), b_scale.stride(0),
-                           SCALE_FORMATS[scale_fmt], block, accp, ldacc, out.data_ptr(), out.stride(0), M, N, K,
-                           _stream(stream, A))
+    if isinstance(workspace, str) and workspace == "auto":
+        nb = gemm_scaled_workspace(a_fmt, b_fmt, scale_fmt, block, M, N, K)
+        workspace = _workspace(nb, A.device, stream) if nb else None
+    ws_ptr, ws_n = None, 0
+    if workspace is not None:
+        _on_gpu(workspace, "workspace")
+        ws_ptr, ws_n = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _call("gemm_scaled_ws", A.data_ptr(), LOWP_FORMATS[a_fmt], A.stride(0), a_scale.data_ptr(), a_scale.stride(0),
+                              Bt.data_ptr(), LOWP_FORMATS[b_fmt], Bt.stride(0), b_scale.data_ptr(), b_scale.stride(0),
+                              SCALE_FORMATS[scale_fmt], block, accp, ldacc, out.data_ptr(), out.stride(0), M, N, K,
+                              ws_ptr, ws_n, _stream(stream, A))
     return out

@@ -59,7 +59,8 @@ struct GemmParams {
   const char* A;  // bf16 (M, K), row stride lda elements
   const char* B;  // bf16 (K, N), row stride ldb elements
   char* C;
-  int64_t lda, ldb, ldc;
+  const float* acc;  // fp32 output only: (M, N) added to the product, row stride ldacc, or null
+  int64_t lda, ldb, ldc, ldacc;
   int64_t M, N, K;
   int64_t n_base;  // first column covered by this launch
   int32_t tiles_m, tiles_n;
@@ -345,7 +346,8 @@ __global__ __launch_bounds__(CF::NT) __attribute__((amdgpu_waves_per_eu(1, 2))) 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t row = m0 + wm * CF::WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (row < p.M) *(float*)(p.C + (row * p.ldc + col) * 4) = acc[i][j][r];
+          if (row < p.M)
+            *(float*)(p.C + (row * p.ldc + col) * 4) = p.acc ? acc[i][j][r] + p.acc[row * p.ldacc + col] : acc[i][j][r];
         }
       }
     return;
@@ -474,7 +476,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
     if (row < p.M && lane < R) {
       const int64_t col = p.n_base + lane;
       if (p.c_f32)
-        *(float*)(p.C + (row * p.ldc + col) * 4) = mine;
+        *(float*)(p.C + (row * p.ldc + col) * 4) = p.acc ? mine + p.acc[row * p.ldacc + col] : mine;
       else
         *(__bf16*)(p.C + (row * p.ldc + col) * 2) = (__bf16)mine;
     }
@@ -494,7 +496,7 @@ int launch(const char* name, GemmParams p, int64_t cols, hipStream_t s) {
   const int64_t n_wg = (int64_t)p.tiles_m * p.tiles_n;
   if (n_wg == 0) return STG_OK;
   launch_kernel(name, gemm_kernel<CF>, dim3((unsigned)n_wg), dim3(CF::NT), (uint32_t)CF::LDS_B, s, p);
-  return check_launch("gemm_bounded");
+  return check_launch(name);
 }
 
 // Raises the kernels' dynamic LDS limit once on each device.
@@ -513,15 +515,17 @@ bool lds_configured() {
 
 using namespace stg;
 
-extern "C" int gemm_bounded(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
-                            int64_t M, int64_t N, int64_t K, int32_t c_dtype, void* stream) {
-  clear_error();
-  const char* name = "gemm_bounded";
+namespace stg {
+
+int gemm_bf16(const GemmNames& names, const void* A, int64_t lda, const void* B, int64_t ldb, const float* acc,
+              int64_t ldacc, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K, int32_t c_dtype, hipStream_t s) {
+  const char* name = names.entry;
   if (M < 0 || N < 0 || K < 0) return fail(STG_ERR_INVALID, "%s: negative size", name);
   if (c_dtype != STG_BF16 && c_dtype != STG_F32)
     return fail(STG_ERR_UNSUPPORTED, "%s: c_dtype must be STG_BF16 or STG_F32", name);
-  if (lda < (K > 0 ? K : 1) || ldb < (N > 0 ? N : 1) || ldc < (N > 0 ? N : 1))
+  if (lda < (K > 0 ? K : 1) || ldb < (N > 0 ? N : 1) || ldc < (N > 0 ? N : 1) || (acc && ldacc < N))
     return fail(STG_ERR_INVALID, "%s: row strides must be >= the row lengths", name);
+  if (acc && c_dtype != STG_F32) return fail(STG_ERR_UNSUPPORTED, "%s: an accumulator input needs fp32 output", name);
   if (M == 0 || N == 0) return STG_OK;
   if (!C || (K > 0 && (!A || !B))) return fail(STG_ERR_INVALID, "%s: null operand", name);
   if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return fail(STG_ERR_RANGE, "%s: size too large", name);
@@ -534,25 +538,34 @@ extern "C" int gemm_bounded(const void* A, int64_t lda, const void* B, int64_t l
   p.A = (const char*)A;
   p.B = (const char*)B;
   p.C = (char*)C;
-  p.lda = lda, p.ldb = ldb, p.ldc = ldc;
+  p.acc = acc;
+  p.lda = lda, p.ldb = ldb, p.ldc = ldc, p.ldacc = ldacc;
   p.M = M, p.N = N, p.K = K;
   p.c_f32 = c_dtype == STG_F32;
-  const hipStream_t s = as_stream(stream);
   const int64_t n_main = (N / MainCfg::BN) * MainCfg::BN;
   int rc;
   p.n_base = 0;
-  if (n_main > 0 && (rc = launch<MainCfg>("gemm_bounded/main", p, n_main, s))) return rc;
+  if (n_main > 0 && (rc = launch<MainCfg>(names.main, p, n_main, s))) return rc;
   p.n_base = n_main;
   const int64_t rem = N - n_main;
-  if (rem > 8) return launch<EdgeCfg>("gemm_bounded/edge", p, rem, s);
+  if (rem > 8) return launch<EdgeCfg>(names.edge, p, rem, s);
   if (rem > 0) {
     const unsigned grid = (unsigned)((M + SK_ROWS - 1) / SK_ROWS);
     switch (rem) {
-#define STG_SK(r) case r: launch_kernel("gemm_bounded/skinny", gemm_skinny_kernel<r>, dim3(grid), dim3(256), 0, s, p); break;
+#define STG_SK(r) case r: launch_kernel(names.skinny, gemm_skinny_kernel<r>, dim3(grid), dim3(256), 0, s, p); break;
       STG_SK(1) STG_SK(2) STG_SK(3) STG_SK(4) STG_SK(5) STG_SK(6) STG_SK(7) STG_SK(8)
 #undef STG_SK
     }
-    return check_launch(name);
+    return check_launch(names.skinny);
   }
   return STG_OK;
+}
+
+}  // namespace stg
+
+extern "C" int gemm_bounded(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                            int64_t M, int64_t N, int64_t K, int32_t c_dtype, void* stream) {
+  clear_error();
+  static const GemmNames names{"gemm_bounded", "gemm_bounded/main", "gemm_bounded/edge", "gemm_bounded/skinny"};
+  return gemm_bf16(names, A, lda, B, ldb, nullptr, 0, C, ldc, M, N, K, c_dtype, as_stream(stream));
 }

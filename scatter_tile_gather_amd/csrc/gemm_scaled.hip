@@ -610,11 +610,19 @@ bool set_lds() {
 
 using namespace stg;
 
-extern "C" int gemm_scaled(const void* A, int32_t a_fmt, int64_t lda, const void* a_scale, int64_t lds_a,
-                           const void* Bt, int32_t b_fmt, int64_t ldb, const void* b_scale, int64_t lds_b,
-                           int32_t scale_fmt, int64_t block, const float* acc, int64_t ldacc, float* C, int64_t ldc,
-                           int64_t M, int64_t N, int64_t K, void* stream) {
-  clear_error();
+namespace {
+
+// the scaled MFMA takes e8m0 scales per 32 K values of two operands of one
+// width; every other case goes to the general path
+bool scaled_mfma_path(int32_t a_fmt, int32_t b_fmt, int32_t scale_fmt, int64_t block) {
+  const int bits = a_fmt == STG_LP_E2M1 ? 4 : 8, bits_b = b_fmt == STG_LP_E2M1 ? 4 : 8;
+  return scale_fmt == STG_SC_E8M0 && block >= 32 && (block & (block - 1)) == 0 && bits == bits_b;
+}
+
+int scaled_impl(const void* A, int32_t a_fmt, int64_t lda, const void* a_scale, int64_t lds_a, const void* Bt,
+                int32_t b_fmt, int64_t ldb, const void* b_scale, int64_t lds_b, int32_t scale_fmt, int64_t block,
+                const float* acc, int64_t ldacc, float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                void* workspace, int64_t workspace_bytes, void* stream) {
   const char* name = "gemm_scaled";
   auto known = [](int32_t f) { return f == STG_LP_E4M3 || f == STG_LP_E5M2 || f == STG_LP_E2M1; };
   if (!known(a_fmt) || !known(b_fmt)) return fail(STG_ERR_UNSUPPORTED, "%s: unknown operand format", name);
@@ -630,13 +638,9 @@ extern "C" int gemm_scaled(const void* A, int32_t a_fmt, int64_t lda, const void
     return fail(STG_ERR_INVALID, "%s: row strides must cover the rows", name);
   if (M == 0 || N == 0) return STG_OK;
   if (!C || (K > 0 && (!A || !Bt || !a_scale || !b_scale))) return fail(STG_ERR_INVALID, "%s: null operand", name);
-  // the scaled MFMA takes e8m0 scales per 32 K values of two operands of one
-  // width; every other case goes to the general path (values scaled while
-  // staged, bf16 MFMA)
-  const bool mfma_path = scale_fmt == STG_SC_E8M0 && block >= 32 && (block & (block - 1)) == 0 && bits == bits_b;
-  if (!mfma_path)
+  if (!scaled_mfma_path(a_fmt, b_fmt, scale_fmt, block))
     return gemm_scaled_general(A, a_fmt, lda, a_scale, lds_a, Bt, b_fmt, ldb, b_scale, lds_b, scale_fmt, block, acc,
-                               ldacc, C, ldc, M, N, K, as_stream(stream));
+                               ldacc, C, ldc, M, N, K, workspace, workspace_bytes, as_stream(stream));
   if ((int64_t)kSBM * lda + 256 >= kMaxOffset32 || (int64_t)kSBN * ldb + 256 >= kMaxOffset32 ||
       M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2 ||
       (M - 1) * lds_a + K / block + 64 >= kMaxOffset32 || (N - 1) * lds_b + K / block + 64 >= kMaxOffset32)
@@ -688,4 +692,39 @@ extern "C" int gemm_scaled(const void* A, int32_t a_fmt, int64_t lda, const void
   if (code_a == 0) return launch_scaled<0, 1, 8>(p, packed, n_wg, n_sk, r_skinny, s);
   if (code_b == 0) return launch_scaled<1, 0, 8>(p, packed, n_wg, n_sk, r_skinny, s);
   return launch_scaled<1, 1, 8>(p, packed, n_wg, n_sk, r_skinny, s);
+}
+
+}  // namespace
+
+extern "C" int gemm_scaled(const void* A, int32_t a_fmt, int64_t lda, const void* a_scale, int64_t lds_a,
+                           const void* Bt, int32_t b_fmt, int64_t ldb, const void* b_scale, int64_t lds_b,
+                           int32_t scale_fmt, int64_t block, const float* acc, int64_t ldacc, float* C, int64_t ldc,
+                           int64_t M, int64_t N, int64_t K, void* stream) {
+  clear_error();
+  return scaled_impl(A, a_fmt, lda, a_scale, lds_a, Bt, b_fmt, ldb, b_scale, lds_b, scale_fmt, block, acc, ldacc, C,
+                     ldc, M, N, K, nullptr, 0, stream);
+}
+
+extern "C" int gemm_scaled_ws(const void* A, int32_t a_fmt, int64_t lda, const void* a_scale, int64_t lds_a,
+                              const void* Bt, int32_t b_fmt, int64_t ldb, const void* b_scale, int64_t lds_b,
+                              int32_t scale_fmt, int64_t block, const float* acc, int64_t ldacc, float* C,
+                              int64_t ldc, int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+                              void* stream) {
+  clear_error();
+  if (workspace_bytes < 0) return fail(STG_ERR_INVALID, "gemm_scaled_ws: negative workspace_bytes");
+  return scaled_impl(A, a_fmt, lda, a_scale, lds_a, Bt, b_fmt, ldb, b_scale, lds_b, scale_fmt, block, acc, ldacc, C,
+                     ldc, M, N, K, workspace, workspace ? workspace_bytes : 0, stream);
+}
+
+extern "C" int64_t gemm_scaled_workspace(int32_t a_fmt, int32_t b_fmt, int32_t scale_fmt, int64_t block, int64_t M,
+                                         int64_t N, int64_t K) {
+  clear_error();
+  const char* name = "gemm_scaled_workspace";
+  auto known = [](int32_t f) { return f == STG_LP_E4M3 || f == STG_LP_E5M2 || f == STG_LP_E2M1; };
+  if (!known(a_fmt) || !known(b_fmt) || (scale_fmt != STG_SC_E8M0 && scale_fmt != STG_SC_E4M3))
+    return -fail(STG_ERR_UNSUPPORTED, "%s: unknown operand or scale format", name);
+  if (M < 0 || N < 0 || K < 0 || block < 1 || K % block)
+    return -fail(STG_ERR_INVALID, "%s: negative size, or K not a multiple of the block", name);
+  if (scaled_mfma_path(a_fmt, b_fmt, scale_fmt, block)) return 0;
+  return gemm_scaled_general_workspace(M, N, K);
 }

@@ -141,6 +141,24 @@ __device__ __forceinline__ void decode16(const u32x4& w, float pow2, float mult,
                    decode2<FMT, 14>(w, pow2, mult)};
 }
 
+// A block scale byte as decode16's pow2 and mult, selected without a branch
+// (a branch in the GEMM's K loop would cut a step into blocks the scheduler
+// cannot interleave): e8m0, 2^(b-127), b = 0 as 2^-126 * 0.5 (an exponent
+// field of 0 is not a power of two for the conversion), 0xFF NaN; e4m3, its
+// value (normal f32, zero or NaN) decoded by the hardware conversion with a
+// unit scale, split into its power of two and the rest.
+__device__ __forceinline__ void split_scale(uint32_t b, int32_t sf, float& pow2, float& mult) {
+  const float p8 = b ? __uint_as_float(b << 23) : 0x1p-126f;
+  const float m8 = b == 0xFF ? __uint_as_float(0x7FC00000u) : b ? 1.f : 0.5f;
+  const float sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(b, 1.0f, false)[0];
+  const bool zero = sc == 0.f, nan = sc != sc;
+  const float p4 = zero || nan ? 1.f : __uint_as_float(__float_as_uint(sc) & 0x7F800000u);
+  const float m4 = zero ? 0.f : nan ? sc : __uint_as_float((__float_as_uint(sc) & 0x807FFFFFu) | 0x3F800000u);
+  const bool e8 = sf == STG_SC_E8M0;
+  pow2 = e8 ? p8 : p4;
+  mult = e8 ? m8 : m4;
+}
+
 // Codes of one lane's 16 K values of one row (16 bytes of fp8 or 8 of fp4)
 // and the scale byte they share (blocks that are multiples of 16).
 struct Codes {
@@ -233,20 +251,8 @@ __global__ __launch_bounds__(kGNT) void gemm_scaled_general_kernel(GeneralParams
     u32x4 out[2];
     if constexpr (BLK16) {
       // one scale for the 16 values; codes past K were loaded as zero
-      // both readings of the byte, selected without a branch (a branch here
-      // would cut the step into blocks the scheduler cannot interleave):
-      // e8m0, 2^(b-127), b = 0 as 2^-126 * 0.5 (an exponent field of 0 is
-      // not a power of two for the conversion), 0xFF NaN; e4m3, its value
-      // (normal f32, zero or NaN) decoded by the hardware conversion with a
-      // unit scale, split into its power of two and the rest
-      const float p8 = c.s ? __uint_as_float(c.s << 23) : 0x1p-126f;
-      const float m8 = c.s == 0xFF ? __uint_as_float(0x7FC00000u) : c.s ? 1.f : 0.5f;
-      const float sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c.s, 1.0f, false)[0];
-      const bool zero = sc == 0.f, nan = sc != sc;
-      const float p4 = zero || nan ? 1.f : __uint_as_float(__float_as_uint(sc) & 0x7F800000u);
-      const float m4 = zero ? 0.f : nan ? sc : __uint_as_float((__float_as_uint(sc) & 0x807FFFFFu) | 0x3F800000u);
-      const bool e8 = p.sf == STG_SC_E8M0;
-      const float pow2 = e8 ? p8 : p4, mult = e8 ? m8 : m4;
+      float pow2, mult;
+      split_scale(c.s, p.sf, pow2, mult);
       decode16<fmt>(c.w, pow2, mult, out);
     } else {
       // blocks that do not hold whole 16-value runs: each value finds its
@@ -431,6 +437,161 @@ __global__ __launch_bounds__(kGNT) void gemm_scaled_general_kernel(GeneralParams
     }
 }
 
+// ---- decoded operands: each value scaled and rounded to bf16 once ---------
+//
+// The kernel above decodes an operand row in every tile that uses it: at
+// (8191, 8193, 4096) each A row 33 times and each Bt row 32 times, so its
+// decode work is as large as its MFMA work.  With a workspace, the operands
+// are instead decoded once, exactly as above (the same conversions, the same
+// bf16 values), into bf16 matrices A' (M, K) and B' (K, N) -- B transposed,
+// the layout the bf16 GEMM stages -- and the bf16 GEMM multiplies them with
+// the same fp32 accumulation: the results differ only by its summation order.
+
+struct DecodeParams {
+  const char* codes;     // (rows, K) operand codes, row stride ld bytes
+  const uint8_t* scale;  // (rows, K / block) scale bytes, row stride lds
+  __bf16* out;           // A': (rows, ldo); B' (transposed): (K, ldo)
+  int64_t ld, lds, ldo, rows, K;
+  int32_t block, sf;
+};
+
+// The 16 codes of run k0 .. k0+15 of row r (k0 < K), values past K as code 0.
+template <int BITS>
+__device__ __forceinline__ u32x4 run_codes(const DecodeParams& d, int64_t r, int64_t k0) {
+  const char* row = d.codes + r * d.ld + k0 * BITS / 8;
+  u32x4 w = {0, 0, 0, 0};
+  if (k0 + 16 <= d.K) {
+    if constexpr (BITS == 8) {
+      w = ld16(row);
+    } else {
+      uint32_t h[2];
+      __builtin_memcpy(h, row, 8);
+      w[0] = h[0], w[1] = h[1];
+    }
+    return w;
+  }
+  const int nv = (int)(d.K - k0);                 // values left in the row, 1..15
+  const int nb = (nv * BITS + 7) / 8;             // their bytes
+  for (int b = 0; b < nb; ++b) w[b >> 2] |= (uint32_t)(uint8_t)row[b] << (8 * (b & 3));
+  if (BITS == 4 && (nv & 1)) w[(nb - 1) >> 2] &= ~(0xF0u << (8 * ((nb - 1) & 3)));  // nibble past K
+  return w;
+}
+
+// 16 bf16 values of run k0 of row r, as the GEMM kernel above decodes them.
+template <int FMT, bool BLK16>
+__device__ __forceinline__ void run_decode(const DecodeParams& d, int64_t r, int64_t k0, u32x4 out[2]) {
+  constexpr int BITS = FMT == STG_LP_E2M1 ? 4 : 8;
+  const u32x4 w = run_codes<BITS>(d, r, k0);
+  const uint8_t* srow = d.scale + r * d.lds;
+  if constexpr (BLK16) {
+    float pow2, mult;
+    split_scale(srow[k0 / d.block], d.sf, pow2, mult);
+    decode16<FMT>(w, pow2, mult, out);
+  } else {
+    for (int e = 0; e < 16; e += 2) {
+      float v[2];
+      for (int u = 0; u < 2; ++u) {
+        const int ee = e + u;
+        const int64_t k = k0 + ee;
+        const uint32_t code = BITS == 8 ? (w[ee >> 2] >> (8 * (ee & 3))) & 0xFF : (w[ee >> 3] >> (4 * (ee & 7))) & 0xF;
+        v[u] = k < d.K ? decode_code(code, FMT) * decode_scale(srow[k / d.block], d.sf) : 0.f;
+      }
+      out[e >> 3][(e >> 1) & 3] = pack_bf16x2((f32x2_g){v[0], v[1]});
+    }
+  }
+}
+
+// A': one thread per run of 16 values; ldo is a multiple of 16, so a row's
+// last run (zero past K) stays inside the row.
+template <int FMT, bool BLK16>
+__global__ __launch_bounds__(256) void decode_rows_kernel(DecodeParams d, int64_t runs_per_row) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= d.rows * runs_per_row) return;
+  const int64_t r = t / runs_per_row, k0 = (t - r * runs_per_row) * 16;
+  u32x4 out[2];
+  run_decode<FMT, BLK16>(d, r, k0, out);
+  char* dst = (char*)(d.out + r * d.ldo + k0);
+  st16(dst, out[0]);
+  st16(dst + 16, out[1]);
+}
+
+// B': a workgroup decodes 64 rows x 64 K values of Bt (four threads per row,
+// one run each) into LDS, then writes them transposed: 64 rows of B', each 64
+// columns as eight 16-byte chunks.  ldo is a multiple of 8, so a chunk that
+// starts before N stays inside its row.
+constexpr int kDecT = 64;
+template <int FMT, bool BLK16>
+__global__ __launch_bounds__(256) void decode_cols_kernel(DecodeParams d, int64_t n_tiles) {
+  constexpr int kPitch = kDecT + 8;  // bf16 per LDS row: 144 bytes, 16-byte aligned, reads spread over banks
+  __shared__ __attribute__((aligned(16))) __bf16 tile[kDecT * kPitch];
+  const int tid = threadIdx.x;
+  // workgroup (row tile, K tile), row tiles fastest
+  const int64_t bt = (int64_t)blockIdx.x / n_tiles;
+  const int64_t n0 = ((int64_t)blockIdx.x - bt * n_tiles) * kDecT, kb = bt * kDecT;
+  {
+    const int n = tid >> 2, q = tid & 3;
+    const int64_t k0 = kb + 16 * q;
+    u32x4 out[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+    if (n0 + n < d.rows && k0 < d.K) run_decode<FMT, BLK16>(d, n0 + n, k0, out);
+    *(u32x4*)(tile + n * kPitch + 16 * q) = out[0];
+    *(u32x4*)(tile + n * kPitch + 16 * q + 8) = out[1];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + 256 * i, kk = c >> 3, nc = c & 7;
+    const int64_t k = kb + kk, n = n0 + 8 * nc;
+    if (k >= d.K || n >= d.rows) continue;
+    u32x4 v;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const uint32_t lo = __builtin_bit_cast(uint16_t, tile[(8 * nc + e) * kPitch + kk]);
+      const uint32_t hi = __builtin_bit_cast(uint16_t, tile[(8 * nc + e + 1) * kPitch + kk]);
+      v[e >> 1] = lo | hi << 16;
+    }
+    st16((char*)(d.out + k * d.ldo + n), v);
+  }
+}
+
+constexpr int64_t kDecAlign = 256;
+inline int64_t dec_up(int64_t x) { return (x + kDecAlign - 1) / kDecAlign * kDecAlign; }
+// leading dimensions of A' and B' (elements)
+inline int64_t dec_lda(int64_t K) { return (K + 15) / 16 * 16; }
+inline int64_t dec_ldb(int64_t N) { return (N + 7) / 8 * 8; }
+
+template <int FMT>
+int launch_decode(bool rows, bool blk16, const DecodeParams& d, hipStream_t s) {
+  if (rows) {
+    const int64_t runs = (d.K + 15) / 16;
+    const int64_t grid = (d.rows * runs + 255) / 256;
+    if (grid > INT32_MAX) return fail(STG_ERR_RANGE, "gemm_scaled: too many values to decode");
+    if (blk16)
+      launch_kernel("gemm_scaled/decode_a", decode_rows_kernel<FMT, true>, dim3((unsigned)grid), dim3(256), 0, s, d,
+                    runs);
+    else
+      launch_kernel("gemm_scaled/decode_a", decode_rows_kernel<FMT, false>, dim3((unsigned)grid), dim3(256), 0, s, d,
+                    runs);
+  } else {
+    const int64_t n_tiles = (d.rows + kDecT - 1) / kDecT, grid = n_tiles * ((d.K + kDecT - 1) / kDecT);
+    if (grid > INT32_MAX) return fail(STG_ERR_RANGE, "gemm_scaled: too many values to decode");
+    if (blk16)
+      launch_kernel("gemm_scaled/decode_b", decode_cols_kernel<FMT, true>, dim3((unsigned)grid), dim3(256), 0, s, d,
+                    n_tiles);
+    else
+      launch_kernel("gemm_scaled/decode_b", decode_cols_kernel<FMT, false>, dim3((unsigned)grid), dim3(256), 0, s, d,
+                    n_tiles);
+  }
+  return check_launch("gemm_scaled");
+}
+
+int decode_operand(int32_t fmt, bool rows, bool blk16, const DecodeParams& d, hipStream_t s) {
+  switch (fmt) {
+    case STG_LP_E4M3: return launch_decode<STG_LP_E4M3>(rows, blk16, d, s);
+    case STG_LP_E5M2: return launch_decode<STG_LP_E5M2>(rows, blk16, d, s);
+    default: return launch_decode<STG_LP_E2M1>(rows, blk16, d, s);
+  }
+}
+
 template <int FA, int FB>
 int launch_general(const GeneralParams& p, int64_t n_wg, hipStream_t s) {
   static OncePerDevice once;  // the kernels' dynamic LDS limit, once on each device
@@ -461,11 +622,44 @@ int launch_general_a(const GeneralParams& p, int64_t n_wg, hipStream_t s) {
 
 }  // namespace
 
+int64_t gemm_scaled_general_workspace(int64_t M, int64_t N, int64_t K) {
+  // decoding first pays once each operand row would be decoded by more than
+  // one tile of the kernel above; the bf16 GEMM takes sizes up to 2^30 and a
+  // stage (256 rows of A', 32 of B') within 2^31 bytes
+  if (M <= kGBM || N <= kGBN || K == 0 || M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return 0;
+  if (256 * dec_lda(K) * 2 + 256 >= kMaxOffset32 || 32 * dec_ldb(N) * 2 + 512 >= kMaxOffset32) return 0;
+  return dec_up(M * dec_lda(K) * 2) + dec_up(K * dec_ldb(N) * 2);
+}
+
 int gemm_scaled_general(const void* A, int32_t a_fmt, int64_t lda, const void* a_scale, int64_t lds_a,
                         const void* Bt, int32_t b_fmt, int64_t ldb, const void* b_scale, int64_t lds_b,
                         int32_t scale_fmt, int64_t block, const float* acc, int64_t ldacc, float* C, int64_t ldc,
-                        int64_t M, int64_t N, int64_t K, hipStream_t s) {
+                        int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes, hipStream_t s) {
   const char* name = "gemm_scaled";
+  const int64_t need = gemm_scaled_general_workspace(M, N, K);
+  if (workspace && need > 0) {
+    if (workspace_bytes < need)
+      return fail(STG_ERR_INVALID, "%s: workspace of %lld bytes, %lld needed", name, (long long)workspace_bytes,
+                  (long long)need);
+    if ((uintptr_t)workspace % kDecAlign) return fail(STG_ERR_INVALID, "%s: workspace must be 256-byte aligned", name);
+    __bf16* ad = (__bf16*)workspace;
+    __bf16* bd = (__bf16*)((char*)workspace + dec_up(M * dec_lda(K) * 2));
+    DecodeParams d{};
+    d.block = (int32_t)block;
+    d.sf = scale_fmt;
+    d.K = K;
+    const bool blk16 = block % 16 == 0;
+    d.codes = (const char*)A, d.scale = (const uint8_t*)a_scale, d.out = ad;
+    d.ld = lda, d.lds = lds_a, d.ldo = dec_lda(K), d.rows = M;
+    int rc = decode_operand(a_fmt, true, blk16, d, s);
+    if (rc) return rc;
+    d.codes = (const char*)Bt, d.scale = (const uint8_t*)b_scale, d.out = bd;
+    d.ld = ldb, d.lds = lds_b, d.ldo = dec_ldb(N), d.rows = N;
+    if ((rc = decode_operand(b_fmt, false, blk16, d, s))) return rc;
+    static const GemmNames names{"gemm_scaled", "gemm_scaled/bf16_main", "gemm_scaled/bf16_edge",
+                                 "gemm_scaled/bf16_skinny"};
+    return gemm_bf16(names, ad, dec_lda(K), bd, dec_ldb(N), acc, ldacc, C, ldc, M, N, K, STG_F32, s);
+  }
   // 32-bit buffer offsets within one tile's rows (codes and scale bytes)
   if ((int64_t)kGBM * lda + 64 >= kMaxOffset32 || (int64_t)kGBN * ldb + 64 >= kMaxOffset32 ||
       (int64_t)kGBM * lds_a + 64 >= kMaxOffset32 || (int64_t)kGBN * lds_b + 64 >= kMaxOffset32 ||

@@ -187,12 +187,34 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t w, uint32_t total) {
 __device__ __forceinline__ uint32_t div_small(uint32_t n, uint32_t magic) { return __umulhi(n << 1, magic); }
 inline uint32_t div_magic(uint32_t d) { return (uint32_t)(((uint64_t(1) << 31) + d - 1) / d); }
 
+// Kernel names a bf16 GEMM call reports (errors, launch tracing).
+struct GemmNames {
+  const char* entry;
+  const char* main;
+  const char* edge;
+  const char* skinny;
+};
+
+// C = A B (+ acc), bf16 operands (A (M, K), B (K, N), row strides in
+// elements), fp32 accumulation, C in c_dtype (STG_BF16 or STG_F32; acc, an
+// fp32 (M, N) matrix added before the store, only with STG_F32): the
+// gemm_bounded kernels (gemm.hip), with the checks of gemm_bounded.
+int gemm_bf16(const GemmNames& names, const void* A, int64_t lda, const void* B, int64_t ldb, const float* acc,
+              int64_t ldacc, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K, int32_t c_dtype, hipStream_t s);
+
 // Block-scaled GEMM for the operand pairs, scale formats and blocks the
 // scaled MFMA does not take (gemm_scaled_general.hip); arguments as
-// gemm_scaled's, already checked by it.
+// gemm_scaled's, already checked by it.  With a workspace of at least
+// gemm_scaled_general_workspace(M, N, K) bytes (256-byte aligned) the
+// operands are decoded to bf16 into it once and multiplied by the bf16 GEMM;
+// without one, values are decoded tile by tile inside the GEMM kernel.
 int gemm_scaled_general(const void* A, int32_t a_fmt, int64_t lda, const void* a_scale, int64_t lds_a,
                         const void* Bt, int32_t b_fmt, int64_t ldb, const void* b_scale, int64_t lds_b,
                         int32_t scale_fmt, int64_t block, const float* acc, int64_t ldacc, float* C, int64_t ldc,
-                        int64_t M, int64_t N, int64_t K, hipStream_t s);
+                        int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes, hipStream_t s);
+// Bytes of the decoded operands for gemm_scaled_general at this shape, or 0
+// where decoding them first does not pay (or the bf16 GEMM's limits rule it
+// out).
+int64_t gemm_scaled_general_workspace(int64_t M, int64_t N, int64_t K);
 
 }  // namespace stg

@@ -103,7 +103,7 @@ def group_bound(orc, ca, fa, sa, cb, fb, sb, block, s_fmt="e8m0"):
 
 
 def run_case(stg, orc, M, N, K, block, fa, fb, seed, with_acc=False, pad=0, scale_lo=118, scale_hi=136,
-             scale_fmt="e8m0"):
+             scale_fmt="e8m0", workspace="auto"):
     rng = np.random.default_rng(seed)
     ca, cb = codes(rng, (M, K), fa), codes(rng, (N, K), fb)
     A, Bt = pack(ca, fa), pack(cb, fb)
@@ -115,7 +115,7 @@ def run_case(stg, orc, M, N, K, block, fa, fb, seed, with_acc=False, pad=0, scal
     Bd = to_dev(np.pad(Bt, ((0, 0), (0, pad)), constant_values=0x5A))[:, :Bt.shape[1]]
     store = torch.full((M, N + pad), 7.0, dtype=torch.float32, device="cuda:0")
     stg.gemm_scaled(Ad, fa, to_dev(sa), Bd, fb, to_dev(sb), K, block, scale_fmt=scale_fmt,
-                    acc=None if acc is None else to_dev(acc), out=store[:, :N])
+                    acc=None if acc is None else to_dev(acc), out=store[:, :N], workspace=workspace)
     torch.cuda.synchronize()
     full = to_host(store)
     got = full[:, :N].astype(np.float64)
@@ -351,14 +351,19 @@ EXACT_SCALES = {"e8m0": [126, 127, 128, 129], "e4m3": [0x30, 0x38, 0x3C, 0x40]} 
 @pytest.mark.parametrize("scale_fmt,block,shape", [("e4m3", 32, (300, 520, 256)), ("e4m3", 16, (257, 259, 96)),
                                                    ("e8m0", 16, (65, 97, 128)), ("e4m3", 1, (33, 70, 40)),
                                                    ("e4m3", 3, (130, 300, 99)), ("e8m0", 48, (260, 513, 144)),
-                                                   ("e4m3", 96, (70, 40, 192))])
-def test_scaled_general_exact(stg, orc, fa, fb, scale_fmt, block, shape):
+                                                   ("e4m3", 96, (70, 40, 192)), ("e4m3", 3, (520, 300, 99)),
+                                                   ("e8m0", 16, (300, 270, 48))])
+@pytest.mark.parametrize("ws", [None, "auto"])
+def test_scaled_general_exact(stg, orc, fa, fb, scale_fmt, block, shape, ws):
     """Values +-1, +-2 and scales 0.5, 1, 1.5, 2: every partial sum is exact
     in fp32, so the general path must match the oracle bit for bit.  This pins
     which scale meets which value (blocks of 1, 3, 16, 48, 96 that do not
     split into 32-value groups), the FP4 nibble order next to fp8 bytes, and
     the ragged M, N and K tails (K = 99 and 40 end inside a 64-value step;
-    fp4 with K = 99 has an odd row length)."""
+    fp4 with K = 99 has an odd row length).  With ws="auto" the shapes whose
+    M and N both exceed 256 take the decoded-operand execution (each operand
+    decoded to bf16 once, then the bf16 GEMM), the others the fused kernel;
+    with ws=None every shape takes the fused kernel."""
     M, N, K = shape
     if mfma_path(fa, fb, block, scale_fmt):
         pytest.skip("runs on the scaled MFMA (covered above)")
@@ -367,9 +372,9 @@ def test_scaled_general_exact(stg, orc, fa, fb, scale_fmt, block, shape):
     cb = np.array(EXACT_CODES[fb], np.uint8)[rng.integers(0, 4, (N, K))]
     sa = np.array(EXACT_SCALES[scale_fmt], np.uint8)[rng.integers(0, 4, (M, K // block))]
     sb = np.array(EXACT_SCALES[scale_fmt], np.uint8)[rng.integers(0, 4, (N, K // block))]
-    say("gemm_scaled general exact", fa, fb, scale_fmt, "block", block, shape)
+    say("gemm_scaled general exact", fa, fb, scale_fmt, "block", block, shape, "workspace", ws)
     C = to_host(stg.gemm_scaled(to_dev(pack(ca, fa)), fa, to_dev(sa), to_dev(pack(cb, fb)), fb, to_dev(sb), K, block,
-                                scale_fmt=scale_fmt))
+                                scale_fmt=scale_fmt, workspace=ws))
     np.testing.assert_array_equal(C.astype(np.float64),
                                   orc.gemm_scaled_f64(pack(ca, fa), fa, sa, pack(cb, fb), fb, sb, K, block,
                                                       s_fmt=scale_fmt))
@@ -378,28 +383,35 @@ def test_scaled_general_exact(stg, orc, fa, fb, scale_fmt, block, shape):
 @pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e2m1", "e4m3"), ("e5m2", "e2m1"),
                                    ("e2m1", "e2m1")])
 @pytest.mark.parametrize("scale_fmt,block", [("e4m3", 16), ("e4m3", 32), ("e8m0", 16), ("e4m3", 5)])
-def test_scaled_general_random(stg, orc, fa, fb, scale_fmt, block):
+@pytest.mark.parametrize("ws", [None, "auto"])
+def test_scaled_general_random(stg, orc, fa, fb, scale_fmt, block, ws):
     """Full-range codes, an accumulator input and padded strides, on a shape
-    with ragged tails in M, N and K: within gamma_K * sum|terms|."""
+    with ragged tails in M, N and K: within gamma_K * sum|terms|.  With a
+    workspace, 300 rows (the decoded-operand execution); without, 131 (the
+    fused kernel)."""
     K = 320 if block != 5 else 325
     if mfma_path(fa, fb, block, scale_fmt):
         pytest.skip("runs on the scaled MFMA (covered above)")
-    say("gemm_scaled general random", fa, fb, scale_fmt, "block", block)
-    run_case(stg, orc, 131, 517, K, block, fa, fb, seed=block + len(fa + fb), with_acc=True, pad=3,
-             scale_fmt=scale_fmt)
+    M = 300 if ws else 131
+    assert (stg.gemm_scaled_workspace(fa, fb, scale_fmt, block, M, 517, K) > 0) == (ws is not None)
+    say("gemm_scaled general random", fa, fb, scale_fmt, "block", block, "workspace", ws)
+    run_case(stg, orc, M, 517, K, block, fa, fb, seed=block + len(fa + fb), with_acc=True, pad=3,
+             scale_fmt=scale_fmt, workspace=ws)
 
 
-def test_scaled_general_large_sampled(stg, orc):
+@pytest.mark.parametrize("ws", [None, "auto"])
+def test_scaled_general_large_sampled(stg, orc, ws):
     """(2048, 2304, 4096) e4m3 x e4m3 with e4m3 scales per 16 values (a
-    layout the scaled MFMA cannot take): sampled rows and columns including
-    the last tile's, within gamma_K * sum|terms|."""
+    layout the scaled MFMA cannot take), fused and decoded-operand
+    executions: sampled rows and columns including the last tile's, within
+    gamma_K * sum|terms|."""
     M, N, K, block = 2048, 2304, 4096, 16
     rng = np.random.default_rng(13)
     ca, cb = codes(rng, (M, K), "e4m3"), codes(rng, (N, K), "e4m3")
     sa, sb = scale_codes(rng, (M, K // block), "e4m3"), scale_codes(rng, (N, K // block), "e4m3")
-    say("gemm_scaled general large (2048,2304,4096) e4m3, e4m3 scales per 16, sampled")
+    say("gemm_scaled general large (2048,2304,4096) e4m3, e4m3 scales per 16, sampled, workspace", ws)
     C = to_host(stg.gemm_scaled(to_dev(ca), "e4m3", to_dev(sa), to_dev(cb), "e4m3", to_dev(sb), K, block,
-                                scale_fmt="e4m3"))
+                                scale_fmt="e4m3", workspace=ws))
     rows = np.concatenate([np.arange(0, 32), np.arange(M - 32, M), rng.integers(0, M, 32)])
     cols = np.concatenate([np.arange(0, 32), np.arange(N - 32, N), rng.integers(0, N, 32)])
     want = orc.gemm_scaled_f64(ca[rows], "e4m3", sa[rows], cb[cols], "e4m3", sb[cols], K, block, s_fmt="e4m3")
@@ -408,6 +420,38 @@ def test_scaled_general_large_sampled(stg, orc):
     tol = K * 2.0 ** -24 / (1 - K * 2.0 ** -24) * mag + 1e-30
     err = np.abs(C[np.ix_(rows, cols)].astype(np.float64) - want)
     assert np.all(err <= tol), float((err - tol).max())
+
+
+def test_scaled_decoded_workspace_reuse_and_errors(stg, orc):
+    """An explicit workspace tensor: two calls in a row, the second smaller
+    (its decoded operands overwrite part of the first's), both bit-exact on
+    exactly summable values; a workspace one byte short or not 256-byte
+    aligned is an argument error."""
+    rng = np.random.default_rng(77)
+    ws = None
+    for (M, N, K) in [(520, 300, 192), (270, 290, 80)]:
+        ca = np.array(EXACT_CODES["e4m3"], np.uint8)[rng.integers(0, 4, (M, K))]
+        cb = np.array(EXACT_CODES["e2m1"], np.uint8)[rng.integers(0, 4, (N, K))]
+        sa = np.array(EXACT_SCALES["e4m3"], np.uint8)[rng.integers(0, 4, (M, K // 16))]
+        sb = np.array(EXACT_SCALES["e4m3"], np.uint8)[rng.integers(0, 4, (N, K // 16))]
+        nb = stg.gemm_scaled_workspace("e4m3", "e2m1", "e4m3", 16, M, N, K)
+        assert nb > 0
+        if ws is None:
+            ws = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
+        say("gemm_scaled decoded, explicit workspace", (M, N, K), nb, "of", ws.numel())
+        C = to_host(stg.gemm_scaled(to_dev(ca), "e4m3", to_dev(sa), to_dev(pack(cb, "e2m1")), "e2m1", to_dev(sb), K, 16,
+                                    scale_fmt="e4m3", workspace=ws))
+        np.testing.assert_array_equal(C.astype(np.float64),
+                                      orc.gemm_scaled_f64(ca, "e4m3", sa, pack(cb, "e2m1"), "e2m1", sb, K, 16,
+                                                          s_fmt="e4m3"))
+    M, N, K = 270, 290, 80
+    nb = stg.gemm_scaled_workspace("e4m3", "e2m1", "e4m3", 16, M, N, K)
+    A, Bt = to_dev(np.zeros((M, K), np.uint8)), to_dev(np.zeros((N, K // 2), np.uint8))
+    sa, sb = to_dev(np.zeros((M, K // 16), np.uint8)), to_dev(np.zeros((N, K // 16), np.uint8))
+    with pytest.raises(stg.StgError, match="workspace"):
+        stg.gemm_scaled(A, "e4m3", sa, Bt, "e2m1", sb, K, 16, scale_fmt="e4m3", workspace=ws[:nb - 1])
+    with pytest.raises(stg.StgError, match="aligned"):
+        stg.gemm_scaled(A, "e4m3", sa, Bt, "e2m1", sb, K, 16, scale_fmt="e4m3", workspace=ws[16:16 + nb])
 
 
 # ---- the scaled MFMA's summation rule --------------------------------------

@@ -70,9 +70,20 @@ def test_prepared_call_uses_the_current_or_given_stream(stg, orc):
     np.testing.assert_array_equal(to_host(out2), a[idx])
 
 
-def test_prepare_rejects_an_auto_workspace(stg):
+def test_prepare_keeps_an_auto_workspace(stg):
+    """workspace="auto" under prepare(): allocated once at preparation and
+    held by the prepared call, which then matches the unprepared call bit for
+    bit, applied once and twice (the grouped backward adds a row's terms in
+    one order onto its current value)."""
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    idx = torch.randint(0, 128, (64,), generator=gen, dtype=torch.int32).to("cuda:0")
+    go = torch.randn((64, 8), generator=gen).to("cuda:0")
+    ref = torch.zeros((128, 8), dtype=torch.float32, device="cuda:0")
     g = torch.zeros((128, 8), dtype=torch.float32, device="cuda:0")
-    idx = torch.zeros(64, dtype=torch.int32, device="cuda:0")
-    go = torch.zeros((64, 8), dtype=torch.float32, device="cuda:0")
-    with pytest.raises(ValueError, match="workspace"):
-        stg.prepare(stg.tile_gather_backward, g, idx, (64, 8), go, workspace="auto")
+    say("prepared grouped backward with an auto workspace")
+    call = stg.prepare(stg.tile_gather_backward, g, idx, (64, 8), go, workspace="auto")
+    for _ in range(2):
+        stg.tile_gather_backward(ref, idx, (64, 8), go, workspace="auto")
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(g, ref)
