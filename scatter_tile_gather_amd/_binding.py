@@ -322,11 +322,31 @@ def _gather_out_shape(tile_shape, n, axis):
     return shape
 
 
+_FAST = None  # the C++ marshalling module (_stg_fast), loaded on first use
+
+
+def _fast():
+    global _FAST
+    if _FAST is None:
+        from . import _stg_fast
+
+        _FAST = (_stg_fast.tile_gather, ctypes.cast(load_library().tile_gather, ctypes.c_void_p).value)
+    return _FAST
+
+
 def tile_gather(a, indices, tile_shape, offset=None, axis: int = 0, out=None, stream=None):
     torch = _torch()
-    n = indices.numel()
     if out is None:
-        out = torch.empty(_gather_out_shape(tile_shape, n, axis), dtype=a.dtype, device=a.device)
+        out = torch.empty(_gather_out_shape(tile_shape, indices.numel(), axis), dtype=a.dtype, device=a.device)
+    if _capturing() is None:
+        # eager: the same checks and call, marshalled in C++ (this call is
+        # latency-bound; see csrc/fastcall.cpp)
+        fn, addr = _FAST or _fast()
+        rc = fn(addr, a, indices, out, tile_shape, offset, axis, None if stream is None else stream.cuda_stream)
+        if rc:
+            raise StgError(rc, load_library().stg_last_error().decode())
+        return out
+    n = indices.numel()
     ad, od = _desc(a, "a"), _desc(out, "out")
     _call("tile_gather", ad, _dev_array(indices, torch.int32, "indices"), n, _i64arr(tile_shape),
                            None if offset is None else _i64arr(offset), axis, od, _stream(stream, a))

@@ -257,3 +257,32 @@ def test_binding_rejects_short_masks(stg):
         stg.tile_gather_masked(a, idx, short, (4, 8), None, 0, -1.0)
     with pytest.raises(ValueError, match="one entry per index"):
         stg.tile_scatter_masked(a, idx, short, (4, 8), torch.ones((4, 8), device="cuda:0"), None, 0)
+
+
+def test_eager_marshalling_matches_the_ctypes_path(stg, orc):
+    """Eager tile_gather calls marshal their arguments in C++; prepare()
+    records the ctypes form.  Both give the oracle's result bit for bit (with
+    and without an offset, on the current and on a given stream), and the
+    eager form rejects what the ctypes form rejects."""
+    rng = np.random.default_rng(41)
+    a = rng.standard_normal((300, 7, 40)).astype(np.float32)
+    idx = rng.integers(-8, 310, 96).astype(np.int32)
+    ad, idd = to_dev(a), to_dev(idx)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for off, stream in [(None, None), ((0, 2, -5), None), ((3, -1, 9), side)]:
+        say("eager vs prepared gather, offset", off, "stream", stream is not None)
+        want = orc.tile_gather(a, idx, (32, 4, 16), off, 0)
+        eager = stg.tile_gather(ad, idd, (32, 4, 16), off, 0, stream=stream)
+        prepared = stg.prepare(stg.tile_gather, ad, idd, (32, 4, 16), off, 0, stream=stream)()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_host(eager), want)
+        np.testing.assert_array_equal(to_host(prepared), want)
+    with pytest.raises(ValueError, match="int32"):
+        stg.tile_gather(ad, idd.to(torch.int64), (32, 4, 16))
+    with pytest.raises(stg.StgError, match="shape"):
+        stg.tile_gather(ad, idd, (32, 4, 16), out=torch.empty((96, 4, 15), device="cuda:0"))
+    with pytest.raises(ValueError, match="rank"):
+        stg.tile_gather(ad.view(300, 7, 40, 1, 1), idd, (32, 4, 16, 1, 1))
+    with pytest.raises(TypeError):
+        stg.tile_gather(ad, idd, (32, 4, 16), out=np.zeros((96, 4, 16), np.float32))
