@@ -394,3 +394,18 @@ def test_gemm_scaled_workspace_query(stg):
     assert lib.gemm_scaled_workspace(0, 0, 1, 16, -1, 300, 32) == -1
     with pytest.raises(stg.StgError):
         q("e4m3", "e4m3", "e4m3", 16, 300, 300, 41)
+
+
+def test_eager_marshalling_module_is_built(stg):
+    """The C++ marshalling module of eager tile_gather calls is built into the
+    package, and it rejects host tensors before any device call, as the
+    ctypes form does."""
+    import torch
+
+    from scatter_tile_gather_amd import _stg_fast
+
+    with pytest.raises(ValueError, match="GPU tensor"):
+        _stg_fast.tile_gather(0, torch.zeros(8, 4), torch.zeros(4, dtype=torch.int32), torch.zeros(4, 4), (4, 4),
+                              None, 0, None)
+    with pytest.raises(TypeError, match="torch tensor"):
+        _stg_fast.tile_gather(0, [1.0], torch.zeros(4, dtype=torch.int32), torch.zeros(4, 4), (4, 4), None, 0, None)
