@@ -246,3 +246,18 @@ def test_backward_auto_workspace_on_side_stream(stg, orc):
     assert all(int(f.min()) == 0xFF for f in fills)
     acc, abs_sum, count = orc.tile_gather_backward(a0, idx, (64, cols), g, None, 0)
     check_backward(to_host(a_dev), a0, acc, abs_sum, count)
+
+
+def test_backward_grouped_many_scan_blocks(stg, orc):
+    """40,000,000 terms onto 2^20 one-value rows: the bucket-count table has
+    512 x 9,766 entries, 4,883 scan blocks, past the 4,096 up to which the
+    offsets kernel sums the blocks before its own itself -- so a separate
+    scan of the block sums runs (the other form is taken by every other
+    grouped case).  Within gamma_k * sum|terms| of the fp64 oracle."""
+    rows, n = 1 << 20, 40_000_000
+    rng = np.random.default_rng(2024)
+    idx = rng.integers(0, rows, n).astype(np.int32)
+    g = rng.standard_normal((n, 1)).astype(np.float32)
+    a0 = np.zeros((rows, 1), np.float32)
+    say("gather backward grouped, 40M terms onto 2^20 rows of one value (many scan blocks)")
+    run_case(stg, orc, a0, idx, (64, 1), g, ws="auto")
