@@ -440,6 +440,7 @@ constexpr int kMaxPieces = 4096;               // pieces of one segment at most
 constexpr int kHotPairs = 16384;               // a bucket with more terms is built by many workgroups
                                                // (one workgroup takes ~50 us over 60,000 terms)
 constexpr int kSlice = 16384;                  // terms per workgroup of a hot bucket
+constexpr int kHotCountWorkgroups = 256;       // build-launch workgroups counting hot slices
 constexpr int kSplitWorkgroups = 1024;         // workgroups on the long segments' pieces, at most
 // Consecutive rounds of list entries per block of such a workgroup.  A block
 // puts that many of a hot row's pieces (the longest ones) one after another
@@ -457,13 +458,16 @@ __device__ __forceinline__ int32_t seg_piece(int32_t c) {
 
 // Step 1: cnt1[b * n_chunks + w] = terms of chunk w whose row is in bucket b.
 __global__ __launch_bounds__(kThreads) void seg_count_kernel(RowParams p, int shift, int nb, int64_t n_chunks,
-                                                             int32_t* cnt1, int32_t* n_split, int32_t* n_hot) {
+                                                             int32_t* cnt1, int32_t* n_split, int32_t* n_hot,
+                                                             int32_t* gcur, int64_t R) {
   __shared__ int32_t lh[kMaxBuckets];
   const int tid = threadIdx.x;
   if (blockIdx.x == 0 && tid == 0) {  // the build appends long segments' pieces and hot buckets' slices
     *n_split = 0;
     *n_hot = 0;
   }
+  // the hot buckets' per-row counters, added to by the build launch
+  for (int64_t r = (int64_t)blockIdx.x * kThreads + tid; r < R; r += (int64_t)gridDim.x * kThreads) gcur[r] = 0;
   for (int b = tid; b < nb; b += kThreads) lh[b] = 0;
   __syncthreads();
   const int64_t g0 = (int64_t)blockIdx.x * kChunk;
@@ -626,6 +630,101 @@ __device__ __forceinline__ int32_t list_pieces_share(const int32_t (&c)[kPer], i
   return total;
 }
 
+// Hot buckets, step 4 spread over workgroups: (a) each slice of kSlice terms
+// counts its terms per row (LDS) and adds the counts into gcur (global
+// atomics, one per row and slice) -- done by the build launch's extra
+// workgroups while the other buckets build; (b) one workgroup per hot bucket
+// scans the counts into segment offsets, sets gcur to them and reserves the
+// long segments' piece entries; (c) each slice counts again, reserves its
+// place in each row's segment with one global atomic per row, places its
+// term ids and lists its share of the piece entries.  Slices are (bucket <<
+// 32 | slice); step (c) strides over the *n_hot entries of hot_list.
+struct HotSlice {
+  int64_t p0, p1, row_lo, row_hi;
+};
+__device__ __forceinline__ HotSlice hot_slice(uint64_t e, int64_t R, int shift, int64_t n_chunks, const int32_t* pos1) {
+  const int b = (int)(e >> 32), g = (int)(uint32_t)e;
+  const int64_t s0 = pos1[(int64_t)b * n_chunks], s1 = pos1[(int64_t)(b + 1) * n_chunks];
+  HotSlice h;
+  h.p0 = s0 + (int64_t)g * kSlice;
+  h.p1 = min(s1, h.p0 + kSlice);
+  h.row_lo = (int64_t)b << shift;
+  h.row_hi = min(R, (int64_t)(b + 1) << shift);
+  return h;
+}
+
+// LDS counts of the slice's terms with rows in [w0, w0 + W)
+__device__ __forceinline__ void hot_window_count(const uint64_t* pairs, int64_t p0, int64_t p1, int64_t w0, int64_t W,
+                                                 int32_t* cnt) {
+  constexpr int kU = 8;
+  const int tid = threadIdx.x;
+  for (int j = tid; j < kWindow; j += kBuildThreads) cnt[j] = 0;
+  __syncthreads();
+  for (int64_t i0 = p0; i0 < p1; i0 += kU * kBuildThreads) {
+    uint64_t pr[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t i = i0 + u * kBuildThreads + tid;
+      pr[u] = i < p1 ? pairs[i] : ~uint64_t(0);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t d = (int64_t)(pr[u] >> 32) - w0;
+      if (d >= 0 && d < W) atomicAdd(&cnt[d], 1);
+    }
+  }
+  __syncthreads();
+}
+
+// The build launch's workgroups past the buckets' count the hot buckets'
+// terms per row into gcur (zeroed by seg_count), one kSlice-term slice at a
+// time, while the other buckets build: each finds the slices from the bucket
+// sizes -- the same slices the hot buckets' own workgroups list for
+// seg_hot_place -- and takes every ne-th of them.
+__device__ __forceinline__ void hot_count_role(int64_t R, int shift, int nb, int64_t n_chunks, const int32_t* pos1,
+                                               const uint64_t* pairs, int32_t* gcur, int e, int ne, int32_t* cnt) {
+  constexpr int kPer = kMaxBuckets / kBuildThreads;  // 4
+  __shared__ int32_t s_first[kMaxBuckets];          // first slice of each bucket
+  const int tid = threadIdx.x;
+  int32_t ns[kPer], mine = 0;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int bb = tid * kPer + q;
+    ns[q] = 0;
+    if (bb < nb) {
+      const int64_t size = pos1[(int64_t)(bb + 1) * n_chunks] - pos1[(int64_t)bb * n_chunks];
+      if (size > kHotPairs) ns[q] = (int32_t)((size + kSlice - 1) / kSlice);
+    }
+    mine += ns[q];
+  }
+  int32_t total;
+  int32_t at = block_exclusive_scan<kBuildThreads>(mine, total);
+  if (total == 0) return;  // uniform in the workgroup
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    s_first[tid * kPer + q] = at;
+    at += ns[q];
+  }
+  __syncthreads();
+  for (int k = e; k < total; k += ne) {
+    // the slice's bucket: the last bucket whose first slice is at or before k
+    int lo = 0, hi = kMaxBuckets - 1;
+#pragma unroll
+    for (int step = 0; step < 12; ++step) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_first[mid] <= k) lo = mid; else hi = mid - 1;
+    }
+    const HotSlice h = hot_slice(((uint64_t)lo << 32) | (uint32_t)(k - s_first[lo]), R, shift, n_chunks, pos1);
+    for (int64_t w0 = h.row_lo; w0 < h.row_hi; w0 += kWindow) {
+      const int64_t W = min((int64_t)kWindow, h.row_hi - w0);
+      hot_window_count(pairs, h.p0, h.p1, w0, W, cnt);
+      for (int j = tid; j < W; j += kBuildThreads)
+        if (cnt[j]) atomicAdd(&gcur[w0 + j], cnt[j]);
+      __syncthreads();
+    }
+  }
+}
+
 // Step 4: one workgroup per bucket.  Its pairs are pairs[s0, s1); its rows
 // [b << shift, min((b + 1) << shift, R)) are taken kWindow at a time: count
 // the terms per row, scan the counts into segment offsets (offs), then place
@@ -641,15 +740,19 @@ __global__ __launch_bounds__(kBuildThreads) void seg_build_kernel(int64_t R, int
   constexpr int kU = 8;                          // pairs in flight per lane
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
+  if (b >= nb) {
+    hot_count_role(R, shift, nb, n_chunks, pos1, pairs, gcur, b - nb, (int)gridDim.x - nb, cur);
+    return;
+  }
   const int64_t s0 = pos1[(int64_t)b * n_chunks], s1 = pos1[(int64_t)(b + 1) * n_chunks];
   const int64_t row_lo = (int64_t)b << shift;
   const int64_t row_hi = min(R, (int64_t)(b + 1) << shift);
   if (b == nb - 1 && tid == 0) offs[R] = (int32_t)s1;
   if (s1 - s0 > kHotPairs) {
-    // a hot bucket: one workgroup would stream all its terms alone; the
-    // seg_hot_* kernels build it with one workgroup per kSlice terms.  Zero
-    // its rows' counters and list its slices.
-    for (int64_t r = row_lo + tid; r < row_hi; r += kBuildThreads) gcur[r] = 0;
+    // a hot bucket: one workgroup would stream all its terms alone; it is
+    // built with one workgroup per kSlice terms (counted by this launch's
+    // extra workgroups, then seg_hot_scan and seg_hot_place).  List its
+    // slices.
     if (tid == 0) {
       hot[b] = 1;
       const int ns = (int)((s1 - s0 + kSlice - 1) / kSlice);
@@ -710,69 +813,6 @@ __global__ __launch_bounds__(kBuildThreads) void seg_build_kernel(int64_t R, int
     }
     base += total;
     __syncthreads();
-  }
-}
-
-// Hot buckets, step 4 spread over workgroups: (a) each slice of kSlice terms
-// counts its terms per row (LDS) and adds the counts into gcur (global
-// atomics, one per row and slice); (b) one workgroup per hot bucket scans
-// the counts into segment offsets, sets gcur to them and lists long
-// segments' pieces; (c) each slice counts again, reserves its place in each
-// row's segment with one global atomic per row, and places its term ids.
-// Slices are entries (bucket << 32 | slice) of hot_list; workgroups stride
-// over the *n_hot entries.
-struct HotSlice {
-  int64_t p0, p1, row_lo, row_hi;
-};
-__device__ __forceinline__ HotSlice hot_slice(uint64_t e, int64_t R, int shift, int64_t n_chunks, const int32_t* pos1) {
-  const int b = (int)(e >> 32), g = (int)(uint32_t)e;
-  const int64_t s0 = pos1[(int64_t)b * n_chunks], s1 = pos1[(int64_t)(b + 1) * n_chunks];
-  HotSlice h;
-  h.p0 = s0 + (int64_t)g * kSlice;
-  h.p1 = min(s1, h.p0 + kSlice);
-  h.row_lo = (int64_t)b << shift;
-  h.row_hi = min(R, (int64_t)(b + 1) << shift);
-  return h;
-}
-
-// LDS counts of the slice's terms with rows in [w0, w0 + W)
-__device__ __forceinline__ void hot_window_count(const uint64_t* pairs, int64_t p0, int64_t p1, int64_t w0, int64_t W,
-                                                 int32_t* cnt) {
-  constexpr int kU = 8;
-  const int tid = threadIdx.x;
-  for (int j = tid; j < kWindow; j += kBuildThreads) cnt[j] = 0;
-  __syncthreads();
-  for (int64_t i0 = p0; i0 < p1; i0 += kU * kBuildThreads) {
-    uint64_t pr[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int64_t i = i0 + u * kBuildThreads + tid;
-      pr[u] = i < p1 ? pairs[i] : ~uint64_t(0);
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int64_t d = (int64_t)(pr[u] >> 32) - w0;
-      if (d >= 0 && d < W) atomicAdd(&cnt[d], 1);
-    }
-  }
-  __syncthreads();
-}
-
-__global__ __launch_bounds__(kBuildThreads) void seg_hot_count_kernel(int64_t R, int shift, int64_t n_chunks,
-                                                                      const int32_t* pos1, const uint64_t* pairs,
-                                                                      const uint64_t* hot_list, const int32_t* n_hot,
-                                                                      int32_t* gcur) {
-  __shared__ int32_t cnt[kWindow];
-  const int nh = *n_hot;
-  for (int e = blockIdx.x; e < nh; e += gridDim.x) {
-    const HotSlice h = hot_slice(hot_list[e], R, shift, n_chunks, pos1);
-    for (int64_t w0 = h.row_lo; w0 < h.row_hi; w0 += kWindow) {
-      const int64_t W = min((int64_t)kWindow, h.row_hi - w0);
-      hot_window_count(pairs, h.p0, h.p1, w0, W, cnt);
-      for (int j = threadIdx.x; j < W; j += kBuildThreads)
-        if (cnt[j]) atomicAdd(&gcur[w0 + j], cnt[j]);
-      __syncthreads();
-    }
   }
 }
 
@@ -1397,7 +1437,7 @@ int launch_segmented(const char* name, int esize, const RowParams& p, int64_t R,
   const int nbk = (int)L.nbk;
   const dim3 chunks((unsigned)L.n_chunks), blk(kThreads);
   launch_kernel("tile_gather_backward/count", seg_count_kernel, chunks, blk, 0, s, p, L.shift, nbk, L.n_chunks, cnt1,
-                n_split, n_hot);
+                n_split, n_hot, gcur, R);
   launch_kernel("tile_gather_backward/bsum", seg_bsum_kernel, dim3((unsigned)L.nb1), blk, 0, s, (const int32_t*)cnt1,
                 L.L1, bsum);
   const int scanned = L.nb1 > kScanFuse;
@@ -1406,14 +1446,15 @@ int launch_segmented(const char* name, int esize, const RowParams& p, int64_t R,
                 (const int32_t*)bsum, pos1, scanned);
   launch_kernel("tile_gather_backward/bucket", seg_bucket_kernel, chunks, blk, 0, s, p, L.shift, nbk, L.n_chunks,
                 (const int32_t*)pos1, pairs);
-  launch_kernel("tile_gather_backward/build", seg_build_kernel, dim3((unsigned)nbk), dim3(kBuildThreads), 0, s, R,
+  // one workgroup per bucket, then kHotCountWorkgroups counting the hot
+  // buckets' slices (usually none)
+  launch_kernel("tile_gather_backward/build", seg_build_kernel, dim3((unsigned)(nbk + kHotCountWorkgroups)),
+                dim3(kBuildThreads), 0, s, R,
                 L.shift, nbk, L.n_chunks, (const int32_t*)pos1, (const uint64_t*)pairs, offs, perm, split, n_split,
                 gcur, hot, hot_list, n_hot);
   // hot buckets (more than kHotPairs terms): many workgroups each; the
   // slice kernels stride over the list the build wrote (usually empty)
   const dim3 hgrid(256), hblk(kBuildThreads);
-  launch_kernel("tile_gather_backward/hot_count", seg_hot_count_kernel, hgrid, hblk, 0, s, R, L.shift, L.n_chunks,
-                (const int32_t*)pos1, (const uint64_t*)pairs, (const uint64_t*)hot_list, (const int32_t*)n_hot, gcur);
   launch_kernel("tile_gather_backward/hot_scan", seg_hot_scan_kernel, dim3((unsigned)nbk), hblk, 0, s, R, L.shift,
                 L.n_chunks, (const int32_t*)pos1, hot, offs, gcur, n_split);
   launch_kernel("tile_gather_backward/hot_place", seg_hot_place_kernel, hgrid, hblk, 0, s, R, L.shift, L.n_chunks,
