@@ -298,6 +298,29 @@ def test_scaled_output_may_alias_the_accumulator(stg, orc):
     assert np.all(np.abs(to_host(inout).astype(np.float64) - want) <= tol)
 
 
+@pytest.mark.parametrize("ws", [None, "auto"])
+def test_scaled_general_output_may_alias_the_accumulator(stg, orc, ws):
+    """The general path in place (out is acc): e4m3 values with e4m3 scales
+    per 16, fused (no workspace) and with decoded operands (the bf16 GEMM's
+    epilogue reads acc and writes out in the same lane), within gamma_K *
+    sum|terms| plus the accumulator's rounding."""
+    M, N, K = 300, 300, 160
+    rng = np.random.default_rng(78)
+    ca, cb = codes(rng, (M, K), "e4m3"), codes(rng, (N, K), "e4m3")
+    sa, sb = scale_codes(rng, (M, K // 16), "e4m3"), scale_codes(rng, (N, K // 16), "e4m3")
+    acc = rng.standard_normal((M, N)).astype(np.float32)
+    say("gemm_scaled general path in place: out is acc, workspace", ws)
+    inout = to_dev(acc)
+    stg.gemm_scaled(to_dev(ca), "e4m3", to_dev(sa), to_dev(cb), "e4m3", to_dev(sb), K, 16, scale_fmt="e4m3",
+                    acc=inout, out=inout, workspace=ws)
+    torch.cuda.synchronize()
+    want = orc.gemm_scaled_f64(ca, "e4m3", sa, cb, "e4m3", sb, K, 16, s_fmt="e4m3", acc=acc)
+    mag = orc.gemm_scaled_f64(ca & 0x7F, "e4m3", sa & 0x7F, cb & 0x7F, "e4m3", sb & 0x7F, K, 16, s_fmt="e4m3")
+    u = 2.0 ** -24
+    tol = K * u / (1 - K * u) * mag + np.abs(acc.astype(np.float64)) * u + 1e-30
+    assert np.all(np.abs(to_host(inout).astype(np.float64) - want) <= tol)
+
+
 @pytest.mark.parametrize("K,block", [(32, 32), (64, 32), (96, 32), (160, 32), (192, 64), (128, 128)])
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
 def test_scaled_small_k_main_kernel(stg, orc, K, block, fmt):
