@@ -370,7 +370,7 @@ int gemm_scaled_ws(const void* A, int32_t a_fmt, int64_t lda, const void* a_scal
 /* Workspace bytes for gemm_scaled_ws: 0 where the call takes the scaled MFMA
  * or decoding first does not pay (M or N at most 256, K = 0, or sizes past
  * the bf16 GEMM's limits); otherwise the bytes of the decoded operands, bf16
- * (M, ceil(K/16)*16) and (K, ceil(N/8)*8), each rounded up to 256.  A
+ * (M, ceil(K/16)*16) and (K, ceil(N/64)*64), each rounded up to 256.  A
  * negative value is minus an error code (unknown formats: STG_ERR_UNSUPPORTED;
  * negative sizes, block < 1, K not a multiple of block: STG_ERR_INVALID). */
 int64_t gemm_scaled_workspace(int32_t a_fmt, int32_t b_fmt, int32_t scale_fmt, int64_t block, int64_t M,

@@ -555,9 +555,12 @@ __global__ __launch_bounds__(256) void decode_cols_kernel(DecodeParams d, int64_
 
 constexpr int64_t kDecAlign = 256;
 inline int64_t dec_up(int64_t x) { return (x + kDecAlign - 1) / kDecAlign * kDecAlign; }
-// leading dimensions of A' and B' (elements)
+// leading dimensions of A' and B' (elements): whole runs of 16 in A' rows;
+// B' rows a multiple of 128 bytes, so the transposed 128-byte chunks are whole
+// cache lines (with rows 16-byte aligned only: decode B 3 us slower, the bf16
+// GEMM 3-6 us)
 inline int64_t dec_lda(int64_t K) { return (K + 15) / 16 * 16; }
-inline int64_t dec_ldb(int64_t N) { return (N + 7) / 8 * 8; }
+inline int64_t dec_ldb(int64_t N) { return (N + 63) / 64 * 64; }
 
 template <int FMT>
 int launch_decode(bool rows, bool blk16, const DecodeParams& d, hipStream_t s) {

@@ -373,7 +373,7 @@ def test_packed_descriptor_and_array_bytes(stg):
 def test_gemm_scaled_workspace_query(stg):
     """gemm_scaled_workspace: 0 where the scaled MFMA runs (e8m0 scales,
     blocks of 32 * 2^k, one operand width) or where M or N is at most 256;
-    otherwise bf16 (M, ceil(K/16)*16) plus (K, ceil(N/8)*8), each rounded up
+    otherwise bf16 (M, ceil(K/16)*16) plus (K, ceil(N/64)*64), each rounded up
     to 256 bytes; bad arguments give minus an error code."""
     up = lambda x: (x + 255) // 256 * 256
     q = stg.gemm_scaled_workspace
@@ -382,9 +382,9 @@ def test_gemm_scaled_workspace_query(stg):
     assert q("e4m3", "e4m3", "e4m3", 16, 256, 8193, 4096) == 0
     assert q("e4m3", "e4m3", "e4m3", 16, 8191, 256, 4096) == 0
     assert q("e4m3", "e4m3", "e4m3", 16, 300, 300, 0) == 0
-    assert q("e4m3", "e4m3", "e4m3", 16, 8191, 8193, 4096) == up(8191 * 4096 * 2) + up(4096 * 8200 * 2)
-    assert q("e2m1", "e4m3", "e8m0", 32, 257, 259, 99 * 32) == up(257 * 3168 * 2) + up(3168 * 264 * 2)
-    assert q("e4m3", "e5m2", "e8m0", 3, 300, 301, 99) == up(300 * 112 * 2) + up(99 * 304 * 2)
+    assert q("e4m3", "e4m3", "e4m3", 16, 8191, 8193, 4096) == up(8191 * 4096 * 2) + up(4096 * 8256 * 2)
+    assert q("e2m1", "e4m3", "e8m0", 32, 257, 259, 99 * 32) == up(257 * 3168 * 2) + up(3168 * 320 * 2)
+    assert q("e4m3", "e5m2", "e8m0", 3, 300, 301, 99) == up(300 * 112 * 2) + up(99 * 320 * 2)
     lib = stg.load_library()
     assert lib.gemm_scaled_workspace(0, 0, 1, 16, 300, 300, 48) == q("e4m3", "e4m3", "e4m3", 16, 300, 300, 48)
     assert lib.gemm_scaled_workspace(7, 0, 1, 16, 300, 300, 64) == -2  # unknown format
