@@ -42,6 +42,8 @@
 //    when at most 8 remain (N = 8193 leaves one), to a skinny vector kernel.
 //    Tile ids are renumbered so that consecutive ids run on one XCD and walk
 //    4-row-panel groups, keeping A and B panels resident in that XCD's L2.
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace stg {
@@ -483,6 +485,273 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
   }
 }
 
+// Main kernel for 16-byte aligned operand rows: 4 waves, one per SIMD, each
+// owning a 128 x 128 block of the 256 x 256 tile (256 fp32 accumulators per
+// lane, held in the accumulation registers).  Against the 8-wave kernel's
+// 128 x 64 wave blocks it reads a third fewer operand bytes from LDS per
+// MFMA (measured at 8192 x 8192 x 4096: 1.31 against 1.19 PFLOP/s).  With
+// one wave per SIMD a DMA instruction that cannot issue holds back the MFMAs
+// behind it, so when the operand feed itself is the bound -- rows not 16-byte
+// aligned, where every 16-byte chunk straddles two -- the 8-wave kernel, whose
+// SIMD partner keeps issuing, is the faster one (odd strides: 1.04 against
+// 1.09), and the host picks this kernel only for aligned rows.
+//  * Same stages, swizzles, zero-fill and ring as the 8-wave kernel (4 slots of
+//    32 K values; stage k+3 in flight during step k, spread 8 DMA instructions
+//    per wave among the step's 32 MFMAs); one descriptor per operand panel
+//    for the whole K loop, the stage selected by the instruction's scalar
+//    offset, so a DMA costs no vector arithmetic.
+//  * The loop is unrolled over the 4 ring slots so that every LDS address is a
+//    per-lane base plus an immediate; the operands of the next 16 K values are
+//    read into a second register set while the current ones feed the MFMAs.
+//  * Epilogue through LDS in 32-row passes, also for fp32 output, so rows
+//    leave as 16-byte chunks.
+constexpr int W4_NS = 4;                           // ring stages
+constexpr int W4_ASTAGE = 256 * BK * 2;            // 256 rows of 64 bytes
+constexpr int W4_BSTAGE = BK * 256 * 2;            // 32 rows of 512 bytes
+constexpr int W4_STAGE = W4_ASTAGE + W4_BSTAGE;
+constexpr int W4_DMA = 8;                          // DMA instructions per wave and stage (4 A, then 4 B)
+constexpr int W4_EPI_PITCH = 128 * 2 + 16;         // bf16 staging: bytes per row of a wave's block
+constexpr int W4_EPI_WAVE = 128 * W4_EPI_PITCH;
+constexpr int W4_F32_PITCH = 128 * 4 + 32;         // fp32 staging: rows 4 apart land 32 banks apart
+constexpr int W4_F32_WAVE = 32 * W4_F32_PITCH;
+constexpr int W4_LDS = W4_NS * W4_STAGE > 4 * W4_EPI_WAVE ? W4_NS * W4_STAGE : 4 * W4_EPI_WAVE;
+static_assert(4 * W4_F32_WAVE <= W4_LDS, "fp32 staging fits");
+
+// LDS DMA of 16 bytes per lane at buffer offset off + soff (soff: scalar)
+__device__ __forceinline__ void dma16s(const u32x4_s& rs, uint32_t off, uint32_t soff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(off), "s"(rs), "s"(soff)
+               : "memory", "m0");
+}
+
+template <int V>
+using Slot = std::integral_constant<int, V>;
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4_kernel(GemmParams p) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_of(xcd_remap(blockIdx.x, gridDim.x), p.tiles_m, p.tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * 256;
+  const int64_t n0 = p.n_base + (int64_t)tn * 256;
+  const int nk = (int)((p.K + BK - 1) / BK);
+  const int nkf = (int)(p.K / BK);  // stages wholly inside K
+
+  // whole panels: A rows m0 .., B columns n0 .. (the host bounds both below 2^31 bytes)
+  const u32x4_s rsa = rsrc_words(p.A + m0 * p.lda * 2, ((p.M - 1 - m0) * p.lda + p.K) * 2);
+  const u32x4_s rsb = rsrc_words(p.B + n0 * 2, ((p.K - 1) * p.ldb + (p.N - n0)) * 2);
+  const uint32_t bstep = (uint32_t)(BK * p.ldb * 2);
+
+  // chunk of DMA instruction q: A row r, logical chunk c (swizzled slot pos & 3);
+  // B row k, logical chunk cb (slot pos & 31)
+  uint32_t a_off[4], b_off[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int pos = (wave * 4 + q) * 64 + lane;
+    const int r = pos >> 2, c = a_phys(r, pos & 3);
+    a_off[q] = m0 + r < p.M ? (uint32_t)(r * p.lda * 2 + c * 16) : kOOB;
+    const int k = pos >> 5, cb = (pos & 31) ^ b_swz<32>(k);
+    b_off[q] = n0 + 8 * cb + 8 <= p.N ? (uint32_t)(k * p.ldb * 2 + cb * 16) : kOOB;
+  }
+  const uint32_t smem_lds =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem);
+
+  // DMA instruction q of stage kt into ring slot `slot`; a stage reaching past K
+  // (part) sends its chunks with no valid value out of range
+  auto dma = [&](int kt, int slot, int q, bool part) {
+    const uint32_t st = smem_lds + slot * W4_STAGE;
+    const int kleft = part ? (int)(p.K - (int64_t)kt * BK) : BK;
+    const int pos = (wave * 4 + (q & 3)) * 64 + lane;
+    if (q < 4) {
+      const uint32_t off = part && 8 * a_phys(pos >> 2, pos & 3) + 8 > kleft ? kOOB : a_off[q];
+      dma16s(rsa, off, (uint32_t)kt * (BK * 2), st + (wave * 4 + q) * 1024);
+    } else {
+      const uint32_t off = part && (pos >> 5) >= kleft ? kOOB : b_off[q - 4];
+      dma16s(rsb, off, (uint32_t)kt * bstep, st + W4_ASTAGE + (wave * 4 + q - 4) * 1024);
+    }
+  };
+  // after this lane's DMA of stage kt landed: A chunks straddling K, which the
+  // DMA left zero, written element by element (the main launch has no N edge)
+  auto fix_stage = [&](int kt) {
+    const int64_t k0 = (int64_t)kt * BK;
+    if (!(k0 + BK > p.K && (p.K & 7))) return;
+    char* st = smem + (kt % W4_NS) * W4_STAGE;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int pos = (wave * 4 + q) * 64 + lane;
+      const int r = pos >> 2, c = a_phys(r, pos & 3);
+      const int64_t col = k0 + 8 * c, left = p.K - col;
+      if (m0 + r < p.M && left > 0 && left < 8) {
+        const uint16_t* src = (const uint16_t*)(p.A + ((m0 + r) * p.lda + col) * 2);
+        u32x4 v = {0, 0, 0, 0};
+        for (int e = 0; e < 8; ++e)
+          if (e < left) vec_set<2>(v, e, src[e]);
+        *(u32x4*)(st + (wave * 4 + q) * 1024 + lane * 16) = v;
+      }
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  bf16x8 fa[2][4], fb[2][4];
+
+  // per-lane LDS offsets within a stage.  A: row ar + 32 i, chunk 2 ks + lane / 32
+  // (rows 32 apart share the swizzle, so i only adds 2048).  B (transposed reads):
+  // lane t of 16-lane group g reads row 16 ks + 8 (g / 2) + 4 h + t / 4 at columns
+  // wn 128 + 32 j + 16 (g % 2) + 4 (t % 4) .. + 3 (ks, h only add immediates)
+  const int ar = wm * 128 + (lane & 31);
+  const uint32_t a_lds0 = ar * 64 + (a_phys(ar, lane >> 5) << 4);
+  const uint32_t a_lds1 = ar * 64 + (a_phys(ar, 2 + (lane >> 5)) << 4);
+  uint32_t b_lds[4];
+  {
+    const int g = lane >> 4, t = lane & 15;
+    const int row = 8 * (g >> 1) + (t >> 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = wn * 128 + j * 32 + 16 * (g & 1) + 4 * (t & 3);
+      b_lds[j] = W4_ASTAGE + row * 512 + ((col >> 3) ^ b_swz<32>(row)) * 16 + (col & 7) * 2;
+    }
+  }
+  // LDS read e of sub-step ks from the stage at `base` into operand set s:
+  // e = 0..3 the A blocks, e = 4..11 the two halves of the B blocks
+  auto rd = [&](const char* base, int ks, int s, int e) {
+    if (e < 4) {
+      fa[s][e] = *(const bf16x8*)(base + (ks ? a_lds1 : a_lds0) + e * 2048);
+    } else {
+      const int j = (e - 4) >> 1, h = (e - 4) & 1;
+      const s16x4 v =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + b_lds[j] + ks * 8192 + h * 2048));
+      s16x8 cur = __builtin_bit_cast(s16x8, fb[s][j]);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) cur[4 * h + x] = v[x];
+      fb[s][j] = __builtin_bit_cast(bf16x8, cur);
+    }
+  };
+  // the 16 MFMAs of operand set s; read e of the other set after MFMA e (when
+  // rdo); DMA instruction q0 + d of stage dkt after MFMA 4 d + 3 (when dmado)
+  auto phase = [&](int s, bool rdo, const char* rbase, int rks, bool dmado, int dkt, int dslot, int q0, bool part) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      acc[m >> 2][m & 3] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][m >> 2], fb[s][m & 3], acc[m >> 2][m & 3], 0, 0, 0);
+      if (rdo && m < 12) {
+        __builtin_amdgcn_sched_barrier(0);
+        rd(rbase, rks, s ^ 1, m);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (dmado && (m & 3) == 3) {
+        __builtin_amdgcn_sched_barrier(0);
+        dma(dkt, dslot, q0 + (m >> 2), part);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // prologue: stages 0 .. 2 in flight, wait for 0 and 1
+  for (int s = 0; s < W4_NS - 1 && s < nk; ++s)
+    for (int q = 0; q < W4_DMA; ++q) dma(s, s, q, s >= nkf);
+  wait_vmcnt(max(0, min(nk, W4_NS - 1) - 2) * W4_DMA);
+  if (nk > 0) fix_stage(0);
+  if (nk > 1) fix_stage(1);
+  __syncthreads();
+  if (nk > 0)
+#pragma unroll
+    for (int e = 0; e < 12; ++e) rd(smem, 0, 0, e);
+
+  // step kt: sub-step 1 of stage kt and sub-step 0 of stage kt + 1 are read
+  // while the MFMAs of sub-steps 0 and 1 run; stage kt + 3 is issued.  Stage
+  // kt + 1 became visible at the previous barrier; this step waits for stage
+  // kt + 2.  A ring slot is refilled only after the barrier that follows its
+  // last reads, which have completed by then (their MFMAs have issued), so the
+  // steady steps use a bare s_barrier.
+  auto step_steady = [&](int kt, auto SLOT) {
+    constexpr int slot = decltype(SLOT)::value;
+    phase(0, true, smem + slot * W4_STAGE, 1, true, kt + 3, (slot + 3) % W4_NS, 0, false);
+    phase(1, true, smem + ((slot + 1) % W4_NS) * W4_STAGE, 0, true, kt + 3, (slot + 3) % W4_NS, 4, false);
+    wait_vmcnt(W4_DMA);
+    __builtin_amdgcn_s_barrier();
+  };
+  int kt = 0;
+  for (; kt + 6 < nkf; kt += 4) {  // every stage issued in these four steps is whole in K
+    step_steady(kt, Slot<0>());
+    step_steady(kt + 1, Slot<1>());
+    step_steady(kt + 2, Slot<2>());
+    step_steady(kt + 3, Slot<3>());
+  }
+  for (; kt < nk; ++kt) {
+    const bool dmado = kt + 3 < nk;
+    const int ds = (kt + 3) % W4_NS;
+    phase(0, true, smem + (kt % W4_NS) * W4_STAGE, 1, dmado, kt + 3, ds, 0, kt + 3 >= nkf);
+    phase(1, kt + 1 < nk, smem + ((kt + 1) % W4_NS) * W4_STAGE, 0, dmado, kt + 3, ds, 4, kt + 3 >= nkf);
+    if (kt + 2 < nk) {
+      wait_vmcnt(dmado ? W4_DMA : 0);
+      fix_stage(kt + 2);
+    }
+    __syncthreads();
+  }
+
+  // clipped epilogue, 32 rows of the wave's block per pass: lane l's
+  // accumulator r of block (i, j) is row 8 (r / 4) + 4 (l / 32) + r % 4,
+  // column l % 32 of that 32 x 32 block
+  if (p.c_f32) {
+    char* ep = smem + wave * W4_F32_WAVE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          *(float*)(ep + (8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * W4_F32_PITCH + (j * 32 + (lane & 31)) * 4) =
+              acc[i][j][r];
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll 4
+      for (int c = lane; c < 32 * 32; c += 64) {
+        const int row = c >> 5, ch = c & 31;
+        const int64_t grow = m0 + wm * 128 + i * 32 + row;
+        const int64_t gcol = n0 + wn * 128 + ch * 4;
+        if (grow >= p.M) continue;
+        u32x4 v = *(const u32x4*)(ep + row * W4_F32_PITCH + ch * 16);
+        if (p.acc) {
+          const u32x4 a = ld16((const char*)(p.acc + grow * p.ldacc + gcol));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = __float_as_uint(__uint_as_float(v[e]) + __uint_as_float(a[e]));
+        }
+        st16(p.C + (grow * p.ldc + gcol) * 4, v);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+    }
+    return;
+  }
+  char* ep = smem + wave * W4_EPI_WAVE;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        *(__bf16*)(ep + row * W4_EPI_PITCH + (j * 32 + (lane & 31)) * 2) = (__bf16)acc[i][j][r];
+      }
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
+  for (int c = lane; c < 128 * 16; c += 64) {
+    const int row = c >> 4, ch = c & 15;
+    const int64_t grow = m0 + wm * 128 + row;
+    if (grow >= p.M) continue;
+    st16(p.C + (grow * p.ldc + n0 + wn * 128 + ch * 8) * 2, *(const u32x4*)(ep + row * W4_EPI_PITCH + ch * 16));
+  }
+}
+
 // main: 8 waves of 128 x 64 accumulators (two waves per SIMD), 4-stage ring;
 // edge strip: small stages, so a deep ring hides the load latency of its
 // long K loop
@@ -505,6 +774,8 @@ bool lds_configured() {
   return once.run([] {
     return hipFuncSetAttribute((const void*)gemm_kernel<MainCfg>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                MainCfg::LDS_B) == hipSuccess &&
+           hipFuncSetAttribute((const void*)gemm_w4_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, W4_LDS) ==
+               hipSuccess &&
            hipFuncSetAttribute((const void*)gemm_kernel<EdgeCfg>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                EdgeCfg::LDS_B) == hipSuccess;
   });
@@ -545,7 +816,19 @@ int gemm_bf16(const GemmNames& names, const void* A, int64_t lda, const void* B,
   const int64_t n_main = (N / MainCfg::BN) * MainCfg::BN;
   int rc;
   p.n_base = 0;
-  if (n_main > 0 && (rc = launch<MainCfg>(names.main, p, n_main, s))) return rc;
+  // 16-byte aligned rows take the 4-wave kernel (its whole-panel descriptors
+  // also need the B panel, read up to a stage past K, below 2^31 bytes)
+  const bool w4 = (lda & 7) == 0 && (ldb & 7) == 0 && ((uintptr_t)A & 15) == 0 && ((uintptr_t)B & 15) == 0 &&
+                  (K + 2 * BK) * ldb * 2 < kMaxOffset32;
+  if (n_main > 0 && w4) {
+    p.tiles_m = (int32_t)((M + 255) / 256);
+    p.tiles_n = (int32_t)(n_main / 256);
+    launch_kernel(names.main, gemm_w4_kernel, dim3((unsigned)((int64_t)p.tiles_m * p.tiles_n)), dim3(256),
+                  (uint32_t)W4_LDS, s, p);
+    if ((rc = check_launch(names.main))) return rc;
+  } else if (n_main > 0 && (rc = launch<MainCfg>(names.main, p, n_main, s))) {
+    return rc;
+  }
   p.n_base = n_main;
   const int64_t rem = N - n_main;
   if (rem > 8) return launch<EdgeCfg>(names.edge, p, rem, s);

@@ -255,3 +255,43 @@ def test_gemm_large_shape_sampled(stg, orc):
     got = inputs.bf16_bits_to_f32(to_host(C[torch.from_numpy(r).cuda(), torch.from_numpy(c).cuda()])).astype(np.float64)
     want = orc.gemm_sample_f64(g["A"], g["B"], r, c)
     check(got, want, False)
+
+
+def _strided(X, ld, fill=0x7FA5):
+    """Device copy of bf16 bits X (rows, cols) stored with row stride ld."""
+    rows, cols = X.shape
+    S = np.full((rows, ld), fill, dtype=np.uint16)
+    S[:, :cols] = X
+    return to_dev(S)[:, :cols]
+
+
+@pytest.mark.parametrize("shape", [(8192, 8192, 4096), (1000, 1280, 4097), (257, 512, 33), (513, 256, 7),
+                                   (256, 768, 1), (700, 1536, 2000)])
+def test_gemm_aligned_rows_kernel_matches_odd_rows_kernel(stg, orc, shape):
+    """Operand rows that start 16-byte aligned take the 4-wave main kernel,
+    others the 8-wave one.  Both sum every output in the same K order (one
+    32x32x16 MFMA per 16 K values, stages in order), so the same operands
+    stored with aligned and with odd row strides must give identical bits,
+    fp32 and bf16 output alike; the aligned result is also held to the oracle
+    (in full, or sampled at 8192 x 8192 x 4096)."""
+    M, N, K = shape
+    g = inputs.gemm(M, N, K, seed=M + 3 * N + K)
+    lda = (K + 7) // 8 * 8
+    Aa, Ao = _strided(g["A"], lda), _strided(g["A"], lda + 1)
+    Ba, Bo = _strided(g["B"], N + 8), _strided(g["B"], N + 1)
+    say("gemm aligned vs odd row strides", shape)
+    for dt in (torch.float32, torch.bfloat16):
+        Ca = torch.full((M, N), 7.0, dtype=dt, device="cuda:0")
+        Co = torch.full((M, N), 7.0, dtype=dt, device="cuda:0")
+        stg.gemm_bounded(Aa, Ba, out=Ca)
+        stg.gemm_bounded(Ao, Bo, out=Co)
+        torch.cuda.synchronize()
+        iv = torch.int32 if dt == torch.float32 else torch.int16
+        assert torch.equal(Ca.view(iv), Co.view(iv)), f"{dt}: kernels differ"
+        if dt == torch.float32:
+            if M * N <= 2_000_000:
+                check(to_host(Ca).astype(np.float64), orc.gemm_f64(g["A"], g["B"]), True)
+            else:
+                r, c = _sample_coords(M, N)
+                got = to_host(Ca[torch.from_numpy(r).cuda(), torch.from_numpy(c).cuda()]).astype(np.float64)
+                check(got, orc.gemm_sample_f64(g["A"], g["B"], r, c), True)
