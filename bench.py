@@ -649,6 +649,30 @@ def run_gemm(stg, inputs, steps, warmup):
     return e
 
 
+def run_gemm_aligned(stg, inputs, steps, warmup):
+    """The same GEMM at 8192 x 8192 x 4096, where every operand row starts
+    16-byte aligned (the 4-wave main kernel; no K edge, no remainder columns),
+    beside hipBLASLt (torch.matmul) on the same operands and output."""
+    import torch
+
+    M, N, K = 8192, 8192, 4096
+    g = inputs.gemm(M, N, K)
+    A, B = _dev(g["A"]), _dev(g["B"])
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    fn = lambda: stg.gemm_bounded(A, B, out=C)
+    ms = time_fn(fn, steps, warmup)
+    kern = traced_kernel_ms(stg, fn, steps)
+    lib = lambda: torch.matmul(A.view(torch.bfloat16), B.view(torch.bfloat16), out=C)
+    lib_ms = time_fn(lib, steps, warmup)
+    flop = 2.0 * M * N * K
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"workload": "bounded GEMM bf16 A(8192,4096) B(4096,8192), aligned rows, fp32 accumulate, bf16 output",
+            "value": round(tf, 1), "unit": "TFLOP/s", "ms": round(ms, 4), "flop": flop,
+            "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4), "kernel_ms": kern,
+            "hipblaslt_same_call": {"value": round(flop / (lib_ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
+                                    "ms": round(lib_ms, 4), "note": "torch.matmul on the same operands, context only"}}
+
+
 def run_gemm_scaled(stg, inputs, steps, warmup):
     """Block-scaled GEMM, fp8 e4m3 and fp4 e2m1 operands with e8m0 scales per
     32 K values, fp32 output, on the bounded GEMM's odd M and N."""
@@ -853,6 +877,7 @@ def main():
         torch.cuda.empty_cache()
     if "gemm" in only:
         ops["gemm_bounded"] = run_gemm(stg, inputs, max(args.steps // 2, 1), args.warmup)
+        ops["gemm_bounded_aligned"] = run_gemm_aligned(stg, inputs, max(args.steps // 2, 1), args.warmup)
         print("[bench] gemm done", file=sys.stderr, flush=True)
     if "scaled" in only:
         ops.update(run_gemm_scaled(stg, inputs, max(args.steps // 2, 1), args.warmup))
