@@ -295,3 +295,21 @@ def test_gemm_aligned_rows_kernel_matches_odd_rows_kernel(stg, orc, shape):
                 r, c = _sample_coords(M, N)
                 got = to_host(Ca[torch.from_numpy(r).cuda(), torch.from_numpy(c).cuda()]).astype(np.float64)
                 check(got, orc.gemm_sample_f64(g["A"], g["B"], r, c), True)
+
+
+@pytest.mark.parametrize("lda_pad", [0, 1])
+def test_gemm_k_zero_whole_tiles_writes_zeros(stg, lda_pad):
+    """K = 0 over whole 256-column tiles, on the 4-wave kernel (aligned
+    strides) and on the 8-wave one (odd strides): both write zeros, the
+    padding of a padded output untouched."""
+    M, N = 300, 512 + 8 * lda_pad
+    ldb = N + 1 if lda_pad else N
+    Ad = torch.zeros((M, 8 + lda_pad), dtype=torch.bfloat16, device="cuda:0")[:, :0]
+    Bd = torch.zeros((1, ldb), dtype=torch.bfloat16, device="cuda:0")[:0, :N]
+    say("gemm K = 0 over whole tiles", "odd strides" if lda_pad else "aligned strides")
+    for dt in (torch.float32, torch.bfloat16):
+        store = torch.full((M, N + 5), 7.0, dtype=dt, device="cuda:0")
+        stg.gemm_bounded(Ad, Bd, out=store[:, :N])
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(store[:, :N]).item() == 0
+        assert torch.all(store[:, N:] == 7.0)
