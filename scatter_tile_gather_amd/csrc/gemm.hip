@@ -38,8 +38,11 @@
 //    are read before the barrier that ends step k, and each step waits only
 //    for stage k+2.  One barrier per 32 K values.
 //  * Grid: a main launch of 256 x 256 tiles over the columns that fill whole
-//    tiles; the remaining columns go to an edge launch of 64 x 32 tiles, or,
-//    when at most 8 remain (N = 8193 leaves one), to a skinny vector kernel.
+//    tiles -- the 4-wave kernel for 16-byte aligned rows, otherwise the
+//    8-wave kernel on 16 x 16 x 32 MFMAs (both below) --; the remaining
+//    columns go to an edge launch of 64 x 32 tiles (the template kernel
+//    here), or, when at most 8 remain (N = 8193 leaves one), to a skinny
+//    vector kernel.
 //    Tile ids are renumbered so that consecutive ids run on one XCD and walk
 //    4-row-panel groups, keeping A and B panels resident in that XCD's L2.
 #include <type_traits>
@@ -487,14 +490,15 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
 
 // Main kernel for 16-byte aligned operand rows: 4 waves, one per SIMD, each
 // owning a 128 x 128 block of the 256 x 256 tile (256 fp32 accumulators per
-// lane, held in the accumulation registers).  Against the 8-wave kernel's
-// 128 x 64 wave blocks it reads a third fewer operand bytes from LDS per
-// MFMA (measured at 8192 x 8192 x 4096: 1.31 against 1.19 PFLOP/s).  With
-// one wave per SIMD a DMA instruction that cannot issue holds back the MFMAs
-// behind it, so when the operand feed itself is the bound -- rows not 16-byte
-// aligned, where every 16-byte chunk straddles two -- the 8-wave kernel, whose
-// SIMD partner keeps issuing, is the faster one (odd strides: 1.04 against
-// 1.09), and the host picks this kernel only for aligned rows.
+// lane, held in the accumulation registers).  Against 8 waves of 128 x 64 it
+// reads a third fewer operand bytes from LDS per MFMA (measured at 8192 x 8192
+// x 4096: 1.31 PFLOP/s against 1.19 on 32 x 32 x 16 and 1.27-1.30 for the
+// 16 x 16 x 32 kernel below).  With one wave per SIMD a DMA instruction that
+// cannot issue holds back the MFMAs behind it, so when the operand feed itself
+// is the bound -- rows not 16-byte aligned, where every 16-byte chunk
+// straddles two -- 8 waves, whose SIMD partner keeps issuing, are faster
+// (odd strides: this kernel 1.04, 8 waves on 32 x 32 x 16 1.09, on 16 x 16 x
+// 32 1.10-1.15), and the host picks this kernel only for aligned rows.
 //  * Same stages, swizzles, zero-fill and ring as the 8-wave kernel (4 slots of
 //    32 K values; stage k+3 in flight during step k, spread 8 DMA instructions
 //    per wave among the step's 32 MFMAs); one descriptor per operand panel
@@ -713,7 +717,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
               acc[i][j][r];
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
       __builtin_amdgcn_wave_barrier();
-#pragma unroll 4
+      // two chunks per lane at a time: four left the epilogue short of registers
+      // beside the 256 accumulators (16 of them spilled to scratch)
+#pragma unroll 2
       for (int c = lane; c < 32 * 32; c += 64) {
         const int row = c >> 5, ch = c & 31;
         const int64_t grow = m0 + wm * 128 + i * 32 + row;
@@ -768,11 +774,280 @@ int launch(const char* name, GemmParams p, int64_t cols, hipStream_t s) {
   return check_launch(name);
 }
 
+// Main kernel for operand rows that are not 16-byte aligned: 8 waves, two per
+// SIMD, each owning a 128 x 64 block of the 256 x 256 tile as 8 x 4 blocks of
+// v_mfma_f32_16x16x32_bf16 (16 x 16 outputs, 32 K values per instruction).
+// At the power limit the 16 x 16 x 32 instruction costs less per flop than
+// the 32 x 32 x 16 one (alone, on random operands held in registers: 2.17
+// against 1.90 PFLOP/s), and at (8191, 8193, 4097) this kernel runs 7-9%
+// faster than the same kernel on 32 x 32 x 16 (1101-1153 against 1030-1060
+// TFLOP/s, with identical output bits in every case compared).
+//  * Stages, ring, swizzles, zero-fill and K-edge patch as the 4-wave kernel
+//    (descriptors rebased per stage, so any stride works); 4 DMA
+//    instructions per wave and stage, one after every 8 MFMAs.
+//  * Operands: a 32-K stage feeds each 16 x 16 x 32 MFMA whole, so the B
+//    blocks of the next stage are read into a second register set during the
+//    current one (8 transposed reads, one after every 4 MFMAs), and A blocks
+//    are read just in time, two 16-row blocks ahead through four rolling
+//    registers (the next stage's first two at the end of the current one):
+//    double-buffering A as well would need 96 operand registers, past what
+//    two waves per SIMD leave beside 128 accumulators.
+//  * The loop is unrolled over the ring's four slots (and the last steps over
+//    the two register sets), so every index into the register arrays is a
+//    constant: a run-time index would put them in scratch memory.
+typedef float f32x4a __attribute__((ext_vector_type(4)));
+template <int V>
+using Ix = std::integral_constant<int, V>;
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_w8_kernel(GemmParams p) {
+  using CF = Cfg<256, 256, 2, 4, 4>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / CF::WN, wn = wave % CF::WN;
+  int tm, tn;
+  tile_of(xcd_remap(blockIdx.x, gridDim.x), p.tiles_m, p.tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * CF::BM;
+  const int64_t n0 = p.n_base + (int64_t)tn * CF::BN;
+  const int nk = (int)((p.K + BK - 1) / BK);
+  const int nkf = (int)(p.K / BK);
+
+  auto a_chunk = [&](int q, int& r, int& c) __attribute__((always_inline)) {
+    const int pos = (wave * CF::A_DMA_W + q) * 64 + lane;
+    r = pos >> 2;
+    c = a_phys(r, pos & 3);
+  };
+  auto b_chunk = [&](int q, int& k, int& c) __attribute__((always_inline)) {
+    const int pos = (wave * CF::B_DMA_W + q) * 64 + lane;
+    k = pos / CF::B_CPR;
+    c = (pos % CF::B_CPR) ^ b_swz<CF::B_CPR>(k);
+  };
+  uint32_t a_off[CF::A_DMA_W], b_off[CF::B_DMA_W];
+  int a_kc[CF::A_DMA_W], b_k[CF::B_DMA_W];
+#pragma unroll
+  for (int q = 0; q < CF::A_DMA_W; ++q) {
+    int r, c;
+    a_chunk(q, r, c);
+    a_kc[q] = 8 * c;
+    a_off[q] = m0 + r < p.M ? (uint32_t)(r * p.lda * 2 + c * 16) : kOOB;
+  }
+#pragma unroll
+  for (int q = 0; q < CF::B_DMA_W; ++q) {
+    int k, c;
+    b_chunk(q, k, c);
+    b_k[q] = k;
+    b_off[q] = n0 + 8 * c + 8 <= p.N ? (uint32_t)(k * p.ldb * 2 + c * 16) : kOOB;
+  }
+  const uint32_t smem_lds =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem);
+  auto stage_rsrc = [&](int kt, u32x4_s& rsa, u32x4_s& rsb) __attribute__((always_inline)) {
+    const int64_t k0 = (int64_t)kt * BK;
+    rsa = rsrc_words(p.A + (m0 * p.lda + k0) * 2, ((p.M - 1 - m0) * p.lda + (p.K - k0)) * 2);
+    rsb = rsrc_words(p.B + (k0 * p.ldb + n0) * 2, ((p.K - 1 - k0) * p.ldb + (p.N - n0)) * 2);
+  };
+  auto dma_one = [&](int kt, int slot, int q, const u32x4_s& rsa, const u32x4_s& rsb) __attribute__((always_inline)) {
+    const uint32_t st = smem_lds + slot * CF::STAGE_B;
+    const int kleft = kt < nkf ? BK : (int)(p.K - (int64_t)kt * BK);
+    if (q < CF::A_DMA_W) {
+      dma16(rsa, a_kc[q] + 8 <= kleft ? a_off[q] : kOOB, st + (wave * CF::A_DMA_W + q) * 1024);
+    } else {
+      const int qb = q - CF::A_DMA_W;
+      dma16(rsb, b_k[qb] < kleft ? b_off[qb] : kOOB, st + CF::A_STAGE_B + (wave * CF::B_DMA_W + qb) * 1024);
+    }
+  };
+  auto fix_stage = [&](int kt) __attribute__((always_inline)) {
+    const int64_t k0 = (int64_t)kt * BK;
+    if (!(k0 + BK > p.K && (p.K & 7))) return;
+    char* st = smem + (kt % CF::NSTAGE) * CF::STAGE_B;
+#pragma unroll
+    for (int q = 0; q < CF::A_DMA_W; ++q) {
+      int r, c;
+      a_chunk(q, r, c);
+      const int64_t col = k0 + 8 * c, left = p.K - col;
+      if (m0 + r < p.M && left > 0 && left < 8) {
+        const uint16_t* src = (const uint16_t*)(p.A + ((m0 + r) * p.lda + col) * 2);
+        u32x4 v = {0, 0, 0, 0};
+        for (int e = 0; e < 8; ++e)
+          if (e < left) vec_set<2>(v, e, src[e]);
+        *(u32x4*)(st + (wave * CF::A_DMA_W + q) * 1024 + lane * 16) = v;
+      }
+    }
+  };
+
+  f32x4a acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
+  constexpr int ALOOK = 2, FAN = 4;  // A blocks read this many rows ahead; rolling registers
+  bf16x8 fa[FAN], fb[2][4];
+  // per-lane LDS offsets within a stage.  A block i: row ar + 16 i, chunk
+  // lane / 16 (rows 16 apart share the swizzle: i adds 1024).  B block j
+  // (transposed reads): lane t of 16-lane group g reads row 8 g + 4 h + t / 4
+  // at columns wn 64 + 16 j + 4 (t % 4) .. + 3 and receives column 16 j + t,
+  // K values 8 g + 4 h .. + 3 (h adds 2048).  The 16x16x32 operand layout:
+  // lane l holds row (column) l % 16, K values 8 (l / 16) .. + 7.
+  const int ar = wm * 128 + (lane & 15);
+  const uint32_t a_lds = ar * 64 + (a_phys(ar, lane >> 4) << 4);
+  uint32_t b_lds[4];
+  {
+    const int g = lane >> 4, t = lane & 15;
+    const int row = 8 * g + (t >> 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = wn * 64 + j * 16 + 4 * (t & 3);
+      b_lds[j] = CF::A_STAGE_B + row * 512 + ((col >> 3) ^ b_swz<32>(row)) * 16 + (col & 7) * 2;
+    }
+  }
+  auto rd_a = [&](const char* base, int i) __attribute__((always_inline)) {
+    fa[i % FAN] = *(const bf16x8*)(base + a_lds + i * 1024);
+  };
+  auto rd_b = [&](const char* base, int s, int e) __attribute__((always_inline)) {
+    const int j = e >> 1, h = e & 1;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + b_lds[j] + h * 2048));
+    s16x8 cur = __builtin_bit_cast(s16x8, fb[s][j]);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) cur[4 * h + x] = v[x];
+    fb[s][j] = __builtin_bit_cast(bf16x8, cur);
+  };
+  // the 32 MFMAs of stage kt (A rolling, B in set s), row by row: A block
+  // i + 2 read at the start of row i (the next stage's blocks 0, 1 at rows 6,
+  // 7); B read e of the next stage into the other set after MFMA 4 e + 1; DMA
+  // instruction d of stage dkt after MFMA 8 d + 7 (scheduling barriers pin
+  // the order: a wave issues in order, and a burst of DMA would hold back the
+  // MFMAs behind it)
+  auto phase = [&](int s, const char* cbase, bool nxt, const char* nbase, bool dmado, int dkt, int dslot,
+                   const u32x4_s& rsa, const u32x4_s& rsb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < 32; ++m) {
+      const int i = m >> 2, j = m & 3;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i % FAN], fb[s][j], acc[i][j], 0, 0, 0);
+      if (j == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + ALOOK < 8) rd_a(cbase, i + ALOOK);
+        else if (nxt) rd_a(nbase, i + ALOOK - 8);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (nxt && (m & 3) == 1) {
+        __builtin_amdgcn_sched_barrier(0);
+        rd_b(nbase, s ^ 1, m >> 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (dmado && (m & 7) == 7) {
+        __builtin_amdgcn_sched_barrier(0);
+        dma_one(dkt, dslot, m >> 3, rsa, rsb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  for (int s = 0; s < CF::NSTAGE - 1 && s < nk; ++s) {
+    u32x4_s rsa, rsb;
+    stage_rsrc(s, rsa, rsb);
+    for (int q = 0; q < CF::DMA_W; ++q) dma_one(s, s, q, rsa, rsb);
+  }
+  wait_vmcnt(max(0, min(nk, CF::NSTAGE - 1) - 2) * CF::DMA_W);
+  if (nk > 0) fix_stage(0);
+  if (nk > 1) fix_stage(1);
+  __syncthreads();
+  if (nk > 0) {
+#pragma unroll
+    for (int i = 0; i < ALOOK; ++i) rd_a(smem, i);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rd_b(smem, 0, e);
+  }
+  // step kt: stage kt + 1 (visible since the last barrier) is read, stage
+  // kt + 3 issued into the slot of stage kt - 1 (its last reads completed
+  // before step kt - 1's MFMAs used them); at the end stage kt + 2 must have
+  // landed.  Steady steps: every stage they issue is whole in K.
+  auto step_steady = [&](int kt, auto SLOT) __attribute__((always_inline)) {
+    constexpr int slot = decltype(SLOT)::value;
+    u32x4_s rsa, rsb;
+    stage_rsrc(kt + 3, rsa, rsb);
+    phase(slot & 1, smem + slot * CF::STAGE_B, true, smem + ((slot + 1) % 4) * CF::STAGE_B, true, kt + 3,
+          (slot + 3) % 4, rsa, rsb);
+    wait_vmcnt(CF::DMA_W);
+    __builtin_amdgcn_s_barrier();
+  };
+  // the last steps, register sets by compile-time parity (kt is even here)
+  auto step_tail = [&](int kt, auto PAR) __attribute__((always_inline)) {
+    constexpr int par = decltype(PAR)::value;
+    const bool dmado = kt + 3 < nk;
+    u32x4_s rsa, rsb;
+    stage_rsrc(kt + 3, rsa, rsb);
+    phase(par, smem + (kt % 4) * CF::STAGE_B, kt + 1 < nk, smem + ((kt + 1) % 4) * CF::STAGE_B, dmado, kt + 3,
+          (kt + 3) % 4, rsa, rsb);
+    if (kt + 2 < nk) {
+      wait_vmcnt(dmado ? CF::DMA_W : 0);
+      fix_stage(kt + 2);
+    }
+    __syncthreads();
+  };
+  int kt = 0;
+  for (; kt + 6 < nkf; kt += 4) {
+    step_steady(kt, Ix<0>());
+    step_steady(kt + 1, Ix<1>());
+    step_steady(kt + 2, Ix<2>());
+    step_steady(kt + 3, Ix<3>());
+  }
+  for (; kt < nk; kt += 2) {
+    step_tail(kt, Ix<0>());
+    if (kt + 1 < nk) step_tail(kt + 1, Ix<1>());
+  }
+
+  // clipped epilogue: lane l's accumulator r of 16x16 block (i, j) is row
+  // 4 (l / 16) + r, column l % 16 of that block
+  if (p.c_f32) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t col = n0 + wn * 64 + j * 16 + (lane & 15);
+        if (col >= p.N) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t row = m0 + wm * 128 + i * 16 + 4 * (lane >> 4) + r;
+          if (row < p.M)
+            *(float*)(p.C + (row * p.ldc + col) * 4) = p.acc ? acc[i][j][r] + p.acc[row * p.ldacc + col] : acc[i][j][r];
+        }
+      }
+    return;
+  }
+  char* ep = smem + wave * CF::EPI_WAVE_B;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *(__bf16*)(ep + (i * 16 + 4 * (lane >> 4) + r) * CF::EPI_PITCH_B + (j * 16 + (lane & 15)) * 2) =
+            (__bf16)acc[i][j][r];
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
+  constexpr int CPR = CF::WTN / 8;
+  for (int c = lane; c < CF::WTM * CPR; c += 64) {
+    const int row = c / CPR, ch = c % CPR;
+    const int64_t grow = m0 + wm * CF::WTM + row;
+    const int64_t gcol = n0 + wn * CF::WTN + ch * 8;
+    if (grow >= p.M || gcol >= p.N) continue;
+    const u32x4 v = *(const u32x4*)(ep + row * CF::EPI_PITCH_B + ch * 16);
+    char* dst = p.C + (grow * p.ldc + gcol) * 2;
+    if (gcol + 8 <= p.N) {
+      st16(dst, v);
+    } else {
+      for (int e = 0; e < 8; ++e)
+        if (gcol + e < p.N) store_elem<2>(dst + e * 2, vec_get<2>(v, e));
+    }
+  }
+}
+
 // Raises the kernels' dynamic LDS limit once on each device.
 bool lds_configured() {
   static OncePerDevice once;
   return once.run([] {
-    return hipFuncSetAttribute((const void*)gemm_kernel<MainCfg>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    return hipFuncSetAttribute((const void*)gemm_w8_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                MainCfg::LDS_B) == hipSuccess &&
            hipFuncSetAttribute((const void*)gemm_w4_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, W4_LDS) ==
                hipSuccess &&
@@ -826,8 +1101,12 @@ int gemm_bf16(const GemmNames& names, const void* A, int64_t lda, const void* B,
     launch_kernel(names.main, gemm_w4_kernel, dim3((unsigned)((int64_t)p.tiles_m * p.tiles_n)), dim3(256),
                   (uint32_t)W4_LDS, s, p);
     if ((rc = check_launch(names.main))) return rc;
-  } else if (n_main > 0 && (rc = launch<MainCfg>(names.main, p, n_main, s))) {
-    return rc;
+  } else if (n_main > 0) {
+    p.tiles_m = (int32_t)((M + MainCfg::BM - 1) / MainCfg::BM);
+    p.tiles_n = (int32_t)(n_main / MainCfg::BN);
+    launch_kernel(names.main, gemm_w8_kernel, dim3((unsigned)((int64_t)p.tiles_m * p.tiles_n)), dim3(MainCfg::NT),
+                  (uint32_t)MainCfg::LDS_B, s, p);
+    if ((rc = check_launch(names.main))) return rc;
   }
   p.n_base = n_main;
   const int64_t rem = N - n_main;
