@@ -54,6 +54,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4y __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -489,24 +490,37 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
 }
 
 // Main kernel for 16-byte aligned operand rows: 4 waves, one per SIMD, each
-// owning a 128 x 128 block of the 256 x 256 tile (256 fp32 accumulators per
-// lane, held in the accumulation registers).  Against 8 waves of 128 x 64 it
-// reads a third fewer operand bytes from LDS per MFMA (measured at 8192 x 8192
-// x 4096: 1.31 PFLOP/s against 1.19 on 32 x 32 x 16 and 1.27-1.30 for the
-// 16 x 16 x 32 kernel below).  With one wave per SIMD a DMA instruction that
-// cannot issue holds back the MFMAs behind it, so when the operand feed itself
-// is the bound -- rows not 16-byte aligned, where every 16-byte chunk
-// straddles two -- 8 waves, whose SIMD partner keeps issuing, are faster
-// (odd strides: this kernel 1.04, 8 waves on 32 x 32 x 16 1.09, on 16 x 16 x
-// 32 1.10-1.15), and the host picks this kernel only for aligned rows.
+// owning a 128 x 128 block of the 256 x 256 tile as 8 x 8 blocks of
+// v_mfma_f32_16x16x32_bf16 (256 fp32 accumulators per lane, held in the
+// accumulation registers).  Against 8 waves of 128 x 64 it reads a third
+// fewer operand bytes from LDS per MFMA, and the 16 x 16 x 32 instruction
+// costs less power per flop than 32 x 32 x 16 (alone on random register
+// operands: 2.17 against 1.90 PFLOP/s).  At 8192 x 8192 x 4096: 1.36-1.37
+// PFLOP/s, against 1.30-1.32 for the same kernel on 32 x 32 x 16, 1.27-1.30
+// for the 8-wave kernel below and 1.34 for hipBLASLt.  With one wave per SIMD
+// a DMA instruction that cannot issue holds back the MFMAs behind it, so when
+// the operand feed itself is the bound -- rows not 16-byte aligned, where
+// every 16-byte chunk straddles two -- 8 waves, whose SIMD partner keeps
+// issuing, are faster (odd strides: 1.03-1.04 here against 1.10-1.15), and
+// the host picks this kernel only for aligned rows.
 //  * Same stages, swizzles, zero-fill and ring as the 8-wave kernel (4 slots of
 //    32 K values; stage k+3 in flight during step k, spread 8 DMA instructions
-//    per wave among the step's 32 MFMAs); one descriptor per operand panel
+//    per wave among the step's 64 MFMAs); one descriptor per operand panel
 //    for the whole K loop, the stage selected by the instruction's scalar
 //    offset, so a DMA costs no vector arithmetic.
-//  * The loop is unrolled over the 4 ring slots so that every LDS address is a
-//    per-lane base plus an immediate; the operands of the next 16 K values are
-//    read into a second register set while the current ones feed the MFMAs.
+//  * Operands: the next stage's B blocks are read into a second register set
+//    during the current stage (16 transposed reads, one after every 4 MFMAs);
+//    A blocks just in time, two 16-row blocks ahead through four rolling
+//    registers.  The loop is unrolled over the 4 ring slots (and the last
+//    steps over the 2 register sets), so every LDS address is a per-lane
+//    base plus an immediate and every register-array index a constant.
+//  * The MFMAs are written out as inline assembly with the accumulator in
+//    accumulation registers: through the builtin, the compiler kept some of
+//    the 64 blocks in VGPRs and copied them after every MFMA behind a 6-cycle
+//    wait.  Nothing else reads an accumulator inside the loop, each block is
+//    rewritten only 64 MFMAs later, and the operand reads feeding an MFMA
+//    are awaited by the compiler (it sees the asm's inputs); after the loop
+//    an explicit wait covers the results' latency.
 //  * Epilogue through LDS in 32-row passes, also for fp32 output, so rows
 //    leave as 16-byte chunks.
 constexpr int W4_NS = 4;                           // ring stages
@@ -598,131 +612,150 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
   };
 
-  f32x16 acc[4][4];
+  f32x4y acc[8][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  bf16x8 fa[2][4], fb[2][4];
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
+  bf16x8 fa[4], fb[2][8];
 
-  // per-lane LDS offsets within a stage.  A: row ar + 32 i, chunk 2 ks + lane / 32
-  // (rows 32 apart share the swizzle, so i only adds 2048).  B (transposed reads):
-  // lane t of 16-lane group g reads row 16 ks + 8 (g / 2) + 4 h + t / 4 at columns
-  // wn 128 + 32 j + 16 (g % 2) + 4 (t % 4) .. + 3 (ks, h only add immediates)
-  const int ar = wm * 128 + (lane & 31);
-  const uint32_t a_lds0 = ar * 64 + (a_phys(ar, lane >> 5) << 4);
-  const uint32_t a_lds1 = ar * 64 + (a_phys(ar, 2 + (lane >> 5)) << 4);
-  uint32_t b_lds[4];
+  // per-lane LDS offsets within a stage.  A block i: row ar + 16 i, chunk
+  // lane / 16 (rows 16 apart share the swizzle: i adds 1024).  B block j
+  // (transposed reads): lane t of 16-lane group g reads row 8 g + 4 h + t / 4
+  // at columns wn 128 + 16 j + 4 (t % 4) .. + 3 and receives column 16 j + t,
+  // K values 8 g + 4 h .. + 3 (h adds 2048)
+  const int ar = wm * 128 + (lane & 15);
+  const uint32_t a_lds = ar * 64 + (a_phys(ar, lane >> 4) << 4);
+  uint32_t b_lds[8];
   {
     const int g = lane >> 4, t = lane & 15;
-    const int row = 8 * (g >> 1) + (t >> 2);
+    const int row = 8 * g + (t >> 2);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = wn * 128 + j * 32 + 16 * (g & 1) + 4 * (t & 3);
+    for (int j = 0; j < 8; ++j) {
+      const int col = wn * 128 + j * 16 + 4 * (t & 3);
       b_lds[j] = W4_ASTAGE + row * 512 + ((col >> 3) ^ b_swz<32>(row)) * 16 + (col & 7) * 2;
     }
   }
-  // LDS read e of sub-step ks from the stage at `base` into operand set s:
-  // e = 0..3 the A blocks, e = 4..11 the two halves of the B blocks
-  auto rd = [&](const char* base, int ks, int s, int e) {
-    if (e < 4) {
-      fa[s][e] = *(const bf16x8*)(base + (ks ? a_lds1 : a_lds0) + e * 2048);
-    } else {
-      const int j = (e - 4) >> 1, h = (e - 4) & 1;
-      const s16x4 v =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + b_lds[j] + ks * 8192 + h * 2048));
-      s16x8 cur = __builtin_bit_cast(s16x8, fb[s][j]);
-#pragma unroll
-      for (int x = 0; x < 4; ++x) cur[4 * h + x] = v[x];
-      fb[s][j] = __builtin_bit_cast(bf16x8, cur);
-    }
+  auto rd_a = [&](const char* base, int i) __attribute__((always_inline)) {
+    fa[i & 3] = *(const bf16x8*)(base + a_lds + i * 1024);
   };
-  // the 16 MFMAs of operand set s; read e of the other set after MFMA e (when
-  // rdo); DMA instruction q0 + d of stage dkt after MFMA 4 d + 3 (when dmado)
-  auto phase = [&](int s, bool rdo, const char* rbase, int rks, bool dmado, int dkt, int dslot, int q0, bool part) {
+  auto rd_b = [&](const char* base, int s, int e) __attribute__((always_inline)) {
+    const int j = e >> 1, h = e & 1;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + b_lds[j] + h * 2048));
+    s16x8 cur = __builtin_bit_cast(s16x8, fb[s][j]);
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      acc[m >> 2][m & 3] =
-          __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][m >> 2], fb[s][m & 3], acc[m >> 2][m & 3], 0, 0, 0);
-      if (rdo && m < 12) {
+    for (int x = 0; x < 4; ++x) cur[4 * h + x] = v[x];
+    fb[s][j] = __builtin_bit_cast(bf16x8, cur);
+  };
+  // the 64 MFMAs of stage kt (A rolling, B in set s), row by row: A block
+  // i + 2 read at the start of row i (the next stage's blocks 0, 1 at rows 6,
+  // 7); B read e of the next stage into the other set after MFMA 4 e + 2; DMA
+  // instruction d of stage dkt after MFMA 8 d + 7
+  auto phase = [&](int s, const char* cbase, bool nxt, const char* nbase, bool dmado, int dkt, int dslot, bool part)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < 64; ++m) {
+      const int i = m >> 3, j = m & 7;
+      // written out so the accumulator stays in its accumulation registers
+      // (through the builtin, the compiler routed some of the 64 blocks
+      // through VGPRs with a copy and a 6-cycle wait after each MFMA)
+      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(fa[i & 3]), "v"(fb[s][j]));
+      if (j == 0) {
         __builtin_amdgcn_sched_barrier(0);
-        rd(rbase, rks, s ^ 1, m);
+        if (i + 2 < 8) rd_a(cbase, i + 2);
+        else if (nxt) rd_a(nbase, i + 2 - 8);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (dmado && (m & 3) == 3) {
+      if (nxt && (m & 3) == 2) {
         __builtin_amdgcn_sched_barrier(0);
-        dma(dkt, dslot, q0 + (m >> 2), part);
+        rd_b(nbase, s ^ 1, m >> 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (dmado && (m & 7) == 7) {
+        __builtin_amdgcn_sched_barrier(0);
+        dma(dkt, dslot, m >> 3, part);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
 
-  // prologue: stages 0 .. 2 in flight, wait for 0 and 1
+  // prologue: stages 0 .. 2 in flight, wait for 0 and 1; stage 0's B blocks
+  // and its first two A blocks into registers
   for (int s = 0; s < W4_NS - 1 && s < nk; ++s)
     for (int q = 0; q < W4_DMA; ++q) dma(s, s, q, s >= nkf);
   wait_vmcnt(max(0, min(nk, W4_NS - 1) - 2) * W4_DMA);
   if (nk > 0) fix_stage(0);
   if (nk > 1) fix_stage(1);
   __syncthreads();
-  if (nk > 0)
+  if (nk > 0) {
+    rd_a(smem, 0);
+    rd_a(smem, 1);
 #pragma unroll
-    for (int e = 0; e < 12; ++e) rd(smem, 0, 0, e);
-
-  // step kt: sub-step 1 of stage kt and sub-step 0 of stage kt + 1 are read
-  // while the MFMAs of sub-steps 0 and 1 run; stage kt + 3 is issued.  Stage
-  // kt + 1 became visible at the previous barrier; this step waits for stage
-  // kt + 2.  A ring slot is refilled only after the barrier that follows its
-  // last reads, which have completed by then (their MFMAs have issued), so the
-  // steady steps use a bare s_barrier.
-  auto step_steady = [&](int kt, auto SLOT) {
+    for (int e = 0; e < 16; ++e) rd_b(smem, 0, e);
+  }
+  // step kt: stage kt + 1 (visible since the last barrier) is read, stage
+  // kt + 3 issued into the slot of stage kt - 1, whose last reads completed
+  // before step kt - 1's MFMAs used them (so a bare s_barrier suffices); at
+  // the end, stage kt + 2 must have landed.  Steady steps: every stage they
+  // issue is whole in K.
+  auto step_steady = [&](int kt, auto SLOT) __attribute__((always_inline)) {
     constexpr int slot = decltype(SLOT)::value;
-    phase(0, true, smem + slot * W4_STAGE, 1, true, kt + 3, (slot + 3) % W4_NS, 0, false);
-    phase(1, true, smem + ((slot + 1) % W4_NS) * W4_STAGE, 0, true, kt + 3, (slot + 3) % W4_NS, 4, false);
+    phase(slot & 1, smem + slot * W4_STAGE, true, smem + ((slot + 1) % W4_NS) * W4_STAGE, true, kt + 3,
+          (slot + 3) % W4_NS, false);
     wait_vmcnt(W4_DMA);
     __builtin_amdgcn_s_barrier();
   };
-  int kt = 0;
-  for (; kt + 6 < nkf; kt += 4) {  // every stage issued in these four steps is whole in K
-    step_steady(kt, Slot<0>());
-    step_steady(kt + 1, Slot<1>());
-    step_steady(kt + 2, Slot<2>());
-    step_steady(kt + 3, Slot<3>());
-  }
-  for (; kt < nk; ++kt) {
+  // the last steps, register sets by compile-time parity (kt is even here)
+  auto step_tail = [&](int kt, auto PAR) __attribute__((always_inline)) {
+    constexpr int par = decltype(PAR)::value;
     const bool dmado = kt + 3 < nk;
-    const int ds = (kt + 3) % W4_NS;
-    phase(0, true, smem + (kt % W4_NS) * W4_STAGE, 1, dmado, kt + 3, ds, 0, kt + 3 >= nkf);
-    phase(1, kt + 1 < nk, smem + ((kt + 1) % W4_NS) * W4_STAGE, 0, dmado, kt + 3, ds, 4, kt + 3 >= nkf);
+    phase(par, smem + (kt % W4_NS) * W4_STAGE, kt + 1 < nk, smem + ((kt + 1) % W4_NS) * W4_STAGE, dmado, kt + 3,
+          (kt + 3) % W4_NS, kt + 3 >= nkf);
     if (kt + 2 < nk) {
       wait_vmcnt(dmado ? W4_DMA : 0);
       fix_stage(kt + 2);
     }
     __syncthreads();
+  };
+  int kt = 0;
+  for (; kt + 6 < nkf; kt += 4) {
+    step_steady(kt, Slot<0>());
+    step_steady(kt + 1, Slot<1>());
+    step_steady(kt + 2, Slot<2>());
+    step_steady(kt + 3, Slot<3>());
   }
+  for (; kt < nk; kt += 2) {
+    step_tail(kt, Slot<0>());
+    if (kt + 1 < nk) step_tail(kt + 1, Slot<1>());
+  }
+  // the MFMAs were written out, so the compiler does not know that the
+  // accumulators are MFMA results: wait out their latency (24 wait states,
+  // above what a 16x16x32 result needs) before the epilogue reads them
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
-  // clipped epilogue, 32 rows of the wave's block per pass: lane l's
-  // accumulator r of block (i, j) is row 8 (r / 4) + 4 (l / 32) + r % 4,
-  // column l % 32 of that 32 x 32 block
+  // clipped epilogue, 32 rows (two block rows) of the wave's block per pass:
+  // lane l's accumulator r of 16x16 block (i, j) is row 4 (l / 16) + r,
+  // column l % 16 of that block
   if (p.c_f32) {
     char* ep = smem + wave * W4_F32_WAVE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int pss = 0; pss < 4; ++pss) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          *(float*)(ep + (8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * W4_F32_PITCH + (j * 32 + (lane & 31)) * 4) =
-              acc[i][j][r];
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            *(float*)(ep + (ii * 16 + 4 * (lane >> 4) + r) * W4_F32_PITCH + (j * 16 + (lane & 15)) * 4) =
+                acc[2 * pss + ii][j][r];
+      __builtin_amdgcn_s_waitcnt(0xc07f);
       __builtin_amdgcn_wave_barrier();
-      // two chunks per lane at a time: four left the epilogue short of registers
-      // beside the 256 accumulators (16 of them spilled to scratch)
 #pragma unroll 2
       for (int c = lane; c < 32 * 32; c += 64) {
         const int row = c >> 5, ch = c & 31;
-        const int64_t grow = m0 + wm * 128 + i * 32 + row;
+        const int64_t grow = m0 + wm * 128 + pss * 32 + row;
         const int64_t gcol = n0 + wn * 128 + ch * 4;
         if (grow >= p.M) continue;
         u32x4 v = *(const u32x4*)(ep + row * W4_F32_PITCH + ch * 16);
@@ -740,14 +773,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   char* ep = smem + wave * W4_EPI_WAVE;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        *(__bf16*)(ep + row * W4_EPI_PITCH + (j * 32 + (lane & 31)) * 2) = (__bf16)acc[i][j][r];
-      }
+      for (int r = 0; r < 4; ++r)
+        *(__bf16*)(ep + (i * 16 + 4 * (lane >> 4) + r) * W4_EPI_PITCH + (j * 16 + (lane & 15)) * 2) =
+            (__bf16)acc[i][j][r];
   __builtin_amdgcn_s_waitcnt(0xc07f);
   __builtin_amdgcn_wave_barrier();
   for (int c = lane; c < 128 * 16; c += 64) {
