@@ -6,7 +6,8 @@
 // converts the f32 accumulator to the destination type and suppresses invalid
 // coordinates, leaving padding untouched).
 //
-// gfx950 design:
+// gfx950 design (the template kernel below; the two main kernels further down
+// keep its staging and differ in waves and MFMA shape):
 //  * Workgroup tile BM x BN x 32, waves WM x WN, each wave owning a
 //    (BM/WM) x (BN/WN) block of v_mfma_f32_32x32x16_bf16 accumulators.  Every
 //    lane issues every MFMA; bounds only select the data that was staged.
@@ -790,9 +791,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
-// main: 8 waves of 128 x 64 accumulators (two waves per SIMD), 4-stage ring;
-// edge strip: small stages, so a deep ring hides the load latency of its
-// long K loop
+// main tile shape (the 8-wave kernel's: 128 x 64 accumulators per wave, two
+// waves per SIMD, 4-stage ring; its stage sizes and LDS footprint come from
+// here); edge strip: the template kernel on small stages, so a deep ring
+// hides the load latency of its long K loop
 using MainCfg = Cfg<256, 256, 2, 4, 4>;
 using EdgeCfg = Cfg<64, 32, 2, 1, 16>;
 
