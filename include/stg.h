@@ -386,7 +386,9 @@ int64_t gemm_scaled_workspace(int32_t a_fmt, int32_t b_fmt, int32_t scale_fmt, i
  *   C  (M, N) row-major, row stride ldc >= N, c_dtype STG_BF16 (f32 rounded to
  *      nearest even) or STG_F32.  Only C[r][c] with r < M, c < N is written.
  * M, N, K >= 0; K == 0 writes zeros.  Summation order is unspecified (results
- * match an exact reference to accumulation rounding). */
+ * match an exact reference to accumulation rounding); it does not depend on
+ * the strides: rows that start 16-byte aligned (lda, ldb multiples of 8, A
+ * and B 16-byte aligned) take a faster kernel that gives the same bits. */
 int gemm_bounded(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
                  int64_t M, int64_t N, int64_t K, int32_t c_dtype, void* stream);
 
