@@ -536,14 +536,6 @@ constexpr int W4_F32_WAVE = 32 * W4_F32_PITCH;
 constexpr int W4_LDS = W4_NS * W4_STAGE > 4 * W4_EPI_WAVE ? W4_NS * W4_STAGE : 4 * W4_EPI_WAVE;
 static_assert(4 * W4_F32_WAVE <= W4_LDS, "fp32 staging fits");
 
-// LDS DMA of 16 bytes per lane at buffer offset off + soff (soff: scalar)
-__device__ __forceinline__ void dma16s(const u32x4_s& rs, uint32_t off, uint32_t soff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(lds_addr), "v"(off), "s"(rs), "s"(soff)
-               : "memory", "m0");
-}
-
 template <int V>
 using Slot = std::integral_constant<int, V>;
 

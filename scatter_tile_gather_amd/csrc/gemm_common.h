@@ -78,5 +78,24 @@ __device__ __forceinline__ void dma16(const u32x4_s& rs, uint32_t off, uint32_t 
                : "memory", "m0");
 }
 
+// The same at buffer offset off + soff, soff and lds_addr wave-uniform: soff
+// is the instruction's scalar offset, so a descriptor can stay fixed while
+// soff walks along K.  The operand takes an SGPR only, never a literal: a
+// caller whose soff may fold to a constant passes it through
+// uniform_sgpr() first.
+__device__ __forceinline__ void dma16s(const u32x4_s& rs, uint32_t off, uint32_t soff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(off), "s"(rs), "s"(soff)
+               : "memory", "m0");
+}
+
+// v made wave-uniform and held in an SGPR as far as the compiler knows
+__device__ __forceinline__ uint32_t uniform_sgpr(uint32_t v) {
+  v = __builtin_amdgcn_readfirstlane(v);
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
 }  // namespace
 }  // namespace stg

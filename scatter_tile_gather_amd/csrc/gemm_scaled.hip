@@ -183,20 +183,38 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
     const int64_t kl = p.K - (int64_t)kt * KS;
     return (int)(kl < 0 ? 0 : kl > INT32_MAX ? INT32_MAX : kl);
   };
+  // Descriptors of stage kt's operand bytes.  fp8: one descriptor per
+  // operand panel for the whole K loop, the stage chosen by the DMA
+  // instruction's scalar offset kt * kRowB (rows past M or N still start
+  // past num_records, since a row stride is at least a row); fp4: one
+  // descriptor per stage starting at the stage's bytes.  The same bytes land
+  // either way; each is the faster one for its width (measured at 8191 x
+  // 8193 x 4096: fp8 2% faster on panels, fp4 3% slower).
+  constexpr bool kPanel = BITS == 8;
   auto stage_rsrc = [&](int kt, u32x4_s& rsa, u32x4_s& rsb) {
-    const int64_t kb = (int64_t)kt * kRowB;  // byte offset of the stage in a row
+    const int64_t kb = kPanel ? 0 : (int64_t)kt * kRowB;  // byte offset of the descriptor in a row
     rsa = rsrc_words(p.A + m0 * p.lda + kb, (p.M - 1 - m0) * p.lda + (row_bytes - kb));
     rsb = rsrc_words(p.B + n0 * p.ldb + kb, (p.N - 1 - n0) * p.ldb + (row_bytes - kb));
   };
   // DMA instruction q of stage kt into its ring slot (A chunks, then B);
   // chunks at or past K land as zeros
-  auto dma_one = [&](int slot, int kleft, int q, const u32x4_s& rsa, const u32x4_s& rsb) {
+  auto dma_one = [&](int slot, int kt, int kleft, int q, const u32x4_s& rsa, const u32x4_s& rsb) {
     const uint32_t st = smem_lds + slot * kSlot;
     if (q < kADma) {
-      dma16(rsa, a_kc[q] < kleft ? a_off[q] : kOOB, st + (wave * kADma + q) * 1024);
+      const uint32_t off = a_kc[q] < kleft ? a_off[q] : kOOB;
+      const uint32_t dst = st + (wave * kADma + q) * 1024;
+      if constexpr (kPanel)
+        dma16s(rsa, off, uniform_sgpr((uint32_t)kt * kRowB), uniform_sgpr(dst));
+      else
+        dma16(rsa, off, dst);
     } else {
       const int qb = q - kADma;
-      dma16(rsb, b_kc[qb] < kleft ? b_off[qb] : kOOB, st + kAStage + (wave * kBDma + qb) * 1024);
+      const uint32_t off = b_kc[qb] < kleft ? b_off[qb] : kOOB;
+      const uint32_t dst = st + kAStage + (wave * kBDma + qb) * 1024;
+      if constexpr (kPanel)
+        dma16s(rsb, off, uniform_sgpr((uint32_t)kt * kRowB), uniform_sgpr(dst));
+      else
+        dma16(rsb, off, dst);
     }
   };
   // window DMA instruction q (A, then B) of group g into buffer g % 2; kb0:
@@ -412,7 +430,7 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
               if (d < NW)
                 wdma_one(g, kbw, d);
               else
-                dma_one(PH, kl_d, d - NW, rsa, rsb);
+                dma_one(PH, kt + kSNS, kl_d, d - NW, rsa, rsb);
               __builtin_amdgcn_sched_barrier(0);
             }
           }
@@ -437,7 +455,7 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
       u32x4_s rsa, rsb;
       stage_rsrc(s, rsa, rsb);
 #pragma unroll
-      for (int q = 0; q < kDma; ++q) dma_one(s, k_left(s), q, rsa, rsb);
+      for (int q = 0; q < kDma; ++q) dma_one(s, s, k_left(s), q, rsa, rsb);
     }
     wait_vmcnt(2 * kDma + kWDma);
     __syncthreads();
