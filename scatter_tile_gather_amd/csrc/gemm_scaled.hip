@@ -186,7 +186,10 @@ __global__ __launch_bounds__(kSNT) __attribute__((amdgpu_waves_per_eu(1, 1))) vo
   // Descriptors of stage kt's operand bytes.  fp8: one descriptor per
   // operand panel for the whole K loop, the stage chosen by the DMA
   // instruction's scalar offset kt * kRowB (rows past M or N still start
-  // past num_records, since a row stride is at least a row); fp4: one
+  // past num_records, since a row stride is at least a row; with the host's
+  // 2^31 bound on 256 row strides, vector plus scalar offset of every chunk
+  // inside the matrix stays below num_records, whether or not the range
+  // check counts the scalar offset); fp4: one
   // descriptor per stage starting at the stage's bytes.  The same bytes land
   // either way; each is the faster one for its width (measured at 8191 x
   // 8193 x 4096: fp8 2% faster on panels, fp4 3% slower).
