@@ -158,6 +158,37 @@ def test_scaled_exact(stg, orc, fa, fb, shape, block):
                                   orc.gemm_scaled_f64(pack(ca, fa), fa, sa, pack(cb, fb), fb, sb, K, block))
 
 
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e5m2"), ("e2m1", "e2m1")])
+@pytest.mark.parametrize("shape", [(9, 259, 65632), (257, 300, 16416)])
+def test_scaled_exact_long_k(stg, orc, fa, fb, shape):
+    """Long K (fp8 rows of 64 KiB: stage offsets far past a descriptor's
+    first bytes; K a multiple of 32 but not of the 64-value stage), bit for
+    bit.  Values +-1, +-2 and scales 2^-1 .. 2^2 make every product a
+    multiple of 2^-2 below 2^6 and every partial sum exact in fp32 (at most
+    2^22 in magnitude), on both the MFMA's grouped sums and the fp32 chain.
+    The expected result is the exact fp64 product of the oracle's decoded
+    values (integers times powers of two: no rounding at these sizes), which
+    the first check holds equal to the oracle's own GEMM on a slice."""
+    M, N, K = shape
+    block = 32
+    rng = np.random.default_rng(M + N + K)
+    ca = np.array(EXACT_CODES[fa], np.uint8)[rng.integers(0, 4, (M, K))]
+    cb = np.array(EXACT_CODES[fb], np.uint8)[rng.integers(0, 4, (N, K))]
+    sa = rng.integers(126, 130, (M, K // block)).astype(np.uint8)
+    sb = rng.integers(126, 130, (N, K // block)).astype(np.uint8)
+    va = values(orc, ca, fa) * np.repeat(values(orc, sa, "e8m0", True), block, axis=1)
+    vb = values(orc, cb, fb) * np.repeat(values(orc, sb, "e8m0", True), block, axis=1)
+    want = va @ vb.T
+    ks = 256  # the decoded product against the oracle's GEMM on the first 256 K values
+    np.testing.assert_array_equal(
+        va[:4, :ks] @ vb[:6, :ks].T,
+        orc.gemm_scaled_f64(pack(ca[:4, :ks], fa), fa, sa[:4, :ks // block], pack(cb[:6, :ks], fb), fb,
+                            sb[:6, :ks // block], ks, block))
+    say("gemm_scaled exact long K", fa, fb, shape)
+    C = to_host(stg.gemm_scaled(to_dev(pack(ca, fa)), fa, to_dev(sa), to_dev(pack(cb, fb)), fb, to_dev(sb), K, block))
+    np.testing.assert_array_equal(C.astype(np.float64), want)
+
+
 @pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e4m3"), ("e5m2", "e5m2"),
                                    ("e2m1", "e2m1")])
 def test_scaled_formats_small(stg, orc, fa, fb):
