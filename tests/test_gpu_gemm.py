@@ -266,15 +266,17 @@ def _strided(X, ld, fill=0x7FA5):
 
 
 @pytest.mark.parametrize("shape", [(8192, 8192, 4096), (1000, 1280, 4097), (257, 512, 33), (513, 256, 7),
-                                   (256, 768, 1), (700, 1536, 2000)])
+                                   (256, 768, 1), (700, 1536, 2000), (300, 1000, 520), (513, 776, 64)])
 def test_gemm_aligned_rows_kernel_matches_odd_rows_kernel(stg, orc, shape):
-    """Operand rows that start 16-byte aligned take the 4-wave main kernel
-    (32x32x16 MFMAs), others the 8-wave one (16x16x32 MFMAs).  Both add the
-    stages into each output in K order, and the two instructions were
-    measured to round their 32 K values of a stage into the accumulator alike,
-    so the same operands stored with aligned and with odd row strides must
-    give identical bits, fp32 and bf16 output alike; the aligned result is
-    also held to the oracle (in full, or sampled at 8192 x 8192 x 4096)."""
+    """Operand rows that start 16-byte aligned take the 4-wave main kernel,
+    others the 8-wave one, both on 16x16x32 MFMAs; columns past the last whole
+    256-column tile go to the same remainder kernels either way (N = 1000
+    leaves 232 for the 64 x 32 edge kernel, N = 776 leaves 8 for the skinny
+    one).  Both main kernels add the stages into each output in K order with
+    the same instruction, so the same operands stored with aligned and with
+    odd row strides must give identical bits, fp32 and bf16 output alike; the
+    aligned result is also held to the oracle (in full, or sampled at
+    8192 x 8192 x 4096)."""
     M, N, K = shape
     g = inputs.gemm(M, N, K, seed=M + 3 * N + K)
     lda = (K + 7) // 8 * 8
